@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs for the DashAttention forward pass.
+
+This module only draws numbers: it holds none of the method's arithmetic and is shared, unchanged,
+by the GPU library's tests and benchmark and by the CPU oracle's tests. Every tensor comes from
+its own seeded stream, so a run is reproducible on a given device.
+
+Recipe (the pages run their efficiency benchmark on synthetic inputs, with no dataset; these
+shapes follow their long-context settings: 32 query heads, 8 KV heads, head dim 128, chunk 64):
+  * values are drawn in float32 and rounded to the working dtype (bf16 round-to-nearest-even);
+  * "plain" workloads: Q, K, V ~ N(0, 1);
+  * "planted" workloads: for every (sequence b, KV head r) a unit direction u[b, r] is drawn;
+    every query of the heads in group r is sqrt(D) * u + N(0, I); keys inside planted chunks are
+    3 * u + N(0, I); every other key and every value is N(0, 1). Planted chunks are chosen
+      - "span":   `per_span` chunks drawn without replacement inside every run of `span` chunks,
+      - "global": `count` chunks drawn without replacement over all complete chunks,
+      - "decode": a count m ~ U{lo..hi} per (b, r), positions uniform over the complete chunks
+                  before the newest token's chunk.
+Bulk N(0, 1) noise is drawn by torch on the target device (Philox on a GPU, so that multi-GiB
+caches are cheap to make); the small planted structure is drawn by numpy's PCG64 on the host.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    n_kv: int              # keys per sequence (prefill: also the number of queries)
+    h_q: int
+    h_kv: int
+    head_dim: int
+    block: int
+    alpha: float
+    gamma: float
+    sigma: float
+    dtype: str = "bf16"    # "bf16" or "f32"
+    decode: bool = False   # one new query per sequence at position n_kv - 1
+    plant: str = "none"    # "none" | "span" | "global" | "decode"
+    plant_args: dict = field(default_factory=dict)
+    seed: int = 0
+
+    @property
+    def n_q(self) -> int:
+        return 1 if self.decode else self.n_kv
+
+    @property
+    def q_pos0(self) -> int:
+        return self.n_kv - 1 if self.decode else 0
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads: tiny fp32, 32K prefill, 16 x 128K decode, the alpha / block sweep at 16K,
+# and the 256K prefill.
+TINY = Workload("tiny fp32 causal, 2q/1kv heads, seq 1024, D 64, block 64", 1, 1024, 2, 1, 64, 64,
+                1.5, 8.0, 10.0, dtype="f32", seed=1)
+PREFILL_32K = Workload("prefill 32K, 32q/8kv heads, D 128, block 64, 4 planted of every 16 chunks",
+                       1, 32768, 32, 8, 128, 64, 1.5, 0.5, 1e8, plant="span",
+                       plant_args=dict(span=16, per_span=4), seed=2)
+DECODE_128K = Workload("decode 16 x 128K context, 32q/8kv heads, D 128, block 64, 1-16 planted chunks",
+                       16, 131072, 32, 8, 128, 64, 1.5, 1.5, 1e8, decode=True, plant="decode",
+                       plant_args=dict(lo=1, hi=16), seed=3)
+SWEEP_16K = Workload("alpha/block sweep at 16K, 32q/8kv heads, D 128", 1, 16384, 32, 8, 128, 64,
+                     1.5, 0.5, 1e8, plant="span", plant_args=dict(span=16, per_span=4), seed=4)
+PREFILL_256K = Workload("prefill 256K, 32q/8kv heads, D 128, block 128, 128 planted of 2048 chunks",
+                        1, 262144, 32, 8, 128, 128, 1.5, 0.5, 1e8, plant="global",
+                        plant_args=dict(count=128), seed=5)
+
+# alpha / block points of the sweep, each with the routing scale gamma used for it
+SWEEP_POINTS = [(a, b) for a in (1.25, 1.5, 2.0) for b in (32, 64, 128)]
+
+
+def sweep_workload(alpha: float, block: int, gamma: float) -> Workload:
+    return SWEEP_16K.with_(alpha=alpha, block=block, gamma=gamma,
+                           name=f"sweep 16K alpha {alpha} block {block} gamma {gamma}")
+
+
+def _streams(seed: int, n: int):
+    return np.random.SeedSequence(seed).spawn(n)
+
+
+def _torch_seed(ss: np.random.SeedSequence) -> int:
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def _randn(shape, ss, device) -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(ss))
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+
+def planted_chunks(w: Workload) -> list[list[np.ndarray]]:
+    """Planted chunk indices per (b, r); empty lists for unplanted workloads."""
+    tc = w.n_kv // w.block
+    ss = _streams(w.seed, 6)[3]
+    rng = np.random.Generator(np.random.PCG64(ss))
+    out = []
+    for _b in range(w.batch):
+        row = []
+        for _r in range(w.h_kv):
+            if w.plant == "span":
+                span, per = w.plant_args["span"], w.plant_args["per_span"]
+                sel = [s + rng.choice(min(span, tc - s), size=min(per, tc - s), replace=False)
+                       for s in range(0, tc, span)]
+                row.append(np.sort(np.concatenate(sel)) if sel else np.zeros(0, np.int64))
+            elif w.plant == "global":
+                row.append(np.sort(rng.choice(tc, size=min(w.plant_args["count"], tc),
+                                              replace=False)))
+            elif w.plant == "decode":
+                visible = (w.n_kv - 1) // w.block  # complete chunks before the newest token's
+                m = int(rng.integers(w.plant_args["lo"], w.plant_args["hi"] + 1))
+                row.append(np.sort(rng.choice(visible, size=min(m, visible), replace=False)))
+            else:
+                row.append(np.zeros(0, np.int64))
+        out.append(row)
+    return out
+
+
+def directions(w: Workload) -> np.ndarray:
+    """Unit directions u[b, r] (float32) of the planted workloads."""
+    ss = _streams(w.seed, 6)[4]
+    rng = np.random.Generator(np.random.PCG64(ss))
+    u = rng.standard_normal((w.batch, w.h_kv, w.head_dim))
+    return (u / np.linalg.norm(u, axis=-1, keepdims=True)).astype(np.float32)
+
+
+def make_inputs(w: Workload, device="cpu") -> dict:
+    """q [B, n_q, Hq, D], k, v [B, n_kv, Hkv, D] in the workload's dtype on `device`."""
+    s_q, s_k, s_v, _, _, _ = _streams(w.seed, 6)
+    dt = w.torch_dtype
+    B, n, nq, hq, hkv, d = w.batch, w.n_kv, w.n_q, w.h_q, w.h_kv, w.head_dim
+    gq = hq // hkv
+    planted = planted_chunks(w)
+    u = torch.from_numpy(directions(w)).to(device) if w.plant != "none" else None
+
+    q = _randn((B, nq, hq, d), s_q, device)
+    if u is not None:
+        # every head of group r gets sqrt(D) * u[b, r]
+        q += math.sqrt(d) * u.repeat_interleave(gq, dim=1)[:, None, :, :]
+    q = q.to(dt)
+
+    # keys and values are drawn one sequence at a time to bound temporary memory
+    k = torch.empty((B, n, hkv, d), dtype=dt, device=device)
+    v = torch.empty((B, n, hkv, d), dtype=dt, device=device)
+    ks, vs = s_k.spawn(B), s_v.spawn(B)
+    for b in range(B):
+        kb = _randn((n, hkv, d), ks[b], device)
+        if u is not None:
+            for r in range(hkv):
+                for c in planted[b][r]:
+                    kb[c * w.block:(c + 1) * w.block, r, :] += 3.0 * u[b, r]
+        k[b] = kb.to(dt)
+        del kb
+        v[b] = _randn((n, hkv, d), vs[b], device).to(dt)
+    return dict(q=q, k=k, v=v, planted=planted)
