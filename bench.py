@@ -1,0 +1,306 @@
+"""Benchmark of the DashAttention forward pass (libdash) on one MI355X.
+
+One step = the whole hot path once: the 32K prefill forward (pool keys, route with alpha-entmax,
+sparse attention) on the 32K workload, plus one decode step (route against the cached chunk
+summaries, split sparse attention) on the 16 x 128K workload. Inputs are seeded synthetic
+tensors already resident in HBM; the decode cache's summaries are pooled once before timing, as a
+decode loop would keep them.
+
+Prints one JSON line. `value` is the prefill's effective TFLOP/s: the FLOPs the method must do on
+the selected (query head, key) pairs, 4 * D per pair, over the time of its three stages. The
+decode rate and the per-kernel rooflines are reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "prefill eff. TFLOP/s @32K + decode tok/s @128K; % of MFMA / HBM roofline"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def popcount32(a: np.ndarray) -> np.ndarray:
+    a = a.astype(np.uint32)
+    a = a - ((a >> 1) & 0x55555555)
+    a = (a & 0x33333333) + ((a >> 2) & 0x33333333)
+    a = (a + (a >> 4)) & 0x0F0F0F0F
+    return ((a * 0x01010101) & 0xFFFFFFFF) >> 24
+
+
+def selected_pairs_prefill(mask: torch.Tensor, w: wl.Workload) -> tuple[int, float]:
+    """Number of selected (query head, key) pairs of a prefill and the routed fraction of the
+    candidate chunks. Routed chunks hold `block` keys each; the query's own chunk contributes its
+    causal prefix. Every head of a group shares the group's selection."""
+    m = mask.cpu().numpy().view(np.uint32)                  # [B, n, Hkv, W]
+    g = w.h_q // w.h_kv
+    pos = np.arange(w.n_q)
+    cp = pos // w.block
+    bits = popcount32(m).sum(axis=-1).astype(np.int64)      # routed + diagonal, per (b, t, r)
+    routed = bits - 1
+    pairs = (routed * w.block).sum() * g + w.batch * w.h_q * (pos - cp * w.block + 1).sum()
+    cand = w.batch * w.h_kv * np.minimum(cp, w.n_kv // w.block).sum()
+    return int(pairs), float(routed.sum() / max(1, cand))
+
+
+def decode_bytes(mask: torch.Tensor, w: wl.Workload) -> tuple[int, float]:
+    """Algorithmic HBM bytes of one decode step: the cached summaries of the complete chunks
+    before the new token's chunk (fp32), the selected K and V chunks including the new token's
+    own chunk, and q / o. Also the mean number of routed chunks per (sequence, group)."""
+    m = mask.cpu().numpy().view(np.uint32)                  # [B, 1, Hkv, W]
+    bits = popcount32(m).sum(axis=-1).astype(np.int64)
+    pos = w.n_kv - 1
+    cp = pos // w.block
+    kbar_bytes = w.batch * min(cp, w.n_kv // w.block) * w.h_kv * w.head_dim * 4
+    routed = (bits - 1).sum()
+    diag_tokens = pos - cp * w.block + 1
+    kv_bytes = (routed * w.block + w.batch * w.h_kv * diag_tokens) * w.head_dim * 2 * 2
+    qo_bytes = 2 * w.batch * w.h_q * w.head_dim * 2
+    return int(kbar_bytes + kv_bytes + qo_bytes), float(routed / (w.batch * w.h_kv))
+
+
+def source_hash() -> str:
+    csrc = os.path.join(ROOT, "sparse_hierarchical_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel)
+    if not ent or ent.get("source_sha") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self):
+        self.spans = {}
+
+    def span(self, name):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        self.spans.setdefault(name, []).append((s, e))
+        return s, e
+
+    def mean_ms(self, name):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.spans[name]]))
+
+
+def cpu_baseline(pre_inp, dec_inp, wp: wl.Workload, wd: wl.Workload, pre_pairs_per_row: float):
+    """The oracle, as it stands, on a bounded sample of the same workloads, on this host."""
+    import oracle
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(np.arange(wp.n_q // 2, wp.n_q), size=384, replace=False))
+    qh, kh, vh = pre_inp["q"].cpu(), pre_inp["k"].cpu(), pre_inp["v"].cpu()
+    t0 = time.perf_counter()
+    ref = oracle.forward(qh, kh, vh, block=wp.block, alpha=wp.alpha, gamma=wp.gamma,
+                         sigma=wp.sigma, rows=rows)
+    t_pre = time.perf_counter() - t0
+    nc = -(-wp.n_kv // wp.block)
+    m = ref["mask"]
+    pos = rows % wp.n_q
+    cp = pos // wp.block
+    routed = popcount32(m).sum(axis=-1).astype(np.int64) - 1
+    pairs = (routed * wp.block).sum() * (wp.h_q // wp.h_kv) + wp.h_q * (pos - cp * wp.block + 1).sum()
+    tflops = 4.0 * wp.head_dim * pairs / t_pre / 1e12
+    # decode: two sequences, summaries pooled by the oracle beforehand (a decode loop's cache)
+    seqs = [0, 1]
+    tok_s = []
+    for b in seqs:
+        qb, kb_, vb = dec_inp["q"][b:b + 1].cpu(), dec_inp["k"][b:b + 1].cpu(), dec_inp["v"][b:b + 1].cpu()
+        kbar = oracle.pool_keys(kb_, wd.block)
+        t0 = time.perf_counter()
+        st = oracle.block_entmax(qb, kbar, n_kv=wd.n_kv, block=wd.block, alpha=wd.alpha,
+                                 gamma=wd.gamma, sigma=wd.sigma, q_pos0=wd.n_kv - 1, h_kv=wd.h_kv)
+        oracle.sparse_attn(qb, kb_, vb, st["mask"], st["bias"], block=wd.block, q_pos0=wd.n_kv - 1)
+        tok_s.append(1.0 / (time.perf_counter() - t0))
+    del nc, ref
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"prefill: {len(rows)} query rows of the 32K workload (Stage 0 in full, "
+                      f"all heads), {t_pre:.1f} s; decode: sequences {seqs} of the 16 x 128K "
+                      f"workload with summaries pooled beforehand",
+            "decode_tok_per_s": round(float(np.mean(tok_s)), 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the path runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import sparse_hierarchical_attention_amd as dash
+    dash.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp, wd = wl.PREFILL_32K, wl.DECODE_128K
+    print(f"[bench] generating inputs", file=sys.stderr, flush=True)
+    pre = wl.make_inputs(wp, dev)
+    dec = wl.make_inputs(wd, dev)
+    q, k, v = pre["q"], pre["k"], pre["v"]
+    qd, kd, vd = dec["q"], dec["k"], dec["v"]
+
+    # outputs and workspaces, allocated once
+    nc = -(-wp.n_kv // wp.block)
+    kbar = torch.empty((1, wp.n_kv // wp.block, wp.h_kv, wp.head_dim), dtype=torch.float32, device=dev)
+    mask = torch.empty((1, wp.n_q, wp.h_kv, -(-nc // 32)), dtype=torch.int32, device=dev)
+    bias = torch.empty((1, wp.n_q, wp.h_kv, nc), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, wp.n_q, wp.h_q), dtype=torch.float32, device=dev)
+    ws_b = dash.dash_block_entmax_workspace_bytes(1, wp.n_q, 0, wp.n_kv, wp.h_q, wp.h_kv,
+                                                  wp.head_dim, wp.block)
+    route_ws = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=dev)
+    kbar_d = dash.dash_pool_keys(kd, wd.block)          # the decode cache's summaries
+    ncd = -(-wd.n_kv // wd.block)
+    mask_d = torch.empty((wd.batch, 1, wd.h_kv, -(-ncd // 32)), dtype=torch.int32, device=dev)
+    bias_d = torch.empty((wd.batch, 1, wd.h_kv, ncd), dtype=torch.float32, device=dev)
+    o_d = torch.empty_like(qd)
+    wsd_b = dash.dash_block_entmax_workspace_bytes(wd.batch, 1, wd.n_kv - 1, wd.n_kv, wd.h_q,
+                                                   wd.h_kv, wd.head_dim, wd.block)
+    route_ws_d = torch.empty(max(wsd_b, 1), dtype=torch.uint8, device=dev)
+    attn_ws_d = torch.empty(dash.dash_decode_workspace_bytes(wd.batch, wd.n_kv, wd.h_q, wd.h_kv,
+                                                             wd.head_dim, wd.block),
+                            dtype=torch.uint8, device=dev)
+
+    def step(timer: Timer | None):
+        def ev(name):
+            return timer.span(name) if timer else (None, None)
+        s, e = ev("pool")
+        s and s.record()
+        dash.dash_pool_keys(k, wp.block, kbar=kbar)
+        e and e.record()
+        s, e = ev("entmax")
+        s and s.record()
+        dash.dash_block_entmax(q, kbar, n_kv=wp.n_kv, block=wp.block, alpha=wp.alpha,
+                               gamma=wp.gamma, sigma=wp.sigma, mask=mask, bias=bias,
+                               want_tau=False, workspace=route_ws)
+        e and e.record()
+        s, e = ev("attn")
+        s and s.record()
+        dash.dash_sparse_attn_prefill(q, k, v, mask, bias, block=wp.block, o=o, lse=lse)
+        e and e.record()
+        s, e = ev("decode")
+        s and s.record()
+        dash.dash_block_entmax(qd, kbar_d, n_kv=wd.n_kv, block=wd.block, alpha=wd.alpha,
+                               gamma=wd.gamma, sigma=wd.sigma, q_pos0=wd.n_kv - 1, mask=mask_d,
+                               bias=bias_d, want_tau=False, workspace=route_ws_d)
+        s2, e2 = ev("decode_attn")
+        s2 and s2.record()
+        dash.dash_sparse_attn_decode(qd, kd, vd, mask_d, bias_d, block=wd.block, o=o_d,
+                                     workspace=attn_ws_d)
+        e2 and e2.record()
+        e and e.record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    timer = Timer()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    pairs, frac = selected_pairs_prefill(mask, wp)
+    flops = 4.0 * wp.head_dim * pairs
+    t_pool, t_ent, t_attn = timer.mean_ms("pool"), timer.mean_ms("entmax"), timer.mean_ms("attn")
+    t_pre = t_pool + t_ent + t_attn
+    pre_tflops = flops / (t_pre * 1e-3) / 1e12
+    attn_tflops = flops / (t_attn * 1e-3) / 1e12
+    dbytes, mean_routed = decode_bytes(mask_d, wd)
+    t_dec = timer.mean_ms("decode")
+    t_dec_attn = timer.mean_ms("decode_attn")
+    dec_gbps = dbytes / (t_dec * 1e-3) / 1e9
+    traffic = measured_traffic("sparse_attn_prefill")
+    dec_traffic = measured_traffic("decode_step")
+
+    out = {
+        "metric": METRIC,
+        "value": round(pre_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, planted chunks; see workloads.py)",
+        "config": {
+            "workload": f"{wp.name} + {wd.name}",
+            "prefill": {"batch": wp.batch, "seq_len": wp.n_kv, "h_q": wp.h_q, "h_kv": wp.h_kv,
+                        "head_dim": wp.head_dim, "block": wp.block, "alpha": wp.alpha,
+                        "gamma": wp.gamma, "sigma": wp.sigma},
+            "decode": {"batch": wd.batch, "context": wd.n_kv, "h_q": wd.h_q, "h_kv": wd.h_kv,
+                       "head_dim": wd.head_dim, "block": wd.block, "alpha": wd.alpha,
+                       "gamma": wd.gamma, "sigma": wd.sigma},
+        },
+        "prefill": {
+            "selected_pairs": pairs, "routed_fraction": round(frac, 4),
+            "algorithmic_tflop": round(flops / 1e12, 4),
+            "ms": {"pool": round(t_pool, 4), "entmax": round(t_ent, 4), "attn": round(t_attn, 4)},
+            "attn_tflops": round(attn_tflops, 3),
+            "end_to_end_tflops": round(pre_tflops, 3),
+        },
+        "decode": {
+            "tok_per_s": round(wd.batch / (t_dec * 1e-3), 1),
+            "us_per_step": round(t_dec * 1e3, 2),
+            "us_attn": round(t_dec_attn * 1e3, 2),
+            "algorithmic_bytes": dbytes,
+            "mean_routed_chunks": round(mean_routed, 3),
+            "gb_per_s": round(dec_gbps, 1),
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": dec_traffic},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 3),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(pre, dec, wp, wd, pairs / wp.n_q)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

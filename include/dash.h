@@ -1,0 +1,154 @@
+/*
+ * dash.h -- C ABI of libdash, the DashAttention forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "DashAttention: Differentiable and Adaptive Sparse Hierarchical Attention"
+ * (arXiv 2605.18753v1), cited as [DA]. Three stages over Q, K, V backed by a cache of chunk
+ * summaries [DA §3.5]:
+ *   Stage 0  dash_pool_keys            chunk summaries kbar              [DA §3.1 Eq. 3; Alg. 1]
+ *   Stage 1  dash_block_entmax         alpha-entmax routing: mask, bias   [DA §3.2 Eq. 4; Alg. 2]
+ *   Stage 2  dash_sparse_attn_prefill  prior-biased sparse softmax        [DA §3.3-3.4 Prop. 1; Alg. 3]
+ *            dash_sparse_attn_decode   the same for one new token per sequence, split over the
+ *                                      selected chunks                   [DA §3.5 "split-KV variant"]
+ *
+ * Notation: B = batch, n = sequence length, H_q / H_kv = query / key-value heads, g = H_q / H_kv
+ * (query head h belongs to KV group floor(h / g)), D = head dim, Bc = chunk (block) size,
+ * Tc = floor(n_kv / Bc) complete chunks (those with a summary), Nc = ceil(n_kv / Bc) chunk slots,
+ * W = ceil(Nc / 32) mask words. A query at absolute position p lies in chunk c_p = floor(p / Bc).
+ *
+ * Layouts (row-major, token-major as in the "Require" clauses of [DA Alg. 1-3]):
+ *   q            [B, n_q, H_q, D]       dtype dt
+ *   k, v         [B, n_kv, H_kv, D]     dtype dt
+ *   kbar         [B, Tc, H_kv, D]       fp32
+ *   mask         [B, n_q, H_kv, W]      uint32; chunk c is bit (c mod 32) of word floor(c / 32)
+ *   bias         [B, n_q, H_kv, Nc]     fp32 routing bias d of [DA Prop. 1]
+ *   tau          [B, n_q, H_q]          fp32 entmax threshold in x-units (see dash_block_entmax)
+ *   o            [B, n_q, H_q, D]       dtype dt;   lse [B, n_q, H_q] fp32
+ *
+ * Conventions
+ *   Ownership:   every pointer is device memory owned by the caller. The library allocates
+ *                nothing and keeps no pointer after a call returns.
+ *   Asynchrony:  every call enqueues its kernels on `stream` and returns without waiting.
+ *                Calls are thread-safe; the only state is the thread-local error string.
+ *   Errors:      arguments are validated before anything is launched. Invalid arguments give
+ *                DASH_ERR_INVALID, valid but unimplemented shapes DASH_ERR_UNSUPPORTED, a short
+ *                workspace DASH_ERR_WORKSPACE, a failed launch DASH_ERR_HIP; nothing is launched
+ *                on a validation error. dash_last_error() gives the detail. Faults inside a
+ *                kernel surface at the caller's next synchronisation. No exception crosses the ABI.
+ *   Determinism: the same inputs give bitwise-equal outputs (no floating-point atomics).
+ *   Supported:   dt in {DASH_F32, DASH_BF16}; D in {64, 128}; Bc in {32, 64, 128};
+ *                g in {1, 2, 4, 8, 16}; Nc <= 8192.
+ */
+#ifndef DASH_H
+#define DASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DASH_OK = 0,
+    DASH_ERR_INVALID = 1,
+    DASH_ERR_UNSUPPORTED = 2,
+    DASH_ERR_WORKSPACE = 3,
+    DASH_ERR_HIP = 4
+} dash_status_t;
+
+typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype_t;
+
+/* Static text naming a status code. */
+const char* dash_status_string(dash_status_t s);
+
+/* Detail of the calling thread's last non-OK return ("" if none). Valid until the next call. */
+const char* dash_last_error(void);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int dash_version(void);
+
+/*
+ * Stage 0 [DA §3.1, Eq. 3 with the learned summary query at its zero initialisation, where the
+ * local softmax is uniform; DA App. G, Alg. 1]: each complete chunk c < Tc of each KV head is
+ * summarised by the mean of its Bc keys, accumulated in fp32.
+ *   k     [B, n_kv, H_kv, D] (dt)      kbar [B, Tc, H_kv, D] fp32 (written in full)
+ * The trailing n_kv - Tc * Bc keys of an incomplete chunk get no summary (kbar may be NULL when
+ * Tc = 0, here and in dash_block_entmax). The summaries only
+ * depend on their own chunk, so a decode loop can pool once and keep kbar as a cache.
+ */
+dash_status_t dash_pool_keys(const void* k, dash_dtype_t dt, float* kbar, int batch, int n_kv,
+                             int h_kv, int head_dim, int block, hipStream_t stream);
+
+/*
+ * Stage 0 with a learned summary query [DA §3.1, Eq. 3; Alg. 1]: kbar_c = sum_t softmax_t(
+ * <qbar^(r), k_t> / sqrt(D)) k_t over the chunk's own keys.  qbar [H_kv, D] fp32.
+ */
+dash_status_t dash_pool_keys_query(const void* k, dash_dtype_t dt, const float* qbar, float* kbar,
+                                   int batch, int n_kv, int h_kv, int head_dim, int block,
+                                   hipStream_t stream);
+
+/*
+ * Stage 1 [DA §3.2, Eq. 4; DA App. G, Alg. 2]. Query row t (t < n_q) sits at absolute position
+ * p = q_pos0 + t of a sequence of n_kv keys (prefill: q_pos0 = 0, n_q = n_kv; decode: n_q = 1,
+ * q_pos0 = n_kv - 1, the new token's key and value already appended). For every query head h it
+ *   1. scores the complete chunks before its own, c < c_p:
+ *        x_c = (alpha - 1) * gamma * <q_p^(h), kbar_c^(h / g)> / sqrt(D)          (x-units)
+ *   2. finds the entmax threshold tau with sum_c [x_c - tau]_+^(1/(alpha-1)) = 1 [DA Eq. 2]
+ *      (Newton steps from the left with a bisection guard, polished in closed form for
+ *      alpha in {1.5, 2}) and p_c = [x_c - tau]_+^(1/(alpha-1));
+ * then for every KV group r
+ *   3. averages the probabilities of the group's g heads, w_c = mean_h p_c [DA §3.2];
+ *   4. routes R = {c < c_p : w_c > 0}, sets their mask bits and the bias
+ *        d_c = (log w_c - mu) / sigma,  mu = mean_{c in R} log w_c       [DA Prop. 1]
+ *      and always sets the bit of the query's own chunk c_p with d = 0  [DA §3.4; Alg. 2].
+ * Mask rows are written in full (bits beyond c_p are 0). Bias entries are written only where the
+ * mask bit is 1; the others are left untouched. tau may be NULL; a row with c_p = 0 has no
+ * candidate and gets tau = +inf. alpha in (1, 2]; gamma > 0; sigma > 0, +inf allowed (d = 0).
+ * Rows with c_p up to 2048 run fully on chip; longer rows (and decode) score into `workspace`
+ * first: dash_block_entmax_workspace_bytes() gives the size it needs (0 if none).
+ */
+size_t dash_block_entmax_workspace_bytes(int batch, int n_q, int q_pos0, int n_kv, int h_q,
+                                         int h_kv, int head_dim, int block);
+dash_status_t dash_block_entmax(const void* q, dash_dtype_t dt, const float* kbar, int batch,
+                                int n_q, int q_pos0, int n_kv, int h_q, int h_kv, int head_dim,
+                                int block, float alpha, float gamma, float sigma, uint32_t* mask,
+                                float* bias, float* tau, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * Stage 2, prefill [DA §3.3-3.4, Prop. 1; DA App. G, Alg. 3]: for every query t of a causal
+ * sequence of n tokens and every head h of group r,
+ *   o = sum_j softmax_j(scale * <q_t, k_j> + d_c(j)) v_j
+ * over the tokens j of the chunks c < c_t whose mask bit is set (bias d_c from `bias`) and the
+ * tokens c_t * Bc .. t of the query's own chunk (d = 0). mask / bias as dash_block_entmax writes
+ * them for n_q = n, q_pos0 = 0. scale is normally 1/sqrt(D). lse (natural log of the softmax
+ * normaliser, bias included) may be NULL. All query heads of a group share one selection.
+ */
+dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void* v,
+                                       dash_dtype_t dt, const uint32_t* mask, const float* bias,
+                                       void* o, float* lse, int batch, int n, int h_q, int h_kv,
+                                       int head_dim, int block, float scale, hipStream_t stream);
+
+/*
+ * Stage 2, decode [DA §3.5, split-KV variant]: the Stage 2 output of one new query per sequence
+ * at position n_ctx - 1 of its cache. The selected chunks are split over many workgroups; their
+ * partial (max, sum, output) triples are merged in a fixed order, so the result is deterministic.
+ *   q, o [B, H_q, D] (dt);  k_cache, v_cache [B, n_ctx, H_kv, D] (dt);
+ *   mask [B, 1, H_kv, W], bias [B, 1, H_kv, Nc] from dash_block_entmax(n_q = 1,
+ *   q_pos0 = n_ctx - 1).  workspace: device scratch of dash_decode_workspace_bytes() bytes.
+ */
+size_t dash_decode_workspace_bytes(int batch, int n_ctx, int h_q, int h_kv, int head_dim,
+                                   int block);
+dash_status_t dash_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                      dash_dtype_t dt, const uint32_t* mask, const float* bias,
+                                      void* o, int batch, int n_ctx, int h_q, int h_kv,
+                                      int head_dim, int block, float scale, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_H */

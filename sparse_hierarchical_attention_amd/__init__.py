@@ -1,0 +1,241 @@
+"""libdash: the DashAttention forward pass on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of the C ABI in ``include/dash.h``; the functions carry the C names.
+Arguments are torch tensors on the GPU: torch only supplies device memory and the current HIP
+stream, every step of the computation runs in libdash's own kernels. There is no fallback: if
+``libdash.so`` is not built, or an argument is rejected, a call raises.
+
+Method: "DashAttention: Differentiable and Adaptive Sparse Hierarchical Attention"
+(arXiv 2605.18753v1), Stage 0 (§3.1), Stage 1 (§3.2) and Stage 2 (§3.3-3.4, Prop. 1).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "DashError", "lib", "library_path",
+    "dash_pool_keys", "dash_pool_keys_query", "dash_block_entmax",
+    "dash_block_entmax_workspace_bytes", "dash_sparse_attn_prefill",
+    "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_version",
+    "forward", "decode_step",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libdash.so")
+_lib = None
+
+DASH_F32, DASH_BF16 = 0, 1
+
+
+class DashError(RuntimeError):
+    """A libdash call returned a non-OK status."""
+
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+        self.status_name = name
+
+
+def lib():
+    """The loaded libdash.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"libdash is not built ({library_path} missing); run "
+                "`python -m sparse_hierarchical_attention_amd.build` first")
+        L = ctypes.CDLL(library_path)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.dash_status_string.argtypes = [i]
+        L.dash_status_string.restype = ctypes.c_char_p
+        L.dash_last_error.restype = ctypes.c_char_p
+        L.dash_version.restype = i
+        L.dash_pool_keys.argtypes = [vp, i, vp, i, i, i, i, i, vp]
+        L.dash_pool_keys_query.argtypes = [vp, i, vp, vp, i, i, i, i, i, vp]
+        L.dash_block_entmax_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+        L.dash_block_entmax_workspace_bytes.restype = sz
+        L.dash_block_entmax.argtypes = [vp, i, vp, i, i, i, i, i, i, i, i, f, f, f, vp, vp, vp,
+                                        vp, sz, vp]
+        L.dash_sparse_attn_prefill.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i,
+                                               f, vp]
+        L.dash_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.dash_decode_workspace_bytes.restype = sz
+        L.dash_sparse_attn_decode.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, f,
+                                              vp, sz, vp]
+        for fn in ("dash_pool_keys", "dash_pool_keys_query", "dash_block_entmax",
+                   "dash_sparse_attn_prefill", "dash_sparse_attn_decode"):
+            getattr(L, fn).restype = i
+        _lib = L
+    return _lib
+
+
+def dash_version() -> int:
+    return int(lib().dash_version())
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise DashError(status, L.dash_status_string(status).decode(),
+                        L.dash_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DASH_BF16
+    if t.dtype == torch.float32:
+        return DASH_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    dev = ts[0].device
+    for t in ts:
+        if t is None:
+            continue
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must live on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def dash_pool_keys(k: torch.Tensor, block: int, kbar: torch.Tensor | None = None) -> torch.Tensor:
+    """Stage 0 (mean pooling): k [B, n, Hkv, D] -> kbar [B, n // block, Hkv, D] fp32."""
+    b, n, hkv, d = k.shape
+    if kbar is None:
+        kbar = torch.empty((b, n // block, hkv, d), dtype=torch.float32, device=k.device)
+    dev = _dev(k, kbar)
+    _check(lib().dash_pool_keys(_ptr(k), _dtype_code(k), _ptr(kbar), b, n, hkv, d, block,
+                                _stream(dev)))
+    return kbar
+
+
+def dash_pool_keys_query(k: torch.Tensor, qbar: torch.Tensor, block: int,
+                         kbar: torch.Tensor | None = None) -> torch.Tensor:
+    """Stage 0 with a learned summary query qbar [Hkv, D] fp32 (Eq. 3)."""
+    b, n, hkv, d = k.shape
+    if kbar is None:
+        kbar = torch.empty((b, n // block, hkv, d), dtype=torch.float32, device=k.device)
+    dev = _dev(k, qbar, kbar)
+    _check(lib().dash_pool_keys_query(_ptr(k), _dtype_code(k), _ptr(qbar), _ptr(kbar), b, n, hkv,
+                                      d, block, _stream(dev)))
+    return kbar
+
+
+def dash_block_entmax_workspace_bytes(batch, n_q, q_pos0, n_kv, h_q, h_kv, head_dim, block) -> int:
+    return int(lib().dash_block_entmax_workspace_bytes(batch, n_q, q_pos0, n_kv, h_q, h_kv,
+                                                       head_dim, block))
+
+
+def dash_block_entmax(q: torch.Tensor, kbar: torch.Tensor, *, n_kv: int, block: int, alpha: float,
+                      gamma: float, sigma: float, q_pos0: int = 0, h_kv: int | None = None,
+                      mask: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+                      tau: torch.Tensor | None = None, want_tau: bool = True,
+                      workspace: torch.Tensor | None = None):
+    """Stage 1: q [B, n_q, Hq, D], kbar [B, Tc, Hkv, D] fp32 ->
+    mask int32 [B, n_q, Hkv, W] (uint32 bit patterns), bias fp32 [B, n_q, Hkv, Nc],
+    tau fp32 [B, n_q, Hq] (None unless want_tau)."""
+    b, n_q, hq, d = q.shape
+    hkv = kbar.shape[2] if h_kv is None else h_kv
+    nc = -(-n_kv // block)
+    nw = -(-nc // 32)
+    dev = q.device
+    if mask is None:
+        mask = torch.empty((b, n_q, hkv, nw), dtype=torch.int32, device=dev)
+    if bias is None:
+        bias = torch.empty((b, n_q, hkv, nc), dtype=torch.float32, device=dev)
+    if tau is None and want_tau:
+        tau = torch.empty((b, n_q, hq), dtype=torch.float32, device=dev)
+    need = dash_block_entmax_workspace_bytes(b, n_q, q_pos0, n_kv, hq, hkv, d, block)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dev = _dev(q, kbar, mask, bias, tau, workspace)
+    _check(lib().dash_block_entmax(
+        _ptr(q), _dtype_code(q), _ptr(kbar), b, n_q, q_pos0, n_kv, hq, hkv, d, block,
+        float(alpha), float(gamma), float(sigma), _ptr(mask), _ptr(bias), _ptr(tau),
+        _ptr(workspace), wsb, _stream(dev)))
+    return mask, bias, tau
+
+
+def dash_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             mask: torch.Tensor, bias: torch.Tensor, *, block: int,
+                             scale: float | None = None, o: torch.Tensor | None = None,
+                             lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Stage 2 prefill: -> (o [B, n, Hq, D] in q's dtype, lse fp32 [B, n, Hq] or None)."""
+    b, n, hq, d = q.shape
+    hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((b, n, hq), dtype=torch.float32, device=q.device)
+    dev = _dev(q, k, v, mask, bias, o, lse)
+    _check(lib().dash_sparse_attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(mask), _ptr(bias), _ptr(o), _ptr(lse),
+        b, n, hq, hkv, d, block, float(scale), _stream(dev)))
+    return o, lse
+
+
+def dash_decode_workspace_bytes(batch, n_ctx, h_q, h_kv, head_dim, block) -> int:
+    return int(lib().dash_decode_workspace_bytes(batch, n_ctx, h_q, h_kv, head_dim, block))
+
+
+def dash_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            mask: torch.Tensor, bias: torch.Tensor, *, block: int,
+                            scale: float | None = None, o: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Stage 2 decode: q [B, Hq, D] (or [B, 1, Hq, D]) -> o of the same shape."""
+    b, n_ctx, hkv, d = k_cache.shape
+    hq = q.shape[-2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    need = dash_decode_workspace_bytes(b, n_ctx, hq, hkv, d, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    dev = _dev(q, k_cache, v_cache, mask, bias, o, workspace)
+    _check(lib().dash_sparse_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(mask), _ptr(bias), _ptr(o),
+        b, n_ctx, hq, hkv, d, block, float(scale), _ptr(workspace), wsb, _stream(dev)))
+    return o
+
+
+def forward(q, k, v, *, block: int, alpha: float, gamma: float, sigma: float,
+            scale: float | None = None):
+    """Whole prefill forward: pool -> route -> sparse attention. Returns a dict of every
+    intermediate (kbar, mask, bias, tau, o, lse)."""
+    kbar = dash_pool_keys(k, block)
+    mask, bias, tau = dash_block_entmax(q, kbar, n_kv=k.shape[1], block=block, alpha=alpha,
+                                        gamma=gamma, sigma=sigma, h_kv=k.shape[2])
+    o, lse = dash_sparse_attn_prefill(q, k, v, mask, bias, block=block, scale=scale)
+    return dict(kbar=kbar, mask=mask, bias=bias, tau=tau, o=o, lse=lse)
+
+
+def decode_step(q, k_cache, v_cache, kbar, *, block: int, alpha: float, gamma: float,
+                sigma: float, scale: float | None = None, route_ws=None, attn_ws=None):
+    """One decode step for a new token per sequence whose key/value are already in the cache:
+    route with the cached summaries, then the split sparse attention. q [B, 1, Hq, D]."""
+    n_ctx = k_cache.shape[1]
+    mask, bias, _ = dash_block_entmax(q, kbar, n_kv=n_ctx, block=block, alpha=alpha, gamma=gamma,
+                                      sigma=sigma, q_pos0=n_ctx - 1, h_kv=k_cache.shape[2],
+                                      want_tau=False, workspace=route_ws)
+    o = dash_sparse_attn_decode(q, k_cache, v_cache, mask, bias, block=block, scale=scale,
+                                workspace=attn_ws)
+    return o, mask, bias

@@ -1,0 +1,192 @@
+// libdash C ABI: argument validation, dispatch and launch (see include/dash.h).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "dash.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dash_status_t fail(dash_status_t s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+dash_status_t ok() {
+    g_last_error.clear();
+    return DASH_OK;
+}
+
+dash_status_t hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return ok();
+    return fail(DASH_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+constexpr int kMaxChunks = 8192;
+
+// Shape checks shared by every entry point. Returns DASH_OK or the failing status.
+dash_status_t check_shape(const char* fn, dash_dtype_t dt, int batch, int n_kv, int h_q, int h_kv,
+                          int head_dim, int block) {
+    if (dt != DASH_F32 && dt != DASH_BF16) return fail(DASH_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+    if (batch <= 0 || n_kv <= 0 || h_q <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0)
+        return fail(DASH_ERR_INVALID, "%s: sizes must be positive (batch=%d n=%d h_q=%d h_kv=%d D=%d block=%d)",
+                    fn, batch, n_kv, h_q, h_kv, head_dim, block);
+    if (h_q % h_kv != 0)
+        return fail(DASH_ERR_INVALID, "%s: h_q=%d is not a multiple of h_kv=%d", fn, h_q, h_kv);
+    const int g = h_q / h_kv;
+    if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+        return fail(DASH_ERR_UNSUPPORTED, "%s: group size h_q/h_kv=%d not in {1,2,4,8,16}", fn, g);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(DASH_ERR_UNSUPPORTED, "%s: head_dim=%d not in {64,128}", fn, head_dim);
+    if (block != 32 && block != 64 && block != 128)
+        return fail(DASH_ERR_UNSUPPORTED, "%s: block=%d not in {32,64,128}", fn, block);
+    if (ceil_div(n_kv, block) > kMaxChunks)
+        return fail(DASH_ERR_UNSUPPORTED, "%s: %d chunks exceed the limit %d", fn, ceil_div(n_kv, block), kMaxChunks);
+    if ((int64_t)batch * n_kv > (int64_t)1 << 31)
+        return fail(DASH_ERR_UNSUPPORTED, "%s: batch * n too large", fn);
+    return DASH_OK;
+}
+
+dash::RouteParams route_params(int batch, int n_q, int q_pos0, int n_kv, int h_q, int h_kv,
+                               int head_dim, int block, float alpha, float gamma, float sigma) {
+    dash::RouteParams p;
+    p.batch = batch; p.n_q = n_q; p.q_pos0 = q_pos0; p.n_kv = n_kv; p.h_q = h_q; p.h_kv = h_kv;
+    p.g = h_q / h_kv; p.head_dim = head_dim; p.block = block; p.tc = n_kv / block;
+    p.nc = ceil_div(n_kv, block); p.nw = ceil_div(p.nc, 32);
+    p.alpha = alpha; p.gamma = gamma; p.inv_sigma = isinf(sigma) ? 0.0f : 1.0f / sigma;
+    return p;
+}
+
+dash::AttnParams attn_params(int batch, int n_q, int q_pos0, int n_kv, int h_q, int h_kv,
+                             int head_dim, int block, float scale) {
+    dash::AttnParams p;
+    p.batch = batch; p.n_q = n_q; p.q_pos0 = q_pos0; p.n_kv = n_kv; p.h_q = h_q; p.h_kv = h_kv;
+    p.g = h_q / h_kv; p.head_dim = head_dim; p.block = block;
+    p.nc = ceil_div(n_kv, block); p.nw = ceil_div(p.nc, 32); p.scale = scale;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dash_status_string(dash_status_t s) {
+    switch (s) {
+        case DASH_OK: return "DASH_OK";
+        case DASH_ERR_INVALID: return "DASH_ERR_INVALID";
+        case DASH_ERR_UNSUPPORTED: return "DASH_ERR_UNSUPPORTED";
+        case DASH_ERR_WORKSPACE: return "DASH_ERR_WORKSPACE";
+        case DASH_ERR_HIP: return "DASH_ERR_HIP";
+    }
+    return "DASH_UNKNOWN_STATUS";
+}
+
+const char* dash_last_error(void) { return g_last_error.c_str(); }
+
+int dash_version(void) { return 100; }
+
+dash_status_t dash_pool_keys(const void* k, dash_dtype_t dt, float* kbar, int batch, int n_kv,
+                             int h_kv, int head_dim, int block, hipStream_t stream) {
+    dash_status_t s = check_shape("dash_pool_keys", dt, batch, n_kv, h_kv, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    // with no complete chunk (n_kv < block) there is nothing to write and kbar may be null
+    if (!k || (!kbar && n_kv / block > 0)) return fail(DASH_ERR_INVALID, "dash_pool_keys: null pointer");
+    return hip_status(dash::launch_pool_mean(k, dt, kbar, batch, n_kv, h_kv, head_dim, block, stream),
+                      "dash_pool_keys");
+}
+
+dash_status_t dash_pool_keys_query(const void* k, dash_dtype_t dt, const float* qbar, float* kbar,
+                                   int batch, int n_kv, int h_kv, int head_dim, int block,
+                                   hipStream_t stream) {
+    dash_status_t s = check_shape("dash_pool_keys_query", dt, batch, n_kv, h_kv, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (!k || !qbar || (!kbar && n_kv / block > 0))
+        return fail(DASH_ERR_INVALID, "dash_pool_keys_query: null pointer");
+    return hip_status(dash::launch_pool_query(k, dt, qbar, kbar, batch, n_kv, h_kv, head_dim, block, stream),
+                      "dash_pool_keys_query");
+}
+
+size_t dash_block_entmax_workspace_bytes(int batch, int n_q, int q_pos0, int n_kv, int h_q,
+                                         int h_kv, int head_dim, int block) {
+    if (batch <= 0 || n_q <= 0 || n_kv <= 0 || h_q <= 0 || h_kv <= 0 || block <= 0 || h_q % h_kv)
+        return 0;
+    return dash::route_workspace_bytes(route_params(batch, n_q, q_pos0, n_kv, h_q, h_kv, head_dim,
+                                                    block, 1.5f, 1.0f, 1.0f));
+}
+
+dash_status_t dash_block_entmax(const void* q, dash_dtype_t dt, const float* kbar, int batch,
+                                int n_q, int q_pos0, int n_kv, int h_q, int h_kv, int head_dim,
+                                int block, float alpha, float gamma, float sigma, uint32_t* mask,
+                                float* bias, float* tau, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    const char* fn = "dash_block_entmax";
+    dash_status_t s = check_shape(fn, dt, batch, n_kv, h_q, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (n_q <= 0 || q_pos0 < 0 || (int64_t)q_pos0 + n_q > n_kv)
+        return fail(DASH_ERR_INVALID, "%s: need n_q > 0 and 0 <= q_pos0, q_pos0 + n_q <= n_kv (n_q=%d q_pos0=%d n_kv=%d)",
+                    fn, n_q, q_pos0, n_kv);
+    if (!(alpha > 1.0f && alpha <= 2.0f)) return fail(DASH_ERR_INVALID, "%s: alpha=%g not in (1, 2]", fn, alpha);
+    if (!(gamma > 0.0f) || isinf(gamma)) return fail(DASH_ERR_INVALID, "%s: gamma=%g must be positive and finite", fn, gamma);
+    if (!(sigma > 0.0f)) return fail(DASH_ERR_INVALID, "%s: sigma=%g must be positive (or +inf)", fn, sigma);
+    if (!q || (!kbar && n_kv / block > 0) || !mask || !bias)
+        return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    dash::RouteParams p = route_params(batch, n_q, q_pos0, n_kv, h_q, h_kv, head_dim, block, alpha,
+                                       gamma, sigma);
+    const size_t need = dash::route_workspace_bytes(p);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(dash::launch_block_entmax(q, dt, kbar, p, mask, bias, tau, workspace, stream), fn);
+}
+
+dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void* v,
+                                       dash_dtype_t dt, const uint32_t* mask, const float* bias,
+                                       void* o, float* lse, int batch, int n, int h_q, int h_kv,
+                                       int head_dim, int block, float scale, hipStream_t stream) {
+    const char* fn = "dash_sparse_attn_prefill";
+    dash_status_t s = check_shape(fn, dt, batch, n, h_q, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (!(scale > 0.0f) || isinf(scale)) return fail(DASH_ERR_INVALID, "%s: scale=%g must be positive and finite", fn, scale);
+    if (!q || !k || !v || !mask || !bias || !o) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    dash::AttnParams p = attn_params(batch, n, 0, n, h_q, h_kv, head_dim, block, scale);
+    return hip_status(dash::launch_attn_prefill(q, k, v, dt, mask, bias, o, lse, p, stream), fn);
+}
+
+size_t dash_decode_workspace_bytes(int batch, int n_ctx, int h_q, int h_kv, int head_dim,
+                                   int block) {
+    if (batch <= 0 || n_ctx <= 0 || h_q <= 0 || h_kv <= 0 || block <= 0 || h_q % h_kv) return 0;
+    return dash::decode_workspace_bytes(attn_params(batch, 1, n_ctx - 1, n_ctx, h_q, h_kv, head_dim,
+                                                    block, 1.0f));
+}
+
+dash_status_t dash_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                      dash_dtype_t dt, const uint32_t* mask, const float* bias,
+                                      void* o, int batch, int n_ctx, int h_q, int h_kv,
+                                      int head_dim, int block, float scale, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "dash_sparse_attn_decode";
+    dash_status_t s = check_shape(fn, dt, batch, n_ctx, h_q, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (!(scale > 0.0f) || isinf(scale)) return fail(DASH_ERR_INVALID, "%s: scale=%g must be positive and finite", fn, scale);
+    if (!q || !k_cache || !v_cache || !mask || !bias || !o) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    dash::AttnParams p = attn_params(batch, 1, n_ctx - 1, n_ctx, h_q, h_kv, head_dim, block, scale);
+    const size_t need = dash::decode_workspace_bytes(p);
+    if (!workspace || workspace_bytes < need)
+        return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(dash::launch_attn_decode(q, k_cache, v_cache, dt, mask, bias, o, p, workspace, stream), fn);
+}
+
+}  // extern "C"

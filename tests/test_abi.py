@@ -1,0 +1,95 @@
+"""Host-side checks of the libdash C ABI: the library loads, exports every function the header
+declares, and rejects bad arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dash.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_hierarchical_attention_amd as d
+    if not os.path.exists(d.library_path):
+        from sparse_hierarchical_attention_amd import build
+        build.build()
+    return d.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dash_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_stages():
+    names = declared_functions()
+    for fn in ("dash_pool_keys", "dash_block_entmax", "dash_sparse_attn_prefill",
+               "dash_sparse_attn_decode"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    missing = [fn for fn in declared_functions() if not hasattr(L, fn)]
+    assert not missing, missing
+
+
+def test_status_strings(L):
+    for code, name in enumerate(["DASH_OK", "DASH_ERR_INVALID", "DASH_ERR_UNSUPPORTED",
+                                 "DASH_ERR_WORKSPACE", "DASH_ERR_HIP"]):
+        assert L.dash_status_string(code).decode() == name
+
+
+def err(L):
+    return L.dash_last_error().decode()
+
+
+def test_pool_rejects_bad_shapes(L):
+    assert L.dash_pool_keys(None, 1, None, 1, 64, 2, 96, 64, None) == 2
+    assert "head_dim" in err(L)
+    assert L.dash_pool_keys(None, 1, None, 1, 64, 2, 128, 48, None) == 2
+    assert "block" in err(L)
+    assert L.dash_pool_keys(None, 1, None, 0, 64, 2, 128, 64, None) == 1
+    assert L.dash_pool_keys(None, 7, None, 1, 64, 2, 128, 64, None) == 1
+    assert L.dash_pool_keys(None, 1, None, 1, 64, 2, 128, 64, None) == 1  # null pointers
+    assert "null" in err(L)
+
+
+def test_block_entmax_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails before any launch
+    args = dict(q=p, dt=1, kbar=p, batch=1, n_q=64, q_pos0=0, n_kv=64, h_q=4, h_kv=2, d=128,
+                block=64, alpha=1.5, gamma=1.0, sigma=1.0, mask=p, bias=p, tau=None, ws=p,
+                wsb=1 << 40, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dash_block_entmax(*a.values())
+
+    assert call(alpha=1.0) == 1 and "alpha" in err(L)
+    assert call(alpha=2.5) == 1
+    assert call(gamma=0.0) == 1 and "gamma" in err(L)
+    assert call(sigma=0.0) == 1 and "sigma" in err(L)
+    assert call(sigma=-1.0) == 1
+    assert call(h_q=5) == 1 and "multiple" in err(L)
+    assert call(h_q=64, h_kv=2) == 2 and "group" in err(L)
+    assert call(q_pos0=1) == 1 and "q_pos0" in err(L)
+    assert call(mask=None) == 1 and "null" in err(L)
+    need = L.dash_block_entmax_workspace_bytes(1, 64, 0, 64, 4, 2, 128, 64)
+    if need:
+        assert call(wsb=need - 1) == 3 and "workspace" in err(L)
+
+
+def test_attention_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(16)
+    assert L.dash_sparse_attn_prefill(p, p, p, 1, p, p, p, None, 1, 64, 4, 2, 128, 64, 0.0, None) == 1
+    assert "scale" in err(L)
+    assert L.dash_sparse_attn_prefill(p, p, p, 1, p, p, None, None, 1, 64, 4, 2, 128, 64, 0.1, None) == 1
+    need = L.dash_decode_workspace_bytes(2, 4096, 8, 2, 128, 64)
+    assert need > 0
+    assert L.dash_sparse_attn_decode(p, p, p, 1, p, p, p, 2, 4096, 8, 2, 128, 64, 0.1, p,
+                                     need - 1, None) == 3
+    assert L.dash_sparse_attn_decode(p, p, p, 1, p, p, p, 2, 4096, 8, 2, 128, 64, 0.1, None,
+                                     0, None) == 3

@@ -1,0 +1,206 @@
+"""GPU parity: libdash (through its C ABI) against the double-precision oracle on the same seeded
+inputs. Small cases compare every row; full-size workloads compare sampled rows."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def dash():
+    import sparse_hierarchical_attention_amd as d
+    d.lib()
+    return d
+
+
+def host(t):
+    return t.detach().cpu()
+
+
+def sample_rows(n_q: int, block: int, count: int, seed: int, batch: int = 1) -> np.ndarray:
+    """Query rows to check: chunk edges, the first and last rows, and random rows."""
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, block - 1, block, block + 1, 2 * block - 1, n_q // 2, n_q - 2, n_q - 1}
+    fixed |= set(range(0, n_q, max(1, n_q // 8)))
+    rows = sorted(r for r in fixed if 0 <= r < n_q)
+    extra = rng.choice(n_q, size=min(count, n_q), replace=False)
+    rows = sorted(set(rows) | set(int(e) for e in extra))
+    return np.array([b * n_q + r for b in range(batch) for r in rows], dtype=np.int64)
+
+
+def flat_rows(t: torch.Tensor, rows: np.ndarray) -> np.ndarray:
+    """[B, n_q, ...] GPU tensor -> host array of the listed rows rho = b * n_q + t."""
+    a = parity.to_host(t)
+    return a.reshape((-1,) + a.shape[2:])[rows]
+
+
+def run_and_compare(dash, orc, w: wl.Workload, alpha, gamma, sigma, rows=None, max_flip_frac=0.02):
+    inp = wl.make_inputs(w, DEV)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    res = dash.forward(q, k, v, block=w.block, alpha=alpha, gamma=gamma, sigma=sigma)
+    torch.cuda.synchronize()
+    qh, kh, vh = host(q), host(k), host(v)
+    ref = orc.forward(qh, kh, vh, block=w.block, alpha=alpha, gamma=gamma, sigma=sigma, rows=rows)
+    all_rows = np.arange(w.batch * w.n_q) if rows is None else rows
+    # Stage 0 in full
+    kb_ref = ref["kbar"]
+    kb = res["kbar"].cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(kb, kb_ref, rtol=1e-6, atol=1e-6)
+    # Stage 1
+    rep = parity.compare_stage1(flat_rows(res["mask"], all_rows), flat_rows(res["bias"], all_rows),
+                                flat_rows(res["tau"], all_rows), ref, n_kv=w.n_kv, block=w.block,
+                                h_kv=w.h_kv, q_pos=all_rows % w.n_q, alpha=alpha, sigma=sigma)
+    assert rep["rows_with_flips"] <= max(1, max_flip_frac * len(all_rows)), rep
+    # Stage 2 on the rows whose support matches
+    orep = parity.compare_output(flat_rows(res["o"], all_rows), ref["o"], w.dtype,
+                                 exclude_rows=rep["row_flip"], gpu_lse=flat_rows(res["lse"], all_rows),
+                                 ref_lse=ref["lse"], cond_row=rep["cond_row"],
+                                 vmax=float(v.abs().max()))
+    return rep, orep
+
+
+# ------------------------------------------------------------------------------ Stage 0
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n,hkv,d,block", [(1024, 1, 64, 64), (1000, 3, 128, 32), (333, 8, 128, 128),
+                                           (64, 2, 64, 64)])
+def test_pool_keys(dash, orc, dtype, n, hkv, d, block):
+    w = wl.Workload("pool", 2, n, hkv, hkv, d, block, 1.5, 1.0, 1.0, dtype=dtype, seed=21)
+    inp = wl.make_inputs(w, DEV)
+    kb = dash.dash_pool_keys(inp["k"], block)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(kb.cpu().numpy(), orc.pool_keys(host(inp["k"]), block), rtol=1e-6,
+                               atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pool_keys_learned_query(dash, orc, dtype):
+    w = wl.Workload("poolq", 2, 640, 4, 4, 128, 64, 1.5, 1.0, 1.0, dtype=dtype, seed=22)
+    inp = wl.make_inputs(w, DEV)
+    qbar = torch.randn(4, 128, generator=torch.Generator().manual_seed(5)) * 0.3
+    kb = dash.dash_pool_keys_query(inp["k"], qbar.to(DEV), 64)
+    torch.cuda.synchronize()
+    ref = orc.pool_keys_query(host(inp["k"]), qbar.double().numpy(), 64)
+    np.testing.assert_allclose(kb.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------------------ tiny fp32 workload, in full
+
+@pytest.mark.parametrize("gamma", [1.0, 8.0, 32.0])
+@pytest.mark.parametrize("sigma", [1.0, 10.0, 1e8])
+def test_tiny_fp32_alpha15(dash, orc, gamma, sigma):
+    run_and_compare(dash, orc, wl.TINY, 1.5, gamma, sigma)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 2.0])
+@pytest.mark.parametrize("gamma", [1.0, 8.0, 32.0])
+def test_tiny_fp32_other_alpha(dash, orc, alpha, gamma):
+    run_and_compare(dash, orc, wl.TINY, alpha, gamma, 10.0)
+
+
+def test_tiny_fp32_sigma_inf(dash, orc):
+    run_and_compare(dash, orc, wl.TINY, 1.5, 8.0, math.inf)
+
+
+# ------------------------------------------------------------- bf16, several tiles, ragged tail
+
+SMALL_BF16 = [
+    # batch, n, hq, hkv, d, block
+    (1, 2048, 8, 2, 128, 64),
+    (2, 2000, 8, 2, 128, 64),     # ragged tail chunk of 16 tokens
+    (1, 1536, 16, 1, 64, 32),     # group of 16
+    (1, 1100, 4, 4, 128, 128),    # group of 1, ragged
+    (1, 777, 4, 2, 64, 64),
+    (1, 40, 4, 2, 128, 64),       # shorter than one chunk: diagonal only
+    (1, 64, 2, 1, 128, 64),       # exactly one chunk
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_BF16)
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_small_bf16_planted(dash, orc, shape, alpha):
+    b, n, hq, hkv, d, block = shape
+    w = wl.Workload("small bf16", b, n, hq, hkv, d, block, alpha, 0.5, 1.0, plant="span",
+                    plant_args=dict(span=8, per_span=2), seed=31)
+    run_and_compare(dash, orc, w, alpha, 0.5 if alpha != 2.0 else 1.0, 1.0)
+
+
+@pytest.mark.parametrize("sigma", [1.0, 1e8, math.inf])
+def test_small_bf16_unplanted(dash, orc, sigma):
+    w = wl.Workload("small bf16 noise", 1, 1500, 8, 2, 128, 64, 1.5, 4.0, sigma, seed=32)
+    run_and_compare(dash, orc, w, 1.5, 4.0, sigma)
+
+
+def test_stage2_on_oracle_selection(dash, orc):
+    """Stage 2 alone: the GPU kernel fed with the oracle's own mask and bias matches the oracle
+    on every row (no near-threshold exclusions)."""
+    w = wl.Workload("stage2", 1, 1200, 8, 2, 128, 64, 1.5, 0.5, 1.0, plant="span",
+                    plant_args=dict(span=8, per_span=2), seed=33)
+    inp = wl.make_inputs(w, DEV)
+    qh, kh, vh = host(inp["q"]), host(inp["k"]), host(inp["v"])
+    ref = orc.forward(qh, kh, vh, block=w.block, alpha=1.5, gamma=0.5, sigma=1.0)
+    mask = torch.from_numpy(ref["mask"].view(np.int32)).reshape(1, w.n_q, w.h_kv, -1).to(DEV)
+    bias = torch.from_numpy(ref["bias"].astype(np.float32)).reshape(1, w.n_q, w.h_kv, -1).to(DEV)
+    o, lse = dash.dash_sparse_attn_prefill(inp["q"], inp["k"], inp["v"], mask, bias, block=w.block)
+    torch.cuda.synchronize()
+    parity.compare_output(parity.to_host(o)[0], ref["o"], "bf16", gpu_lse=parity.to_host(lse)[0],
+                          ref_lse=ref["lse"])
+
+
+# ------------------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("n_ctx,block", [(4096 + 17, 64), (3000, 32), (1024, 128)])
+def test_decode_small(dash, orc, n_ctx, block):
+    w = wl.Workload("decode small", 3, n_ctx, 8, 2, 128, block, 1.5, 1.5, 1.0, decode=True,
+                    plant="decode", plant_args=dict(lo=1, hi=8), seed=41)
+    inp = wl.make_inputs(w, DEV)
+    kbar = dash.dash_pool_keys(inp["k"], block)
+    o, mask, bias = dash.decode_step(inp["q"], inp["k"], inp["v"], kbar, block=block, alpha=1.5,
+                                     gamma=1.5, sigma=1.0)
+    torch.cuda.synchronize()
+    qh, kh, vh = host(inp["q"]), host(inp["k"]), host(inp["v"])
+    ref = orc.forward(qh, kh, vh, block=block, alpha=1.5, gamma=1.5, sigma=1.0, q_pos0=n_ctx - 1)
+    rows = np.arange(w.batch)
+    rep = parity.compare_stage1(flat_rows(mask, rows), flat_rows(bias, rows), None, ref, n_kv=n_ctx,
+                                block=block, h_kv=w.h_kv, q_pos=np.full(w.batch, n_ctx - 1),
+                                alpha=1.5, sigma=1.0)
+    parity.compare_output(flat_rows(o, rows), ref["o"], "bf16", exclude_rows=rep["row_flip"],
+                          cond_row=rep["cond_row"], vmax=float(inp["v"].abs().max()))
+
+
+# ------------------------------------------------------------------------------ properties
+
+def test_deterministic(dash):
+    w = wl.Workload("det", 1, 2048, 8, 2, 128, 64, 1.5, 0.5, 1.0, plant="span",
+                    plant_args=dict(span=8, per_span=2), seed=51)
+    inp = wl.make_inputs(w, DEV)
+    a = dash.forward(inp["q"], inp["k"], inp["v"], block=64, alpha=1.5, gamma=0.5, sigma=1.0)
+    b = dash.forward(inp["q"], inp["k"], inp["v"], block=64, alpha=1.5, gamma=0.5, sigma=1.0)
+    torch.cuda.synchronize()
+    for key in ("kbar", "mask", "tau", "o", "lse"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_errors_raise(dash):
+    q = torch.zeros(1, 64, 4, 96, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(dash.DashError, match="head_dim"):
+        dash.dash_pool_keys(q, 64)
+    k = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16, device=DEV)
+    kb = dash.dash_pool_keys(k, 64)
+    q = torch.zeros(1, 64, 4, 128, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(dash.DashError, match="alpha"):
+        dash.dash_block_entmax(q, kb, n_kv=64, block=64, alpha=2.5, gamma=1.0, sigma=1.0)
+    with pytest.raises(dash.DashError, match="DASH_ERR_WORKSPACE"):
+        m, bsz, _ = dash.dash_block_entmax(q, kb, n_kv=64, block=64, alpha=1.5, gamma=1.0, sigma=1.0)
+        dash.dash_sparse_attn_decode(q[:, :1], k, k, m[:, :1], bsz[:, :1], block=64,
+                                     workspace=torch.empty(1, dtype=torch.uint8, device=DEV))

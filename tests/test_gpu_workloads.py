@@ -1,0 +1,103 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times:
+the whole GPU pass runs at full size and sampled rows are checked against the oracle, which
+computes those rows one by one (Stage 0 in full, since every row depends on it)."""
+from __future__ import annotations
+
+import json
+import os
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests import parity
+from tests.test_gpu_parity import flat_rows, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def dash():
+    import sparse_hierarchical_attention_amd as d
+    d.lib()
+    return d
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def prefill_parity(dash, orc, w: wl.Workload, sigma: float, rows: np.ndarray):
+    log(f"{w.name}: generating inputs")
+    inp = wl.make_inputs(w, DEV)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    log("GPU forward")
+    res = dash.forward(q, k, v, block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=sigma)
+    torch.cuda.synchronize()
+    log(f"oracle on {len(rows)} rows")
+    ref = orc.forward(q.cpu(), k.cpu(), v.cpu(), block=w.block, alpha=w.alpha, gamma=w.gamma,
+                      sigma=sigma, rows=rows)
+    np.testing.assert_allclose(res["kbar"].cpu().numpy(), ref["kbar"], rtol=1e-6, atol=1e-6)
+    rep = parity.compare_stage1(flat_rows(res["mask"], rows), flat_rows(res["bias"], rows),
+                                flat_rows(res["tau"], rows), ref, n_kv=w.n_kv, block=w.block,
+                                h_kv=w.h_kv, q_pos=rows % w.n_q, alpha=w.alpha, sigma=sigma)
+    assert rep["rows_with_flips"] <= max(2, 0.02 * len(rows)), rep
+    out = parity.compare_output(flat_rows(res["o"], rows), ref["o"], w.dtype,
+                                exclude_rows=rep["row_flip"], gpu_lse=flat_rows(res["lse"], rows),
+                                ref_lse=ref["lse"], cond_row=rep["cond_row"],
+                                vmax=float(v.abs().max()))
+    log(f"support {rep['support_frac']:.4f} flips {rep['flips']} out {out}")
+    return rep, out
+
+
+@pytest.mark.parametrize("sigma", [1e8, 1.0])
+def test_prefill_32k(dash, orc, sigma):
+    w = wl.PREFILL_32K
+    prefill_parity(dash, orc, w, sigma, sample_rows(w.n_q, w.block, 160, seed=61))
+
+
+def _sweep_points():
+    with open(os.path.join(GOLDEN, "sweep_gamma.json")) as f:
+        return [(p["alpha"], p["block"], p["gamma"]) for p in json.load(f)["points"]]
+
+
+@pytest.mark.parametrize("alpha,block,gamma", _sweep_points())
+def test_sweep_16k(dash, orc, alpha, block, gamma):
+    w = wl.sweep_workload(alpha, block, gamma)
+    rep, _ = prefill_parity(dash, orc, w, 1.0, sample_rows(w.n_q, w.block, 64, seed=62))
+
+
+def test_prefill_256k(dash, orc):
+    w = wl.PREFILL_256K
+    prefill_parity(dash, orc, w, w.sigma, sample_rows(w.n_q, w.block, 48, seed=63))
+
+
+@pytest.mark.parametrize("sigma", [1e8, 1.0])
+def test_decode_128k(dash, orc, sigma):
+    w = wl.DECODE_128K
+    log(f"{w.name}: generating inputs")
+    inp = wl.make_inputs(w, DEV)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    kbar = dash.dash_pool_keys(k, w.block)
+    o, mask, bias = dash.decode_step(q, k, v, kbar, block=w.block, alpha=w.alpha, gamma=w.gamma,
+                                     sigma=sigma)
+    torch.cuda.synchronize()
+    for b in (0, 7, 15):  # the oracle regenerates nothing: it reads these sequences' inputs
+        log(f"oracle on sequence {b}")
+        ref = orc.forward(q[b:b + 1].cpu(), k[b:b + 1].cpu(), v[b:b + 1].cpu(), block=w.block,
+                          alpha=w.alpha, gamma=w.gamma, sigma=sigma, q_pos0=w.n_kv - 1)
+        np.testing.assert_allclose(kbar[b:b + 1].cpu().numpy(), ref["kbar"], rtol=1e-6, atol=1e-6)
+        rep = parity.compare_stage1(parity.to_host(mask[b]), parity.to_host(bias[b]), None, ref,
+                                    n_kv=w.n_kv, block=w.block, h_kv=w.h_kv,
+                                    q_pos=np.array([w.n_kv - 1]), alpha=w.alpha, sigma=sigma)
+        # the planted chunks are what the router finds
+        routed = parity.bits(ref["mask"], -(-w.n_kv // w.block))[0]
+        for r in range(w.h_kv):
+            sel = set(np.flatnonzero(routed[r][:-1]).tolist())
+            assert set(inp["planted"][b][r].tolist()) <= sel
+        parity.compare_output(parity.to_host(o[b]), ref["o"], "bf16", exclude_rows=rep["row_flip"],
+                              cond_row=rep["cond_row"], vmax=float(v[b].abs().max()))
