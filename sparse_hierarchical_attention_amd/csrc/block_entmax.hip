@@ -1,14 +1,17 @@
 // Stage 1: alpha-entmax chunk routing ("DashAttention", arXiv 2605.18753v1, §3.2 Eq. 4,
 // §3.4 Prop. 1; App. G Alg. 2).
 //
-// Two kernels. score_kernel computes the entmax arguments
+// Two kernels. A score kernel computes the entmax arguments
 //     x[b, t, h, c] = (alpha - 1) * gamma * <q_t^(h), kbar_c^(h / g)> / sqrt(D),   c < c_t
-// into a workspace; route_kernel then takes one (sequence, query, KV group) per wave, solves
-// each head's threshold tau on the row held in LDS, averages the group's probabilities and
-// writes the bit-packed mask and the bias.
+// into a workspace; a route kernel then solves each head's threshold tau on the row held in
+// LDS, averages the group's probabilities and writes the bit-packed mask and the bias.
+// Many queries: score_kernel (64 x 64 tiles) and route_kernel (one wave per query and group).
+// One query per sequence (decode): score_one_kernel (a coalesced stream over the summaries) and
+// route_group_kernel (one wave per head).
 #include <math.h>
 
 #include "common.h"
+#include "entmax.h"
 #include "kernels.h"
 
 namespace dash {
@@ -84,157 +87,215 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ q,
     }
 }
 
-// ----------------------------------------------------------------------------- tau
+// ----------------------------------------------------------------------------- one query per row
 
-// Exponent kinds of [x - tau]_+^(1/(alpha-1)): alpha = 2 -> 1, alpha = 1.5 -> 2, else general.
-enum { kPowGeneral = 0, kPowOne = 1, kPowTwo = 2 };
-
-struct PowE {
-    int kind;
-    float e;  // 1 / (alpha - 1)
-    __device__ __forceinline__ float val(float t) const {  // t^e, t > 0
-        if (kind == kPowOne) return t;
-        if (kind == kPowTwo) return t * t;
-        return exp2f(e * __log2f(t));
+// Scores of a single query per sequence (decode): a bandwidth-bound stream over the cached
+// summaries. A quad of lanes owns one chunk summary: lane k of the quad loads 16-byte pieces
+// k, k + 4, ... of the row (all of its loads in flight at once), forms partial dot products
+// with every head of the group (the group's queries sit in LDS and are read as broadcasts), and
+// two DPP steps sum the quad; lane k then writes heads k, k + 4, ....
+template <typename T, int D>
+__global__ __launch_bounds__(256) void score_one_kernel(const T* __restrict__ q,
+                                                        const float* __restrict__ kbar,
+                                                        float* __restrict__ x, RouteParams p,
+                                                        float coef) {
+    constexpr int NV = D / 16;  // float4 pieces per lane
+    __shared__ __align__(16) float qs[16 * D];
+    const int b = blockIdx.y / p.h_kv, r = blockIdx.y % p.h_kv;
+    const int m = min(p.q_pos0 / p.block, p.tc);  // complete chunks before the query's own
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x * 64 + tid / 4;
+    const int k = tid & 3;
+    for (int e = tid; e < p.g * D; e += 256) {
+        const int gg = e / D, d = e % D;
+        qs[gg * D + d] = to_f32(q[(((int64_t)b * p.n_q) * p.h_q + r * p.g + gg) * D + d]);
     }
-    __device__ __forceinline__ float der(float t) const {  // t^(e - 1), t > 0
-        if (kind == kPowOne) return 1.0f;
-        if (kind == kPowTwo) return t;
-        return exp2f((e - 1.0f) * __log2f(t));
-    }
-};
-
-// Threshold of one row x[0..m-1] (m >= 1) held in LDS, solved by the whole wave.
-// f(tau) = sum_c [x_c - tau]_+^e - 1 is decreasing and convex on tau < max x, with the root in
-// [max x - 1, max x - m^(1-alpha)]. Newton steps from the left end increase monotonically to
-// the root; a bisection step replaces any step that leaves the current bracket (rounding).
-// For alpha in {1.5, 2} the result is then polished with the closed form on its support.
-__device__ float solve_tau(const float* xs, int m, float alpha, const PowE& pw, int lane) {
-    float xmax = -INFINITY;
-    for (int c = lane; c < m; c += kWave) xmax = fmaxf(xmax, xs[c]);
-    xmax = wave_max(xmax);
-    if (m == 1) return xmax - 1.0f;
-    float lo = xmax - 1.0f;
-    float hi = xmax - exp2f((1.0f - alpha) * __log2f((float)m));
-    float tau = lo;
-    for (int it = 0; it < 64; ++it) {
-        float s = 0.f, ds = 0.f;
-        for (int c = lane; c < m; c += kWave) {
-            const float t = xs[c] - tau;
-            if (t > 0.f) {
-                s += pw.val(t);
-                ds += pw.der(t);
+    float4 kv[NV];
+    const float4* src = reinterpret_cast<const float4*>(kbar + (((int64_t)b * p.tc + min(c, p.tc - 1)) * p.h_kv + r) * D);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) kv[i] = src[k + 4 * i];
+    __syncthreads();
+    for (int g0 = 0; g0 < p.g; g0 += 4) {
+        float part[4];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+            const int gg = g0 + hh;
+            float a = 0.f;
+            if (gg < p.g) {
+                const float4* qv = reinterpret_cast<const float4*>(&qs[gg * D]);
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const float4 qq = qv[k + 4 * i];
+                    a = fmaf(kv[i].x, qq.x, a);
+                    a = fmaf(kv[i].y, qq.y, a);
+                    a = fmaf(kv[i].z, qq.z, a);
+                    a = fmaf(kv[i].w, qq.w, a);
+                }
             }
+            // sum over the quad: swap pairs, then halves
+            a += dpp_f<0xb1, 0xf>(0.f, a);
+            a += dpp_f<0x4e, 0xf>(0.f, a);
+            part[hh] = a;
         }
-        s = wave_sum(s);
-        ds = wave_sum(ds);
-        const float f = s - 1.0f;
-        if (f >= 0.f) lo = fmaxf(lo, tau); else hi = fminf(hi, tau);
-        float tn = ds > 0.f ? tau + f / (pw.e * ds) : 0.5f * (lo + hi);
-        if (!(tn >= lo && tn <= hi)) tn = 0.5f * (lo + hi);
-        const bool done = fabsf(tn - tau) <= 1e-7f * fmaxf(1.0f, fabsf(tau));
-        tau = tn;
-        if (done) break;
+        const int gg = g0 + k;
+        if (c < m && gg < p.g)
+            x[(((int64_t)b * p.n_q) * p.h_q + r * p.g + gg) * p.nc + c] = coef * part[k];
     }
-    if (pw.kind == kPowGeneral) return tau;
-    // closed form on the support S = {x > tau}: sum_S (x - tau)^e = 1 with e in {1, 2}
-    for (int rep = 0; rep < 3; ++rep) {
-        float s1 = 0.f;
-        int k = 0;
-        for (int c = lane; c < m; c += kWave)
-            if (xs[c] > tau) { s1 += xs[c]; ++k; }
-        s1 = wave_sum(s1);
-        k = wave_sum_int(k);
-        if (k == 0) break;
-        float tn;
-        if (pw.kind == kPowOne) {
-            tn = (s1 - 1.0f) / (float)k;
-        } else {
-            const float mean = s1 / (float)k;
-            float v = 0.f;
-            for (int c = lane; c < m; c += kWave)
-                if (xs[c] > tau) { const float dx = xs[c] - mean; v += dx * dx; }
-            v = wave_sum(v);
-            const float delta = (1.0f - v) / (float)k;  // (1 - k * variance) / k
-            if (delta < 0.f) break;
-            tn = mean - sqrtf(delta);
-        }
-        int k2 = 0;
-        for (int c = lane; c < m; c += kWave) k2 += xs[c] > tn;
-        k2 = wave_sum_int(k2);
-        if (!(tn >= lo - 1e-6f && tn <= hi + 1e-6f)) break;
-        tau = tn;
-        if (k2 == k) break;
-    }
-    return tau;
 }
 
-// One wave per (query t, KV group r, sequence b). Dynamic LDS: 2 * tc floats.
+// ----------------------------------------------------------------------------- routing
+
+// Mask words and bias of one (query, group) row from the group-averaged probabilities w held in
+// registers (chunk c in lane c % 64, slot c / 64): mu = mean log w over R = {c < m : w_c > 0},
+// d_c = (log w_c - mu) / sigma on R; the query's own chunk cp always gets its bit and d = 0.
+template <int NPL>
+__device__ __forceinline__ void write_route_row(const float (&w)[NPL], int m, int cp, int lane,
+                                                uint32_t* mrow, float* brow, const RouteParams& p) {
+    float sl = 0.f;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+        if (w[i] > 0.f) { sl += __logf(w[i]); ++cnt; }
+    sl = wave_sum(sl);
+    cnt = wave_sum_int(cnt);
+    const float mu = cnt > 0 ? sl / (float)cnt : 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        if (2 * i >= p.nw) break;
+        const int c = 64 * i + lane;
+        const bool sel = c < m && w[i] > 0.f;
+        if (sel) brow[c] = (__logf(w[i]) - mu) * p.inv_sigma;
+        const uint64_t bal = __ballot(sel || c == cp);
+        if (lane == 0) {
+            mrow[2 * i] = (uint32_t)bal;
+            if (2 * i + 1 < p.nw) mrow[2 * i + 1] = (uint32_t)(bal >> 32);
+        }
+    }
+    if (lane == 0) brow[cp] = 0.f;
+}
+
+// Many queries: one wave per (query t, group r, sequence b); the g heads in turn, each row read
+// once from the score workspace into registers, probabilities summed in registers.
+template <int NPL, int KIND>
 __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ x,
                                                    uint32_t* __restrict__ mask,
                                                    float* __restrict__ bias,
                                                    float* __restrict__ tau_out, RouteParams p) {
     const int t = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
-    extern __shared__ float lds[];
-    float* xs = lds;
-    float* ws = lds + p.tc;
     const int pos = p.q_pos0 + t;
     const int cp = pos / p.block;
     const int m = min(cp, p.tc);
     const int64_t qrow = (int64_t)b * p.n_q + t;
-
-    PowE pw;
-    pw.e = 1.0f / (p.alpha - 1.0f);
-    pw.kind = p.alpha == 2.0f ? kPowOne : (p.alpha == 1.5f ? kPowTwo : kPowGeneral);
-
-    for (int c = lane; c < m; c += kWave) ws[c] = 0.f;
+    const float e = 1.0f / (p.alpha - 1.0f);
+    float w[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) w[i] = 0.f;
     for (int gg = 0; gg < p.g; ++gg) {
         const int h = r * p.g + gg;
         const float* xr = x + (qrow * p.h_q + h) * p.nc;
-        for (int c = lane; c < m; c += kWave) xs[c] = xr[c];
-        __syncthreads();
+        float xv[NPL];
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const int c = 64 * i + lane;
+            xv[i] = c < m ? xr[c] : -INFINITY;
+        }
         float tau = INFINITY;
         if (m > 0) {
-            tau = solve_tau(xs, m, p.alpha, pw, lane);
-            for (int c = lane; c < m; c += kWave) {
-                const float d = xs[c] - tau;
-                if (d > 0.f) ws[c] += pw.val(d);
-            }
+            tau = solve_tau_reg<NPL, KIND>(xv, m, p.alpha);
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) w[i] += pow_e<KIND>(xv[i] - tau, e);
         }
         if (tau_out && lane == 0) tau_out[qrow * p.h_q + h] = tau;
-        __syncthreads();
     }
-    // GQA mean, routed set, mu = mean log w over it
     const float inv_g = 1.0f / (float)p.g;
-    float sl = 0.f;
-    int cnt = 0;
-    for (int c = lane; c < m; c += kWave) {
-        const float w = ws[c] * inv_g;
-        ws[c] = w;
-        if (w > 0.f) { sl += __logf(w); ++cnt; }
-    }
-    sl = wave_sum(sl);
-    cnt = wave_sum_int(cnt);
-    const float mu = cnt > 0 ? sl / (float)cnt : 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) w[i] *= inv_g;
+    write_route_row<NPL>(w, m, cp, lane, mask + (qrow * p.h_kv + r) * p.nw,
+                         bias + (qrow * p.h_kv + r) * p.nc, p);
+}
 
-    uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
-    float* brow = bias + (qrow * p.h_kv + r) * p.nc;
-    for (int base = 0; base < p.nw * 32; base += kWave) {
-        const int c = base + lane;
-        const bool sel = c < m && ws[c] > 0.f;
-        if (sel) brow[c] = (__logf(ws[c]) - mu) * p.inv_sigma;
-        const uint64_t bal = __ballot(sel || c == cp);
-        if (lane == 0) {
-            mrow[base / 32] = (uint32_t)bal;
-            if (base / 32 + 1 < p.nw) mrow[base / 32 + 1] = (uint32_t)(bal >> 32);
+// One query per sequence (decode): one wave per head solves its threshold; the probabilities
+// meet in LDS (g x 64 NPL floats) and wave 0 writes the row. Heads are added in order.
+template <int NPL, int KIND>
+__global__ __launch_bounds__(NPL >= 64 ? 256 : 1024) void route_group_kernel(const float* __restrict__ x,
+                                                           uint32_t* __restrict__ mask,
+                                                           float* __restrict__ bias,
+                                                           float* __restrict__ tau_out,
+                                                           RouteParams p) {
+    const int t = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    extern __shared__ float ps[];
+    const int pos = p.q_pos0 + t;
+    const int cp = pos / p.block;
+    const int m = min(cp, p.tc);
+    const int64_t qrow = (int64_t)b * p.n_q + t;
+    const float e = 1.0f / (p.alpha - 1.0f);
+    if (wave < p.g) {
+        const int h = r * p.g + wave;
+        const float* xr = x + (qrow * p.h_q + h) * p.nc;
+        float xv[NPL];
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const int c = 64 * i + lane;
+            xv[i] = c < m ? xr[c] : -INFINITY;
         }
+        float tau = INFINITY;
+        if (m > 0) tau = solve_tau_reg<NPL, KIND>(xv, m, p.alpha);
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) ps[(wave * NPL + i) * 64 + lane] = m > 0 ? pow_e<KIND>(xv[i] - tau, e) : 0.f;
+        if (tau_out && lane == 0) tau_out[qrow * p.h_q + h] = tau;
     }
-    if (lane == 0) brow[cp] = 0.f;
+    __syncthreads();
+    if (wave != 0) return;
+    const float inv_g = 1.0f / (float)p.g;
+    float w[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        float s = 0.f;
+        for (int gg = 0; gg < p.g; ++gg) s += ps[(gg * NPL + i) * 64 + lane];
+        w[i] = s * inv_g;
+    }
+    write_route_row<NPL>(w, m, cp, lane, mask + (qrow * p.h_kv + r) * p.nw,
+                         bias + (qrow * p.h_kv + r) * p.nc, p);
 }
 
 size_t route_workspace_bytes(const RouteParams& p) {
     return (size_t)p.batch * p.n_q * p.h_q * p.nc * sizeof(float);
+}
+
+template <int NPL>
+static void launch_route_npl(bool group, const float* x, uint32_t* mask, float* bias, float* tau,
+                             const RouteParams& p, hipStream_t st) {
+    const int kind = pow_kind(p.alpha);
+    if (group) {
+        const int threads = (p.g < 4 ? 4 : p.g) * kWave;
+        const size_t lds = (size_t)p.g * NPL * 64 * sizeof(float);
+        dim3 grid(p.n_q, p.h_kv, p.batch);
+#define DASH_RG(K) hipLaunchKernelGGL((route_group_kernel<NPL, K>), grid, dim3(threads), lds, st, \
+                                      x, mask, bias, tau, p)
+        if (kind == kPowOne) DASH_RG(kPowOne); else if (kind == kPowTwo) DASH_RG(kPowTwo); else DASH_RG(kPowGeneral);
+#undef DASH_RG
+    } else {
+        dim3 grid(p.n_q, p.h_kv, p.batch);
+#define DASH_RR(K) hipLaunchKernelGGL((route_kernel<NPL, K>), grid, dim3(64), 0, st, x, mask, bias, tau, p)
+        if (kind == kPowOne) DASH_RR(kPowOne); else if (kind == kPowTwo) DASH_RR(kPowTwo); else DASH_RR(kPowGeneral);
+#undef DASH_RR
+    }
+}
+
+static void launch_route(bool group, const float* x, uint32_t* mask, float* bias, float* tau,
+                         const RouteParams& p, hipStream_t st) {
+    switch (slots_for(p.nc)) {
+        case 1: launch_route_npl<1>(group, x, mask, bias, tau, p, st); break;
+        case 2: launch_route_npl<2>(group, x, mask, bias, tau, p, st); break;
+        case 4: launch_route_npl<4>(group, x, mask, bias, tau, p, st); break;
+        case 8: launch_route_npl<8>(group, x, mask, bias, tau, p, st); break;
+        case 16: launch_route_npl<16>(group, x, mask, bias, tau, p, st); break;
+        case 32: launch_route_npl<32>(group, x, mask, bias, tau, p, st); break;
+        case 64: launch_route_npl<64>(group, x, mask, bias, tau, p, st); break;
+        default: launch_route_npl<128>(group, x, mask, bias, tau, p, st); break;
+    }
 }
 
 hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const RouteParams& p,
@@ -242,23 +303,39 @@ hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const R
                                hipStream_t st) {
     float* x = static_cast<float*>(ws);
     const float coef = (p.alpha - 1.0f) * p.gamma / sqrtf((float)p.head_dim);
+    const size_t group_lds = (size_t)p.g * slots_for(p.nc) * 64 * sizeof(float);
+    const bool one = p.n_q == 1;
     if (p.tc > 0) {
-        dim3 grid(div_up(p.tc, kScoreTile), div_up(p.n_q * p.g, kScoreTile), p.batch * p.h_kv);
-#define DASH_SCORE(T, DD)                                                                    \
-        hipLaunchKernelGGL((score_kernel<T, DD>), grid, dim3(256), 0, st,                    \
-                           static_cast<const T*>(q), kbar, x, p, coef)
-        if (dt == kBF16) {
-            if (p.head_dim == 64) DASH_SCORE(bf16_t, 64); else DASH_SCORE(bf16_t, 128);
+        if (one) {
+            // one query per sequence: a coalesced stream over the summaries
+            dim3 grid(div_up(p.tc, 64), p.batch * p.h_kv);
+#define DASH_SCORE1(T, DD)                                                                 \
+            hipLaunchKernelGGL((score_one_kernel<T, DD>), grid, dim3(256), 0, st,          \
+                               static_cast<const T*>(q), kbar, x, p, coef)
+            if (dt == kBF16) {
+                if (p.head_dim == 64) DASH_SCORE1(bf16_t, 64); else DASH_SCORE1(bf16_t, 128);
+            } else {
+                if (p.head_dim == 64) DASH_SCORE1(float, 64); else DASH_SCORE1(float, 128);
+            }
+#undef DASH_SCORE1
         } else {
-            if (p.head_dim == 64) DASH_SCORE(float, 64); else DASH_SCORE(float, 128);
-        }
+            dim3 grid(div_up(p.tc, kScoreTile), div_up(p.n_q * p.g, kScoreTile), p.batch * p.h_kv);
+#define DASH_SCORE(T, DD)                                                                    \
+            hipLaunchKernelGGL((score_kernel<T, DD>), grid, dim3(256), 0, st,                    \
+                               static_cast<const T*>(q), kbar, x, p, coef)
+            if (dt == kBF16) {
+                if (p.head_dim == 64) DASH_SCORE(bf16_t, 64); else DASH_SCORE(bf16_t, 128);
+            } else {
+                if (p.head_dim == 64) DASH_SCORE(float, 64); else DASH_SCORE(float, 128);
+            }
 #undef DASH_SCORE
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const size_t lds = 2 * (size_t)(p.tc > 0 ? p.tc : 1) * sizeof(float);
-    hipLaunchKernelGGL(route_kernel, dim3(p.n_q, p.h_kv, p.batch), dim3(64), lds, st, x, mask,
-                       bias, tau, p);
+    // the per-head kernel runs up to 16 waves (64 slots and more: up to 4, for its registers)
+    const bool group = one && group_lds <= 128 * 1024 && (slots_for(p.nc) < 64 || p.g <= 4);
+    launch_route(group, x, mask, bias, tau, p, st);
     return hipGetLastError();
 }
 

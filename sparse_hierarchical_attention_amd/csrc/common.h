@@ -39,21 +39,48 @@ __device__ __forceinline__ void load8(const float* p, float (&out)[8]) {
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
-// Butterfly reductions over the 64 lanes of a wave; every lane gets the result.
+// Reductions over the 64 lanes of a wave with DPP (data-parallel primitives of the gfx9 ISA):
+// swaps within quads, mirrors within half-rows and rows of 16 lanes, then the row broadcasts
+// of lane 15 and lane 31 fold the four rows into lane 63, which every lane then reads.
+// DPP controls: quad_perm [1,0,3,2] = 0xb1, [2,3,0,1] = 0x4e, row_half_mirror = 0x141,
+// row_mirror = 0x140, row_bcast:15 = 0x142 (rows 1, 3), row_bcast:31 = 0x143 (rows 2, 3).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                  __builtin_bit_cast(int, v),
+                                                                  CTRL, ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+    v += dpp_f<0xb1, 0xf>(0.f, v);
+    v += dpp_f<0x4e, 0xf>(0.f, v);
+    v += dpp_f<0x141, 0xf>(0.f, v);
+    v += dpp_f<0x140, 0xf>(0.f, v);
+    v += dpp_f<0x142, 0xa>(0.f, v);
+    v += dpp_f<0x143, 0xc>(0.f, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+    v = fmaxf(v, dpp_f<0xb1, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<0x4e, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<0x141, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<0x140, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<0x142, 0xa>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<0x143, 0xc>(-INFINITY, v));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+    v += dpp_i<0xb1, 0xf>(0, v);
+    v += dpp_i<0x4e, 0xf>(0, v);
+    v += dpp_i<0x141, 0xf>(0, v);
+    v += dpp_i<0x140, 0xf>(0, v);
+    v += dpp_i<0x142, 0xa>(0, v);
+    v += dpp_i<0x143, 0xc>(0, v);
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 __host__ __device__ constexpr int div_up(int a, int b) { return (a + b - 1) / b; }

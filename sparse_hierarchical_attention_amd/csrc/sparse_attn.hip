@@ -1,7 +1,7 @@
 // Stage 2: prior-induced sparse softmax attention ("DashAttention", arXiv 2605.18753v1,
 // §3.3-3.4 Eq. 7-10 in the bias form of Prop. 1; App. G Alg. 3).
 //
-// attn_row_kernel is the fp32 path (and the decode path): one wave per (query, KV group), all g
+// attn_row_kernel is the fp32 prefill path: one wave per (query, KV group), all g
 // heads of the group at once, walking the set bits of the query's mask row chunk by chunk with
 // an online softmax. Lanes own keys for the scores and head dimensions for the value
 // accumulation. bf16 prefill runs on MFMA tiles (sparse_attn_mfma.hip).
@@ -145,21 +145,6 @@ hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, int 
                                const AttnParams& p, hipStream_t st) {
     if (dt == kBF16) return launch_attn_prefill_mfma(q, k, v, mask, bias, o, lse, p, st);
     launch_row_any(q, k, v, dt, mask, bias, o, lse, p, st);
-    return hipGetLastError();
-}
-
-constexpr int kDecodeSplits = 16;
-
-size_t decode_workspace_bytes(const AttnParams& p) {
-    const int splits = p.nc < kDecodeSplits ? p.nc : kDecodeSplits;
-    return (size_t)p.batch * p.h_kv * splits * p.g * (p.head_dim + 2) * sizeof(float);
-}
-
-hipError_t launch_attn_decode(const void* q, const void* k, const void* v, int dt,
-                              const uint32_t* mask, const float* bias, void* o,
-                              const AttnParams& p, void* ws, hipStream_t st) {
-    (void)ws;
-    launch_row_any(q, k, v, dt, mask, bias, o, nullptr, p, st);
     return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@ __device__ __forceinline__ int xcd_remap(int x, int bh, int* gr) {
 }
 
 template <int D, int BLK, int GQ>
-__global__ __launch_bounds__(kMfmaThreads) void attn_mfma_kernel(
+__global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const uint32_t* __restrict__ mask, const float* __restrict__ bias, bf16_t* __restrict__ o,
     float* __restrict__ lse, AttnParams p, int n_tiles) {
