@@ -156,6 +156,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one half of the step (for profiling); no JSON line is printed")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -180,16 +182,16 @@ def main():
     bias = torch.empty((1, wp.n_q, wp.h_kv, nc), dtype=torch.float32, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((1, wp.n_q, wp.h_q), dtype=torch.float32, device=dev)
-    ws_b = dash.dash_block_entmax_workspace_bytes(1, wp.n_q, 0, wp.n_kv, wp.h_q, wp.h_kv,
+    ws_b = dash.dash_block_entmax_workspace_bytes(q.dtype, 1, wp.n_q, 0, wp.n_kv, wp.h_q, wp.h_kv,
                                                   wp.head_dim, wp.block)
-    route_ws = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=dev)
+    route_ws = torch.empty(ws_b, dtype=torch.uint8, device=dev) if ws_b else None
     kbar_d = dash.dash_pool_keys(kd, wd.block)          # the decode cache's summaries
     ncd = -(-wd.n_kv // wd.block)
     mask_d = torch.empty((wd.batch, 1, wd.h_kv, -(-ncd // 32)), dtype=torch.int32, device=dev)
     bias_d = torch.empty((wd.batch, 1, wd.h_kv, ncd), dtype=torch.float32, device=dev)
     o_d = torch.empty_like(qd)
-    wsd_b = dash.dash_block_entmax_workspace_bytes(wd.batch, 1, wd.n_kv - 1, wd.n_kv, wd.h_q,
-                                                   wd.h_kv, wd.head_dim, wd.block)
+    wsd_b = dash.dash_block_entmax_workspace_bytes(qd.dtype, wd.batch, 1, wd.n_kv - 1, wd.n_kv,
+                                                   wd.h_q, wd.h_kv, wd.head_dim, wd.block)
     route_ws_d = torch.empty(max(wsd_b, 1), dtype=torch.uint8, device=dev)
     attn_ws_d = torch.empty(dash.dash_decode_workspace_bytes(wd.batch, wd.n_kv, wd.h_q, wd.h_kv,
                                                              wd.head_dim, wd.block),
@@ -198,6 +200,12 @@ def main():
     def step(timer: Timer | None):
         def ev(name):
             return timer.span(name) if timer else (None, None)
+        if args.only != "decode":
+            prefill_step(ev)
+        if args.only != "prefill":
+            decode_step(ev)
+
+    def prefill_step(ev):
         s, e = ev("pool")
         s and s.record()
         dash.dash_pool_keys(k, wp.block, kbar=kbar)
@@ -212,6 +220,8 @@ def main():
         s and s.record()
         dash.dash_sparse_attn_prefill(q, k, v, mask, bias, block=wp.block, o=o, lse=lse)
         e and e.record()
+
+    def decode_step(ev):
         s, e = ev("decode")
         s and s.record()
         dash.dash_block_entmax(qd, kbar_d, n_kv=wd.n_kv, block=wd.block, alpha=wd.alpha,
@@ -237,6 +247,9 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    if args.only:
+        print(f"[bench] {args.only} only: {ms_step:.3f} ms per step", file=sys.stderr, flush=True)
+        return
 
     pairs, frac = selected_pairs_prefill(mask, wp)
     flops = 4.0 * wp.head_dim * pairs

@@ -56,7 +56,7 @@ def lib():
         L.dash_version.restype = i
         L.dash_pool_keys.argtypes = [vp, i, vp, i, i, i, i, i, vp]
         L.dash_pool_keys_query.argtypes = [vp, i, vp, vp, i, i, i, i, i, vp]
-        L.dash_block_entmax_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+        L.dash_block_entmax_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
         L.dash_block_entmax_workspace_bytes.restype = sz
         L.dash_block_entmax.argtypes = [vp, i, vp, i, i, i, i, i, i, i, i, f, f, f, vp, vp, vp,
                                         vp, sz, vp]
@@ -135,8 +135,11 @@ def dash_pool_keys_query(k: torch.Tensor, qbar: torch.Tensor, block: int,
     return kbar
 
 
-def dash_block_entmax_workspace_bytes(batch, n_q, q_pos0, n_kv, h_q, h_kv, head_dim, block) -> int:
-    return int(lib().dash_block_entmax_workspace_bytes(batch, n_q, q_pos0, n_kv, h_q, h_kv,
+def dash_block_entmax_workspace_bytes(dtype, batch, n_q, q_pos0, n_kv, h_q, h_kv, head_dim,
+                                      block) -> int:
+    """Workspace bytes dash_block_entmax needs; dtype is a torch dtype (bf16 / fp32)."""
+    code = DASH_BF16 if dtype == torch.bfloat16 else DASH_F32
+    return int(lib().dash_block_entmax_workspace_bytes(code, batch, n_q, q_pos0, n_kv, h_q, h_kv,
                                                        head_dim, block))
 
 
@@ -159,7 +162,7 @@ def dash_block_entmax(q: torch.Tensor, kbar: torch.Tensor, *, n_kv: int, block: 
         bias = torch.empty((b, n_q, hkv, nc), dtype=torch.float32, device=dev)
     if tau is None and want_tau:
         tau = torch.empty((b, n_q, hq), dtype=torch.float32, device=dev)
-    need = dash_block_entmax_workspace_bytes(b, n_q, q_pos0, n_kv, hq, hkv, d, block)
+    need = dash_block_entmax_workspace_bytes(q.dtype, b, n_q, q_pos0, n_kv, hq, hkv, d, block)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()

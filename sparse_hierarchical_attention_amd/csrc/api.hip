@@ -118,12 +118,12 @@ dash_status_t dash_pool_keys_query(const void* k, dash_dtype_t dt, const float* 
                       "dash_pool_keys_query");
 }
 
-size_t dash_block_entmax_workspace_bytes(int batch, int n_q, int q_pos0, int n_kv, int h_q,
-                                         int h_kv, int head_dim, int block) {
+size_t dash_block_entmax_workspace_bytes(dash_dtype_t dt, int batch, int n_q, int q_pos0,
+                                         int n_kv, int h_q, int h_kv, int head_dim, int block) {
     if (batch <= 0 || n_q <= 0 || n_kv <= 0 || h_q <= 0 || h_kv <= 0 || block <= 0 || h_q % h_kv)
         return 0;
     return dash::route_workspace_bytes(route_params(batch, n_q, q_pos0, n_kv, h_q, h_kv, head_dim,
-                                                    block, 1.5f, 1.0f, 1.0f));
+                                                    block, 1.5f, 1.0f, 1.0f), (int)dt);
 }
 
 dash_status_t dash_block_entmax(const void* q, dash_dtype_t dt, const float* kbar, int batch,
@@ -144,7 +144,7 @@ dash_status_t dash_block_entmax(const void* q, dash_dtype_t dt, const float* kba
         return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
     dash::RouteParams p = route_params(batch, n_q, q_pos0, n_kv, h_q, h_kv, head_dim, block, alpha,
                                        gamma, sigma);
-    const size_t need = dash::route_workspace_bytes(p);
+    const size_t need = dash::route_workspace_bytes(p, (int)dt);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace ? workspace_bytes : (size_t)0);

@@ -5,7 +5,9 @@
 //     x[b, t, h, c] = (alpha - 1) * gamma * <q_t^(h), kbar_c^(h / g)> / sqrt(D),   c < c_t
 // into a workspace; a route kernel then solves each head's threshold tau on the row held in
 // LDS, averages the group's probabilities and writes the bit-packed mask and the bias.
-// Many queries: score_kernel (64 x 64 tiles) and route_kernel (one wave per query and group).
+// Many queries with bf16 inputs and up to 2048 chunks run in one pass instead (route_fused.hip).
+// Other many-query cases: score_kernel (64 x 64 tiles) and route_kernel (one wave per query and
+// group).
 // One query per sequence (decode): score_one_kernel (a coalesced stream over the summaries) and
 // route_group_kernel (one wave per head).
 #include <math.h>
@@ -13,6 +15,7 @@
 #include "common.h"
 #include "entmax.h"
 #include "kernels.h"
+#include "route_common.h"
 
 namespace dash {
 
@@ -145,35 +148,6 @@ __global__ __launch_bounds__(256) void score_one_kernel(const T* __restrict__ q,
 
 // ----------------------------------------------------------------------------- routing
 
-// Mask words and bias of one (query, group) row from the group-averaged probabilities w held in
-// registers (chunk c in lane c % 64, slot c / 64): mu = mean log w over R = {c < m : w_c > 0},
-// d_c = (log w_c - mu) / sigma on R; the query's own chunk cp always gets its bit and d = 0.
-template <int NPL>
-__device__ __forceinline__ void write_route_row(const float (&w)[NPL], int m, int cp, int lane,
-                                                uint32_t* mrow, float* brow, const RouteParams& p) {
-    float sl = 0.f;
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-        if (w[i] > 0.f) { sl += __logf(w[i]); ++cnt; }
-    sl = wave_sum(sl);
-    cnt = wave_sum_int(cnt);
-    const float mu = cnt > 0 ? sl / (float)cnt : 0.f;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        if (2 * i >= p.nw) break;
-        const int c = 64 * i + lane;
-        const bool sel = c < m && w[i] > 0.f;
-        if (sel) brow[c] = (__logf(w[i]) - mu) * p.inv_sigma;
-        const uint64_t bal = __ballot(sel || c == cp);
-        if (lane == 0) {
-            mrow[2 * i] = (uint32_t)bal;
-            if (2 * i + 1 < p.nw) mrow[2 * i + 1] = (uint32_t)(bal >> 32);
-        }
-    }
-    if (lane == 0) brow[cp] = 0.f;
-}
-
 // Many queries: one wave per (query t, group r, sequence b); the g heads in turn, each row read
 // once from the score workspace into registers, probabilities summed in registers.
 template <int NPL, int KIND>
@@ -193,13 +167,8 @@ __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ x,
     for (int i = 0; i < NPL; ++i) w[i] = 0.f;
     for (int gg = 0; gg < p.g; ++gg) {
         const int h = r * p.g + gg;
-        const float* xr = x + (qrow * p.h_q + h) * p.nc;
         float xv[NPL];
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            const int c = 64 * i + lane;
-            xv[i] = c < m ? xr[c] : -INFINITY;
-        }
+        load_row<NPL>(x + (qrow * p.h_q + h) * p.nc, m, lane, xv);
         float tau = INFINITY;
         if (m > 0) {
             tau = solve_tau_reg<NPL, KIND>(xv, m, p.alpha);
@@ -235,11 +204,7 @@ __global__ __launch_bounds__(NPL >= 64 ? 256 : 1024) void route_group_kernel(con
         const int h = r * p.g + wave;
         const float* xr = x + (qrow * p.h_q + h) * p.nc;
         float xv[NPL];
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            const int c = 64 * i + lane;
-            xv[i] = c < m ? xr[c] : -INFINITY;
-        }
+        load_row<NPL>(xr, m, lane, xv);
         float tau = INFINITY;
         if (m > 0) tau = solve_tau_reg<NPL, KIND>(xv, m, p.alpha);
 #pragma unroll
@@ -260,7 +225,8 @@ __global__ __launch_bounds__(NPL >= 64 ? 256 : 1024) void route_group_kernel(con
                          bias + (qrow * p.h_kv + r) * p.nc, p);
 }
 
-size_t route_workspace_bytes(const RouteParams& p) {
+size_t route_workspace_bytes(const RouteParams& p, int dt) {
+    if (route_fused_supported(p, dt)) return 0;  // scores stay on chip
     return (size_t)p.batch * p.n_q * p.h_q * p.nc * sizeof(float);
 }
 
@@ -301,6 +267,7 @@ static void launch_route(bool group, const float* x, uint32_t* mask, float* bias
 hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const RouteParams& p,
                                uint32_t* mask, float* bias, float* tau, void* ws,
                                hipStream_t st) {
+    if (route_fused_supported(p, dt)) return launch_route_fused(q, kbar, mask, bias, tau, p, st);
     float* x = static_cast<float*>(ws);
     const float coef = (p.alpha - 1.0f) * p.gamma / sqrtf((float)p.head_dim);
     const size_t group_lds = (size_t)p.g * slots_for(p.nc) * 64 * sizeof(float);

@@ -73,6 +73,15 @@ __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_f<0x143, 0xc>(-INFINITY, v));
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+__device__ __forceinline__ float wave_min(float v) {
+    v = fminf(v, dpp_f<0xb1, 0xf>(INFINITY, v));
+    v = fminf(v, dpp_f<0x4e, 0xf>(INFINITY, v));
+    v = fminf(v, dpp_f<0x141, 0xf>(INFINITY, v));
+    v = fminf(v, dpp_f<0x140, 0xf>(INFINITY, v));
+    v = fminf(v, dpp_f<0x142, 0xa>(INFINITY, v));
+    v = fminf(v, dpp_f<0x143, 0xc>(INFINITY, v));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 __device__ __forceinline__ int wave_sum_int(int v) {
     v += dpp_i<0xb1, 0xf>(0, v);
     v += dpp_i<0x4e, 0xf>(0, v);

@@ -159,19 +159,26 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     const int lane = threadIdx.x;
     const float* base = ws + (((int64_t)b * p.h_kv + r) * S * p.g + hh) * (D + 2);
     const int64_t split_stride = (int64_t)p.g * (D + 2);
+    // all partial maxima and sums first (independent loads), then the weighted outputs
+    float ms[kDecodeSplits], ls[kDecodeSplits];
     float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, base[s * split_stride + D]);
+#pragma unroll
+    for (int s = 0; s < kDecodeSplits; ++s) {
+        ms[s] = s < S ? base[s * split_stride + D] : -INFINITY;
+        ls[s] = s < S ? base[s * split_stride + D + 1] : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < kDecodeSplits; ++s) mx = fmaxf(mx, ms[s]);
     float l = 0.f, acc[DPL];
 #pragma unroll
     for (int dd = 0; dd < DPL; ++dd) acc[dd] = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float* part = base + s * split_stride;
-        const float ms = part[D];
-        if (ms == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(ms - mx);
-        l = fmaf(f, part[D + 1], l);
 #pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) acc[dd] = fmaf(f, part[lane + 64 * dd], acc[dd]);
+    for (int s = 0; s < kDecodeSplits; ++s) {
+        if (s >= S) break;
+        const float f = ms[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[s] - mx);
+        l = fmaf(f, ls[s], l);
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) acc[dd] = fmaf(f, base[s * split_stride + lane + 64 * dd], acc[dd]);
     }
     const float inv = 1.0f / l;
     T* orow = o + ((int64_t)b * p.h_q + h) * D;

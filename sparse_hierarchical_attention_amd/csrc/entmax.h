@@ -29,83 +29,137 @@ __device__ __forceinline__ float pow_e(float t, float e) {
     return t > 0.f ? exp2f(e * __log2f(t)) : 0.f;
 }
 
-// Threshold tau with sum_c [x_c - tau]_+^e = 1 for a row of m >= 1 entries.
+// ---- lane-group reductions. A "row" here is a DPP row of 16 lanes.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xb1, 0xf>(0.f, v);
+    v += dpp_f<0x4e, 0xf>(0.f, v);
+    v += dpp_f<0x141, 0xf>(0.f, v);
+    v += dpp_f<0x140, 0xf>(0.f, v);
+    return v;
+}
+__device__ __forceinline__ float row16_min(float v) {
+    v = fminf(v, dpp_f<0xb1, 0xf>(INFINITY, v));
+    v = fminf(v, dpp_f<0x4e, 0xf>(INFINITY, v));
+    v = fminf(v, dpp_f<0x141, 0xf>(INFINITY, v));
+    v = fminf(v, dpp_f<0x140, 0xf>(INFINITY, v));
+    return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<0xb1, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<0x4e, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<0x141, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<0x140, 0xf>(-INFINITY, v));
+    return v;
+}
+// Sums across the four 16-lane rows: partner lanes l ^ 16 and l ^ 32 through ds_bpermute.
+__device__ __forceinline__ float pair16_sum(float v) { return v + __shfl_xor(v, 16, 64); }
+__device__ __forceinline__ float pair32_sum(float v) { return v + __shfl_xor(v, 32, 64); }
+
+// Reductions over a lane group: a 16-lane DPP row, or the whole wave (common.h).
+template <int LANES> __device__ __forceinline__ float grp_sum(float v) {
+    return LANES == 64 ? wave_sum(v) : row16_sum(v);
+}
+template <int LANES> __device__ __forceinline__ float grp_min(float v) {
+    return LANES == 64 ? wave_min(v) : row16_min(v);
+}
+template <int LANES> __device__ __forceinline__ float grp_max(float v) {
+    return LANES == 64 ? wave_max(v) : row16_max(v);
+}
+
+// Threshold tau of a row held by a group of LANES lanes (16: one DPP row; 64: the wave), with
+// sum_c [x_c - tau]_+^e = 1 for its m >= 0 entries. Slot s of a lane holds entry
+// s * LANES + (lane % LANES); slots at or past ns (wave-uniform) are not visited and slots past
+// the row hold -inf. A row with m = 0 gets +inf.
+//
 // f(tau) = sum [x - tau]_+^e - 1 is decreasing and convex on tau < max x, with its root in
-// [max x - 1, max x - m^(1 - alpha)]. Newton steps from the left end increase monotonically to
-// the root; a step that leaves the bracket (rounding) is replaced by bisection. For e in {1, 2}
-// tau is then taken in closed form on its support S = {x > tau}: sum_S (x - tau)^e = 1.
-template <int NPL, int KIND>
-__device__ float solve_tau_reg(const float (&x)[NPL], int m, float alpha) {
+// [max x - 1, max x - m^(1 - alpha)]. Starting from the left end, each pass gathers over the
+// current support S = {x > tau}: its size k, sum of t = x - tau, sum of t^2 and smallest t.
+//   e = 2 (alpha = 1.5): sum_S (t - d)^2 = 1 has the root d = (Q - 1) / (P + sqrt(P^2 - k(Q - 1)))
+//   e = 1 (alpha = 2):   sum_S (t - d)   = 1 has the root d = (P - 1) / k
+// If d is below the smallest t, S is also the support at tau + d, which is then exact.
+// Otherwise a Newton step (tangent of the convex f, so it stays left of the root) moves tau
+// and the pass repeats; a step that leaves the bracket is replaced by bisection. For other
+// exponents only the Newton steps apply, until the step falls below fp32 resolution.
+template <int NS, int KIND, int LANES>
+__device__ float solve_tau_exact(const float (&x)[NS], int ns, int m, float alpha) {
     const float e = 1.0f / (alpha - 1.0f);
-    float xmax = -INFINITY;
+    float xm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) xmax = fmaxf(xmax, x[i]);
-    xmax = wave_max(xmax);
-    if (m == 1) return xmax - 1.0f;
-    float lo = xmax - 1.0f;
-    float hi = xmax - exp2f((1.0f - alpha) * __log2f((float)m));
-    float tau = lo;
+    for (int s = 0; s < NS; ++s)
+        if (s < ns) xm = fmaxf(xm, x[s]);
+    xm = grp_max<LANES>(xm);
+    float lo = xm - 1.0f;
+    float hi = m > 1 ? xm - exp2f((1.0f - alpha) * __log2f((float)m)) : lo;
+    float tau = m > 0 ? lo : INFINITY;
+    bool done = m <= 1;
     for (int it = 0; it < 64; ++it) {
-        float s = 0.f, ds = 0.f;
+        if (__all(done)) break;
+        const float tr = done ? INFINITY : tau;
+        float k = 0.f, p1 = 0.f, p2 = 0.f, tmin = INFINITY;
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            const float t = x[i] - tau;
-            if (KIND == kPowOne) {
-                s += fmaxf(t, 0.f);
-                ds += t > 0.f ? 1.f : 0.f;
-            } else if (KIND == kPowTwo) {
-                const float u = fmaxf(t, 0.f);
-                s = fmaf(u, u, s);
-                ds += u;
-            } else if (t > 0.f) {
-                const float lt = __log2f(t);
-                s += exp2f(e * lt);
-                ds += exp2f((e - 1.0f) * lt);
+        for (int s = 0; s < NS; ++s) {
+            if (s >= ns) break;
+            const float t = x[s] - tr;
+            const bool in = t > 0.f;
+            if (KIND == kPowGeneral) {
+                if (in) {
+                    const float lt = __log2f(t);
+                    p2 += exp2f(e * lt);           // sum t^e
+                    p1 += exp2f((e - 1.0f) * lt);  // sum t^(e-1)
+                }
+            } else {
+                const float u = in ? t : 0.f;
+                k += in ? 1.f : 0.f;
+                p1 += u;
+                if (KIND == kPowTwo) p2 = fmaf(u, u, p2);
+                tmin = in ? fminf(tmin, t) : tmin;
             }
         }
-        s = wave_sum(s);
-        ds = wave_sum(ds);
-        const float f = s - 1.0f;
-        if (f >= 0.f) lo = fmaxf(lo, tau); else hi = fminf(hi, tau);
-        float tn = ds > 0.f ? tau + f / (e * ds) : 0.5f * (lo + hi);
-        if (!(tn >= lo && tn <= hi)) tn = 0.5f * (lo + hi);
-        const bool done = fabsf(tn - tau) <= 1e-7f * fmaxf(1.0f, fabsf(tau));
-        tau = tn;
-        if (done) break;
-    }
-    if (KIND == kPowGeneral) return tau;
-    for (int rep = 0; rep < 3; ++rep) {
-        float s1 = 0.f;
-        int k = 0;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i)
-            if (x[i] > tau) { s1 += x[i]; ++k; }
-        s1 = wave_sum(s1);
-        k = wave_sum_int(k);
-        if (k == 0) break;
-        float tn;
-        if (KIND == kPowOne) {
-            tn = (s1 - 1.0f) / (float)k;
-        } else {
-            const float mean = s1 / (float)k;
-            float v = 0.f;
-#pragma unroll
-            for (int i = 0; i < NPL; ++i)
-                if (x[i] > tau) { const float dx = x[i] - mean; v = fmaf(dx, dx, v); }
-            v = wave_sum(v);
-            const float delta = (1.0f - v) / (float)k;  // (1 - k * variance) / k
-            if (delta < 0.f) break;
-            tn = mean - sqrtf(delta);
+        p1 = grp_sum<LANES>(p1);
+        if (KIND != kPowOne) p2 = grp_sum<LANES>(p2);
+        if (KIND != kPowGeneral) {
+            k = grp_sum<LANES>(k);
+            tmin = grp_min<LANES>(tmin);
         }
-        int k2 = 0;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) k2 += x[i] > tn ? 1 : 0;
-        k2 = wave_sum_int(k2);
-        if (!(tn >= lo - 1e-6f * fmaxf(1.0f, fabsf(lo)) && tn <= hi + 1e-6f * fmaxf(1.0f, fabsf(hi)))) break;
+        if (done) continue;
+        float f, tn;
+        if (KIND == kPowTwo) {
+            f = p2 - 1.0f;
+            const float disc = p1 * p1 - k * f;
+            if (f >= 0.f && k > 0.f && disc >= 0.f) {
+                const float d = f / (p1 + sqrtf(disc));
+                if (d < tmin) {
+                    tau += d;
+                    done = true;
+                    continue;
+                }
+            }
+            tn = p1 > 0.f ? tau + f / (2.0f * p1) : 0.5f * (lo + hi);
+        } else if (KIND == kPowOne) {
+            f = p1 - 1.0f;
+            const float d = k > 0.f ? f / k : 0.f;
+            if (f >= 0.f && k > 0.f && d < tmin) {
+                tau += d;
+                done = true;
+                continue;
+            }
+            tn = k > 0.f ? tau + d : 0.5f * (lo + hi);
+        } else {
+            f = p2 - 1.0f;
+            tn = p1 > 0.f ? tau + f / (e * p1) : 0.5f * (lo + hi);
+        }
+        if (f >= 0.f) lo = fmaxf(lo, tau); else hi = fminf(hi, tau);
+        if (!(tn >= lo && tn <= hi)) tn = 0.5f * (lo + hi);
+        done = fabsf(tn - tau) <= 1e-7f * fmaxf(1.0f, fabsf(tau));
         tau = tn;
-        if (k2 == k) break;
     }
     return tau;
+}
+
+// One row over the whole wave (64 lanes, slot s holds entry 64 s + lane).
+template <int NPL, int KIND>
+__device__ __forceinline__ float solve_tau_reg(const float (&x)[NPL], int m, float alpha) {
+    return solve_tau_exact<NPL, KIND, 64>(x, (m + 63) / 64, m, alpha);
 }
 
 // Smallest slot count NPL (a power of two) with 64 * NPL >= n.

@@ -22,7 +22,10 @@ struct RouteParams {
     int batch, n_q, q_pos0, n_kv, h_q, h_kv, g, head_dim, block, tc, nc, nw;
     float alpha, gamma, inv_sigma;
 };
-size_t route_workspace_bytes(const RouteParams& p);
+size_t route_workspace_bytes(const RouteParams& p, int dt);
+bool route_fused_supported(const RouteParams& p, int dt);
+hipError_t launch_route_fused(const void* q, const float* kbar, uint32_t* mask, float* bias,
+                              float* tau, const RouteParams& p, hipStream_t st);
 hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const RouteParams& p,
                                uint32_t* mask, float* bias, float* tau, void* ws,
                                hipStream_t st);

@@ -1,0 +1,265 @@
+// Stage 1 for many queries in one pass, without a score workspace ("DashAttention",
+// arXiv 2605.18753v1, §3.2 Eq. 4, §3.4 Prop. 1; App. G Alg. 2 with the score rows kept on chip).
+//
+// A workgroup of NW waves owns 32 query rows of one (sequence b, KV group r): T = 32 / g
+// consecutive tokens times the g heads of the group (row = token * g + head).
+// Phase 1, scores: X^T = Kbar Q^T on v_mfma_f32_32x32x16_bf16. The fp32 summaries are split as
+// kbar = hi + mid + lo, each a bf16 (hi = bf16(kbar), mid = bf16(kbar - hi), lo = bf16 of the
+// rest), so three bf16 products carry about 24 mantissa bits of the summary (Q is bf16 already)
+// with fp32 accumulation. Wave w computes the 32-chunk tiles w, w + NW, ... of all rows.
+// The score rows then go through LDS (row-major, odd stride) so that one wave can own a token.
+// Phase 2: per token, the same register-resident threshold solver and row writer as the
+// workspace path (entmax.h, route_common.h): the g heads in turn, the GQA mean, mask and bias.
+#include <math.h>
+
+#include "common.h"
+#include "entmax.h"
+#include "kernels.h"
+#include "route_common.h"
+
+namespace dash {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int D, int GQ, int MT, int NW, int KIND>
+__global__ __launch_bounds__(NW * 64) void route_fused_kernel(
+    const bf16_t* __restrict__ q, const float* __restrict__ kbar, uint32_t* __restrict__ mask,
+    float* __restrict__ bias, float* __restrict__ tau_out, RouteParams p, int n_tiles,
+    float coef) {
+    constexpr int ROWS = 32;                 // one MFMA N-tile of query rows
+    constexpr int T = ROWS / GQ;             // tokens per workgroup
+    constexpr int CMAX = 32 * NW * MT;       // chunks the workgroup can hold
+    constexpr int NPL = CMAX / 64;           // row slots per lane when a wave owns a row
+    constexpr int XS = CMAX + 17;            // LDS row stride of the scores (bank spread for the
+                                             // MFMA-layout writes and the 16-lane-group reads)
+    constexpr int QS = D + 8;                // LDS row stride of Q (elements)
+    static_assert(NPL >= 1, "at least one slot");
+    // Q (phase 1) and the score rows (phase 2) share the LDS
+    __shared__ __align__(16) float lds[ROWS * XS > (ROWS * QS) / 2 ? ROWS * XS : (ROWS * QS) / 2];
+    bf16_t* qs = reinterpret_cast<bf16_t*>(lds);
+    float* xs = lds;
+
+    const int bh = p.batch * p.h_kv;
+    const int x = blockIdx.x;
+    const int gr = bh % 8 == 0 ? (x % 8) + 8 * ((x / 8) % (bh / 8)) : x % bh;
+    const int tile = n_tiles - 1 - x / bh;
+    const int b = gr / p.h_kv, r = gr % p.h_kv;
+    const int tile0 = tile * T;
+    const int tile_end = min(tile0 + T, p.n_q);
+    const int m_max = min((p.q_pos0 + tile_end - 1) / p.block, p.tc);
+    const int n_ct = div_up(m_max, 32);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 31, G = lane >> 5;
+
+    // ---- phase 1: scores X^T = kbar Q^T on MFMA, kbar = hi + mid + lo in bf16
+    for (int idx = tid; idx < ROWS * (D / 8); idx += NW * 64) {
+        const int row = idx / (D / 8), d8 = idx % (D / 8);
+        const int t = tile0 + row / GQ;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (t < p.n_q)
+            u = *reinterpret_cast<const uint4*>(
+                q + (((int64_t)b * p.n_q + t) * p.h_q + r * GQ + row % GQ) * D + 8 * d8);
+        *reinterpret_cast<uint4*>(&qs[row * QS + 8 * d8]) = u;
+    }
+    __syncthreads();
+    f32x16_t X[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) X[mt] = f32x16_t{};
+    const float* kb_base = kbar + ((int64_t)b * p.tc * p.h_kv + r) * D;
+    // summary rows of this lane's chunk in each tile; the 16-d slice ks + 1 is in flight while
+    // slice ks is split and multiplied
+    const float4* src[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int c = min(32 * (wave + NW * mt) + j, p.tc - 1);
+        src[mt] = reinterpret_cast<const float4*>(kb_base + (int64_t)c * p.h_kv * D + 8 * G);
+    }
+    float4 cur[MT][2], nxt[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        if (wave + NW * mt < n_ct) { cur[mt][0] = src[mt][0]; cur[mt][1] = src[mt][1]; }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        if (ks + 1 < D / 16) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                if (wave + NW * mt < n_ct) {
+                    nxt[mt][0] = src[mt][4 * (ks + 1)];
+                    nxt[mt][1] = src[mt][4 * (ks + 1) + 1];
+                }
+        }
+        const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(&qs[j * QS + 16 * ks + 8 * G]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (wave + NW * mt >= n_ct) break;
+            const float4 v0 = cur[mt][0], v1 = cur[mt][1];
+            const float kv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            bf16x8_t hi, mid, lo;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const __bf16 h = (__bf16)kv[u];
+                const float r1 = kv[u] - (float)h;
+                const __bf16 md = (__bf16)r1;
+                hi[u] = h;
+                mid[u] = md;
+                lo[u] = (__bf16)(r1 - (float)md);
+            }
+            X[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, qf, X[mt], 0, 0, 0);
+            X[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, qf, X[mt], 0, 0, 0);
+            X[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, qf, X[mt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) { cur[mt][0] = nxt[mt][0]; cur[mt][1] = nxt[mt][1]; }
+    }
+    __syncthreads();  // Q is dead; its LDS now takes the score rows
+    // lane (j, G) holds row j, chunks 32 ct + 8 (rr / 4) + 4 G + rr % 4
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int ct = wave + NW * mt;
+        if (ct >= n_ct) break;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            xs[j * XS + 32 * ct + 8 * (rr >> 2) + 4 * G + (rr & 3)] = coef * X[mt][rr];
+    }
+    __syncthreads();
+
+    // ---- phase 2: a wave takes 4 rows at a time, one per 16-lane DPP row (lane group); entry c
+    // of a row sits in lane c % 16 of its group, slot c / 16. A unit is one token when g >= 4
+    // (its heads in g / 4 passes of 4) or 4 / g tokens when g < 4 (one pass).
+    constexpr int NS = CMAX / 16;
+    constexpr int PASSES = GQ >= 4 ? GQ / 4 : 1;        // passes per unit
+    constexpr int UROWS = 4 * PASSES;                  // rows per unit
+    constexpr int UNITS = ROWS / UROWS;
+    const float e = 1.0f / (p.alpha - 1.0f);
+    const float inv_g = 1.0f / (float)GQ;
+    const int grp = lane >> 4, li = lane & 15;
+    for (int u = wave; u < UNITS; u += NW) {
+        const int row0 = u * UROWS;
+        // this lane group's token (for g < 4 the groups hold different tokens)
+        const int my_row_first = row0 + grp;                  // row of this group in pass 0
+        const int my_tok = (GQ >= 4 ? row0 : my_row_first) / GQ;
+        const int tok = tile0 + my_tok;
+        const bool tvalid = tok < p.n_q;
+        const int pos = p.q_pos0 + tok;
+        const int cp = pos / p.block;
+        const int m = tvalid ? min(cp, p.tc) : 0;
+        // slots to visit: the unit's last token has the most candidates
+        const int last_tok = min(tile0 + (row0 + UROWS - 1) / GQ, p.n_q - 1);
+        const int ns = div_up(min((p.q_pos0 + last_tok) / p.block, p.tc), 16);
+        float wsum[NS];
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) wsum[sl] = 0.f;
+#pragma unroll 1
+        for (int ps = 0; ps < PASSES; ++ps) {
+            const int row = row0 + 4 * ps + grp;
+            const float* xr = xs + row * XS;
+            float xv[NS];
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                xv[sl] = -INFINITY;
+                if (sl >= ns) continue;
+                const int c = 16 * sl + li;
+                const float v = xr[c];
+                xv[sl] = c < m ? v : -INFINITY;
+            }
+            const float tau = solve_tau_exact<NS, KIND, 16>(xv, ns, m, p.alpha);
+            if (tau_out && tvalid && li == 0)
+                tau_out[((int64_t)b * p.n_q + tok) * p.h_q + r * GQ + row % GQ] = tau;
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                if (sl >= ns) break;
+                float pv = pow_e<KIND>(xv[sl] - tau, e);
+                if (GQ >= 2) pv = pair16_sum(pv);   // heads in groups 0+1 and 2+3
+                if (GQ >= 4) pv = pair32_sum(pv);   // all four groups
+                wsum[sl] += pv;
+            }
+        }
+        // GQA mean and mu for this group's token (every lane of the group holds the same row)
+        float lsum = 0.f, lcnt = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            if (sl >= ns) break;
+            wsum[sl] *= inv_g;
+            if (wsum[sl] > 0.f) { lsum += __logf(wsum[sl]); lcnt += 1.f; }
+        }
+        lsum = row16_sum(lsum);
+        lcnt = row16_sum(lcnt);
+        const float mu = lcnt > 0.f ? lsum / lcnt : 0.f;
+        // the groups that write: one per token of the unit
+        const bool writer = GQ >= 4 ? grp == 0 : (GQ == 2 ? (grp & 1) == 0 : true);
+        const int64_t qrow = (int64_t)b * p.n_q + tok;
+        uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
+        float* brow = bias + (qrow * p.h_kv + r) * p.nc;
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+            if (sl >= ns) break;
+            const int c = 16 * sl + li;
+            if (writer && tvalid && wsum[sl] > 0.f) brow[c] = (__logf(wsum[sl]) - mu) * p.inv_sigma;
+        }
+#pragma unroll
+        for (int wd = 0; wd < NS / 2; ++wd) {
+            if (wd >= p.nw) break;
+            const uint64_t b0 = 2 * wd < ns ? __ballot(wsum[2 * wd] > 0.f) : 0ull;
+            const uint64_t b1 = 2 * wd + 1 < ns ? __ballot(wsum[2 * wd + 1] > 0.f) : 0ull;
+            if (writer && tvalid && li == 0) {
+                uint32_t word = (uint32_t)((b0 >> (16 * grp)) & 0xffffu) |
+                                ((uint32_t)((b1 >> (16 * grp)) & 0xffffu) << 16);
+                if (cp / 32 == wd) word |= 1u << (cp % 32);
+                mrow[wd] = word;
+            }
+        }
+        if (writer && tvalid && li == 0) brow[cp] = 0.f;
+    }
+}
+
+// (MT, NW) with NW * MT * 32 >= tc chunks: up to 512 in 4 waves, up to 1024 in 8 waves
+bool route_fused_supported(const RouteParams& p, int dt) {
+    return dt == kBF16 && p.tc <= 1024 && p.n_q > 1 && p.nw <= 2 * (p.tc <= 512 ? 8 : 16);
+}
+
+template <int D, int GQ, int MT, int NW>
+static void launch_fused_shape(const void* q, const float* kbar, uint32_t* mask, float* bias,
+                               float* tau, const RouteParams& p, float coef, hipStream_t st) {
+    constexpr int T = 32 / GQ;
+    const int n_tiles = div_up(p.n_q, T);
+    dim3 grid(p.batch * p.h_kv * n_tiles), block(NW * 64);
+    const int kind = pow_kind(p.alpha);
+#define DASH_FUSED(K)                                                                        \
+    hipLaunchKernelGGL((route_fused_kernel<D, GQ, MT, NW, K>), grid, block, 0, st,          \
+                       static_cast<const bf16_t*>(q), kbar, mask, bias, tau, p, n_tiles, coef)
+    if (kind == kPowOne) DASH_FUSED(kPowOne);
+    else if (kind == kPowTwo) DASH_FUSED(kPowTwo);
+    else DASH_FUSED(kPowGeneral);
+#undef DASH_FUSED
+}
+
+template <int D, int GQ>
+static void launch_fused_g(const void* q, const float* kbar, uint32_t* mask, float* bias,
+                           float* tau, const RouteParams& p, float coef, hipStream_t st) {
+    if (p.tc <= 512) launch_fused_shape<D, GQ, 4, 4>(q, kbar, mask, bias, tau, p, coef, st);
+    else launch_fused_shape<D, GQ, 4, 8>(q, kbar, mask, bias, tau, p, coef, st);
+}
+
+template <int D>
+static void launch_fused_d(const void* q, const float* kbar, uint32_t* mask, float* bias,
+                           float* tau, const RouteParams& p, float coef, hipStream_t st) {
+    switch (p.g) {
+        case 1: launch_fused_g<D, 1>(q, kbar, mask, bias, tau, p, coef, st); break;
+        case 2: launch_fused_g<D, 2>(q, kbar, mask, bias, tau, p, coef, st); break;
+        case 4: launch_fused_g<D, 4>(q, kbar, mask, bias, tau, p, coef, st); break;
+        case 8: launch_fused_g<D, 8>(q, kbar, mask, bias, tau, p, coef, st); break;
+        default: launch_fused_g<D, 16>(q, kbar, mask, bias, tau, p, coef, st); break;
+    }
+}
+
+hipError_t launch_route_fused(const void* q, const float* kbar, uint32_t* mask, float* bias,
+                              float* tau, const RouteParams& p, hipStream_t st) {
+    const float coef = (p.alpha - 1.0f) * p.gamma / sqrtf((float)p.head_dim);
+    if (p.head_dim == 64) launch_fused_d<64>(q, kbar, mask, bias, tau, p, coef, st);
+    else launch_fused_d<128>(q, kbar, mask, bias, tau, p, coef, st);
+    return hipGetLastError();
+}
+
+}  // namespace dash

@@ -77,9 +77,13 @@ def test_block_entmax_rejects_bad_arguments(L):
     assert call(h_q=64, h_kv=2) == 2 and "group" in err(L)
     assert call(q_pos0=1) == 1 and "q_pos0" in err(L)
     assert call(mask=None) == 1 and "null" in err(L)
-    need = L.dash_block_entmax_workspace_bytes(1, 64, 0, 64, 4, 2, 128, 64)
-    if need:
-        assert call(wsb=need - 1) == 3 and "workspace" in err(L)
+    need = L.dash_block_entmax_workspace_bytes(1, 1, 64, 0, 64, 4, 2, 128, 64)
+    assert need == 0  # bf16 prefill routes on chip
+    need = L.dash_block_entmax_workspace_bytes(0, 1, 64, 0, 64, 4, 2, 128, 64)
+    assert need == 64 * 4 * 1 * 4  # fp32 scores through the workspace
+    assert call(dt=0, wsb=need - 1) == 3 and "workspace" in err(L)
+    need = L.dash_block_entmax_workspace_bytes(1, 2, 1, 4095, 4096, 8, 2, 128, 64)
+    assert need == 2 * 8 * 64 * 4  # decode scores through the workspace
 
 
 def test_attention_rejects_bad_arguments(L):
