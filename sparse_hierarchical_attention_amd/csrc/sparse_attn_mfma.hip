@@ -5,19 +5,22 @@
 // consecutive tokens times the g heads of the group, row = token * g + head. All rows share the
 // group's chunk selection per token, so the workgroup walks the union of its tokens' selected
 // chunks (their own diagonal chunks included) and masks, per row, the chunks its token did not
-// select. Each chunk is staged through LDS in sub-tiles of up to 64 keys: K as stored, V
-// transposed, both read by all four waves.
+// select. Chunks are cut into tiles of up to 64 keys; K and V tiles are staged through LDS in
+// their stored layout, double-buffered: the next tile's global loads are in flight while the
+// current one is multiplied, and one barrier per tile hands the buffers over.
 //
-// Per wave (32 rows) and sub-tile, with v_mfma_f32_32x32x16_bf16:
-//   S^T = K Q^T   A = K rows from LDS, B = the wave's Q rows held in registers for the whole
-//                 kernel; the accumulator gives lane l the column l % 32 (its query row) and
-//                 16 keys, so a row's maximum and sum need one exchange with lane l ^ 32.
-//   O^T += V^T P^T  B = P straight from the S accumulator registers (converted to bf16): the
-//                 k-slots of a lane are its own 8 keys, and A = V^T is read from LDS in the
-//                 same key order, so P never moves between lanes.
-// Logits live in the log2 domain: x = s * scale * log2(e) + d * log2(e), online softmax with
-// exp2. A row whose token did not select the chunk gets x = -inf; the query's own chunk is
-// causally masked.
+// Per wave (32 rows) and tile, with v_mfma_f32_32x32x16_bf16:
+//   S^T = K Q^T   A = K rows (ds_read_b128), B = the wave's Q rows held in registers for the
+//                 whole kernel; lane l of the accumulator holds query row l % 32 and 16 keys.
+//   O^T += V^T P^T  B = P straight from the S accumulator (converted to bf16), A = V^T read with
+//                 ds_read_b64_tr_b16: inside each 16-lane group the four 64-bit loads of lanes
+//                 4v .. 4v + 3 form key v, and lane i receives dimension i of keys 0..3, which
+//                 is the run of four keys the lane's P slots refer to.
+// Softmax in the log2 domain: x = s * scale * log2(e) + d * log2(e). The running maximum m is
+// only raised when a tile's maximum exceeds it by more than 8 (so exp2(x - m) <= 256 and the
+// output, normalised by the sum taken against the same m, is unchanged); p = exp2(x - m) is a
+// single FMA and exp2 per score. A row whose token did not select the chunk has x = -inf; the
+// query's own chunk is causally masked.
 #include <math.h>
 
 #include "common.h"
@@ -27,6 +30,7 @@ namespace dash {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMfmaRows = 128;
@@ -34,17 +38,13 @@ constexpr int kMfmaThreads = 256;
 constexpr int kMaxMaskWords = 256;  // 8192 chunks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.0f;    // log2 headroom before the running maximum is raised
 
-__device__ __forceinline__ int xcd_remap(int x, int bh, int* gr) {
-    // Workgroups are dispatched round-robin over the 8 XCDs (x % 8). When the (sequence, group)
-    // pairs split evenly over them, keep every tile of a pair on one XCD so its K/V chunks stay
-    // in that XCD's L2; tile ranks count up, so the longest (last) tiles start first.
-    if (bh % 8 == 0) {
-        *gr = (x % 8) + 8 * ((x / 8) % (bh / 8));
-    } else {
-        *gr = x % bh;
-    }
-    return x / bh;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ i16x4 ds_read_tr16(const bf16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(__attribute__((address_space(3))) void*)(p));
 }
 
 template <int D, int BLK, int GQ>
@@ -53,24 +53,30 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
     const uint32_t* __restrict__ mask, const float* __restrict__ bias, bf16_t* __restrict__ o,
     float* __restrict__ lse, AttnParams p, int n_tiles) {
     constexpr int T = kMfmaRows / GQ;        // tokens per tile
-    constexpr int KT = BLK < 64 ? BLK : 64;  // keys per LDS sub-tile
+    constexpr int KT = BLK < 64 ? BLK : 64;  // keys per LDS tile
     constexpr int NSUB = BLK / KT;
     constexpr int KS = D + 8;                // K row stride in LDS (elements)
-    constexpr int VS = KT + 4;               // V^T row stride in LDS (elements)
+    constexpr int VS = D + 16;               // V row stride in LDS (elements)
     constexpr int MT = KT / 32;              // 32-key M-tiles of S^T
     constexpr int KSTEP = KT / 16;           // 16-key k-steps of P V
     constexpr int DT = D / 32;               // 32-dim M-tiles of O^T
-    __shared__ __align__(16) bf16_t Ks[KT * KS];
-    __shared__ __align__(16) bf16_t Vt[D * VS];
+    constexpr int LOADS = KT * (D / 8) / kMfmaThreads;  // 16-byte loads per thread and tensor
+    static_assert(LOADS >= 1, "tile too small");
+    __shared__ __align__(16) bf16_t Ks[2][KT * KS];
+    __shared__ __align__(16) bf16_t Vs[2][KT * VS];
     __shared__ uint32_t uni[kMaxMaskWords];
 
     int gr;
-    const int tile = n_tiles - 1 - xcd_remap(blockIdx.x, p.batch * p.h_kv, &gr);
+    {
+        const int bh = p.batch * p.h_kv, x = blockIdx.x;
+        gr = bh % 8 == 0 ? (x % 8) + 8 * ((x / 8) % (bh / 8)) : x % bh;
+    }
+    const int tile = n_tiles - 1 - blockIdx.x / (p.batch * p.h_kv);
     const int b = gr / p.h_kv, r = gr % p.h_kv;
     const int n = p.n_kv;
     const int tile0 = tile * T;
     const int tile_end = min(tile0 + T, n);
-    const int c_last = (tile_end - 1) / BLK;
+    const int c_first = tile0 / BLK, c_last = (tile_end - 1) / BLK;
     const int nwt = c_last / 32 + 1;
 
     const int tid = threadIdx.x;
@@ -99,6 +105,18 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
         if (hi < 32) word |= 1u << hi;
         if (word) atomicOr(&uni[w], word);
     }
+    __syncthreads();
+    // the union's next chunk after c (-1 when none): the same walk in every thread
+    auto next_chunk = [&](int c) -> int {
+        int w = (c + 1) >> 5;
+        if (w >= nwt) return -1;
+        uint32_t word = uni[w] & (~0u << ((c + 1) & 31));
+        while (true) {
+            if (word) return 32 * w + __builtin_ctz(word);
+            if (++w >= nwt) return -1;
+            word = uni[w];
+        }
+    };
 
     // this wave's Q rows as the B operand of S^T = K Q^T (k-slot order shared with K's reads)
     bf16x8 qf[D / 16];
@@ -113,130 +131,149 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
     f32x16 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_used = -INFINITY, l_run = 0.f;
     const float qk_scale = p.scale * kLog2e;
     const int64_t kv_row_stride = (int64_t)p.h_kv * D;
     const bf16_t* kbase = k + (int64_t)b * n * kv_row_stride + (int64_t)r * D;
     const bf16_t* vbase = v + (int64_t)b * n * kv_row_stride + (int64_t)r * D;
+
+    // global -> registers -> LDS for one tile (chunk c, 64-key part sub); thread tid moves the
+    // 16-byte pieces tid + 256 i
+    uint4 pk[LOADS], pv[LOADS];
+    auto fetch = [&](int c, int sub) {
+        const int key0 = c * BLK + sub * KT;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int e = tid + i * kMfmaThreads;
+            const int kk = e / (D / 8), d8 = e % (D / 8);
+            const int key = key0 + kk;
+            pk[i] = make_uint4(0, 0, 0, 0);
+            pv[i] = make_uint4(0, 0, 0, 0);
+            if (key < n) {
+                pk[i] = *reinterpret_cast<const uint4*>(kbase + key * kv_row_stride + 8 * d8);
+                pv[i] = *reinterpret_cast<const uint4*>(vbase + key * kv_row_stride + 8 * d8);
+            }
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int e = tid + i * kMfmaThreads;
+            const int kk = e / (D / 8), d8 = e % (D / 8);
+            *reinterpret_cast<uint4*>(&Ks[buf][kk * KS + 8 * d8]) = pk[i];
+            *reinterpret_cast<uint4*>(&Vs[buf][kk * VS + 8 * d8]) = pv[i];
+        }
+    };
+    int c = next_chunk(-1), sub = 0;  // every tile has at least its own chunk
+    fetch(c, 0);
+    stash(0);
     __syncthreads();
 
-    for (int w = 0; w < nwt; ++w) {
-        uint32_t word = uni[w];
-        uint32_t myword = 0u;
-        if (valid && 32 * w <= cpos) {
-            const int hi = cpos - 32 * w;
-            myword = mrow[w];
-            if (hi < 31) myword &= (2u << hi) - 1u;
-            if (hi < 32) myword |= 1u << hi;
-        }
-        while (word) {
-            const int bit = __builtin_ctz(word);
-            word &= word - 1u;
-            const int c = 32 * w + bit;
-            const bool sel = (myword >> bit) & 1u;
-            const bool diag = c == cpos;
-            float off = -INFINITY, sc = 0.f;
-            if (sel) {
-                sc = qk_scale;
-                off = diag ? 0.f : brow[c] * kLog2e;
-            }
-            const bool causal = diag;  // only the query's own chunk holds keys after it
-#pragma unroll 1
-            for (int sub = 0; sub < NSUB; ++sub) {
-                const int key0 = c * BLK + sub * KT;
-                __syncthreads();  // the previous sub-tile has been consumed
-                // K sub-tile, rows as stored
-                for (int e = tid; e < KT * (D / 8); e += kMfmaThreads) {
-                    const int kk = e / (D / 8), d8 = e % (D / 8);
-                    const int key = key0 + kk;
-                    uint4 u = make_uint4(0, 0, 0, 0);
-                    if (key < n) u = *reinterpret_cast<const uint4*>(kbase + key * kv_row_stride + 8 * d8);
-                    *reinterpret_cast<uint4*>(&Ks[kk * KS + 8 * d8]) = u;
-                }
-                // V sub-tile, transposed: 4 keys x 8 dims per item, written as 8 runs of 4 keys
-                for (int e = tid; e < (KT / 4) * (D / 8); e += kMfmaThreads) {
-                    const int d8 = e % (D / 8), kq = e / (D / 8);
-                    uint4 u[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = key0 + 4 * kq + i;
-                        u[i] = key < n ? *reinterpret_cast<const uint4*>(vbase + key * kv_row_stride + 8 * d8)
-                                       : make_uint4(0, 0, 0, 0);
-                    }
-                    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&u[0]);
-                    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&u[1]);
-                    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&u[2]);
-                    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&u[3]);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        // dims 2jj (low halves) and 2jj + 1 (high halves) of the four keys
-                        const uint32_t lo01 = (w0[jj] & 0xffffu) | (w1[jj] << 16);
-                        const uint32_t lo23 = (w2[jj] & 0xffffu) | (w3[jj] << 16);
-                        const uint32_t hi01 = (w0[jj] >> 16) | (w1[jj] & 0xffff0000u);
-                        const uint32_t hi23 = (w2[jj] >> 16) | (w3[jj] & 0xffff0000u);
-                        *reinterpret_cast<uint2*>(&Vt[(8 * d8 + 2 * jj) * VS + 4 * kq]) = make_uint2(lo01, lo23);
-                        *reinterpret_cast<uint2*>(&Vt[(8 * d8 + 2 * jj + 1) * VS + 4 * kq]) = make_uint2(hi01, hi23);
-                    }
-                }
-                __syncthreads();
+    // transposed V reads: lane kl of 16-lane group grp reads key (kl / 4) of its 4-key run at
+    // dimensions d0 + 4 (kl % 4)
+    const int grp = lane >> 4, kl = lane & 15;
+    const int v_key = 4 * (grp >> 1) + (kl >> 2);           // + 16 ks (+ 8 for the second run)
+    const int v_dim = 16 * (grp & 1) + 4 * (kl & 3);        // + 32 dt
 
-                // S^T = K Q^T
-                f32x16 s[MT];
+    for (int buf = 0; c >= 0; buf ^= 1) {
+        const int key0 = c * BLK + sub * KT;
+        // the tile after this one: the chunk's next 64 keys, or the union's next chunk
+        const int c_nx = sub + 1 < NSUB ? c : next_chunk(c);
+        const int sub_nx = sub + 1 < NSUB ? sub + 1 : 0;
+        if (c_nx >= 0) fetch(c_nx, sub_nx);
+        // this row's view of the chunk
+        bool sel = false;
+        if (valid && c <= cpos) sel = c == cpos || ((mrow[c >> 5] >> (c & 31)) & 1u);
+        const float sc = sel ? qk_scale : 0.f;
+        const float off = sel ? (c == cpos ? 0.f : brow[c] * kLog2e) : -INFINITY;
+        const bool causal = c >= c_first;  // some row's own chunk: mask keys past each row
+
+        // S^T = K Q^T
+        f32x16 s[MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    s[mt] = f32x16{};
+        for (int mt = 0; mt < MT; ++mt) {
+            s[mt] = f32x16{};
 #pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(32 * mt + j) * KS + 16 * ks + 8 * G]);
-                        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mt], 0, 0, 0);
-                    }
-                }
-                // logits, masking, row maximum
-                float rmax = -INFINITY;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) {
-                        float x = s[mt][rr] * sc + off;
-                        if (causal) {
-                            const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
-                            if (key > pos) x = -INFINITY;
-                        }
-                        s[mt][rr] = x;
-                        rmax = fmaxf(rmax, x);
-                    }
-                rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
-                const float m_new = fmaxf(m_run, rmax);
-                const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-                const float corr = __builtin_amdgcn_exp2f(m_run - m_ref);
-                float rsum = 0.f;
-                bf16x8 pf[KSTEP];
-#pragma unroll
-                for (int ks = 0; ks < KSTEP; ++ks)
-#pragma unroll
-                    for (int vv = 0; vv < 8; ++vv) {
-                        const float pv = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + vv] - m_ref);
-                        rsum += pv;
-                        pf[ks][vv] = (__bf16)pv;
-                    }
-                rsum += __shfl_xor(rsum, 32, kWave);
-                l_run = l_run * corr + rsum;
-                m_run = m_new;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
-                // O^T += V^T P^T
-#pragma unroll
-                for (int ks = 0; ks < KSTEP; ++ks)
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const bf16_t* vp = &Vt[(32 * dt + j) * VS + 16 * ks + 4 * G];
-                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vp);
-                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vp + 8);
-                        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[dt], 0, 0, 0);
-                    }
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * mt + j) * KS + 16 * ks + 8 * G]);
+                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mt], 0, 0, 0);
             }
         }
+        // row maximum of x = s * sc + off (sc >= 0)
+        float xmax;
+        if (causal) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
+                    const float x = fmaf(s[mt][rr], sc, off);
+                    s[mt][rr] = key > pos ? -INFINITY : x;
+                }
+            xmax = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) xmax = fmaxf(xmax, s[mt][rr]);
+        } else {
+            float smax = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) smax = fmaxf(smax, s[mt][rr]);
+            xmax = sel ? fmaf(smax, sc, off) : -INFINITY;
+        }
+        xmax = fmaxf(xmax, __shfl_xor(xmax, 32, kWave));
+        // raise the running maximum only when needed (rare once a row has seen its peak)
+        const bool raise = xmax > m_used + kLazyMax;
+        if (__any(raise)) {
+            const float m_new = raise ? xmax : m_used;
+            const float corr = m_used == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used - m_new);
+            l_run *= corr;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
+            m_used = m_new;
+        }
+        const float m_ref = m_used == -INFINITY ? 0.f : m_used;
+        float rsum = 0.f;
+        bf16x8 pf[KSTEP];
+        if (causal) {
+#pragma unroll
+            for (int ks = 0; ks < KSTEP; ++ks)
+#pragma unroll
+                for (int vv = 0; vv < 8; ++vv) {
+                    const float pe = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + vv] - m_ref);
+                    rsum += pe;
+                    pf[ks][vv] = (__bf16)pe;
+                }
+        } else {
+            const float off_m = off - m_ref;
+#pragma unroll
+            for (int ks = 0; ks < KSTEP; ++ks)
+#pragma unroll
+                for (int vv = 0; vv < 8; ++vv) {
+                    const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + vv], sc, off_m));
+                    rsum += pe;
+                    pf[ks][vv] = (__bf16)pe;
+                }
+        }
+        l_run += rsum + __shfl_xor(rsum, 32, kWave);
+
+        // O^T += V^T P^T, V^T from the stored rows through transposing reads
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const bf16_t* vp = &Vs[buf][(16 * ks + v_key) * VS + 32 * dt + v_dim];
+                const i16x4 lo = ds_read_tr16(vp);
+                const i16x4 hi = ds_read_tr16(vp + 8 * VS);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[dt], 0, 0, 0);
+            }
+        if (c_nx >= 0) stash(buf ^ 1);
+        __syncthreads();
+        c = c_nx;
+        sub = sub_nx;
     }
 
     if (!valid) return;
@@ -252,7 +289,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
             for (int u = 0; u < 4; ++u) ov[u] = (__bf16)(acc[dt][4 * qd + u] * inv_l);
             *reinterpret_cast<bf16x4*>(orow + d0) = ov;
         }
-    if (lse && G == 0) lse[qrow * p.h_q + r * GQ + hl] = (m_run + __log2f(l_run)) * kLn2;
+    if (lse && G == 0) lse[qrow * p.h_q + r * GQ + hl] = (m_used + __log2f(l_run)) * kLn2;
 }
 
 template <int D, int BLK>
