@@ -75,25 +75,33 @@ def decode_bytes(mask: torch.Tensor, w: wl.Workload) -> tuple[int, float]:
     return int(kbar_bytes + kv_bytes + qo_bytes), float(routed / (w.batch * w.h_kv))
 
 
-def source_hash() -> str:
+# Sources each measured launch is built from: a counter summary taken on other sources is stale.
+KERNEL_SOURCES = {
+    "sparse_attn_prefill": ["common.h", "kernels.h", "sparse_attn_mfma.hip"],
+    "decode_step": ["common.h", "kernels.h", "entmax.h", "route_common.h", "block_entmax.hip",
+                    "decode.hip"],
+}
+
+
+def source_hash(kernel: str) -> str:
     csrc = os.path.join(ROOT, "sparse_hierarchical_attention_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, if it was taken on
-    the current kernel sources (else None)."""
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy) from the
+    committed counter summary, if it was taken on the current sources of that kernel; else None."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
     ent = data.get(kernel)
-    if not ent or ent.get("source_sha") != source_hash():
+    if not ent or ent.get("source_sha") != source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -158,16 +166,29 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one half of the step (for profiling); no JSON line is printed")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB `steps` times: the "
+                         "reference for scaling HBM byte counters; no JSON line is printed")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               f"(the path runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 
-    import sparse_hierarchical_attention_amd as dash
-    dash.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {n} bytes x {args.steps}", file=sys.stderr, flush=True)
+        return
+
+    import sparse_hierarchical_attention_amd as dash
+    dash.lib()
     wp, wd = wl.PREFILL_32K, wl.DECODE_128K
     print(f"[bench] generating inputs", file=sys.stderr, flush=True)
     pre = wl.make_inputs(wp, dev)
