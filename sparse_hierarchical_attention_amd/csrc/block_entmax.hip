@@ -9,7 +9,8 @@
 // Other many-query cases: score_kernel (64 x 64 tiles) and route_kernel (one wave per query and
 // group).
 // One query per sequence (decode): score_one_kernel (a coalesced stream over the summaries) and
-// route_group_kernel (one wave per head).
+// route_decode_kernel (one workgroup per group, several waves per head; route_group_kernel, one
+// wave per head, for rows too long for it).
 #include <math.h>
 
 #include "common.h"
@@ -225,6 +226,196 @@ __global__ __launch_bounds__(NPL >= 64 ? 256 : 1024) void route_group_kernel(con
                          bias + (qrow * p.h_kv + r) * p.nc, p);
 }
 
+// Reductions of the threshold solver over the WPH waves that hold one row, for a workgroup
+// whose waves all run the solver together (each reduction is one barrier). red: LDS scratch of
+// 2 x 16 x 5 floats, double-buffered so that one barrier per pass suffices. The loop of the
+// solver ends for the whole workgroup once every wave reported done at the start of a pass.
+template <int WPH>
+struct WaveSetReduce {
+    float* red;
+    int wave, lane, w0, nwaves;
+    int buf;
+    bool all_done;
+    __device__ float max(float v) {
+        v = wave_max(v);
+        if (lane == 0) red[wave * 5] = v;
+        __syncthreads();
+        float m = red[w0 * 5];
+#pragma unroll
+        for (int i = 1; i < WPH; ++i) m = fmaxf(m, red[(w0 + i) * 5]);
+        buf = 1;
+        all_done = false;
+        return m;
+    }
+    __device__ bool all(bool) { return all_done; }
+    __device__ void gather(float& k, float& p1, float& p2, float& tmin, bool done) {
+        k = wave_sum(k);
+        p1 = wave_sum(p1);
+        p2 = wave_sum(p2);
+        tmin = wave_min(tmin);
+        float* rb = red + buf * 80;
+        if (lane == 0) {
+            rb[wave * 5 + 0] = k;
+            rb[wave * 5 + 1] = p1;
+            rb[wave * 5 + 2] = p2;
+            rb[wave * 5 + 3] = tmin;
+            rb[wave * 5 + 4] = done ? 1.f : 0.f;
+        }
+        __syncthreads();
+        k = rb[w0 * 5];
+        p1 = rb[w0 * 5 + 1];
+        p2 = rb[w0 * 5 + 2];
+        tmin = rb[w0 * 5 + 3];
+#pragma unroll
+        for (int i = 1; i < WPH; ++i) {
+            k += rb[(w0 + i) * 5];
+            p1 += rb[(w0 + i) * 5 + 1];
+            p2 += rb[(w0 + i) * 5 + 2];
+            tmin = fminf(tmin, rb[(w0 + i) * 5 + 3]);
+        }
+        bool ad = true;
+        for (int i = 0; i < nwaves; ++i) ad = ad && rb[i * 5 + 4] != 0.f;
+        all_done = ad;
+        buf ^= 1;
+    }
+};
+
+// One query per sequence (decode), one workgroup per (sequence, group): the g heads' rows are
+// each spread over WPH waves (entry c in lane c % 64 of the head's wave (c / 64) % WPH, slot
+// c / (64 WPH)), which solve the head's threshold together; the heads' probabilities are added
+// in head order in LDS, and all waves then write the mask words and the bias.
+template <int NS, int KIND, int WPH>
+__global__ __launch_bounds__(1024) void route_decode_kernel(const float* __restrict__ x,
+                                                            uint32_t* __restrict__ mask,
+                                                            float* __restrict__ bias,
+                                                            float* __restrict__ tau_out,
+                                                            RouteParams p) {
+    constexpr int L = 64 * WPH;  // lanes per row
+    __shared__ float red[2 * 16 * 5];
+    __shared__ float stat_s[16];
+    __shared__ int stat_n[16];
+    extern __shared__ float wsum[];  // group sum of probabilities, one per chunk
+    const int r = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int hh = wave / WPH, wq = wave % WPH;
+    const int h = r * p.g + hh;
+    const int cp = p.q_pos0 / p.block;
+    const int m = min(cp, p.tc);
+    const int ns = (m + L - 1) / L;
+    const float e = 1.0f / (p.alpha - 1.0f);
+
+    // the row, loads unconditional (clamped into the row) so that all are in flight together
+    const float* xr = x + ((int64_t)b * p.h_q + h) * p.nc;
+    const int last = m > 0 ? m - 1 : 0;
+    float xv[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) xv[i] = xr[min(i * L + wq * 64 + lane, last)];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+        if (i * L + wq * 64 + lane >= m) xv[i] = -INFINITY;
+
+    WaveSetReduce<WPH> rd{red, wave, lane, hh * WPH, nwaves, 0, false};
+    const float tau = solve_tau_core<NS, KIND>(xv, ns, m, p.alpha, rd);
+    if (tau_out && wq == 0 && lane == 0) tau_out[(int64_t)b * p.h_q + h] = tau;
+
+    for (int g0 = 0; g0 < p.g; ++g0) {
+        if (hh == g0) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int c = i * L + wq * 64 + lane;
+                if (c < m) {
+                    const float pv = pow_e<KIND>(xv[i] - tau, e);
+                    wsum[c] = g0 == 0 ? pv : wsum[c] + pv;
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // mu = mean of log w over R, in a fixed order (waves, then lanes by DPP)
+    const float inv_g = 1.0f / (float)p.g;
+    float sl = 0.f;
+    int cnt = 0;
+    for (int c = tid; c < m; c += blockDim.x) {
+        const float w = wsum[c] * inv_g;
+        if (w > 0.f) {
+            sl += __logf(w);
+            ++cnt;
+        }
+    }
+    sl = wave_sum(sl);
+    cnt = wave_sum_int(cnt);
+    if (lane == 0) {
+        stat_s[wave] = sl;
+        stat_n[wave] = cnt;
+    }
+    __syncthreads();
+    float tot = 0.f;
+    int n_r = 0;
+    for (int i = 0; i < nwaves; ++i) {
+        tot += stat_s[i];
+        n_r += stat_n[i];
+    }
+    const float mu = n_r > 0 ? tot / (float)n_r : 0.f;
+    uint32_t* mrow = mask + ((int64_t)b * p.h_kv + r) * p.nw;
+    float* brow = bias + ((int64_t)b * p.h_kv + r) * p.nc;
+    for (int base = wave * 64; base < p.nw * 32; base += nwaves * 64) {
+        const int c = base + lane;
+        const float w = c < m ? wsum[c] * inv_g : 0.f;
+        const bool sel = c < m && w > 0.f;
+        if (sel) brow[c] = (__logf(w) - mu) * p.inv_sigma;
+        const uint64_t bal = __ballot(sel || c == cp);
+        if (lane == 0) {
+            mrow[base / 32] = (uint32_t)bal;
+            if (base / 32 + 1 < p.nw) mrow[base / 32 + 1] = (uint32_t)(bal >> 32);
+        }
+    }
+    if (tid == 0) brow[cp] = 0.f;
+}
+
+// waves per head row of route_decode_kernel (16 waves at most), and its slots per lane
+__host__ inline int route_decode_wph(int g) { return g <= 4 ? 4 : 16 / g; }
+__host__ inline int route_decode_slots(const RouteParams& p) {
+    int ns = 1;
+    while (ns * 64 * route_decode_wph(p.g) < p.tc) ns *= 2;
+    return ns;
+}
+
+template <int NS, int WPH>
+static void launch_route_decode_ns(const float* x, uint32_t* mask, float* bias, float* tau,
+                                   const RouteParams& p, hipStream_t st) {
+    const int kind = pow_kind(p.alpha);
+    const size_t lds = (size_t)(p.tc > 0 ? p.tc : 1) * sizeof(float);
+    dim3 grid(p.h_kv, p.batch), block(64 * WPH * p.g);
+#define DASH_RD(K) hipLaunchKernelGGL((route_decode_kernel<NS, K, WPH>), grid, block, lds, st, \
+                                      x, mask, bias, tau, p)
+    if (kind == kPowOne) DASH_RD(kPowOne); else if (kind == kPowTwo) DASH_RD(kPowTwo); else DASH_RD(kPowGeneral);
+#undef DASH_RD
+}
+
+template <int WPH>
+static void launch_route_decode_wph(const float* x, uint32_t* mask, float* bias, float* tau,
+                                    const RouteParams& p, hipStream_t st) {
+    switch (route_decode_slots(p)) {
+        case 1: launch_route_decode_ns<1, WPH>(x, mask, bias, tau, p, st); break;
+        case 2: launch_route_decode_ns<2, WPH>(x, mask, bias, tau, p, st); break;
+        case 4: launch_route_decode_ns<4, WPH>(x, mask, bias, tau, p, st); break;
+        case 8: launch_route_decode_ns<8, WPH>(x, mask, bias, tau, p, st); break;
+        case 16: launch_route_decode_ns<16, WPH>(x, mask, bias, tau, p, st); break;
+        default: launch_route_decode_ns<32, WPH>(x, mask, bias, tau, p, st); break;
+    }
+}
+
+static void launch_route_decode(const float* x, uint32_t* mask, float* bias, float* tau,
+                                const RouteParams& p, hipStream_t st) {
+    switch (route_decode_wph(p.g)) {
+        case 4: launch_route_decode_wph<4>(x, mask, bias, tau, p, st); break;
+        case 2: launch_route_decode_wph<2>(x, mask, bias, tau, p, st); break;
+        default: launch_route_decode_wph<1>(x, mask, bias, tau, p, st); break;
+    }
+}
+
 size_t route_workspace_bytes(const RouteParams& p, int dt) {
     if (route_fused_supported(p, dt)) return 0;  // scores stay on chip
     return (size_t)p.batch * p.n_q * p.h_q * p.nc * sizeof(float);
@@ -299,6 +490,10 @@ hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const R
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    if (one && route_decode_slots(p) <= 32) {
+        launch_route_decode(x, mask, bias, tau, p, st);
+        return hipGetLastError();
     }
     // the per-head kernel runs up to 16 waves (64 slots and more: up to 4, for its registers)
     const bool group = one && group_lds <= 128 * 1024 && (slots_for(p.nc) < 64 || p.g <= 4);

@@ -66,10 +66,24 @@ template <int LANES> __device__ __forceinline__ float grp_max(float v) {
     return LANES == 64 ? wave_max(v) : row16_max(v);
 }
 
-// Threshold tau of a row held by a group of LANES lanes (16: one DPP row; 64: the wave), with
-// sum_c [x_c - tau]_+^e = 1 for its m >= 0 entries. Slot s of a lane holds entry
-// s * LANES + (lane % LANES); slots at or past ns (wave-uniform) are not visited and slots past
-// the row hold -inf. A row with m = 0 gets +inf.
+// Reductions of the threshold solver over a group of LANES lanes (16: one DPP row; 64: the wave).
+template <int LANES>
+struct LaneGroupReduce {
+    __device__ __forceinline__ float max(float v) { return grp_max<LANES>(v); }
+    // true once every lane of the wave is done (the loop exit must be wave-uniform)
+    __device__ __forceinline__ bool all(bool done) { return __all(done); }
+    __device__ __forceinline__ void gather(float& k, float& p1, float& p2, float& tmin, bool) {
+        p1 = grp_sum<LANES>(p1);
+        p2 = grp_sum<LANES>(p2);
+        k = grp_sum<LANES>(k);
+        tmin = grp_min<LANES>(tmin);
+    }
+};
+
+// Threshold tau of a row held by a lane group, with sum_c [x_c - tau]_+^e = 1 for its m >= 0
+// entries. Each lane holds NS slots; slots at or past ns (uniform over the group) are not
+// visited and slots past the row hold -inf. A row with m = 0 gets +inf. RED supplies the group's
+// reductions (LaneGroupReduce, or a workgroup-wide one).
 //
 // f(tau) = sum [x - tau]_+^e - 1 is decreasing and convex on tau < max x, with its root in
 // [max x - 1, max x - m^(1 - alpha)]. Starting from the left end, each pass gathers over the
@@ -80,20 +94,21 @@ template <int LANES> __device__ __forceinline__ float grp_max(float v) {
 // Otherwise a Newton step (tangent of the convex f, so it stays left of the root) moves tau
 // and the pass repeats; a step that leaves the bracket is replaced by bisection. For other
 // exponents only the Newton steps apply, until the step falls below fp32 resolution.
-template <int NS, int KIND, int LANES>
-__device__ float solve_tau_exact(const float (&x)[NS], int ns, int m, float alpha) {
+template <int NS, int KIND, class RED>
+__device__ __forceinline__ float solve_tau_core(const float (&x)[NS], int ns, int m, float alpha,
+                                                RED& red) {
     const float e = 1.0f / (alpha - 1.0f);
     float xm = -INFINITY;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         if (s < ns) xm = fmaxf(xm, x[s]);
-    xm = grp_max<LANES>(xm);
+    xm = red.max(xm);
     float lo = xm - 1.0f;
     float hi = m > 1 ? xm - exp2f((1.0f - alpha) * __log2f((float)m)) : lo;
     float tau = m > 0 ? lo : INFINITY;
     bool done = m <= 1;
     for (int it = 0; it < 64; ++it) {
-        if (__all(done)) break;
+        if (red.all(done)) break;
         const float tr = done ? INFINITY : tau;
         float k = 0.f, p1 = 0.f, p2 = 0.f, tmin = INFINITY;
 #pragma unroll
@@ -115,12 +130,7 @@ __device__ float solve_tau_exact(const float (&x)[NS], int ns, int m, float alph
                 tmin = in ? fminf(tmin, t) : tmin;
             }
         }
-        p1 = grp_sum<LANES>(p1);
-        if (KIND != kPowOne) p2 = grp_sum<LANES>(p2);
-        if (KIND != kPowGeneral) {
-            k = grp_sum<LANES>(k);
-            tmin = grp_min<LANES>(tmin);
-        }
+        red.gather(k, p1, p2, tmin, done);
         if (done) continue;
         float f, tn;
         if (KIND == kPowTwo) {
@@ -154,6 +164,14 @@ __device__ float solve_tau_exact(const float (&x)[NS], int ns, int m, float alph
         tau = tn;
     }
     return tau;
+}
+
+// A row held by a group of LANES lanes (16 or 64): slot s of a lane holds entry
+// s * LANES + (lane % LANES).
+template <int NS, int KIND, int LANES>
+__device__ float solve_tau_exact(const float (&x)[NS], int ns, int m, float alpha) {
+    LaneGroupReduce<LANES> red;
+    return solve_tau_core<NS, KIND>(x, ns, m, alpha, red);
 }
 
 // One row over the whole wave (64 lanes, slot s holds entry 64 s + lane).
