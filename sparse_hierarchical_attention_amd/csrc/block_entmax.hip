@@ -280,6 +280,8 @@ struct WaveSetReduce {
     }
 };
 
+constexpr int kDecCand = 256;  // packed candidates per head row
+
 // One query per sequence (decode), one workgroup per (sequence, group): the g heads' rows are
 // each spread over WPH waves (entry c in lane c % 64 of the head's wave (c / 64) % WPH, slot
 // c / (64 WPH)), which solve the head's threshold together; the heads' probabilities are added
@@ -294,6 +296,9 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(const float* __restr
     __shared__ float red[2 * 16 * 5];
     __shared__ float stat_s[16];
     __shared__ int stat_n[16];
+    __shared__ int cand_n[16];
+    __shared__ float tau_h[16];
+    __shared__ float cand[16 * kDecCand];
     extern __shared__ float wsum[];  // group sum of probabilities, one per chunk
     const int r = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -315,8 +320,56 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(const float* __restr
     for (int i = 0; i < NS; ++i)
         if (i * L + wq * 64 + lane >= m) xv[i] = -INFINITY;
 
+    // tau never falls below max x - 1, so only entries above it can enter the support. When no
+    // head has more than kDecCand of them, they are packed into LDS and each head's first wave
+    // solves on its packed list alone; otherwise the head's waves solve on the whole row.
     WaveSetReduce<WPH> rd{red, wave, lane, hh * WPH, nwaves, 0, false};
-    const float tau = solve_tau_core<NS, KIND>(xv, ns, m, p.alpha, rd);
+    float xm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) xm = fmaxf(xm, xv[i]);
+    const float lo = rd.max(xm) - 1.0f;
+    int ncand = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) ncand += __popcll(__ballot(xv[i] > lo));
+    if (lane == 0) cand_n[wave] = ncand;
+    __syncthreads();
+    int before = 0, head_n = 0, most = 0;
+    for (int w = 0; w < nwaves; ++w) {
+        const int cw = cand_n[w];
+        if (w / WPH == hh) {
+            head_n += cw;
+            before += w < wave ? cw : 0;
+        }
+        if (w % WPH == WPH - 1) {
+            int hn = 0;
+            for (int v = w - WPH + 1; v <= w; ++v) hn += cand_n[v];
+            most = max(most, hn);
+        }
+    }
+    float tau;
+    if (most <= kDecCand) {
+        const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const bool in = xv[i] > lo;
+            const uint64_t bal = __ballot(in);
+            if (in) cand[hh * kDecCand + before + __popcll(bal & below)] = xv[i];
+            before += __popcll(bal);
+        }
+        __syncthreads();
+        if (wq == 0) {
+            float cv[kDecCand / 64];
+#pragma unroll
+            for (int i = 0; i < kDecCand / 64; ++i)
+                cv[i] = 64 * i + lane < head_n ? cand[hh * kDecCand + 64 * i + lane] : -INFINITY;
+            const float t = solve_tau_exact<kDecCand / 64, KIND, 64>(cv, (head_n + 63) / 64, head_n, p.alpha);
+            if (lane == 0) tau_h[hh] = t;
+        }
+        __syncthreads();
+        tau = tau_h[hh];
+    } else {
+        tau = solve_tau_core<NS, KIND>(xv, ns, m, p.alpha, rd);
+    }
     if (tau_out && wq == 0 && lane == 0) tau_out[(int64_t)b * p.h_q + h] = tau;
 
     for (int g0 = 0; g0 < p.g; ++g0) {
