@@ -22,8 +22,9 @@ namespace dash {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// 16 waves per CU (four per SIMD): NW waves per workgroup, 16 / NW workgroups per CU
 template <int D, int GQ, int MT, int NW, int KIND>
-__global__ __launch_bounds__(NW * 64) void route_fused_kernel(
+__global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
     const bf16_t* __restrict__ q, const float* __restrict__ kbar, uint32_t* __restrict__ mask,
     float* __restrict__ bias, float* __restrict__ tau_out, RouteParams p, int n_tiles,
     float coef) {
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void route_fused_kernel(
     }
 }
 
-// (MT, NW) with NW * MT * 32 >= tc chunks: up to 512 in 4 waves, up to 1024 in 8 waves
+// (MT, NW) with NW * MT * 32 >= tc chunks: up to 1024 chunks in 16 waves
 bool route_fused_supported(const RouteParams& p, int dt) {
     return dt == kBF16 && p.tc <= 1024 && p.n_q > 1 && p.nw <= 2 * (p.tc <= 512 ? 8 : 16);
 }
@@ -235,11 +236,13 @@ static void launch_fused_shape(const void* q, const float* kbar, uint32_t* mask,
 #undef DASH_FUSED
 }
 
+// two 32-chunk tiles per wave; the LDS of a workgroup (32 score rows) then allows 16 waves per CU
 template <int D, int GQ>
 static void launch_fused_g(const void* q, const float* kbar, uint32_t* mask, float* bias,
                            float* tau, const RouteParams& p, float coef, hipStream_t st) {
-    if (p.tc <= 512) launch_fused_shape<D, GQ, 4, 4>(q, kbar, mask, bias, tau, p, coef, st);
-    else launch_fused_shape<D, GQ, 4, 8>(q, kbar, mask, bias, tau, p, coef, st);
+    if (p.tc <= 256) launch_fused_shape<D, GQ, 2, 4>(q, kbar, mask, bias, tau, p, coef, st);
+    else if (p.tc <= 512) launch_fused_shape<D, GQ, 2, 8>(q, kbar, mask, bias, tau, p, coef, st);
+    else launch_fused_shape<D, GQ, 2, 16>(q, kbar, mask, bias, tau, p, coef, st);
 }
 
 template <int D>

@@ -119,6 +119,7 @@ SMALL_BF16 = [
     (1, 2048, 8, 2, 128, 64),
     (2, 2000, 8, 2, 128, 64),     # ragged tail chunk of 16 tokens
     (1, 1536, 16, 1, 64, 32),     # group of 16
+    (1, 1500, 16, 2, 128, 64),    # group of 8, ragged
     (1, 1100, 4, 4, 128, 128),    # group of 1, ragged
     (1, 777, 4, 2, 64, 64),
     (1, 40, 4, 2, 128, 64),       # shorter than one chunk: diagonal only

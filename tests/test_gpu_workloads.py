@@ -60,6 +60,13 @@ def test_prefill_32k(dash, orc, sigma):
     prefill_parity(dash, orc, w, sigma, sample_rows(w.n_q, w.block, 160, seed=61))
 
 
+def test_prefill_long_rows(dash, orc):
+    """Rows of more than 512 chunks (the widest fused Stage 1 shape): 30017 tokens in chunks of
+    32, so 938 complete chunks and a one-token tail chunk."""
+    w = wl.PREFILL_32K.with_(n_kv=30017, block=32, name="prefill 30017 tokens, chunk 32")
+    prefill_parity(dash, orc, w, 1.0, sample_rows(w.n_q, w.block, 64, seed=64))
+
+
 def _sweep_points():
     with open(os.path.join(GOLDEN, "sweep_gamma.json")) as f:
         return [(p["alpha"], p["block"], p["gamma"]) for p in json.load(f)["points"]]
