@@ -228,7 +228,7 @@ __global__ __launch_bounds__(NPL >= 64 ? 256 : 1024) void route_group_kernel(con
 
 // Reductions of the threshold solver over the WPH waves that hold one row, for a workgroup
 // whose waves all run the solver together (each reduction is one barrier). red: LDS scratch of
-// 2 x 16 x 5 floats, double-buffered so that one barrier per pass suffices. The loop of the
+// 2 x 16 x 6 floats, double-buffered so that one barrier per pass suffices. The loop of the
 // solver ends for the whole workgroup once every wave reported done at the start of a pass.
 template <int WPH>
 struct WaveSetReduce {
@@ -238,43 +238,47 @@ struct WaveSetReduce {
     bool all_done;
     __device__ float max(float v) {
         v = wave_max(v);
-        if (lane == 0) red[wave * 5] = v;
+        if (lane == 0) red[wave * 6] = v;
         __syncthreads();
-        float m = red[w0 * 5];
+        float m = red[w0 * 6];
 #pragma unroll
-        for (int i = 1; i < WPH; ++i) m = fmaxf(m, red[(w0 + i) * 5]);
+        for (int i = 1; i < WPH; ++i) m = fmaxf(m, red[(w0 + i) * 6]);
         buf = 1;
         all_done = false;
         return m;
     }
     __device__ bool all(bool) { return all_done; }
-    __device__ void gather(float& k, float& p1, float& p2, float& tmin, bool done) {
+    __device__ void gather(float& k, float& p1, float& p2, float& tmin, float& tout, bool done) {
         k = wave_sum(k);
         p1 = wave_sum(p1);
         p2 = wave_sum(p2);
         tmin = wave_min(tmin);
-        float* rb = red + buf * 80;
+        tout = wave_max(tout);
+        float* rb = red + buf * 96;
         if (lane == 0) {
-            rb[wave * 5 + 0] = k;
-            rb[wave * 5 + 1] = p1;
-            rb[wave * 5 + 2] = p2;
-            rb[wave * 5 + 3] = tmin;
-            rb[wave * 5 + 4] = done ? 1.f : 0.f;
+            rb[wave * 6 + 0] = k;
+            rb[wave * 6 + 1] = p1;
+            rb[wave * 6 + 2] = p2;
+            rb[wave * 6 + 3] = tmin;
+            rb[wave * 6 + 4] = tout;
+            rb[wave * 6 + 5] = done ? 1.f : 0.f;
         }
         __syncthreads();
-        k = rb[w0 * 5];
-        p1 = rb[w0 * 5 + 1];
-        p2 = rb[w0 * 5 + 2];
-        tmin = rb[w0 * 5 + 3];
+        k = rb[w0 * 6];
+        p1 = rb[w0 * 6 + 1];
+        p2 = rb[w0 * 6 + 2];
+        tmin = rb[w0 * 6 + 3];
+        tout = rb[w0 * 6 + 4];
 #pragma unroll
         for (int i = 1; i < WPH; ++i) {
-            k += rb[(w0 + i) * 5];
-            p1 += rb[(w0 + i) * 5 + 1];
-            p2 += rb[(w0 + i) * 5 + 2];
-            tmin = fminf(tmin, rb[(w0 + i) * 5 + 3]);
+            k += rb[(w0 + i) * 6];
+            p1 += rb[(w0 + i) * 6 + 1];
+            p2 += rb[(w0 + i) * 6 + 2];
+            tmin = fminf(tmin, rb[(w0 + i) * 6 + 3]);
+            tout = fmaxf(tout, rb[(w0 + i) * 6 + 4]);
         }
         bool ad = true;
-        for (int i = 0; i < nwaves; ++i) ad = ad && rb[i * 5 + 4] != 0.f;
+        for (int i = 0; i < nwaves; ++i) ad = ad && rb[i * 6 + 5] != 0.f;
         all_done = ad;
         buf ^= 1;
     }
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(const float* __restr
                                                             float* __restrict__ tau_out,
                                                             RouteParams p) {
     constexpr int L = 64 * WPH;  // lanes per row
-    __shared__ float red[2 * 16 * 5];
+    __shared__ float red[2 * 16 * 6];
     __shared__ float stat_s[16];
     __shared__ int stat_n[16];
     __shared__ int cand_n[16];

@@ -72,11 +72,13 @@ struct LaneGroupReduce {
     __device__ __forceinline__ float max(float v) { return grp_max<LANES>(v); }
     // true once every lane of the wave is done (the loop exit must be wave-uniform)
     __device__ __forceinline__ bool all(bool done) { return __all(done); }
-    __device__ __forceinline__ void gather(float& k, float& p1, float& p2, float& tmin, bool) {
+    __device__ __forceinline__ void gather(float& k, float& p1, float& p2, float& tmin,
+                                           float& tout, bool) {
         p1 = grp_sum<LANES>(p1);
         p2 = grp_sum<LANES>(p2);
         k = grp_sum<LANES>(k);
         tmin = grp_min<LANES>(tmin);
+        tout = grp_max<LANES>(tout);
     }
 };
 
@@ -87,13 +89,18 @@ struct LaneGroupReduce {
 //
 // f(tau) = sum [x - tau]_+^e - 1 is decreasing and convex on tau < max x, with its root in
 // [max x - 1, max x - m^(1 - alpha)]. Starting from the left end, each pass gathers over the
-// current support S = {x > tau}: its size k, sum of t = x - tau, sum of t^2 and smallest t.
+// current support S = {x > tau}: its size k, sum of t = x - tau, sum of t^2, the smallest t in S
+// and the largest t outside it (t_out <= 0), and solves the root d of f restricted to S:
 //   e = 2 (alpha = 1.5): sum_S (t - d)^2 = 1 has the root d = (Q - 1) / (P + sqrt(P^2 - k(Q - 1)))
 //   e = 1 (alpha = 2):   sum_S (t - d)   = 1 has the root d = (P - 1) / k
-// If d is below the smallest t, S is also the support at tau + d, which is then exact.
-// Otherwise a Newton step (tangent of the convex f, so it stays left of the root) moves tau
-// and the pass repeats; a step that leaves the bracket is replaced by bisection. For other
-// exponents only the Newton steps apply, until the step falls below fp32 resolution.
+// If t_out <= d < t_min, S is also the support at tau + d, which is then exact.
+// e = 1: from the left the restricted root is a lower bound (the terms of S that would turn
+// negative pull it down), so tau + d is the next point and tau rises monotonically.
+// e = 2: the restricted root over a superset of the support is an upper bound (its dropped terms
+// are squares, so positive), over a subset a lower bound; tau + d is taken in turn from either
+// side, while the bracket shrinks by those bounds and by the points where S changes (tau + t_min
+// from the left, tau + t_out from the right). A step leaving the bracket is replaced by bisection.
+// Other exponents: Newton steps from the left, until the step falls below fp32 resolution.
 template <int NS, int KIND, class RED>
 __device__ __forceinline__ float solve_tau_core(const float (&x)[NS], int ns, int m, float alpha,
                                                 RED& red) {
@@ -110,7 +117,7 @@ __device__ __forceinline__ float solve_tau_core(const float (&x)[NS], int ns, in
     for (int it = 0; it < 64; ++it) {
         if (red.all(done)) break;
         const float tr = done ? INFINITY : tau;
-        float k = 0.f, p1 = 0.f, p2 = 0.f, tmin = INFINITY;
+        float k = 0.f, p1 = 0.f, p2 = 0.f, tmin = INFINITY, tout = -INFINITY;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             if (s >= ns) break;
@@ -126,25 +133,40 @@ __device__ __forceinline__ float solve_tau_core(const float (&x)[NS], int ns, in
                 const float u = in ? t : 0.f;
                 k += in ? 1.f : 0.f;
                 p1 += u;
-                if (KIND == kPowTwo) p2 = fmaf(u, u, p2);
+                if (KIND == kPowTwo) {
+                    p2 = fmaf(u, u, p2);
+                    tout = in ? tout : fmaxf(tout, t);
+                }
                 tmin = in ? fminf(tmin, t) : tmin;
             }
         }
-        red.gather(k, p1, p2, tmin, done);
+        red.gather(k, p1, p2, tmin, tout, done);
         if (done) continue;
         float f, tn;
         if (KIND == kPowTwo) {
             f = p2 - 1.0f;
             const float disc = p1 * p1 - k * f;
-            if (f >= 0.f && k > 0.f && disc >= 0.f) {
-                const float d = f / (p1 + sqrtf(disc));
-                if (d < tmin) {
-                    tau += d;
-                    done = true;
-                    continue;
+            const bool root = k > 0.f && disc >= 0.f;
+            const float d = root ? f / (p1 + sqrtf(disc)) : 0.f;
+            if (root && d >= tout && d < tmin) {
+                tau += d;
+                done = true;
+                continue;
+            }
+            if (f >= 0.f) {
+                lo = fmaxf(lo, tau);
+                if (root) {
+                    hi = fminf(hi, tau + d);
+                    if (d >= tmin) lo = fmaxf(lo, tau + tmin);
+                }
+            } else {
+                hi = fminf(hi, tau);
+                if (root) {
+                    lo = fmaxf(lo, tau + d);
+                    if (d < tout) hi = fminf(hi, tau + tout);
                 }
             }
-            tn = p1 > 0.f ? tau + f / (2.0f * p1) : 0.5f * (lo + hi);
+            tn = root ? tau + d : (p1 > 0.f ? tau + f / (2.0f * p1) : 0.5f * (lo + hi));
         } else if (KIND == kPowOne) {
             f = p1 - 1.0f;
             const float d = k > 0.f ? f / k : 0.f;
@@ -154,13 +176,14 @@ __device__ __forceinline__ float solve_tau_core(const float (&x)[NS], int ns, in
                 continue;
             }
             tn = k > 0.f ? tau + d : 0.5f * (lo + hi);
+            if (f >= 0.f) lo = fmaxf(lo, tau); else hi = fminf(hi, tau);
         } else {
             f = p2 - 1.0f;
             tn = p1 > 0.f ? tau + f / (e * p1) : 0.5f * (lo + hi);
+            if (f >= 0.f) lo = fmaxf(lo, tau); else hi = fminf(hi, tau);
         }
-        if (f >= 0.f) lo = fmaxf(lo, tau); else hi = fminf(hi, tau);
         if (!(tn >= lo && tn <= hi)) tn = 0.5f * (lo + hi);
-        done = fabsf(tn - tau) <= 1e-7f * fmaxf(1.0f, fabsf(tau));
+        done = hi - lo <= 1e-7f * fmaxf(1.0f, fabsf(tau)) || fabsf(tn - tau) <= 1e-7f * fmaxf(1.0f, fabsf(tau));
         tau = tn;
     }
     return tau;
