@@ -130,14 +130,15 @@ __device__ __forceinline__ float solve_tau_core(const float (&x)[NS], int ns, in
                     p1 += exp2f((e - 1.0f) * lt);  // sum t^(e-1)
                 }
             } else {
-                const float u = in ? t : 0.f;
+                // t is never NaN: entries past the row and rows already done give t = -inf
+                const float u = fmaxf(t, 0.f);
                 k += in ? 1.f : 0.f;
                 p1 += u;
                 if (KIND == kPowTwo) {
                     p2 = fmaf(u, u, p2);
-                    tout = in ? tout : fmaxf(tout, t);
+                    tout = fmaxf(tout, in ? -INFINITY : t);
                 }
-                tmin = in ? fminf(tmin, t) : tmin;
+                tmin = fminf(tmin, in ? t : INFINITY);
             }
         }
         red.gather(k, p1, p2, tmin, tout, done);

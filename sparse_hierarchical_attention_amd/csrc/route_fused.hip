@@ -22,6 +22,89 @@ namespace dash {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// One unit of the fused route's phase 2 (see route_fused_kernel): rows row0 .. of the score
+// tile xr (row stride xstride), NSS slots of 16 lanes per row, for the token(s) of the unit.
+template <int NSS, int KIND, int GQ>
+__device__ __forceinline__ void route_unit(const float* __restrict__ xr0, int xstride, int row0,
+                                           int tile0, int b, int r, uint32_t* __restrict__ mask,
+                                           float* __restrict__ bias, float* __restrict__ tau_out,
+                                           const RouteParams& p) {
+    constexpr int PASSES = GQ >= 4 ? GQ / 4 : 1;        // passes per unit
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4, li = lane & 15;
+    const float e = 1.0f / (p.alpha - 1.0f);
+    const float inv_g = 1.0f / (float)GQ;
+    // this lane group's token (for g < 4 the groups hold different tokens)
+    const int my_tok = (GQ >= 4 ? row0 : row0 + grp) / GQ;
+    const int tok = tile0 + my_tok;
+    const bool tvalid = tok < p.n_q;
+    const int pos = p.q_pos0 + tok;
+    const int cp = pos / p.block;
+    const int m = tvalid ? min(cp, p.tc) : 0;
+    float wsum[NSS];
+#pragma unroll
+    for (int sl = 0; sl < NSS; ++sl) wsum[sl] = 0.f;
+#pragma unroll 1
+    for (int ps = 0; ps < PASSES; ++ps) {
+        const int rl = 4 * ps + grp;  // row within the unit
+        const float* xr = xr0 + rl * xstride;
+        float xv[NSS];
+#pragma unroll
+        for (int sl = 0; sl < NSS; ++sl) {
+            const int c = 16 * sl + li;
+            const float v = xr[c];
+            xv[sl] = c < m ? v : -INFINITY;
+        }
+        const float tau = solve_tau_exact<NSS, KIND, 16>(xv, NSS, m, p.alpha);
+        if (tau_out && tvalid && li == 0)
+            tau_out[((int64_t)b * p.n_q + tok) * p.h_q + r * GQ + (row0 + rl) % GQ] = tau;
+#pragma unroll
+        for (int sl = 0; sl < NSS; ++sl) {
+            float pv = pow_e<KIND>(xv[sl] - tau, e);
+            if (GQ >= 2) pv = pair16_sum(pv);   // heads in groups 0+1 and 2+3
+            if (GQ >= 4) pv = pair32_sum(pv);   // all four groups
+            wsum[sl] += pv;
+        }
+    }
+    // GQA mean and mu for this group's token (every lane of the group holds the same row)
+    float lsum = 0.f, lcnt = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < NSS; ++sl) {
+        wsum[sl] *= inv_g;
+        const bool in = wsum[sl] > 0.f;
+        lsum += in ? __logf(wsum[sl]) : 0.f;
+        lcnt += in ? 1.f : 0.f;
+    }
+    lsum = row16_sum(lsum);
+    lcnt = row16_sum(lcnt);
+    const float mu = lcnt > 0.f ? lsum / lcnt : 0.f;
+    // the groups that write: one per token of the unit
+    const bool writer = tvalid && (GQ >= 4 ? grp == 0 : (GQ == 2 ? (grp & 1) == 0 : true));
+    const int64_t qrow = (int64_t)b * p.n_q + tok;
+    uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
+    float* brow = bias + (qrow * p.h_kv + r) * p.nc;
+#pragma unroll
+    for (int sl = 0; sl < NSS; ++sl) {
+        const int c = 16 * sl + li;
+        if (writer && wsum[sl] > 0.f) brow[c] = (__logf(wsum[sl]) - mu) * p.inv_sigma;
+    }
+#pragma unroll
+    for (int wd = 0; wd < NSS / 2; ++wd) {
+        const uint64_t b0 = __ballot(wsum[2 * wd] > 0.f);
+        const uint64_t b1 = __ballot(wsum[2 * wd + 1] > 0.f);
+        if (writer && li == 0 && wd < p.nw) {
+            uint32_t word = (uint32_t)((b0 >> (16 * grp)) & 0xffffu) |
+                            ((uint32_t)((b1 >> (16 * grp)) & 0xffffu) << 16);
+            if (cp / 32 == wd) word |= 1u << (cp % 32);
+            mrow[wd] = word;
+        }
+    }
+    // words past the bucket: only the query's own chunk can be set there
+    for (int wd = NSS / 2 + li; wd < p.nw; wd += 16)
+        if (writer) mrow[wd] = cp / 32 == wd ? 1u << (cp % 32) : 0u;
+    if (writer && li == 0) brow[cp] = 0.f;
+}
+
 // 16 waves per CU (four per SIMD): NW waves per workgroup, 16 / NW workgroups per CU
 template <int D, int GQ, int MT, int NW, int KIND>
 __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
@@ -128,90 +211,19 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
 
     // ---- phase 2: a wave takes 4 rows at a time, one per 16-lane DPP row (lane group); entry c
     // of a row sits in lane c % 16 of its group, slot c / 16. A unit is one token when g >= 4
-    // (its heads in g / 4 passes of 4) or 4 / g tokens when g < 4 (one pass).
-    constexpr int NS = CMAX / 16;
-    constexpr int PASSES = GQ >= 4 ? GQ / 4 : 1;        // passes per unit
-    constexpr int UROWS = 4 * PASSES;                  // rows per unit
-    constexpr int UNITS = ROWS / UROWS;
-    const float e = 1.0f / (p.alpha - 1.0f);
-    const float inv_g = 1.0f / (float)GQ;
-    const int grp = lane >> 4, li = lane & 15;
-    for (int u = wave; u < UNITS; u += NW) {
+    // (its heads in g / 4 passes of 4) or 4 / g tokens when g < 4 (one pass). The slot count is
+    // a compile-time bucket (the unit's longest row, rounded up to 4, 8, 16, ...) so that every
+    // slot loop unrolls; slots past a row hold -inf.
+    constexpr int UROWS = 4 * (GQ >= 4 ? GQ / 4 : 1);  // rows per unit
+    for (int u = wave; u < ROWS / UROWS; u += NW) {
         const int row0 = u * UROWS;
-        // this lane group's token (for g < 4 the groups hold different tokens)
-        const int my_row_first = row0 + grp;                  // row of this group in pass 0
-        const int my_tok = (GQ >= 4 ? row0 : my_row_first) / GQ;
-        const int tok = tile0 + my_tok;
-        const bool tvalid = tok < p.n_q;
-        const int pos = p.q_pos0 + tok;
-        const int cp = pos / p.block;
-        const int m = tvalid ? min(cp, p.tc) : 0;
-        // slots to visit: the unit's last token has the most candidates
         const int last_tok = min(tile0 + (row0 + UROWS - 1) / GQ, p.n_q - 1);
         const int ns = div_up(min((p.q_pos0 + last_tok) / p.block, p.tc), 16);
-        float wsum[NS];
-#pragma unroll
-        for (int sl = 0; sl < NS; ++sl) wsum[sl] = 0.f;
-#pragma unroll 1
-        for (int ps = 0; ps < PASSES; ++ps) {
-            const int row = row0 + 4 * ps + grp;
-            const float* xr = xs + row * XS;
-            float xv[NS];
-#pragma unroll
-            for (int sl = 0; sl < NS; ++sl) {
-                xv[sl] = -INFINITY;
-                if (sl >= ns) continue;
-                const int c = 16 * sl + li;
-                const float v = xr[c];
-                xv[sl] = c < m ? v : -INFINITY;
-            }
-            const float tau = solve_tau_exact<NS, KIND, 16>(xv, ns, m, p.alpha);
-            if (tau_out && tvalid && li == 0)
-                tau_out[((int64_t)b * p.n_q + tok) * p.h_q + r * GQ + row % GQ] = tau;
-#pragma unroll
-            for (int sl = 0; sl < NS; ++sl) {
-                if (sl >= ns) break;
-                float pv = pow_e<KIND>(xv[sl] - tau, e);
-                if (GQ >= 2) pv = pair16_sum(pv);   // heads in groups 0+1 and 2+3
-                if (GQ >= 4) pv = pair32_sum(pv);   // all four groups
-                wsum[sl] += pv;
-            }
-        }
-        // GQA mean and mu for this group's token (every lane of the group holds the same row)
-        float lsum = 0.f, lcnt = 0.f;
-#pragma unroll
-        for (int sl = 0; sl < NS; ++sl) {
-            if (sl >= ns) break;
-            wsum[sl] *= inv_g;
-            if (wsum[sl] > 0.f) { lsum += __logf(wsum[sl]); lcnt += 1.f; }
-        }
-        lsum = row16_sum(lsum);
-        lcnt = row16_sum(lcnt);
-        const float mu = lcnt > 0.f ? lsum / lcnt : 0.f;
-        // the groups that write: one per token of the unit
-        const bool writer = GQ >= 4 ? grp == 0 : (GQ == 2 ? (grp & 1) == 0 : true);
-        const int64_t qrow = (int64_t)b * p.n_q + tok;
-        uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
-        float* brow = bias + (qrow * p.h_kv + r) * p.nc;
-#pragma unroll
-        for (int sl = 0; sl < NS; ++sl) {
-            if (sl >= ns) break;
-            const int c = 16 * sl + li;
-            if (writer && tvalid && wsum[sl] > 0.f) brow[c] = (__logf(wsum[sl]) - mu) * p.inv_sigma;
-        }
-#pragma unroll
-        for (int wd = 0; wd < NS / 2; ++wd) {
-            if (wd >= p.nw) break;
-            const uint64_t b0 = 2 * wd < ns ? __ballot(wsum[2 * wd] > 0.f) : 0ull;
-            const uint64_t b1 = 2 * wd + 1 < ns ? __ballot(wsum[2 * wd + 1] > 0.f) : 0ull;
-            if (writer && tvalid && li == 0) {
-                uint32_t word = (uint32_t)((b0 >> (16 * grp)) & 0xffffu) |
-                                ((uint32_t)((b1 >> (16 * grp)) & 0xffffu) << 16);
-                if (cp / 32 == wd) word |= 1u << (cp % 32);
-                mrow[wd] = word;
-            }
-        }
-        if (writer && tvalid && li == 0) brow[cp] = 0.f;
+        if (ns <= 4) route_unit<4, KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
+        else if (ns <= 8) route_unit<8, KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
+        else if (ns <= 16) route_unit<16, KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
+        else if (CMAX >= 512 && ns <= 32) route_unit<(CMAX >= 512 ? 32 : 16), KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
+        else if (CMAX >= 1024) route_unit<(CMAX >= 1024 ? 64 : 16), KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
     }
 }
 
