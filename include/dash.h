@@ -106,10 +106,11 @@ dash_status_t dash_pool_keys_query(const void* k, dash_dtype_t dt, const float* 
  * Mask rows are written in full (bits beyond c_p are 0). Bias entries are written only where the
  * mask bit is 1; the others are left untouched. tau may be NULL; a row with c_p = 0 has no
  * candidate and gets tau = +inf. alpha in (1, 2]; gamma > 0; sigma > 0, +inf allowed (d = 0).
- * bf16 queries with n_q > 1 and Tc <= 2048 run in one pass with the scores on chip and need no
- * workspace; other calls (fp32, decode, longer rows) first score into `workspace`, fp32
+ * bf16 queries with n_q > 1 and Tc <= 1024 run in one pass with the scores on chip; their
+ * workspace holds the summaries split into three bf16 terms (6 bytes per summary element, Tc
+ * rounded up to a multiple of 32). Other calls (fp32, decode, longer rows) first score into `workspace`, fp32
  * [B, n_q, H_q, Nc]. dash_block_entmax_workspace_bytes() gives the bytes a call needs (0 if
- * none); the workspace may be NULL when it is 0.
+ * none); the workspace may be NULL when it is 0. The workspace holds nothing between calls.
  */
 size_t dash_block_entmax_workspace_bytes(dash_dtype_t dt, int batch, int n_q, int q_pos0,
                                          int n_kv, int h_q, int h_kv, int head_dim, int block);

@@ -474,7 +474,7 @@ static void launch_route_decode(const float* x, uint32_t* mask, float* bias, flo
 }
 
 size_t route_workspace_bytes(const RouteParams& p, int dt) {
-    if (route_fused_supported(p, dt)) return 0;  // scores stay on chip
+    if (route_fused_supported(p, dt)) return route_fused_workspace_bytes(p);  // scores stay on chip
     return (size_t)p.batch * p.n_q * p.h_q * p.nc * sizeof(float);
 }
 
@@ -515,7 +515,7 @@ static void launch_route(bool group, const float* x, uint32_t* mask, float* bias
 hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const RouteParams& p,
                                uint32_t* mask, float* bias, float* tau, void* ws,
                                hipStream_t st) {
-    if (route_fused_supported(p, dt)) return launch_route_fused(q, kbar, mask, bias, tau, p, st);
+    if (route_fused_supported(p, dt)) return launch_route_fused(q, kbar, mask, bias, tau, p, ws, st);
     float* x = static_cast<float*>(ws);
     const float coef = (p.alpha - 1.0f) * p.gamma / sqrtf((float)p.head_dim);
     const size_t group_lds = (size_t)p.g * slots_for(p.nc) * 64 * sizeof(float);

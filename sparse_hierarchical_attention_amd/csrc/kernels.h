@@ -24,8 +24,9 @@ struct RouteParams {
 };
 size_t route_workspace_bytes(const RouteParams& p, int dt);
 bool route_fused_supported(const RouteParams& p, int dt);
+size_t route_fused_workspace_bytes(const RouteParams& p);
 hipError_t launch_route_fused(const void* q, const float* kbar, uint32_t* mask, float* bias,
-                              float* tau, const RouteParams& p, hipStream_t st);
+                              float* tau, const RouteParams& p, void* ws, hipStream_t st);
 hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const RouteParams& p,
                                uint32_t* mask, float* bias, float* tau, void* ws,
                                hipStream_t st);

@@ -1,12 +1,13 @@
 // Stage 1 for many queries in one pass, without a score workspace ("DashAttention",
 // arXiv 2605.18753v1, §3.2 Eq. 4, §3.4 Prop. 1; App. G Alg. 2 with the score rows kept on chip).
 //
-// A workgroup of NW waves owns 32 query rows of one (sequence b, KV group r): T = 32 / g
+// A workgroup of NW waves owns 32 NR query rows of one (sequence b, KV group r): T = 32 NR / g
 // consecutive tokens times the g heads of the group (row = token * g + head).
-// Phase 1, scores: X^T = Kbar Q^T on v_mfma_f32_32x32x16_bf16. The fp32 summaries are split as
-// kbar = hi + mid + lo, each a bf16 (hi = bf16(kbar), mid = bf16(kbar - hi), lo = bf16 of the
-// rest), so three bf16 products carry about 24 mantissa bits of the summary (Q is bf16 already)
-// with fp32 accumulation. Wave w computes the 32-chunk tiles w, w + NW, ... of all rows.
+// Phase 1, scores: X^T = Kbar Q^T on v_mfma_f32_32x32x16_bf16. The fp32 summaries are split once
+// per call (split_kbar_kernel, into the workspace) as kbar = hi + mid + lo, each a bf16
+// (hi = bf16(kbar), mid = bf16(kbar - hi), lo = bf16 of the rest), so three bf16 products carry
+// about 24 mantissa bits of the summary (Q is bf16 already) with fp32 accumulation. Wave w
+// computes the 32-chunk tiles w, w + NW, ... of all rows.
 // The score rows then go through LDS (row-major, odd stride) so that one wave can own a token.
 // Phase 2: per token, the same register-resident threshold solver and row writer as the
 // workspace path (entmax.h, route_common.h): the g heads in turn, the GQA mean, mask and bias.
@@ -21,6 +22,52 @@ namespace dash {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// The fp32 summaries as three bf16 terms, hi = bf16(kbar), mid = bf16(kbar - hi),
+// lo = bf16(kbar - hi - mid), each rounded to nearest even (together about 24 mantissa bits),
+// stored in the order phase 1 loads them as MFMA A fragments:
+//   [B][H_kv][ct = c / 32][ks = d / 16][term][lane = c % 32 + 32 ((d / 8) % 2)][8 bf16]
+// so that one fragment load of a wave reads 1 KiB contiguous. Chunks of the last tile past Tc
+// are zero. One thread per (b, r, ct, ks, lane): 8 elements.
+__global__ __launch_bounds__(256) void split_kbar_kernel(const float* __restrict__ kbar,
+                                                         bf16_t* __restrict__ planes, int batch,
+                                                         int tc, int h_kv, int D) {
+    const int ks_n = D / 16, ct_n = div_up(tc, 32);
+    const int64_t n = (int64_t)batch * h_kv * ct_n * ks_n * 64;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int lane = (int)(i % 64);
+    int64_t rest = i / 64;
+    const int ks = (int)(rest % ks_n);
+    rest /= ks_n;
+    const int ct = (int)(rest % ct_n);
+    rest /= ct_n;
+    const int r = (int)(rest % h_kv);
+    const int b = (int)(rest / h_kv);
+    const int c = 32 * ct + (lane & 31);
+    float kv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c < tc) {
+        const float4* src = reinterpret_cast<const float4*>(
+            kbar + (((int64_t)b * tc + c) * h_kv + r) * D + 16 * ks + 8 * (lane >> 5));
+        const float4 x0 = src[0], x1 = src[1];
+        kv[0] = x0.x; kv[1] = x0.y; kv[2] = x0.z; kv[3] = x0.w;
+        kv[4] = x1.x; kv[5] = x1.y; kv[6] = x1.z; kv[7] = x1.w;
+    }
+    bf16x8_t hi, mid, lo;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const __bf16 h = (__bf16)kv[u];
+        const float r1 = kv[u] - (float)h;
+        const __bf16 md = (__bf16)r1;
+        hi[u] = h;
+        mid[u] = md;
+        lo[u] = (__bf16)(r1 - (float)md);
+    }
+    uint4* out = reinterpret_cast<uint4*>(planes) + (((int64_t)(b * h_kv + r) * ct_n + ct) * ks_n + ks) * 3 * 64 + lane;
+    out[0] = __builtin_bit_cast(uint4, hi);
+    out[64] = __builtin_bit_cast(uint4, mid);
+    out[128] = __builtin_bit_cast(uint4, lo);
+}
 
 // One unit of the fused route's phase 2 (see route_fused_kernel): rows row0 .. of the score
 // tile xr (row stride xstride), NSS slots of 16 lanes per row, for the token(s) of the unit.
@@ -105,13 +152,14 @@ __device__ __forceinline__ void route_unit(const float* __restrict__ xr0, int xs
     if (writer && li == 0) brow[cp] = 0.f;
 }
 
-// 16 waves per CU (four per SIMD): NW waves per workgroup, 16 / NW workgroups per CU
-template <int D, int GQ, int MT, int NW, int KIND>
+// 16 waves per CU (four per SIMD): NW waves per workgroup, 16 / NW workgroups per CU. NR MFMA
+// N-tiles of 32 query rows share every summary fragment a wave loads.
+template <int D, int GQ, int MT, int NW, int NR, int KIND>
 __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
-    const bf16_t* __restrict__ q, const float* __restrict__ kbar, uint32_t* __restrict__ mask,
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ planes, uint32_t* __restrict__ mask,
     float* __restrict__ bias, float* __restrict__ tau_out, RouteParams p, int n_tiles,
     float coef) {
-    constexpr int ROWS = 32;                 // one MFMA N-tile of query rows
+    constexpr int ROWS = 32 * NR;            // NR MFMA N-tiles of query rows
     constexpr int T = ROWS / GQ;             // tokens per workgroup
     constexpr int CMAX = 32 * NW * MT;       // chunks the workgroup can hold
     constexpr int NPL = CMAX / 64;           // row slots per lane when a wave owns a row
@@ -148,64 +196,69 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
         *reinterpret_cast<uint4*>(&qs[row * QS + 8 * d8]) = u;
     }
     __syncthreads();
-    f32x16_t X[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) X[mt] = f32x16_t{};
-    const float* kb_base = kbar + ((int64_t)b * p.tc * p.h_kv + r) * D;
-    // summary rows of this lane's chunk in each tile; the 16-d slice ks + 1 is in flight while
-    // slice ks is split and multiplied
-    const float4* src[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int c = min(32 * (wave + NW * mt) + j, p.tc - 1);
-        src[mt] = reinterpret_cast<const float4*>(kb_base + (int64_t)c * p.h_kv * D + 8 * G);
-    }
-    float4 cur[MT][2], nxt[MT][2];
+    f32x16_t X[MT][NR];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        if (wave + NW * mt < n_ct) { cur[mt][0] = src[mt][0]; cur[mt][1] = src[mt][1]; }
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr) X[mt][nr] = f32x16_t{};
+    // A fragments of this wave's chunk tiles (hi, mid, lo of each 16-d slice, 1 KiB per wave and
+    // term); the slice ks + 1 is in flight while slice ks is multiplied
+    const int ct_n = div_up(p.tc, 32);
+    const uint4* src[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int ct = min(wave + NW * mt, ct_n - 1);
+        src[mt] = reinterpret_cast<const uint4*>(planes) +
+                  ((int64_t)(b * p.h_kv + r) * ct_n + ct) * (D / 16) * 3 * 64 + lane;
+    }
+    uint4 cur[MT][3], nxt[MT][3];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        if (wave + NW * mt < n_ct) {
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) cur[mt][pl] = src[mt][pl * 64];
+        }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         if (ks + 1 < D / 16) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 if (wave + NW * mt < n_ct) {
-                    nxt[mt][0] = src[mt][4 * (ks + 1)];
-                    nxt[mt][1] = src[mt][4 * (ks + 1) + 1];
+#pragma unroll
+                    for (int pl = 0; pl < 3; ++pl) nxt[mt][pl] = src[mt][((ks + 1) * 3 + pl) * 64];
                 }
         }
-        const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(&qs[j * QS + 16 * ks + 8 * G]);
+        bf16x8_t qf[NR];
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr)
+            qf[nr] = *reinterpret_cast<const bf16x8_t*>(&qs[(32 * nr + j) * QS + 16 * ks + 8 * G]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             if (wave + NW * mt >= n_ct) break;
-            const float4 v0 = cur[mt][0], v1 = cur[mt][1];
-            const float kv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            bf16x8_t hi, mid, lo;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const __bf16 h = (__bf16)kv[u];
-                const float r1 = kv[u] - (float)h;
-                const __bf16 md = (__bf16)r1;
-                hi[u] = h;
-                mid[u] = md;
-                lo[u] = (__bf16)(r1 - (float)md);
+            for (int nr = 0; nr < NR; ++nr) {
+#pragma unroll
+                for (int pl = 2; pl >= 0; --pl)  // lo, mid, hi: the small terms first
+                    X[mt][nr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, cur[mt][pl]), qf[nr], X[mt][nr], 0, 0, 0);
             }
-            X[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, qf, X[mt], 0, 0, 0);
-            X[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, qf, X[mt], 0, 0, 0);
-            X[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, qf, X[mt], 0, 0, 0);
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) { cur[mt][0] = nxt[mt][0]; cur[mt][1] = nxt[mt][1]; }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) cur[mt][pl] = nxt[mt][pl];
     }
     __syncthreads();  // Q is dead; its LDS now takes the score rows
-    // lane (j, G) holds row j, chunks 32 ct + 8 (rr / 4) + 4 G + rr % 4
+    // lane (j, G) holds row 32 nr + j, chunks 32 ct + 8 (rr / 4) + 4 G + rr % 4
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int ct = wave + NW * mt;
         if (ct >= n_ct) break;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-            xs[j * XS + 32 * ct + 8 * (rr >> 2) + 4 * G + (rr & 3)] = coef * X[mt][rr];
+        for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+                xs[(32 * nr + j) * XS + 32 * ct + 8 * (rr >> 2) + 4 * G + (rr & 3)] = coef * X[mt][nr][rr];
     }
     __syncthreads();
 
@@ -232,15 +285,15 @@ bool route_fused_supported(const RouteParams& p, int dt) {
     return dt == kBF16 && p.tc <= 1024 && p.n_q > 1 && p.nw <= 2 * (p.tc <= 512 ? 8 : 16);
 }
 
-template <int D, int GQ, int MT, int NW>
-static void launch_fused_shape(const void* q, const float* kbar, uint32_t* mask, float* bias,
+template <int D, int GQ, int MT, int NW, int NR>
+static void launch_fused_shape(const void* q, const bf16_t* kbar, uint32_t* mask, float* bias,
                                float* tau, const RouteParams& p, float coef, hipStream_t st) {
-    constexpr int T = 32 / GQ;
+    constexpr int T = 32 * NR / GQ;
     const int n_tiles = div_up(p.n_q, T);
     dim3 grid(p.batch * p.h_kv * n_tiles), block(NW * 64);
     const int kind = pow_kind(p.alpha);
 #define DASH_FUSED(K)                                                                        \
-    hipLaunchKernelGGL((route_fused_kernel<D, GQ, MT, NW, K>), grid, block, 0, st,          \
+    hipLaunchKernelGGL((route_fused_kernel<D, GQ, MT, NW, NR, K>), grid, block, 0, st,      \
                        static_cast<const bf16_t*>(q), kbar, mask, bias, tau, p, n_tiles, coef)
     if (kind == kPowOne) DASH_FUSED(kPowOne);
     else if (kind == kPowTwo) DASH_FUSED(kPowTwo);
@@ -248,17 +301,18 @@ static void launch_fused_shape(const void* q, const float* kbar, uint32_t* mask,
 #undef DASH_FUSED
 }
 
-// two 32-chunk tiles per wave; the LDS of a workgroup (32 score rows) then allows 16 waves per CU
+// (MT, NW, NR) per row length: 16 waves per CU, and as many query rows per workgroup as the LDS
+// of their score rows allows (each summary fragment is loaded once per workgroup)
 template <int D, int GQ>
-static void launch_fused_g(const void* q, const float* kbar, uint32_t* mask, float* bias,
+static void launch_fused_g(const void* q, const bf16_t* kbar, uint32_t* mask, float* bias,
                            float* tau, const RouteParams& p, float coef, hipStream_t st) {
-    if (p.tc <= 256) launch_fused_shape<D, GQ, 2, 4>(q, kbar, mask, bias, tau, p, coef, st);
-    else if (p.tc <= 512) launch_fused_shape<D, GQ, 2, 8>(q, kbar, mask, bias, tau, p, coef, st);
-    else launch_fused_shape<D, GQ, 2, 16>(q, kbar, mask, bias, tau, p, coef, st);
+    if (p.tc <= 256) launch_fused_shape<D, GQ, 2, 4, 1>(q, kbar, mask, bias, tau, p, coef, st);
+    else if (p.tc <= 512) launch_fused_shape<D, GQ, 2, 8, 1>(q, kbar, mask, bias, tau, p, coef, st);
+    else launch_fused_shape<D, GQ, 2, 16, 1>(q, kbar, mask, bias, tau, p, coef, st);
 }
 
 template <int D>
-static void launch_fused_d(const void* q, const float* kbar, uint32_t* mask, float* bias,
+static void launch_fused_d(const void* q, const bf16_t* kbar, uint32_t* mask, float* bias,
                            float* tau, const RouteParams& p, float coef, hipStream_t st) {
     switch (p.g) {
         case 1: launch_fused_g<D, 1>(q, kbar, mask, bias, tau, p, coef, st); break;
@@ -269,11 +323,21 @@ static void launch_fused_d(const void* q, const float* kbar, uint32_t* mask, flo
     }
 }
 
+size_t route_fused_workspace_bytes(const RouteParams& p) {
+    return (size_t)p.batch * p.h_kv * div_up(p.tc, 32) * 32 * 3 * p.head_dim * sizeof(bf16_t);
+}
+
 hipError_t launch_route_fused(const void* q, const float* kbar, uint32_t* mask, float* bias,
-                              float* tau, const RouteParams& p, hipStream_t st) {
+                              float* tau, const RouteParams& p, void* ws, hipStream_t st) {
     const float coef = (p.alpha - 1.0f) * p.gamma / sqrtf((float)p.head_dim);
-    if (p.head_dim == 64) launch_fused_d<64>(q, kbar, mask, bias, tau, p, coef, st);
-    else launch_fused_d<128>(q, kbar, mask, bias, tau, p, coef, st);
+    bf16_t* planes = static_cast<bf16_t*>(ws);
+    if (p.tc > 0) {
+        const int64_t n = (int64_t)p.batch * p.h_kv * div_up(p.tc, 32) * (p.head_dim / 16) * 64;
+        hipLaunchKernelGGL(split_kbar_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           kbar, planes, p.batch, p.tc, p.h_kv, p.head_dim);
+    }
+    if (p.head_dim == 64) launch_fused_d<64>(q, planes, mask, bias, tau, p, coef, st);
+    else launch_fused_d<128>(q, planes, mask, bias, tau, p, coef, st);
     return hipGetLastError();
 }
 

@@ -78,7 +78,8 @@ def test_block_entmax_rejects_bad_arguments(L):
     assert call(q_pos0=1) == 1 and "q_pos0" in err(L)
     assert call(mask=None) == 1 and "null" in err(L)
     need = L.dash_block_entmax_workspace_bytes(1, 1, 64, 0, 64, 4, 2, 128, 64)
-    assert need == 0  # bf16 prefill routes on chip
+    assert need == 1 * 2 * 32 * 3 * 128 * 2  # bf16 prefill: a tile of 32 summaries, three bf16 terms
+    assert L.dash_block_entmax_workspace_bytes(1, 1, 40, 0, 40, 4, 2, 128, 64) == 0  # no summary
     need = L.dash_block_entmax_workspace_bytes(0, 1, 64, 0, 64, 4, 2, 128, 64)
     assert need == 64 * 4 * 1 * 4  # fp32 scores through the workspace
     assert call(dt=0, wsb=need - 1) == 3 and "workspace" in err(L)
