@@ -42,6 +42,9 @@ hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, int 
 hipError_t launch_attn_prefill_mfma(const void* q, const void* k, const void* v,
                                    const uint32_t* mask, const float* bias, void* o, float* lse,
                                    const AttnParams& p, hipStream_t st);
+hipError_t launch_attn_prefill_dma(const void* q, const void* k, const void* v,
+                                  const uint32_t* mask, const float* bias, void* o, float* lse,
+                                  const AttnParams& p, hipStream_t st);
 size_t decode_workspace_bytes(const AttnParams& p);
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, int dt,
                               const uint32_t* mask, const float* bias, void* o,

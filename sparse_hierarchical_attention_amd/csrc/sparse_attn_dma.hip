@@ -1,0 +1,367 @@
+// Stage 2 prefill for head dim 128 on bf16 MFMA, with K and V tiles moved by direct global->LDS
+// loads ("DashAttention", arXiv 2605.18753v1, §3.3-3.4 Prop. 1; App. G Alg. 3), gfx950.
+//
+// A workgroup (4 waves) owns 128 query rows of one (sequence b, KV group r): T = 128 / g
+// consecutive tokens times the g heads of the group, row = token * g + head. All rows share the
+// group's chunk selection per token, so the workgroup walks the union of its tokens' selected
+// chunks (their own diagonal chunks included) and masks, per row, the chunks its token did not
+// select. Chunks are cut into tiles of up to 64 keys.
+//
+// Tiles reach LDS through global_load_lds_dwordx4: each wave instruction writes 1 KiB (lane i at
+// byte 16 i) straight into LDS, so the next tile streams in while the current one is multiplied,
+// with no registers held and nothing for the compiler to reorder. K and V tiles are stored as
+// rows of 256 bytes with the 16-byte piece p of row r at slot p ^ swz(r), swz(r) = 4 (r % 4) +
+// (r / 4) % 4; a lane chooses which piece it fetches so that the slots come out swizzled. With
+// this layout the K reads of a 16-lane group (16 rows, one piece) and the transposing V reads of
+// a 32-lane group (4 rows, 4 pieces, 2 halves) touch distinct banks. Two buffers each for K and
+// V are separate LDS objects and the tile loop is unrolled by two, so the compiler sees that the
+// reads of one buffer never wait for the loads into the other.
+//
+// Per wave (32 rows) and tile, with v_mfma_f32_32x32x16_bf16:
+//   S^T = K Q^T   A = K rows (ds_read_b128), B = the wave's Q rows held in registers for the
+//                 whole kernel; lane l of the accumulator holds query row l % 32 and 16 keys.
+//   O^T += V^T P^T  B = P straight from the S accumulator (converted to bf16), A = V^T read with
+//                 ds_read_b64_tr_b16: inside each 16-lane group the four 64-bit loads of lanes
+//                 4v .. 4v + 3 form key v, and lane i receives dimension i of keys 0..3, which
+//                 is the run of four keys the lane's P slots refer to.
+// Softmax in the log2 domain: x = s * scale * log2(e) + d * log2(e). The running maximum m is
+// only raised when a tile's maximum exceeds it by more than 8 (so exp2(x - m) <= 256 and the
+// output, normalised by the sum taken against the same m, is unchanged); p = exp2(x - m) is a
+// single FMA and exp2 per score. A row whose token did not select the chunk has x = -inf; the
+// query's own chunk is causally masked.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dash {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kD = 128;              // head dim of this kernel
+constexpr int kRows = 128;           // query rows per workgroup
+constexpr int kThreads = 256;
+constexpr int kTile = 64;            // keys per LDS tile (at most)
+constexpr int kWords = 256;          // mask words of the union (8192 chunks)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.0f;     // log2 headroom before the running maximum is raised
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+__device__ __forceinline__ i16x4 ds_read_tr16(const bf16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)(p));
+}
+
+}  // namespace
+
+template <int BLK, int GQ>
+__global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const uint32_t* __restrict__ mask, const float* __restrict__ bias, bf16_t* __restrict__ o,
+    float* __restrict__ lse, AttnParams p, int n_tiles) {
+    constexpr int T = kRows / GQ;            // tokens per workgroup
+    constexpr int KT = BLK < kTile ? BLK : kTile;  // keys per tile
+    constexpr int NSUB = BLK / KT;
+    constexpr int MT = KT / 32;              // 32-key M-tiles of S^T
+    constexpr int KSTEP = KT / 16;           // 16-key k-steps of P V
+    constexpr int DT = kD / 32;              // 32-dim M-tiles of O^T
+    constexpr int ROWS_W = KT / 4;           // tile rows each wave loads
+    constexpr int NLD = ROWS_W / 4;          // load instructions per wave and tensor (4 rows each)
+    __shared__ __align__(16) bf16_t K0[KT * kD];
+    __shared__ __align__(16) bf16_t K1[KT * kD];
+    __shared__ __align__(16) bf16_t V0[KT * kD];
+    __shared__ __align__(16) bf16_t V1[KT * kD];
+    __shared__ uint32_t uni[kWords];
+
+    int gr;
+    {
+        const int bh = p.batch * p.h_kv, x = blockIdx.x;
+        gr = bh % 8 == 0 ? (x % 8) + 8 * ((x / 8) % (bh / 8)) : x % bh;
+    }
+    const int tile = n_tiles - 1 - blockIdx.x / (p.batch * p.h_kv);
+    const int b = gr / p.h_kv, r = gr % p.h_kv;
+    const int n = p.n_kv;
+    const int tile0 = tile * T;
+    const int tile_end = min(tile0 + T, n);
+    const int c_first = tile0 / BLK, c_last = (tile_end - 1) / BLK;
+    const int nwt = c_last / 32 + 1;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 31, G = lane >> 5;
+    const int row = wave * 32 + j;
+    const int tok = row / GQ, hl = row % GQ;
+    const int pos = tile0 + tok;
+    const bool valid = pos < n;
+    const int cpos = pos / BLK;
+    const int64_t qrow = (int64_t)b * p.n_q + pos;
+    const int64_t qrow_c = (int64_t)b * p.n_q + min(pos, n - 1);  // rows past the end read row n - 1
+    const uint32_t* mrow = mask + (qrow_c * p.h_kv + r) * p.nw;
+    const float* brow = bias + (qrow_c * p.h_kv + r) * p.nc;
+
+    // union of the tile tokens' selections (bits past a token's own chunk ignored)
+    for (int w = tid; w < nwt; w += kThreads) uni[w] = 0u;
+    __syncthreads();
+    for (int idx = tid; idx < T * nwt; idx += kThreads) {
+        const int t = idx / nwt, w = idx % nwt;
+        const int ps = tile0 + t;
+        if (ps >= n) continue;
+        const int hi = ps / BLK - 32 * w;
+        if (hi < 0) continue;
+        uint32_t word = mask[(((int64_t)b * p.n_q + ps) * p.h_kv + r) * p.nw + w];
+        if (hi < 31) word &= (2u << hi) - 1u;
+        if (hi < 32) word |= 1u << hi;
+        if (word) atomicOr(&uni[w], word);
+    }
+    __syncthreads();
+    // the union's next chunk after c (-1 when none): the same walk in every thread
+    auto next_chunk = [&](int c) -> int {
+        int w = (c + 1) >> 5;
+        if (w >= nwt) return -1;
+        uint32_t word = uni[w] & (~0u << ((c + 1) & 31));
+        while (true) {
+            if (word) return 32 * w + __builtin_ctz(word);
+            if (++w >= nwt) return -1;
+            word = uni[w];
+        }
+    };
+
+    // this wave's Q rows as the B operand of S^T = K Q^T (k-slot order shared with K's reads)
+    bf16x8 qf[kD / 16];
+    {
+        const bf16_t* qp = q + (qrow_c * p.h_q + r * GQ + hl) * kD + 8 * G;
+#pragma unroll
+        for (int s = 0; s < kD / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 16 * s));
+    }
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+    float m_used = -INFINITY, l_run = 0.f;
+    const float qk_scale = p.scale * kLog2e;
+    const int64_t kv_row_stride = (int64_t)p.h_kv * kD;
+    const bf16_t* kbase = k + (int64_t)b * n * kv_row_stride + (int64_t)r * kD;
+    const bf16_t* vbase = v + (int64_t)b * n * kv_row_stride + (int64_t)r * kD;
+
+    // LDS element offsets of this lane's reads: K piece 2 ks + G of row j (+ 32 mt rows), and the
+    // transposing V reads of rows v_key (+ 8) at dims 32 dt + v_dim (+ 16 ks rows)
+    int koff[kD / 16];
+    {
+        const int gs = G ^ swz(j);
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) koff[ks] = j * kD + ((2 * ks) ^ gs) * 8;
+    }
+    int voff[DT][2];
+    {
+        const int grp = lane >> 4, kl = lane & 15;
+        const int v_key = 4 * (grp >> 1) + (kl >> 2);
+        const int c1 = 2 * (grp & 1) + ((kl & 3) >> 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rr = v_key + 8 * h;
+                voff[dt][h] = rr * kD + ((4 * dt) ^ c1 ^ swz(rr)) * 8 + 4 * (kl & 1);
+            }
+    }
+
+    // one tile (chunk c, 64-key part sub) into K / V buffers: wave w fills rows
+    // ROWS_W w .. ROWS_W (w + 1) - 1, four rows per instruction; lane i fetches the piece that
+    // lands at slot i % 16 of row i / 16. Rows past the sequence are clamped to its last row
+    // (every query masks them causally, and real rows keep P V finite).
+    auto dma = [&](bf16_t* Kd, bf16_t* Vd, int c, int sub) __attribute__((always_inline)) {
+        const int key0 = c * BLK + sub * KT;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int row0 = ROWS_W * wave + 4 * i;
+            const int rr = row0 + (lane >> 4);
+            const int key = min(key0 + rr, n - 1);
+            const int piece = (lane & 15) ^ swz(rr);
+            const int64_t go = key * kv_row_stride + piece * 8;
+            __builtin_amdgcn_global_load_lds(kbase + go, (lds_void*)(Kd + row0 * kD), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vbase + go, (lds_void*)(Vd + row0 * kD), 16, 0, 0);
+        }
+    };
+
+    int c = next_chunk(-1), sub = 0;  // every tile has at least its own chunk
+    // this row's mask word and bias for a chunk, loaded without a branch (chunk clamped into
+    // range); they are loaded one tile ahead, before that tile's K and V, so that they have
+    // landed by the barrier that ends the tile before and are read without waiting
+    uint32_t mword;
+    float dval;
+    auto row_view = [&](int cc) __attribute__((always_inline)) {
+        const int cq = valid ? min(cc, cpos) : 0;
+        mword = mrow[cq >> 5];
+        dval = brow[cq];
+    };
+
+    // the work on one tile held in (Kc, Vc), while the next one streams into (Kn, Vn)
+    auto step = [&](const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn)
+        __attribute__((always_inline)) {
+        const int key0 = c * BLK + sub * KT;
+        const bool sel = valid && c <= cpos && (c == cpos || ((mword >> (c & 31)) & 1u));
+        const float dcur = dval;
+        const int c_nx = sub + 1 < NSUB ? c : next_chunk(c);
+        const int sub_nx = sub + 1 < NSUB ? sub + 1 : 0;
+        // after the last tile the current one is loaded again into the idle buffers (never read)
+        const int c_ld = c_nx >= 0 ? c_nx : c;
+        row_view(c_ld);
+        dma(Kn, Vn, c_ld, c_nx >= 0 ? sub_nx : sub);
+        const float sc = sel ? qk_scale : 0.f;
+        const float off = sel ? (c == cpos ? 0.f : dcur * kLog2e) : -INFINITY;
+        const bool causal = c >= c_first;  // some row's own chunk: mask keys past each row
+
+        // S^T = K Q^T
+        f32x16 s[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            s[mt] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < kD / 16; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + koff[ks] + mt * 32 * kD);
+                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mt], 0, 0, 0);
+            }
+        }
+        // row maximum of x = s * sc + off (sc >= 0)
+        float xmax;
+        if (causal) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
+                    const float x = fmaf(s[mt][rr], sc, off);
+                    s[mt][rr] = key > pos ? -INFINITY : x;
+                }
+            xmax = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) xmax = fmaxf(xmax, s[mt][rr]);
+        } else {
+            float smax = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) smax = fmaxf(smax, s[mt][rr]);
+            xmax = sel ? fmaf(smax, sc, off) : -INFINITY;
+        }
+        xmax = fmaxf(xmax, __shfl_xor(xmax, 32, kWave));
+        // raise the running maximum only when needed (rare once a row has seen its peak)
+        const bool raise = xmax > m_used + kLazyMax;
+        if (__any(raise)) {
+            const float m_new = raise ? xmax : m_used;
+            const float corr = m_used == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used - m_new);
+            l_run *= corr;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
+            m_used = m_new;
+        }
+        const float m_ref = m_used == -INFINITY ? 0.f : m_used;
+        float rsum = 0.f;
+        bf16x8 pf[KSTEP];
+        if (causal) {
+#pragma unroll
+            for (int ks = 0; ks < KSTEP; ++ks)
+#pragma unroll
+                for (int vv = 0; vv < 8; ++vv) {
+                    const float pe = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + vv] - m_ref);
+                    rsum += pe;
+                    pf[ks][vv] = (__bf16)pe;
+                }
+        } else {
+            const float off_m = off - m_ref;
+#pragma unroll
+            for (int ks = 0; ks < KSTEP; ++ks)
+#pragma unroll
+                for (int vv = 0; vv < 8; ++vv) {
+                    const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + vv], sc, off_m));
+                    rsum += pe;
+                    pf[ks][vv] = (__bf16)pe;
+                }
+        }
+        l_run += rsum + __shfl_xor(rsum, 32, kWave);
+
+        // O^T += V^T P^T, V^T through transposing reads
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const i16x4 lo = ds_read_tr16(Vc + voff[dt][0] + ks * 16 * kD);
+                const i16x4 hi = ds_read_tr16(Vc + voff[dt][1] + ks * 16 * kD);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[dt], 0, 0, 0);
+            }
+        // the next tile has landed in every wave's part, and every wave is done with this one
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        __syncthreads();
+        c = c_nx;
+        sub = sub_nx;
+    };
+
+    row_view(c);
+    dma(K0, V0, c, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    while (true) {
+        step(K0, V0, K1, V1);
+        if (c < 0) break;
+        step(K1, V1, K0, V0);
+        if (c < 0) break;
+    }
+
+    if (!valid) return;
+    const float inv_l = 1.0f / l_run;
+    bf16_t* orow = o + (qrow * p.h_q + r * GQ + hl) * kD;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const int d0 = 32 * dt + 8 * qd + 4 * G;
+            bf16x4 ov;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ov[u] = (__bf16)(acc[dt][4 * qd + u] * inv_l);
+            *reinterpret_cast<bf16x4*>(orow + d0) = ov;
+        }
+    if (lse && G == 0) lse[qrow * p.h_q + r * GQ + hl] = (m_used + __log2f(l_run)) * kLn2;
+}
+
+template <int BLK>
+static void launch_dma_blk(const void* q, const void* k, const void* v, const uint32_t* mask,
+                           const float* bias, void* o, float* lse, const AttnParams& p,
+                           hipStream_t st) {
+    const int T = kRows / p.g;
+    const int n_tiles = div_up(p.n_kv, T);
+    dim3 grid(p.batch * p.h_kv * n_tiles);
+#define DASH_DMA(GG)                                                                        \
+    hipLaunchKernelGGL((attn_dma_kernel<BLK, GG>), grid, dim3(kThreads), 0, st,             \
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),        \
+                       static_cast<const bf16_t*>(v), mask, bias, static_cast<bf16_t*>(o), \
+                       lse, p, n_tiles)
+    switch (p.g) {
+        case 1: DASH_DMA(1); break;
+        case 2: DASH_DMA(2); break;
+        case 4: DASH_DMA(4); break;
+        case 8: DASH_DMA(8); break;
+        default: DASH_DMA(16); break;
+    }
+#undef DASH_DMA
+}
+
+hipError_t launch_attn_prefill_dma(const void* q, const void* k, const void* v,
+                                  const uint32_t* mask, const float* bias, void* o, float* lse,
+                                  const AttnParams& p, hipStream_t st) {
+    if (p.block == 32) launch_dma_blk<32>(q, k, v, mask, bias, o, lse, p, st);
+    else if (p.block == 64) launch_dma_blk<64>(q, k, v, mask, bias, o, lse, p, st);
+    else launch_dma_blk<128>(q, k, v, mask, bias, o, lse, p, st);
+    return hipGetLastError();
+}
+
+}  // namespace dash

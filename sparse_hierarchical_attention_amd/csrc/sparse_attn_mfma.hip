@@ -323,11 +323,12 @@ static void launch_mfma_d(const void* q, const void* k, const void* v, const uin
     else launch_mfma_blk<D, 128>(q, k, v, mask, bias, o, lse, p, st);
 }
 
+// head dim 64 here; head dim 128 streams its tiles with direct LDS loads (sparse_attn_dma.hip)
 hipError_t launch_attn_prefill_mfma(const void* q, const void* k, const void* v,
                                    const uint32_t* mask, const float* bias, void* o, float* lse,
                                    const AttnParams& p, hipStream_t st) {
-    if (p.head_dim == 64) launch_mfma_d<64>(q, k, v, mask, bias, o, lse, p, st);
-    else launch_mfma_d<128>(q, k, v, mask, bias, o, lse, p, st);
+    if (p.head_dim != 64) return launch_attn_prefill_dma(q, k, v, mask, bias, o, lse, p, st);
+    launch_mfma_d<64>(q, k, v, mask, bias, o, lse, p, st);
     return hipGetLastError();
 }
 
