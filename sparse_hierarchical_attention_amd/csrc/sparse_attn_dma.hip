@@ -218,17 +218,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
         const float off = sel ? (c == cpos ? 0.f : dcur * kLog2e) : -INFINITY;
         const bool causal = c >= c_first;  // some row's own chunk: mask keys past each row
 
-        // S^T = K Q^T
+        // S^T = K Q^T, the M-tiles' accumulation chains interleaved
         f32x16 s[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            s[mt] = f32x16{};
+        for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < kD / 16; ++ks) {
+        for (int ks = 0; ks < kD / 16; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + koff[ks] + mt * 32 * kD);
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mt], 0, 0, 0);
             }
-        }
         // row maximum of x = s * sc + off (sc >= 0)
         float xmax;
         if (causal) {
