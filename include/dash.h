@@ -128,6 +128,8 @@ dash_status_t dash_block_entmax(const void* q, dash_dtype_t dt, const float* kba
  * tokens c_t * Bc .. t of the query's own chunk (d = 0). mask / bias as dash_block_entmax writes
  * them for n_q = n, q_pos0 = 0. scale is normally 1/sqrt(D). lse (natural log of the softmax
  * normaliser, bias included) may be NULL. All query heads of a group share one selection.
+ * bf16 with D = 128 needs one sequence's keys to fit 2 GiB (n * H_kv * D * 2 bytes), else
+ * DASH_ERR_UNSUPPORTED.
  */
 dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                        dash_dtype_t dt, const uint32_t* mask, const float* bias,

@@ -1,5 +1,6 @@
 // libdash C ABI: argument validation, dispatch and launch (see include/dash.h).
 #include <math.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -160,6 +161,9 @@ dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void*
     if (s != DASH_OK) return s;
     if (!(scale > 0.0f) || isinf(scale)) return fail(DASH_ERR_INVALID, "%s: scale=%g must be positive and finite", fn, scale);
     if (!q || !k || !v || !mask || !bias || !o) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    // bf16 head dim 128 addresses one sequence's keys (and values) with 32-bit byte offsets
+    if (dt == DASH_BF16 && head_dim == 128 && (int64_t)n * h_kv * head_dim * 2 > INT32_MAX)
+        return fail(DASH_ERR_UNSUPPORTED, "%s: one sequence's keys (n * h_kv * head_dim bf16) exceed 2 GiB", fn);
     dash::AttnParams p = attn_params(batch, n, 0, n, h_q, h_kv, head_dim, block, scale);
     return hip_status(dash::launch_attn_prefill(q, k, v, dt, mask, bias, o, lse, p, stream), fn);
 }

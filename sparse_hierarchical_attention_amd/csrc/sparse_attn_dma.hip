@@ -7,8 +7,8 @@
 // chunks (their own diagonal chunks included) and masks, per row, the chunks its token did not
 // select. Chunks are cut into tiles of up to 64 keys.
 //
-// Tiles reach LDS through global_load_lds_dwordx4: each wave instruction writes 1 KiB (lane i at
-// byte 16 i) straight into LDS, so the next tile streams in while the current one is multiplied,
+// Tiles reach LDS through buffer_load_dwordx4 ... lds: each wave instruction writes 1 KiB (lane i
+// at byte 16 i) straight into LDS, so the next tile streams in while the current one is multiplied,
 // with no registers held and nothing for the compiler to reorder. K and V tiles are stored as
 // rows of 256 bytes with the 16-byte piece p of row r at slot p ^ swz(r), swz(r) = 4 (r % 4) +
 // (r / 4) % 4; a lane chooses which piece it fetches so that the slots come out swizzled. With
@@ -67,6 +67,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const uint32_t* __restrict__ mask, const float* __restrict__ bias, bf16_t* __restrict__ o,
     float* __restrict__ lse, AttnParams p, int n_tiles) {
+    // the body is device code only: the buffer descriptors it builds have no host type, and the
+    // host pass needs just the launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
     constexpr int T = kRows / GQ;            // tokens per workgroup
     constexpr int KT = BLK < kTile ? BLK : kTile;  // keys per tile
     constexpr int NSUB = BLK / KT;
@@ -174,19 +177,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
 
     // one tile (chunk c, 64-key part sub) into K / V buffers: wave w fills rows
     // ROWS_W w .. ROWS_W (w + 1) - 1, four rows per instruction; lane i fetches the piece that
-    // lands at slot i % 16 of row i / 16. Rows past the sequence are clamped to its last row
-    // (every query masks them causally, and real rows keep P V finite).
+    // lands at slot i % 16 of row i / 16. The loads go through buffer descriptors over this
+    // (sequence, KV head)'s rows: each lane's byte offset within a tile is fixed, the tile's start
+    // is one scalar offset, and rows past the sequence fall outside the descriptor's range and
+    // read as zero (every query masks them causally).
+    const uint32_t row_bytes = (uint32_t)kv_row_stride * 2u;
+    const uint32_t span = (uint32_t)((n - 1) * kv_row_stride + kD) * 2u;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, (int)span, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, (int)span, 0x00020000);
+    uint32_t loff[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int rr = ROWS_W * wave + 4 * i + (lane >> 4);
+        loff[i] = rr * row_bytes + (uint32_t)(((lane & 15) ^ swz(rr)) * 16);
+    }
     auto dma = [&](bf16_t* Kd, bf16_t* Vd, int c, int sub) __attribute__((always_inline)) {
-        const int key0 = c * BLK + sub * KT;
+        const uint32_t soff = (uint32_t)(c * BLK + sub * KT) * row_bytes;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int row0 = ROWS_W * wave + 4 * i;
-            const int rr = row0 + (lane >> 4);
-            const int key = min(key0 + rr, n - 1);
-            const int piece = (lane & 15) ^ swz(rr);
-            const int64_t go = key * kv_row_stride + piece * 8;
-            __builtin_amdgcn_global_load_lds(kbase + go, (lds_void*)(Kd + row0 * kD), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vbase + go, (lds_void*)(Vd + row0 * kD), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(Kd + row0 * kD), 16, loff[i], soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(Vd + row0 * kD), 16, loff[i], soff, 0, 0);
         }
     };
 
@@ -331,6 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
             *reinterpret_cast<bf16x4*>(orow + d0) = ov;
         }
     if (lse && G == 0) lse[qrow * p.h_q + r * GQ + hl] = (m_used + __log2f(l_run)) * kLn2;
+#endif
 }
 
 template <int BLK>
