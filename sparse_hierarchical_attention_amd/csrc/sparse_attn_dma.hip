@@ -229,7 +229,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
         const float off = sel ? (c == cpos ? 0.f : dcur * kLog2e) : -INFINITY;
         const bool causal = c >= c_first;  // some row's own chunk: mask keys past each row
 
-        // S^T = K Q^T, the M-tiles' accumulation chains interleaved
+        // S^T = K Q^T, the M-tiles' accumulation chains interleaved. The MFMA blocks run at a
+        // raised wave priority, so that of the two waves sharing a SIMD the one starting its
+        // matrix work issues first and the other's softmax fills the issue slots meanwhile.
+        __builtin_amdgcn_s_setprio(1);
         f32x16 s[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
@@ -240,6 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + koff[ks] + mt * 32 * kD);
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mt], 0, 0, 0);
             }
+        __builtin_amdgcn_s_setprio(0);
         // row maximum of x = s * sc + off (sc >= 0)
         float xmax;
         if (causal) {
@@ -301,6 +305,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
         l_run += rsum + __shfl_xor(rsum, 32, kWave);
 
         // O^T += V^T P^T, V^T through transposing reads
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KSTEP; ++ks)
 #pragma unroll
@@ -310,6 +315,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
                 const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[dt], 0, 0, 0);
             }
+        __builtin_amdgcn_s_setprio(0);
         // the next tile has landed in every wave's part, and every wave is done with this one
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();
