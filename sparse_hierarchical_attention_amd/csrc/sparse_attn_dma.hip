@@ -9,13 +9,13 @@
 //
 // Tiles reach LDS through buffer_load_dwordx4 ... lds: each wave instruction writes 1 KiB (lane i
 // at byte 16 i) straight into LDS, so the next tile streams in while the current one is multiplied,
-// with no registers held and nothing for the compiler to reorder. K and V tiles are stored as
-// rows of 256 bytes with the 16-byte piece p of row r at slot p ^ swz(r), swz(r) = 4 (r % 4) +
-// (r / 4) % 4; a lane chooses which piece it fetches so that the slots come out swizzled. With
-// this layout the K reads of a 16-lane group (16 rows, one piece) and the transposing V reads of
-// a 32-lane group (4 rows, 4 pieces, 2 halves) touch distinct banks. Two buffers each for K and
-// V are separate LDS objects and the tile loop is unrolled by two, so the compiler sees that the
-// reads of one buffer never wait for the loads into the other.
+// with no registers held and nothing for the compiler to reorder. A tile's rows are stored in
+// NB = KT / 4 blocks of four 256-byte rows (row r in block r % NB at slot r / NB, one load
+// instruction per block); K blocks are 1040 bytes apart and V blocks 1088, so that the K reads
+// of a 16-lane group (16 rows, one piece) and the transposing V reads of a 32-lane group (4 rows,
+// 8 dims each) fall on distinct banks, and every read is a lane base plus a constant offset. Two
+// buffers each for K and V are separate LDS objects and the tile loop is unrolled by two, so
+// the compiler sees that the reads of one buffer never wait for the loads into the other.
 //
 // Per wave (32 rows) and tile, with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T   A = K rows (ds_read_b128), B = the wave's Q rows held in registers for the
@@ -54,7 +54,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 8.0f;     // log2 headroom before the running maximum is raised
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+constexpr int kKBlock = 520;         // elements between K blocks (1040 bytes)
+constexpr int kVBlock = 544;         // elements between V blocks (1088 bytes)
 
 __device__ __forceinline__ i16x4 ds_read_tr16(const bf16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)(p));
@@ -76,12 +77,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
     constexpr int MT = KT / 32;              // 32-key M-tiles of S^T
     constexpr int KSTEP = KT / 16;           // 16-key k-steps of P V
     constexpr int DT = kD / 32;              // 32-dim M-tiles of O^T
-    constexpr int ROWS_W = KT / 4;           // tile rows each wave loads
-    constexpr int NLD = ROWS_W / 4;          // load instructions per wave and tensor (4 rows each)
-    __shared__ __align__(16) bf16_t K0[KT * kD];
-    __shared__ __align__(16) bf16_t K1[KT * kD];
-    __shared__ __align__(16) bf16_t V0[KT * kD];
-    __shared__ __align__(16) bf16_t V1[KT * kD];
+    constexpr int NB = KT / 4;               // blocks of four rows per tile
+    constexpr int NLD = NB / 4;              // load instructions (blocks) per wave and tensor
+    __shared__ __align__(16) bf16_t K0[NB * kKBlock];
+    __shared__ __align__(16) bf16_t K1[NB * kKBlock];
+    __shared__ __align__(16) bf16_t V0[NB * kVBlock];
+    __shared__ __align__(16) bf16_t V1[NB * kVBlock];
     __shared__ uint32_t uni[kWords];
 
     int gr;
@@ -155,29 +156,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
 
     // LDS element offsets of this lane's reads: K piece 2 ks + G of row j (+ 32 mt rows), and the
     // transposing V reads of rows v_key (+ 8) at dims 32 dt + v_dim (+ 16 ks rows)
-    int koff[kD / 16];
-    {
-        const int gs = G ^ swz(j);
-#pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) koff[ks] = j * kD + ((2 * ks) ^ gs) * 8;
-    }
-    int voff[DT][2];
+    const int kl_base = (j % NB) * kKBlock + (j / NB) * kD + 8 * G;   // + mt (32 / NB) kD + 16 ks
+    int vl_base[2];                                                    // + ks (16 / NB) kD + 32 dt
     {
         const int grp = lane >> 4, kl = lane & 15;
         const int v_key = 4 * (grp >> 1) + (kl >> 2);
-        const int c1 = 2 * (grp & 1) + ((kl & 3) >> 1);
+        const int v_dim = 16 * (grp & 1) + 4 * (kl & 3);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int rr = v_key + 8 * h;
-                voff[dt][h] = rr * kD + ((4 * dt) ^ c1 ^ swz(rr)) * 8 + 4 * (kl & 1);
-            }
+        for (int h = 0; h < 2; ++h) {
+            const int rr = v_key + 8 * h;
+            vl_base[h] = (rr % NB) * kVBlock + (rr / NB) * kD + v_dim;
+        }
     }
 
-    // one tile (chunk c, 64-key part sub) into K / V buffers: wave w fills rows
-    // ROWS_W w .. ROWS_W (w + 1) - 1, four rows per instruction; lane i fetches the piece that
-    // lands at slot i % 16 of row i / 16. The loads go through buffer descriptors over this
+    // one tile (chunk c, 64-key part sub) into K / V buffers: wave w fills blocks
+    // NLD w .. NLD (w + 1) - 1, one instruction each; lane i fetches piece i % 16 of the block's
+    // row i / 16, i.e. tile row b + NB (i / 16). The loads go through buffer descriptors over this
     // (sequence, KV head)'s rows: each lane's byte offset within a tile is fixed, the tile's start
     // is one scalar offset, and rows past the sequence fall outside the descriptor's range and
     // read as zero (every query masks them causally).
@@ -188,16 +182,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
     uint32_t loff[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-        const int rr = ROWS_W * wave + 4 * i + (lane >> 4);
-        loff[i] = rr * row_bytes + (uint32_t)(((lane & 15) ^ swz(rr)) * 16);
+        const int rr = NLD * wave + i + NB * (lane >> 4);
+        loff[i] = rr * row_bytes + (uint32_t)((lane & 15) * 16);
     }
     auto dma = [&](bf16_t* Kd, bf16_t* Vd, int c, int sub) __attribute__((always_inline)) {
         const uint32_t soff = (uint32_t)(c * BLK + sub * KT) * row_bytes;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            const int row0 = ROWS_W * wave + 4 * i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(Kd + row0 * kD), 16, loff[i], soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(Vd + row0 * kD), 16, loff[i], soff, 0, 0);
+            const int blk = NLD * wave + i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(Kd + blk * kKBlock), 16, loff[i], soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(Vd + blk * kVBlock), 16, loff[i], soff, 0, 0);
         }
     };
 
@@ -231,18 +225,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
 
         // S^T = K Q^T, the M-tiles' accumulation chains interleaved. The MFMA blocks run at a
         // raised wave priority, so that of the two waves sharing a SIMD the one starting its
-        // matrix work issues first and the other's softmax fills the issue slots meanwhile.
+        // matrix work issues first and the other's softmax fills the issue slots meanwhile. K
+        // fragments are read two k-steps ahead of their MFMAs (a ring of three), so that LDS
+        // latency stays off the matrix pipe.
         __builtin_amdgcn_s_setprio(1);
         f32x16 s[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
+        {
+            constexpr int KS = kD / 16;
+            bf16x8 ka[3][MT];
+            auto kread = [&](int ks, bf16x8 (&dst)[MT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks)
+                for (int mt = 0; mt < MT; ++mt)
+                    dst[mt] = *reinterpret_cast<const bf16x8*>(Kc + kl_base + mt * (32 / NB) * kD + 16 * ks);
+            };
+            kread(0, ka[0]);
+            kread(1, ka[1]);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + koff[ks] + mt * 32 * kD);
-                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mt], 0, 0, 0);
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 2 < KS) kread(ks + 2, ka[(ks + 2) % 3]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % 3][mt], qf[ks], s[mt], 0, 0, 0);
             }
+        }
         __builtin_amdgcn_s_setprio(0);
         // row maximum of x = s * sc + off (sc >= 0)
         float xmax;
@@ -304,17 +311,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
         }
         l_run += rsum + __shfl_xor(rsum, 32, kWave);
 
-        // O^T += V^T P^T, V^T through transposing reads
+        // O^T += V^T P^T, V^T through transposing reads issued one k-step ahead of their MFMAs
         __builtin_amdgcn_s_setprio(1);
+        {
+            bf16x8 va[2][DT];
+            auto vread = [&](int ks, bf16x8 (&dst)[DT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < KSTEP; ++ks)
+                for (int dt = 0; dt < DT; ++dt) {
+                    const i16x4 lo = ds_read_tr16(Vc + vl_base[0] + ks * (16 / NB) * kD + 32 * dt);
+                    const i16x4 hi = ds_read_tr16(Vc + vl_base[1] + ks * (16 / NB) * kD + 32 * dt);
+                    dst[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+            };
+            vread(0, va[0]);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const i16x4 lo = ds_read_tr16(Vc + voff[dt][0] + ks * 16 * kD);
-                const i16x4 hi = ds_read_tr16(Vc + voff[dt][1] + ks * 16 * kD);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[dt], 0, 0, 0);
+            for (int ks = 0; ks < KSTEP; ++ks) {
+                if (ks + 1 < KSTEP) vread(ks + 1, va[(ks + 1) & 1]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks & 1][dt], pf[ks], acc[dt], 0, 0, 0);
             }
+        }
         __builtin_amdgcn_s_setprio(0);
         // the next tile has landed in every wave's part, and every wave is done with this one
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
