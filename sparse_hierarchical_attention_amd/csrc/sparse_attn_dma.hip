@@ -5,7 +5,8 @@
 // consecutive tokens times the g heads of the group, row = token * g + head. All rows share the
 // group's chunk selection per token, so the workgroup walks the union of its tokens' selected
 // chunks (their own diagonal chunks included) and masks, per row, the chunks its token did not
-// select. Chunks are cut into tiles of up to 64 keys.
+// select. Chunks are cut into tiles of up to 32 keys, which keeps a workgroup at 35 KiB of LDS and
+// 167 VGPRs, so that three workgroups (three waves per SIMD) share a CU.
 //
 // Tiles reach LDS through buffer_load_dwordx4 ... lds: each wave instruction writes 1 KiB (lane i
 // at byte 16 i) straight into LDS, so the next tile streams in while the current one is multiplied,
@@ -48,7 +49,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kD = 128;              // head dim of this kernel
 constexpr int kRows = 128;           // query rows per workgroup
 constexpr int kThreads = 256;
-constexpr int kTile = 64;            // keys per LDS tile (at most)
+constexpr int kTile = 32;            // keys per LDS tile (at most)
 constexpr int kWords = 256;          // mask words of the union (8192 chunks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -64,7 +65,7 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const bf16_t* p) {
 }  // namespace
 
 template <int BLK, int GQ>
-__global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
+__global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const uint32_t* __restrict__ mask, const float* __restrict__ bias, bf16_t* __restrict__ o,
     float* __restrict__ lse, AttnParams p, int n_tiles) {
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dma_kernel(
         }
     }
 
-    // one tile (chunk c, 64-key part sub) into K / V buffers: wave w fills blocks
+    // one tile (chunk c, 32-key part sub) into K / V buffers: wave w fills blocks
     // NLD w .. NLD (w + 1) - 1, one instruction each; lane i fetches piece i % 16 of the block's
     // row i / 16, i.e. tile row b + NB (i / 16). The loads go through buffer descriptors over this
     // (sequence, KV head)'s rows: each lane's byte offset within a tile is fixed, the tile's start
