@@ -214,9 +214,9 @@ def main():
     wsd_b = dash.dash_block_entmax_workspace_bytes(qd.dtype, wd.batch, 1, wd.n_kv - 1, wd.n_kv,
                                                    wd.h_q, wd.h_kv, wd.head_dim, wd.block)
     route_ws_d = torch.empty(max(wsd_b, 1), dtype=torch.uint8, device=dev)
-    attn_ws_d = torch.empty(dash.dash_decode_workspace_bytes(wd.batch, wd.n_kv, wd.h_q, wd.h_kv,
-                                                             wd.head_dim, wd.block),
-                            dtype=torch.uint8, device=dev)
+    attn_ws_b = dash.dash_decode_workspace_bytes(wd.batch, wd.n_kv, wd.h_q, wd.h_kv, wd.head_dim,
+                                                 wd.block)
+    attn_ws_d = torch.empty(attn_ws_b, dtype=torch.uint8, device=dev) if attn_ws_b else None
 
     def step(timer: Timer | None):
         def ev(name):

@@ -210,9 +210,9 @@ def dash_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     if o is None:
         o = torch.empty_like(q)
     need = dash_decode_workspace_bytes(b, n_ctx, hq, hkv, d, block)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    wsb = workspace.numel() * workspace.element_size()
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dev = _dev(q, k_cache, v_cache, mask, bias, o, workspace)
     _check(lib().dash_sparse_attn_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(mask), _ptr(bias), _ptr(o),

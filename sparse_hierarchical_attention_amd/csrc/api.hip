@@ -187,7 +187,7 @@ dash_status_t dash_sparse_attn_decode(const void* q, const void* k_cache, const 
     if (!q || !k_cache || !v_cache || !mask || !bias || !o) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
     dash::AttnParams p = attn_params(batch, 1, n_ctx - 1, n_ctx, h_q, h_kv, head_dim, block, scale);
     const size_t need = dash::decode_workspace_bytes(p);
-    if (!workspace || workspace_bytes < need)
+    if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace ? workspace_bytes : (size_t)0);
     return hip_status(dash::launch_attn_decode(q, k_cache, v_cache, dt, mask, bias, o, p, workspace, stream), fn);

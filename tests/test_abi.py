@@ -98,3 +98,5 @@ def test_attention_rejects_bad_arguments(L):
                                      need - 1, None) == 3
     assert L.dash_sparse_attn_decode(p, p, p, 1, p, p, p, 2, 4096, 8, 2, 128, 64, 0.1, None,
                                      0, None) == 3
+    assert L.dash_sparse_attn_decode(p, p, p, 1, p, p, p, 2, 4096, 8, 2, 128, 64, 0.0, None,
+                                     0, None) == 1 and "scale" in err(L)

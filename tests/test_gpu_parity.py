@@ -202,6 +202,6 @@ def test_errors_raise(dash):
     with pytest.raises(dash.DashError, match="alpha"):
         dash.dash_block_entmax(q, kb, n_kv=64, block=64, alpha=2.5, gamma=1.0, sigma=1.0)
     with pytest.raises(dash.DashError, match="DASH_ERR_WORKSPACE"):
-        m, bsz, _ = dash.dash_block_entmax(q, kb, n_kv=64, block=64, alpha=1.5, gamma=1.0, sigma=1.0)
-        dash.dash_sparse_attn_decode(q[:, :1], k, k, m[:, :1], bsz[:, :1], block=64,
-                                     workspace=torch.empty(1, dtype=torch.uint8, device=DEV))
+        # one query per sequence scores through the workspace; one byte is too small
+        dash.dash_block_entmax(q[:, :1], kb, n_kv=64, block=64, alpha=1.5, gamma=1.0, sigma=1.0,
+                               q_pos0=63, workspace=torch.empty(1, dtype=torch.uint8, device=DEV))
