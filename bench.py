@@ -77,7 +77,7 @@ def decode_bytes(mask: torch.Tensor, w: wl.Workload) -> tuple[int, float]:
 
 # Sources each measured launch is built from: a counter summary taken on other sources is stale.
 KERNEL_SOURCES = {
-    "sparse_attn_prefill": ["common.h", "kernels.h", "sparse_attn_mfma.hip"],
+    "sparse_attn_prefill": ["common.h", "kernels.h", "sparse_attn_dma.hip"],
     "decode_step": ["common.h", "kernels.h", "entmax.h", "route_common.h", "block_entmax.hip",
                     "decode.hip"],
 }
