@@ -158,6 +158,115 @@ def cpu_baseline(pre_inp, dec_inp, wp: wl.Workload, wd: wl.Workload, pre_pairs_p
             "decode_tok_per_s": round(float(np.mean(tok_s)), 3)}
 
 
+def _time_ms(fn, reps: int, warm: int = 1) -> float:
+    """Mean HIP-event time of fn() on torch's current stream (the stream the library launches on)."""
+    for _ in range(warm):
+        fn()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def _sdpa_ms(q, k, v, causal: bool, reps: int):
+    """torch's fused scaled-dot-product attention (flash or memory-efficient kernel only, never
+    the math path) on [B, H, n, D] views, or None where this build offers neither for the shape."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import torch.nn.functional as F
+    qt, kt, vt = (x.transpose(1, 2) for x in (q, k, v))
+    for backend in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel([backend]):
+                return _time_ms(lambda: F.scaled_dot_product_attention(
+                    qt, kt, vt, is_causal=causal, enable_gqa=True), reps), backend.name
+        except RuntimeError:
+            continue
+    return None, None
+
+
+def random_mask_sweep(dash, dev, reps: int):
+    """The pages' efficiency sweep: Hq 32, Hkv 2, D 128, chunk 64, N in {16, 32, 64, 96}K, chunk
+    sparsity s in {75, 87.5, 93.75} %, prefill at batch 1 and decode at batch 24, with Stage 2
+    given a random selection at sparsity s in place of the router's (Stages 0 and 1 still run
+    in full, their cost does not depend on s). Prints one JSON line per (mode, N) with each
+    stage's time, the speedup over dense causal attention through the same Stage 2 kernel (every
+    chunk selected) and over torch's fused attention kernel, where this build has one."""
+    rows = []
+    for n in wl.TABLE5_CONTEXTS:
+        for decode in (False, True):
+            w = wl.table5_workload(n, decode)
+            print(f"[bench] sweep: {w.name}", file=sys.stderr, flush=True)
+            inp = wl.make_inputs(w, dev)
+            q, k, v = inp["q"], inp["k"], inp["v"]
+            nc = -(-n // w.block)
+            nw = -(-nc // 32)
+            kbar = dash.dash_pool_keys(k, w.block)
+            mask = torch.empty((w.batch, w.n_q, w.h_kv, nw), dtype=torch.int32, device=dev)
+            bias = torch.empty((w.batch, w.n_q, w.h_kv, nc), dtype=torch.float32, device=dev)
+            wsb = dash.dash_block_entmax_workspace_bytes(q.dtype, w.batch, w.n_q, w.q_pos0, n,
+                                                         w.h_q, w.h_kv, w.head_dim, w.block)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+            o = torch.empty_like(q)
+            lse = torch.empty((w.batch, w.n_q, w.h_q), dtype=torch.float32, device=dev)
+            t_pool = 0.0 if decode else _time_ms(lambda: dash.dash_pool_keys(k, w.block, kbar=kbar), reps)
+            t_route = _time_ms(lambda: dash.dash_block_entmax(
+                q, kbar, n_kv=n, block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma,
+                q_pos0=w.q_pos0, mask=mask, bias=bias, want_tau=False, workspace=ws), reps)
+            del ws
+            if decode:
+                awb = dash.dash_decode_workspace_bytes(w.batch, n, w.h_q, w.h_kv, w.head_dim, w.block)
+                aws = torch.empty(awb, dtype=torch.uint8, device=dev) if awb else None
+
+                def stage2(m, bi):
+                    dash.dash_sparse_attn_decode(q, k, v, m, bi, block=w.block, o=o, workspace=aws)
+            else:
+                def stage2(m, bi):
+                    dash.dash_sparse_attn_prefill(q, k, v, m, bi, block=w.block, o=o, lse=lse)
+            point = {"mode": "decode" if decode else "prefill", "n": n, "batch": w.batch,
+                     "ms": {"pool": round(t_pool, 4), "route": round(t_route, 4)}, "sparsity": {}}
+            for s in (0.0,) + wl.TABLE5_SPARSITY:
+                m, bi = wl.random_selection(w.batch, w.n_q, w.q_pos0, n, w.h_kv, w.block, s,
+                                            seed=1000 + int(s * 1e4), device=dev)
+                t = _time_ms(lambda: stage2(m, bi), reps)
+                ent = {"stage2_ms": round(t, 4)}
+                if not decode:
+                    pairs, frac = selected_pairs_prefill(m, w)
+                    ent["selected_fraction"] = round(frac, 4)
+                    ent["stage2_tflops"] = round(4.0 * w.head_dim * pairs / (t * 1e-3) / 1e12, 2)
+                point["sparsity"][str(s)] = ent
+                del m, bi
+            t_dense = point["sparsity"]["0.0"]["stage2_ms"]
+            t_sdpa, backend = _sdpa_ms(q, k, v, causal=not decode, reps=reps)
+            point["dense_ms"] = {"same_kernel": t_dense,
+                                 "torch_sdpa": None if t_sdpa is None else round(t_sdpa, 4),
+                                 "torch_backend": backend}
+            for s in wl.TABLE5_SPARSITY:
+                ent = point["sparsity"][str(s)]
+                total = t_pool + t_route + ent["stage2_ms"]
+                ent["total_ms"] = round(total, 4)
+                ent["speedup_vs_same_kernel_dense"] = round(t_dense / total, 3)
+                ent["speedup_vs_torch_sdpa"] = None if t_sdpa is None else round(t_sdpa / total, 3)
+            print(json.dumps(point), flush=True)
+            rows.append(point)
+            del inp, q, k, v, kbar, mask, bias, o, lse
+            torch.cuda.empty_cache()
+    print("mode     N     " + "  ".join(f"s={s:<6}" for s in wl.TABLE5_SPARSITY)
+          + "  (speedup over dense causal, same Stage 2 kernel / torch fused attention)",
+          file=sys.stderr)
+    for p in rows:
+        cells = []
+        for s in wl.TABLE5_SPARSITY:
+            e = p["sparsity"][str(s)]
+            t = e["speedup_vs_torch_sdpa"]
+            cells.append(f"{e['speedup_vs_same_kernel_dense']:.2f}/{'-' if t is None else f'{t:.2f}'}")
+        print(f"{p['mode']:8} {p['n'] // 1024:3}K  " + "  ".join(f"{c:8}" for c in cells),
+              file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +278,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB `steps` times: the "
                          "reference for scaling HBM byte counters; no JSON line is printed")
+    ap.add_argument("--random-mask-sweep", action="store_true",
+                    help="run the pages' random-selection efficiency sweep instead of the step "
+                         "(Hq 32, Hkv 2, N 16-96K, three sparsities); one JSON line per point")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -189,6 +301,9 @@ def main():
 
     import sparse_hierarchical_attention_amd as dash
     dash.lib()
+    if args.random_mask_sweep:
+        random_mask_sweep(dash, dev, reps=max(1, args.steps // 2))
+        return
     wp, wd = wl.PREFILL_32K, wl.DECODE_128K
     print(f"[bench] generating inputs", file=sys.stderr, flush=True)
     pre = wl.make_inputs(wp, dev)

@@ -158,6 +158,48 @@ def test_stage2_on_oracle_selection(dash, orc):
                           ref_lse=ref["lse"])
 
 
+# ------------------------------------------------- injected random selections (g = 16, Hkv = 2)
+
+def _compact(mask: torch.Tensor, bias: torch.Tensor):
+    """[B, n_q, Hkv, W] / [B, n_q, Hkv, Nc] GPU tensors -> the oracle's per-row host arrays."""
+    m = parity.to_host(mask).view(np.uint32)
+    bi = parity.to_host(bias).astype(np.float64)
+    return m.reshape((-1,) + m.shape[2:]), bi.reshape((-1,) + bi.shape[2:])
+
+
+@pytest.mark.parametrize("sparsity", [0.0, 0.75, 0.9375])
+def test_stage2_random_selection_prefill(dash, orc, sparsity):
+    """Stage 2 fed a random selection, as the pages' efficiency sweep injects it (32 query heads
+    over 2 KV heads, so groups of 16), with a random bias: every row against the oracle."""
+    w = wl.Workload("random selection", 1, 2000, 32, 2, 128, 64, 1.5, 0.5, 1e8, seed=34)
+    inp = wl.make_inputs(w, DEV)
+    mask, bias = wl.random_selection(1, w.n_q, 0, w.n_kv, w.h_kv, w.block, sparsity, seed=7,
+                                     device=DEV, bias_std=0.5)
+    o, lse = dash.dash_sparse_attn_prefill(inp["q"], inp["k"], inp["v"], mask, bias, block=w.block)
+    torch.cuda.synchronize()
+    m, bi = _compact(mask, bias)
+    ref_o, ref_lse = orc.sparse_attn(host(inp["q"]), host(inp["k"]), host(inp["v"]), m, bi,
+                                     block=w.block)
+    parity.compare_output(parity.to_host(o)[0], ref_o, "bf16", gpu_lse=parity.to_host(lse)[0],
+                          ref_lse=ref_lse)
+
+
+@pytest.mark.parametrize("n_ctx", [3000, 4096 + 17])
+def test_decode_random_selection(dash, orc, n_ctx):
+    """Decode at batch 24 with groups of 16 on a random selection at sparsity 87.5 %."""
+    w = wl.Workload("decode random selection", 24, n_ctx, 32, 2, 128, 64, 1.5, 0.5, 1e8,
+                    decode=True, seed=43)
+    inp = wl.make_inputs(w, DEV)
+    mask, bias = wl.random_selection(w.batch, 1, n_ctx - 1, n_ctx, w.h_kv, w.block, 0.875, seed=8,
+                                     device=DEV, bias_std=0.5)
+    o = dash.dash_sparse_attn_decode(inp["q"], inp["k"], inp["v"], mask, bias, block=w.block)
+    torch.cuda.synchronize()
+    m, bi = _compact(mask, bias)
+    ref_o, _ = orc.sparse_attn(host(inp["q"]), host(inp["k"]), host(inp["v"]), m, bi,
+                               block=w.block, q_pos0=n_ctx - 1)
+    parity.compare_output(parity.to_host(o).reshape(w.batch, w.h_q, -1), ref_o, "bf16")
+
+
 # ------------------------------------------------------------------------------ decode
 
 @pytest.mark.parametrize("n_ctx,block", [(4096 + 17, 64), (3000, 32), (1024, 128)])

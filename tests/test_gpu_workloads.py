@@ -108,3 +108,45 @@ def test_decode_128k(dash, orc, sigma):
             assert set(inp["planted"][b][r].tolist()) <= sel
         parity.compare_output(parity.to_host(o[b]), ref["o"], "bf16", exclude_rows=rep["row_flip"],
                               cond_row=rep["cond_row"], vmax=float(v[b].abs().max()))
+
+
+# ------------------------------------------- the pages' efficiency sweep: injected random selection
+
+def test_table5_prefill_16k_random_selection(dash, orc):
+    """Stage 2 at the sweep's 16K prefill shape (32 query heads over 2 KV heads) on a random
+    selection at sparsity 75 %, sampled rows against the oracle."""
+    w = wl.table5_workload(16384, decode=False)
+    log(f"{w.name}: generating inputs")
+    inp = wl.make_inputs(w, DEV)
+    mask, bias = wl.random_selection(1, w.n_q, 0, w.n_kv, w.h_kv, w.block, 0.75, seed=11,
+                                     device=DEV, bias_std=0.5)
+    o, lse = dash.dash_sparse_attn_prefill(inp["q"], inp["k"], inp["v"], mask, bias, block=w.block)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.n_q, w.block, 96, seed=71)
+    log(f"oracle on {len(rows)} rows")
+    m = flat_rows(mask, rows).view(np.uint32)
+    ref_o, ref_lse = orc.sparse_attn(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), m,
+                                     flat_rows(bias, rows).astype(np.float64), block=w.block,
+                                     rows=rows)
+    out = parity.compare_output(flat_rows(o, rows), ref_o, "bf16", gpu_lse=flat_rows(lse, rows),
+                                ref_lse=ref_lse)
+    log(f"out {out}")
+
+
+def test_table5_decode_96k_random_selection(dash, orc):
+    """Decode at the sweep's largest shape, 24 sequences of 96K context with groups of 16, on a
+    random selection at sparsity 93.75 %, every sequence against the oracle."""
+    w = wl.table5_workload(98304, decode=True)
+    log(f"{w.name}: generating inputs")
+    inp = wl.make_inputs(w, DEV)
+    mask, bias = wl.random_selection(w.batch, 1, w.n_kv - 1, w.n_kv, w.h_kv, w.block, 0.9375,
+                                     seed=12, device=DEV, bias_std=0.5)
+    o = dash.dash_sparse_attn_decode(inp["q"], inp["k"], inp["v"], mask, bias, block=w.block)
+    torch.cuda.synchronize()
+    log("oracle")
+    m = parity.to_host(mask).view(np.uint32).reshape(w.batch, w.h_kv, -1)
+    bi = parity.to_host(bias).astype(np.float64).reshape(w.batch, w.h_kv, -1)
+    ref_o, _ = orc.sparse_attn(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), m, bi,
+                               block=w.block, q_pos0=w.n_kv - 1)
+    out = parity.compare_output(parity.to_host(o).reshape(w.batch, w.h_q, -1), ref_o, "bf16")
+    log(f"out {out}")

@@ -164,3 +164,56 @@ def make_inputs(w: Workload, device="cpu") -> dict:
         del kb
         v[b] = _randn((n, hkv, d), vs[b], device).to(dt)
     return dict(q=q, k=k, v=v, planted=planted)
+
+
+# ------------------------------------------------------------------ injected random selections
+# The pages' efficiency benchmark sweeps Stage 2 at a set chunk sparsity s by replacing the
+# router's selection with a random bit-packed mask: Hq = 32, Hkv = 2, D = 128, chunk 64,
+# N in {16, 32, 64, 96}K, s in {75, 87.5, 93.75} %, prefill at batch 1 and decode at batch 24.
+TABLE5_CONTEXTS = (16384, 32768, 65536, 98304)
+TABLE5_SPARSITY = (0.75, 0.875, 0.9375)
+
+
+def table5_workload(n: int, decode: bool) -> Workload:
+    kind = "decode 24 x" if decode else "prefill"
+    return Workload(f"{kind} {n // 1024}K, 32q/2kv heads, D 128, block 64, random selection",
+                    24 if decode else 1, n, 32, 2, 128, 64, 1.5, 0.5, 1e8, decode=decode,
+                    seed=6 + (1 if decode else 0))
+
+
+def random_selection(batch: int, n_q: int, q_pos0: int, n_kv: int, h_kv: int, block: int,
+                     sparsity: float, seed: int, device="cpu", bias_std: float = 0.0,
+                     slab: int = 4096) -> tuple[torch.Tensor, torch.Tensor]:
+    """A random selection in the layout Stage 1 writes: mask [B, n_q, Hkv, ceil(Nc / 32)] int32
+    (chunk c is bit c % 32 of word c // 32) and bias [B, n_q, Hkv, Nc] float32, Nc = ceil(n_kv /
+    block). For the query at position p, each complete chunk before its own chunk c_p = p // block
+    is selected independently with probability 1 - sparsity; c_p itself is always selected, and
+    no chunk after it. Selected chunks before c_p get bias ~ N(0, bias_std^2) (0 when bias_std is
+    0); every other entry is 0. Queries are drawn in slabs of `slab` rows, each from its own
+    stream, to bound temporary memory."""
+    nc = -(-n_kv // block)
+    nw = -(-nc // 32)
+    mask = torch.empty((batch, n_q, h_kv, nw), dtype=torch.int32, device=device)
+    bias = torch.zeros((batch, n_q, h_kv, nc), dtype=torch.float32, device=device)
+    weights = (torch.ones(32, dtype=torch.int64, device=device) << torch.arange(32, device=device))
+    chunk = torch.arange(nw * 32, device=device)
+    n_slabs = -(-n_q // slab)
+    streams = np.random.SeedSequence(seed).spawn(batch * n_slabs)
+    for b in range(batch):
+        for si in range(n_slabs):
+            t0, t1 = si * slab, min(n_q, (si + 1) * slab)
+            ss_sel, ss_bias = streams[b * n_slabs + si].spawn(2)
+            g = torch.Generator(device=device)
+            g.manual_seed(_torch_seed(ss_sel))
+            u = torch.rand((t1 - t0, h_kv, nw * 32), generator=g, device=device)
+            cp = (q_pos0 + torch.arange(t0, t1, device=device)) // block
+            before = chunk[None, :] < torch.minimum(cp, torch.tensor(n_kv // block, device=device))[:, None]
+            sel = (u >= sparsity) & before[:, None, :]
+            if bias_std > 0.0:
+                d = _randn((t1 - t0, h_kv, nw * 32), ss_bias, device) * bias_std
+                bias[b, t0:t1] = torch.where(sel, d, torch.zeros_like(d))[..., :nc]
+            sel |= (chunk[None, :] == cp[:, None])[:, None, :]
+            words = (sel.view(t1 - t0, h_kv, nw, 32).to(torch.int64) * weights).sum(-1)
+            mask[b, t0:t1] = (words - ((words >> 31) << 32)).to(torch.int32)  # two's complement
+            del u, sel, words
+    return mask, bias
