@@ -69,51 +69,19 @@ __global__ __launch_bounds__(256) void split_kbar_kernel(const float* __restrict
     out[128] = __builtin_bit_cast(uint4, lo);
 }
 
-// One unit of the fused route's phase 2 (see route_fused_kernel): rows row0 .. of the score
-// tile xr (row stride xstride), NSS slots of 16 lanes per row, for the token(s) of the unit.
-template <int NSS, int KIND, int GQ>
-__device__ __forceinline__ void route_unit(const float* __restrict__ xr0, int xstride, int row0,
-                                           int tile0, int b, int r, uint32_t* __restrict__ mask,
-                                           float* __restrict__ bias, float* __restrict__ tau_out,
-                                           const RouteParams& p) {
-    constexpr int PASSES = GQ >= 4 ? GQ / 4 : 1;        // passes per unit
+// The mask words and bias of one token's row from its group-summed probabilities wsum (entry c
+// in lane c % 16 of a 16-lane group, slot c / 16; every group holds the same row when g >= 4,
+// the rows of 4 / g tokens otherwise): w = wsum / g, mu = mean log w over R = {w > 0},
+// d = (log w - mu) / sigma on R, the query's own chunk cp always set with d = 0.
+template <int NSS, int GQ>
+__device__ __forceinline__ void route_write_token(float (&wsum)[NSS], int tok, int b, int r,
+                                                  uint32_t* __restrict__ mask,
+                                                  float* __restrict__ bias, const RouteParams& p) {
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4, li = lane & 15;
-    const float e = 1.0f / (p.alpha - 1.0f);
-    const float inv_g = 1.0f / (float)GQ;
-    // this lane group's token (for g < 4 the groups hold different tokens)
-    const int my_tok = (GQ >= 4 ? row0 : row0 + grp) / GQ;
-    const int tok = tile0 + my_tok;
     const bool tvalid = tok < p.n_q;
-    const int pos = p.q_pos0 + tok;
-    const int cp = pos / p.block;
-    const int m = tvalid ? min(cp, p.tc) : 0;
-    float wsum[NSS];
-#pragma unroll
-    for (int sl = 0; sl < NSS; ++sl) wsum[sl] = 0.f;
-#pragma unroll 1
-    for (int ps = 0; ps < PASSES; ++ps) {
-        const int rl = 4 * ps + grp;  // row within the unit
-        const float* xr = xr0 + rl * xstride;
-        float xv[NSS];
-#pragma unroll
-        for (int sl = 0; sl < NSS; ++sl) {
-            const int c = 16 * sl + li;
-            const float v = xr[c];
-            xv[sl] = c < m ? v : -INFINITY;
-        }
-        const float tau = solve_tau_exact<NSS, KIND, 16>(xv, NSS, m, p.alpha);
-        if (tau_out && tvalid && li == 0)
-            tau_out[((int64_t)b * p.n_q + tok) * p.h_q + r * GQ + (row0 + rl) % GQ] = tau;
-#pragma unroll
-        for (int sl = 0; sl < NSS; ++sl) {
-            float pv = pow_e<KIND>(xv[sl] - tau, e);
-            if (GQ >= 2) pv = pair16_sum(pv);   // heads in groups 0+1 and 2+3
-            if (GQ >= 4) pv = pair32_sum(pv);   // all four groups
-            wsum[sl] += pv;
-        }
-    }
-    // GQA mean and mu for this group's token (every lane of the group holds the same row)
+    const int cp = (p.q_pos0 + tok) / p.block;
+    const float inv_g = 1.0f / (float)GQ;
     float lsum = 0.f, lcnt = 0.f;
 #pragma unroll
     for (int sl = 0; sl < NSS; ++sl) {
@@ -125,7 +93,7 @@ __device__ __forceinline__ void route_unit(const float* __restrict__ xr0, int xs
     lsum = row16_sum(lsum);
     lcnt = row16_sum(lcnt);
     const float mu = lcnt > 0.f ? lsum / lcnt : 0.f;
-    // the groups that write: one per token of the unit
+    // the groups that write: one per token
     const bool writer = tvalid && (GQ >= 4 ? grp == 0 : (GQ == 2 ? (grp & 1) == 0 : true));
     const int64_t qrow = (int64_t)b * p.n_q + tok;
     uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
@@ -150,6 +118,86 @@ __device__ __forceinline__ void route_unit(const float* __restrict__ xr0, int xs
     for (int wd = NSS / 2 + li; wd < p.nw; wd += 16)
         if (writer) mrow[wd] = cp / 32 == wd ? 1u << (cp % 32) : 0u;
     if (writer && li == 0) brow[cp] = 0.f;
+}
+
+// One pass of the fused route's phase 2 (see route_fused_kernel): the four rows xr0 + k xstride,
+// k = 0..3, one per 16-lane group, rows row0 .. row0 + 3 of the tile. Solves each row's threshold
+// and returns its probabilities, summed over the heads of the pass that share a token, in wsum.
+template <int NSS, int KIND, int GQ>
+__device__ __forceinline__ void route_pass(const float* __restrict__ xr0, int xstride, int row0,
+                                           int tile0, int b, int r, float* __restrict__ tau_out,
+                                           const RouteParams& p, float (&wsum)[NSS]) {
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4, li = lane & 15;
+    const float e = 1.0f / (p.alpha - 1.0f);
+    const int row = row0 + grp;
+    const int tok = tile0 + row / GQ;
+    const bool tvalid = tok < p.n_q;
+    const int m = tvalid ? min((p.q_pos0 + tok) / p.block, p.tc) : 0;
+    const float* xr = xr0 + grp * xstride;
+    float xv[NSS];
+#pragma unroll
+    for (int sl = 0; sl < NSS; ++sl) {
+        const int c = 16 * sl + li;
+        const float v = xr[c];
+        xv[sl] = c < m ? v : -INFINITY;
+    }
+    const float tau = solve_tau_exact<NSS, KIND, 16>(xv, NSS, m, p.alpha);
+    if (tau_out && tvalid && li == 0)
+        tau_out[((int64_t)b * p.n_q + tok) * p.h_q + r * GQ + row % GQ] = tau;
+#pragma unroll
+    for (int sl = 0; sl < NSS; ++sl) {
+        float pv = pow_e<KIND>(xv[sl] - tau, e);
+        if (GQ >= 2) pv = pair16_sum(pv);   // heads in groups 0+1 and 2+3
+        if (GQ >= 4) pv = pair32_sum(pv);   // all four groups
+        wsum[sl] = pv;
+    }
+}
+
+// A whole unit of phase 2 for g <= 4: 4 / g tokens (g < 4) or one token (g = 4) in one pass.
+template <int NSS, int KIND, int GQ>
+__device__ __forceinline__ void route_unit(const float* __restrict__ xr0, int xstride, int row0,
+                                           int tile0, int b, int r, uint32_t* __restrict__ mask,
+                                           float* __restrict__ bias, float* __restrict__ tau_out,
+                                           const RouteParams& p) {
+    static_assert(GQ <= 4, "groups of more than four heads take one pass per unit");
+    const int grp = (threadIdx.x & 63) >> 4;
+    float wsum[NSS];
+    route_pass<NSS, KIND, GQ>(xr0, xstride, row0, tile0, b, r, tau_out, p, wsum);
+    route_write_token<NSS, GQ>(wsum, tile0 + (GQ >= 4 ? row0 : row0 + grp) / GQ, b, r, mask, bias, p);
+}
+
+// One pass of a token's heads for g > 4: its probabilities, summed over the pass's four heads,
+// replace the first of the pass's score rows in LDS (this wave has read all four).
+template <int NSS, int KIND, int GQ>
+__device__ __forceinline__ void route_head_pass(float* __restrict__ xr0, int xstride, int row0,
+                                                int tile0, int b, int r,
+                                                float* __restrict__ tau_out, const RouteParams& p) {
+    const int lane = threadIdx.x & 63;
+    float wsum[NSS];
+    route_pass<NSS, KIND, GQ>(xr0, xstride, row0, tile0, b, r, tau_out, p, wsum);
+    if (lane < 16) {
+#pragma unroll
+        for (int sl = 0; sl < NSS; ++sl) xr0[16 * sl + lane] = wsum[sl];
+    }
+}
+
+// The token's rows for g > 4 once every pass has left its partial sum in LDS: the partials
+// (rows 0, 4, 8, ... of the token) added in pass order, then the token's mask and bias.
+template <int NSS, int GQ>
+__device__ __forceinline__ void route_finish_token(const float* __restrict__ xt, int xstride,
+                                                   int tok, int b, int r,
+                                                   uint32_t* __restrict__ mask,
+                                                   float* __restrict__ bias, const RouteParams& p) {
+    const int li = threadIdx.x & 15;
+    float wsum[NSS];
+#pragma unroll
+    for (int sl = 0; sl < NSS; ++sl) wsum[sl] = 0.f;
+#pragma unroll
+    for (int ps = 0; ps < GQ / 4; ++ps)
+#pragma unroll
+        for (int sl = 0; sl < NSS; ++sl) wsum[sl] += xt[4 * ps * xstride + 16 * sl + li];
+    route_write_token<NSS, GQ>(wsum, tok, b, r, mask, bias, p);
 }
 
 // 16 waves per CU (four per SIMD): NW waves per workgroup, 16 / NW workgroups per CU. NR MFMA
@@ -263,21 +311,45 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
     __syncthreads();
 
     // ---- phase 2: a wave takes 4 rows at a time, one per 16-lane DPP row (lane group); entry c
-    // of a row sits in lane c % 16 of its group, slot c / 16. A unit is one token when g >= 4
-    // (its heads in g / 4 passes of 4) or 4 / g tokens when g < 4 (one pass). The slot count is
-    // a compile-time bucket (the unit's longest row, rounded up to 4, 8, 16, ...) so that every
-    // slot loop unrolls; slots past a row hold -inf.
-    constexpr int UROWS = 4 * (GQ >= 4 ? GQ / 4 : 1);  // rows per unit
-    for (int u = wave; u < ROWS / UROWS; u += NW) {
-        const int row0 = u * UROWS;
-        const int last_tok = min(tile0 + (row0 + UROWS - 1) / GQ, p.n_q - 1);
-        const int ns = div_up(min((p.q_pos0 + last_tok) / p.block, p.tc), 16);
-        if (ns <= 4) route_unit<4, KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
-        else if (ns <= 8) route_unit<8, KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
-        else if (ns <= 16) route_unit<16, KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
-        else if (CMAX >= 512 && ns <= 32) route_unit<(CMAX >= 512 ? 32 : 16), KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
-        else if (CMAX >= 1024) route_unit<(CMAX >= 1024 ? 64 : 16), KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p);
+    // of a row sits in lane c % 16 of its group, slot c / 16. For g <= 4 a unit is one pass over
+    // 4 / g tokens or one token; for g > 4 it is one pass over four heads of a token, and the
+    // token's passes, spread over the waves, leave partial sums in LDS that one wave then adds.
+    // The slot count is a compile-time bucket (the unit's longest row, rounded up to 4, 8, 16,
+    // ...) so that every slot loop unrolls; slots past a row hold -inf.
+#define DASH_BUCKETS(NS_, CALL)                                                                 \
+    if ((NS_) <= 4) CALL(4);                                                                    \
+    else if ((NS_) <= 8) CALL(8);                                                               \
+    else if ((NS_) <= 16) CALL(16);                                                             \
+    else if (CMAX >= 512 && (NS_) <= 32) CALL(CMAX >= 512 ? 32 : 16);                           \
+    else if (CMAX >= 1024) CALL(CMAX >= 1024 ? 64 : 16)
+    auto slots_of = [&](int tok) {  // 16-lane slots of a token's row
+        return div_up(min((p.q_pos0 + min(tok, p.n_q - 1)) / p.block, p.tc), 16);
+    };
+    if constexpr (GQ <= 4) {
+        for (int u = wave; u < ROWS / 4; u += NW) {
+            const int row0 = u * 4;
+            const int ns = slots_of(tile0 + (row0 + 3) / GQ);
+#define DASH_UNIT(NS) route_unit<NS, KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, mask, bias, tau_out, p)
+            DASH_BUCKETS(ns, DASH_UNIT);
+#undef DASH_UNIT
+        }
+    } else {
+        for (int u = wave; u < ROWS / 4; u += NW) {
+            const int row0 = u * 4;
+            const int ns = slots_of(tile0 + row0 / GQ);
+#define DASH_PASS(NS) route_head_pass<NS, KIND, GQ>(xs + row0 * XS, XS, row0, tile0, b, r, tau_out, p)
+            DASH_BUCKETS(ns, DASH_PASS);
+#undef DASH_PASS
+        }
+        __syncthreads();
+        for (int t = wave; t < T; t += NW) {
+            const int ns = slots_of(tile0 + t);
+#define DASH_FINISH(NS) route_finish_token<NS, GQ>(xs + t * GQ * XS, XS, tile0 + t, b, r, mask, bias, p)
+            DASH_BUCKETS(ns, DASH_FINISH);
+#undef DASH_FINISH
+        }
     }
+#undef DASH_BUCKETS
 }
 
 // (MT, NW) with NW * MT * 32 >= tc chunks: up to 1024 chunks in 16 waves

@@ -220,120 +220,123 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
         const int c_ld = c_nx >= 0 ? c_nx : c;
         row_view(c_ld);
         dma(Kn, Vn, c_ld, c_nx >= 0 ? sub_nx : sub);
-        const float sc = sel ? qk_scale : 0.f;
-        const float off = sel ? (c == cpos ? 0.f : dcur * kLog2e) : -INFINITY;
-        const bool causal = c >= c_first;  // some row's own chunk: mask keys past each row
+        // a wave none of whose rows selected the chunk has nothing to add (every score -inf)
+        if (__any(sel)) {
+            const float sc = sel ? qk_scale : 0.f;
+            const float off = sel ? (c == cpos ? 0.f : dcur * kLog2e) : -INFINITY;
+            const bool causal = c >= c_first;  // some row's own chunk: mask keys past each row
 
-        // S^T = K Q^T, the M-tiles' accumulation chains interleaved. The MFMA blocks run at a
-        // raised wave priority, so that of the two waves sharing a SIMD the one starting its
-        // matrix work issues first and the other's softmax fills the issue slots meanwhile. K
-        // fragments are read two k-steps ahead of their MFMAs (a ring of three), so that LDS
-        // latency stays off the matrix pipe.
-        __builtin_amdgcn_s_setprio(1);
-        f32x16 s[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
-        {
-            constexpr int KS = kD / 16;
-            bf16x8 ka[3][MT];
-            auto kread = [&](int ks, bf16x8 (&dst)[MT]) __attribute__((always_inline)) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    dst[mt] = *reinterpret_cast<const bf16x8*>(Kc + kl_base + mt * (32 / NB) * kD + 16 * ks);
-            };
-            kread(0, ka[0]);
-            kread(1, ka[1]);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (ks + 2 < KS) kread(ks + 2, ka[(ks + 2) % 3]);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % 3][mt], qf[ks], s[mt], 0, 0, 0);
+            // S^T = K Q^T, the M-tiles' accumulation chains interleaved. The MFMA blocks run at a
+            // raised wave priority, so that of the two waves sharing a SIMD the one starting its
+            // matrix work issues first and the other's softmax fills the issue slots meanwhile. K
+            // fragments are read two k-steps ahead of their MFMAs (a ring of three), so that LDS
+            // latency stays off the matrix pipe.
+            __builtin_amdgcn_s_setprio(1);
+            f32x16 s[MT];
+    #pragma unroll
+            for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
+            {
+                constexpr int KS = kD / 16;
+                bf16x8 ka[3][MT];
+                auto kread = [&](int ks, bf16x8 (&dst)[MT]) __attribute__((always_inline)) {
+    #pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        dst[mt] = *reinterpret_cast<const bf16x8*>(Kc + kl_base + mt * (32 / NB) * kD + 16 * ks);
+                };
+                kread(0, ka[0]);
+                kread(1, ka[1]);
+    #pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + 2 < KS) kread(ks + 2, ka[(ks + 2) % 3]);
+    #pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % 3][mt], qf[ks], s[mt], 0, 0, 0);
+                }
             }
-        }
-        __builtin_amdgcn_s_setprio(0);
-        // row maximum of x = s * sc + off (sc >= 0)
-        float xmax;
-        if (causal) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
-                    const float x = fmaf(s[mt][rr], sc, off);
-                    s[mt][rr] = key > pos ? -INFINITY : x;
-                }
-            xmax = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) xmax = fmaxf(xmax, s[mt][rr]);
-        } else {
-            float smax = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) smax = fmaxf(smax, s[mt][rr]);
-            xmax = sel ? fmaf(smax, sc, off) : -INFINITY;
-        }
-        xmax = fmaxf(xmax, __shfl_xor(xmax, 32, kWave));
-        // raise the running maximum only when needed (rare once a row has seen its peak)
-        const bool raise = xmax > m_used + kLazyMax;
-        if (__any(raise)) {
-            const float m_new = raise ? xmax : m_used;
-            const float corr = m_used == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used - m_new);
-            l_run *= corr;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
-            m_used = m_new;
-        }
-        const float m_ref = m_used == -INFINITY ? 0.f : m_used;
-        float rsum = 0.f;
-        bf16x8 pf[KSTEP];
-        if (causal) {
-#pragma unroll
-            for (int ks = 0; ks < KSTEP; ++ks)
-#pragma unroll
-                for (int vv = 0; vv < 8; ++vv) {
-                    const float pe = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + vv] - m_ref);
-                    rsum += pe;
-                    pf[ks][vv] = (__bf16)pe;
-                }
-        } else {
-            const float off_m = off - m_ref;
-#pragma unroll
-            for (int ks = 0; ks < KSTEP; ++ks)
-#pragma unroll
-                for (int vv = 0; vv < 8; ++vv) {
-                    const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + vv], sc, off_m));
-                    rsum += pe;
-                    pf[ks][vv] = (__bf16)pe;
-                }
-        }
-        l_run += rsum + __shfl_xor(rsum, 32, kWave);
+            __builtin_amdgcn_s_setprio(0);
+            // row maximum of x = s * sc + off (sc >= 0)
+            float xmax;
+            if (causal) {
+    #pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+    #pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) {
+                        const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
+                        const float x = fmaf(s[mt][rr], sc, off);
+                        s[mt][rr] = key > pos ? -INFINITY : x;
+                    }
+                xmax = -INFINITY;
+    #pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+    #pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) xmax = fmaxf(xmax, s[mt][rr]);
+            } else {
+                float smax = -INFINITY;
+    #pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+    #pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) smax = fmaxf(smax, s[mt][rr]);
+                xmax = sel ? fmaf(smax, sc, off) : -INFINITY;
+            }
+            xmax = fmaxf(xmax, __shfl_xor(xmax, 32, kWave));
+            // raise the running maximum only when needed (rare once a row has seen its peak)
+            const bool raise = xmax > m_used + kLazyMax;
+            if (__any(raise)) {
+                const float m_new = raise ? xmax : m_used;
+                const float corr = m_used == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_used - m_new);
+                l_run *= corr;
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
+                m_used = m_new;
+            }
+            const float m_ref = m_used == -INFINITY ? 0.f : m_used;
+            float rsum = 0.f;
+            bf16x8 pf[KSTEP];
+            if (causal) {
+    #pragma unroll
+                for (int ks = 0; ks < KSTEP; ++ks)
+    #pragma unroll
+                    for (int vv = 0; vv < 8; ++vv) {
+                        const float pe = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + vv] - m_ref);
+                        rsum += pe;
+                        pf[ks][vv] = (__bf16)pe;
+                    }
+            } else {
+                const float off_m = off - m_ref;
+    #pragma unroll
+                for (int ks = 0; ks < KSTEP; ++ks)
+    #pragma unroll
+                    for (int vv = 0; vv < 8; ++vv) {
+                        const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + vv], sc, off_m));
+                        rsum += pe;
+                        pf[ks][vv] = (__bf16)pe;
+                    }
+            }
+            l_run += rsum + __shfl_xor(rsum, 32, kWave);
 
-        // O^T += V^T P^T, V^T through transposing reads issued one k-step ahead of their MFMAs
-        __builtin_amdgcn_s_setprio(1);
-        {
-            bf16x8 va[2][DT];
-            auto vread = [&](int ks, bf16x8 (&dst)[DT]) __attribute__((always_inline)) {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const i16x4 lo = ds_read_tr16(Vc + vl_base[0] + ks * (16 / NB) * kD + 32 * dt);
-                    const i16x4 hi = ds_read_tr16(Vc + vl_base[1] + ks * (16 / NB) * kD + 32 * dt);
-                    dst[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            // O^T += V^T P^T, V^T through transposing reads issued one k-step ahead of their MFMAs
+            __builtin_amdgcn_s_setprio(1);
+            {
+                bf16x8 va[2][DT];
+                auto vread = [&](int ks, bf16x8 (&dst)[DT]) __attribute__((always_inline)) {
+    #pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const i16x4 lo = ds_read_tr16(Vc + vl_base[0] + ks * (16 / NB) * kD + 32 * dt);
+                        const i16x4 hi = ds_read_tr16(Vc + vl_base[1] + ks * (16 / NB) * kD + 32 * dt);
+                        dst[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+                };
+                vread(0, va[0]);
+    #pragma unroll
+                for (int ks = 0; ks < KSTEP; ++ks) {
+                    if (ks + 1 < KSTEP) vread(ks + 1, va[(ks + 1) & 1]);
+    #pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks & 1][dt], pf[ks], acc[dt], 0, 0, 0);
                 }
-            };
-            vread(0, va[0]);
-#pragma unroll
-            for (int ks = 0; ks < KSTEP; ++ks) {
-                if (ks + 1 < KSTEP) vread(ks + 1, va[(ks + 1) & 1]);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks & 1][dt], pf[ks], acc[dt], 0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
-        __builtin_amdgcn_s_setprio(0);
         // the next tile has landed in every wave's part, and every wave is done with this one
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();
