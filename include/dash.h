@@ -9,6 +9,10 @@
  *   Stage 2  dash_sparse_attn_prefill  prior-biased sparse softmax        [DA §3.3-3.4 Prop. 1; Alg. 3]
  *            dash_sparse_attn_decode   the same for one new token per sequence, split over the
  *                                      selected chunks                   [DA §3.5 "split-KV variant"]
+ * Incremental decoding with a length per sequence (a cache of capacity n_cap, sequence b holding
+ * ctx_lens[b] tokens): dash_pool_keys_append writes the summary of a chunk the newest token
+ * completed [DA §3.1, §3.5]; dash_block_entmax_ex and dash_sparse_attn_decode_varlen take the
+ * lengths. dash_block_entmax_ex also takes the attention window of [DA App. B.1.1].
  *
  * Notation: B = batch, n = sequence length, H_q / H_kv = query / key-value heads, g = H_q / H_kv
  * (query head h belongs to KV group floor(h / g)), D = head dim, Bc = chunk (block) size,
@@ -90,14 +94,29 @@ dash_status_t dash_pool_keys_query(const void* k, dash_dtype_t dt, const float* 
                                    hipStream_t stream);
 
 /*
+ * Stage 0, streaming [DA §3.1 (a summary is final once its chunk is complete), §3.5 (the chunk
+ * cache persisted across decoding steps)]: after the newest token of sequence b was appended
+ * (ctx_lens[b] tokens in the cache, device int32 [B]), the summary of chunk ctx_lens[b] / Bc - 1
+ * is written into kbar when ctx_lens[b] is a positive multiple of Bc; otherwise nothing is
+ * written for that sequence. The mean (qbar NULL) or the learned-query form (qbar [H_kv, D]
+ * fp32), as dash_pool_keys / dash_pool_keys_query.
+ *   k_cache [B, n_cap, H_kv, D] (dt)     kbar [B, floor(n_cap / Bc), H_kv, D] fp32
+ * Lengths outside [0, n_cap] are clamped into it on the device (no error can be reported there).
+ */
+dash_status_t dash_pool_keys_append(const void* k_cache, dash_dtype_t dt, const float* qbar,
+                                    const int32_t* ctx_lens, float* kbar, int batch, int n_cap,
+                                    int h_kv, int head_dim, int block, hipStream_t stream);
+
+/*
  * Stage 1 [DA §3.2, Eq. 4; DA App. G, Alg. 2]. Query row t (t < n_q) sits at absolute position
  * p = q_pos0 + t of a sequence of n_kv keys (prefill: q_pos0 = 0, n_q = n_kv; decode: n_q = 1,
  * q_pos0 = n_kv - 1, the new token's key and value already appended). For every query head h it
  *   1. scores the complete chunks before its own, c < c_p:
  *        x_c = (alpha - 1) * gamma * <q_p^(h), kbar_c^(h / g)> / sqrt(D)          (x-units)
  *   2. finds the entmax threshold tau with sum_c [x_c - tau]_+^(1/(alpha-1)) = 1 [DA Eq. 2]
- *      (Newton steps from the left with a bisection guard, polished in closed form for
- *      alpha in {1.5, 2}) and p_c = [x_c - tau]_+^(1/(alpha-1));
+ *      (alpha in {1.5, 2}: closed-form roots on the current support inside a shrinking bracket,
+ *      ending when the support is stable; other alpha: Newton steps with a bisection guard)
+ *      and p_c = [x_c - tau]_+^(1/(alpha-1));
  * then for every KV group r
  *   3. averages the probabilities of the group's g heads, w_c = mean_h p_c [DA §3.2];
  *   4. routes R = {c < c_p : w_c > 0}, sets their mask bits and the bias
@@ -119,6 +138,27 @@ dash_status_t dash_block_entmax(const void* q, dash_dtype_t dt, const float* kba
                                 int block, float alpha, float gamma, float sigma, uint32_t* mask,
                                 float* bias, float* tau, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/*
+ * Stage 1 with two more inputs; dash_block_entmax is this call with ctx_lens = NULL and
+ * window_blocks = 1.
+ * window_blocks (>= 1) [DA App. B.1.1, the training-time window of the diagonal block and the
+ * block before it, 64-127 tokens for Bc = 64]: the query's own chunk and the window_blocks - 1
+ * chunks before it are always attended with d = 0 (mask bits set); routing scores only the
+ * complete chunks before them, c < c_p - window_blocks + 1. window_blocks = 2 is the pages'
+ * window. Chunks before 0 do not exist: a query whose window reaches chunk 0 routes nothing.
+ * ctx_lens (device int32 [B], or NULL): decode with a length per sequence, n_q = 1; the query of
+ * sequence b sits at p = ctx_lens[b] - 1 (q_pos0 is ignored), n_kv is the cache capacity n_cap
+ * (kbar, mask and bias are laid out for it), and only the summaries of the complete chunks
+ * below ctx_lens[b] / Bc are read. Lengths outside [1, n_cap] are clamped into it on the device.
+ * The workspace is the one of dash_block_entmax with the same sizes.
+ */
+dash_status_t dash_block_entmax_ex(const void* q, dash_dtype_t dt, const float* kbar,
+                                   const int32_t* ctx_lens, int batch, int n_q, int q_pos0,
+                                   int n_kv, int h_q, int h_kv, int head_dim, int block,
+                                   float alpha, float gamma, float sigma, int window_blocks,
+                                   uint32_t* mask, float* bias, float* tau, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Stage 2, prefill [DA §3.3-3.4, Prop. 1; DA App. G, Alg. 3]: for every query t of a causal
@@ -151,6 +191,22 @@ dash_status_t dash_sparse_attn_decode(const void* q, const void* k_cache, const 
                                       void* o, int batch, int n_ctx, int h_q, int h_kv,
                                       int head_dim, int block, float scale, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Stage 2, decode with a length per sequence [DA §3.5]: as dash_sparse_attn_decode for a cache
+ * of capacity n_cap (the row layout of k_cache, v_cache, mask and bias), the query of sequence b
+ * at p = ctx_lens[b] - 1 (device int32 [B], clamped into [1, n_cap]), attending to the selected
+ * chunks below its own and to the tokens c_p * Bc .. p of its own chunk. mask / bias as
+ * dash_block_entmax_ex writes them with the same ctx_lens. Workspace as
+ * dash_decode_workspace_bytes(batch, n_cap, ...).
+ */
+dash_status_t dash_sparse_attn_decode_varlen(const void* q, const void* k_cache,
+                                             const void* v_cache, dash_dtype_t dt,
+                                             const int32_t* ctx_lens, const uint32_t* mask,
+                                             const float* bias, void* o, int batch, int n_cap,
+                                             int h_q, int h_kv, int head_dim, int block,
+                                             float scale, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

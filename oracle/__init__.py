@@ -52,7 +52,7 @@ def lib():
         L.orc_entmax_tau.argtypes = [vp, i, d]
         L.orc_entmax_tau.restype = d
         L.orc_entmax_probs.argtypes = [vp, i, d, d, vp]
-        L.orc_block_entmax.argtypes = [vp, i, vp, i, i, i, i, i, i, i, i, d, d, d, vp, i64,
+        L.orc_block_entmax.argtypes = [vp, i, vp, i, i, i, i, i, i, i, i, d, d, d, i, vp, i64,
                                        vp, vp, vp, vp, vp]
         L.orc_sparse_attn.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, i, d, vp, i64,
                                       vp, vp]
@@ -146,9 +146,10 @@ def entmax(x, alpha: float, method: str = "auto") -> np.ndarray:
 
 
 def block_entmax(q, kbar, *, n_kv: int, block: int, alpha: float, gamma: float, sigma: float,
-                 q_pos0: int = 0, h_kv: int | None = None, rows=None):
+                 q_pos0: int = 0, h_kv: int | None = None, rows=None, window: int = 1):
     """Stage 1. Returns dict(mask uint32 [R,Hkv,W], bias [R,Hkv,Nc], tau [R,Hq], x [R,Hq,Nc],
-    w [R,Hkv,Nc]) for the listed rows rho = b * n_q + t (all rows when rows is None)."""
+    w [R,Hkv,Nc]) for the listed rows rho = b * n_q + t (all rows when rows is None).
+    window: blocks always attended (the query's own and window - 1 before it, DA App. B.1.1)."""
     qa, dt = _host(q)
     kb = np.ascontiguousarray(np.asarray(kbar, dtype=np.float64))
     b, n_q, hq, d = qa.shape
@@ -163,7 +164,8 @@ def block_entmax(q, kbar, *, n_kv: int, block: int, alpha: float, gamma: float, 
     w = np.zeros((nr, hkv, nc), dtype=np.float64)
     _check(lib().orc_block_entmax(
         _ptr(qa), dt, _ptr(kb), b, n_q, q_pos0, n_kv, hq, hkv, d, block, alpha, gamma, sigma,
-        None if r is None else _ptr(r), nr, _ptr(mask), _ptr(bias), _ptr(tau), _ptr(x), _ptr(w)),
+        int(window), None if r is None else _ptr(r), nr, _ptr(mask), _ptr(bias), _ptr(tau),
+        _ptr(x), _ptr(w)),
         "block_entmax")
     return dict(mask=mask, bias=bias, tau=tau, x=x, w=w)
 
@@ -215,12 +217,12 @@ def sparse_attn_prior(q, k, v, w, *, block: int, sigma: float, scale: float | No
 
 
 def forward(q, k, v, *, block: int, alpha: float, gamma: float, sigma: float,
-            scale: float | None = None, q_pos0: int = 0, rows=None):
+            scale: float | None = None, q_pos0: int = 0, rows=None, window: int = 1):
     """The whole forward pass for the listed rows: pool, route, attend (bias form)."""
     kbar = pool_keys(k, block)
     n_kv = (k.shape[1])
     st1 = block_entmax(q, kbar, n_kv=n_kv, block=block, alpha=alpha, gamma=gamma, sigma=sigma,
-                       q_pos0=q_pos0, h_kv=k.shape[2], rows=rows)
+                       q_pos0=q_pos0, h_kv=k.shape[2], rows=rows, window=window)
     o, lse = sparse_attn(q, k, v, st1["mask"], st1["bias"], block=block, scale=scale,
                          q_pos0=q_pos0, rows=rows)
     return dict(kbar=kbar, o=o, lse=lse, **st1)

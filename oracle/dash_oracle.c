@@ -175,9 +175,9 @@ void orc_entmax_probs(const double* x, int m, double alpha, double tau, double* 
 
 int orc_block_entmax(const void* q, int dtype, const double* kbar, int batch, int n_q, int q_pos0,
                      int n_kv, int h_q, int h_kv, int head_dim, int block, double alpha,
-                     double gamma, double sigma, const int64_t* rows, int64_t n_rows,
+                     double gamma, double sigma, int window, const int64_t* rows, int64_t n_rows,
                      uint32_t* mask, double* bias, double* tau, double* x, double* w) {
-    if (!q || !kbar || !mask || !bias || !tau) return -1;
+    if (!q || !kbar || !mask || !bias || !tau || window < 1) return -1;
     if (batch <= 0 || n_q <= 0 || n_kv <= 0 || h_q <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0)
         return -1;
     if (h_q % h_kv != 0 || q_pos0 < 0 || q_pos0 + n_q > n_kv) return -1;
@@ -196,8 +196,12 @@ int orc_block_entmax(const void* q, int dtype, const double* kbar, int batch, in
         const int pos = q_pos0 + t;
         const int ci = pos / block; /* the query's own (diagonal) chunk */
         /* READING: routing covers the complete chunks strictly before the query's own chunk,
-         * c < c_i [DA App. G, Alg. 2, line 5]; c_i <= Tc always holds. */
-        const int m = ci < tc ? ci : tc;
+         * c < c_i [DA App. G, Alg. 2]; c_i <= Tc always holds. READING: with a window of W
+         * blocks [DA App. B.1.1: the diagonal block and the block before it], the W - 1 blocks
+         * before c_i are attended like the diagonal (always, d = 0) and leave the routing
+         * candidates, which become c < c_i - W + 1; chunks below 0 do not exist. */
+        const int lo = ci - (window - 1) > 0 ? ci - (window - 1) : 0; /* first window chunk */
+        const int m = lo < tc ? lo : tc;
         double* xr = malloc(sizeof(double) * (m > 0 ? m : 1) * gq);
         double* pr = malloc(sizeof(double) * (m > 0 ? m : 1) * gq);
         double* wr = malloc(sizeof(double) * (m > 0 ? m : 1));
@@ -248,9 +252,12 @@ int orc_block_entmax(const void* q, int dtype, const double* kbar, int batch, in
                     mw[c / 32] |= 1u << (c % 32);
                     bo[c] = isinf(sigma) ? 0.0 : (log(wr[c]) - mu) / sigma;
                 }
-            /* the diagonal chunk: always attended, no bias [DA §3.4; Alg. 2, line 20] */
-            mw[ci / 32] |= 1u << (ci % 32);
-            bo[ci] = 0.0;
+            /* the diagonal chunk [DA §3.4; Alg. 2] and the window's chunks before it
+             * [DA App. B.1.1]: always attended, no bias */
+            for (int c = lo; c <= ci; ++c) {
+                mw[c / 32] |= 1u << (c % 32);
+                bo[c] = 0.0;
+            }
             if (w) {
                 double* wo = w + (kk * h_kv + r) * (int64_t)nc;
                 for (int c = 0; c < nc; ++c) wo[c] = c < m ? wr[c] : 0.0;

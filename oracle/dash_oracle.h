@@ -69,10 +69,13 @@ double orc_entmax_tau(const double* x, int m, double alpha);
 /* p_c = [x_c - tau]_+^(1/(alpha-1)) */
 void orc_entmax_probs(const double* x, int m, double alpha, double tau, double* p);
 
-/* Stage 1 for the listed query rows: chunk scores, per-head entmax, GQA mean, mask and bias. */
+/* Stage 1 for the listed query rows: chunk scores, per-head entmax, GQA mean, mask and bias.
+ * window >= 1 blocks are always attended: the query's own chunk and the window - 1 before it
+ * (the training window of [DA App. B.1.1] is window = 2); routing covers the complete chunks
+ * before them. window = 1 is [DA Alg. 2] as printed. */
 int orc_block_entmax(const void* q, int dtype, const double* kbar, int batch, int n_q, int q_pos0,
                      int n_kv, int h_q, int h_kv, int head_dim, int block, double alpha,
-                     double gamma, double sigma, const int64_t* rows, int64_t n_rows,
+                     double gamma, double sigma, int window, const int64_t* rows, int64_t n_rows,
                      uint32_t* mask, double* bias, double* tau, double* x, double* w);
 
 /* Stage 2, bias form (Prop. 1): softmax of scale * <q, k_j> + d_c(j) over the tokens of the

@@ -18,10 +18,10 @@ import torch
 
 __all__ = [
     "DashError", "lib", "library_path",
-    "dash_pool_keys", "dash_pool_keys_query", "dash_block_entmax",
-    "dash_block_entmax_workspace_bytes", "dash_sparse_attn_prefill",
-    "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_version",
-    "forward", "decode_step",
+    "dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append", "dash_block_entmax",
+    "dash_block_entmax_ex", "dash_block_entmax_workspace_bytes", "dash_sparse_attn_prefill",
+    "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
+    "dash_version", "forward", "decode_step",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -56,18 +56,24 @@ def lib():
         L.dash_version.restype = i
         L.dash_pool_keys.argtypes = [vp, i, vp, i, i, i, i, i, vp]
         L.dash_pool_keys_query.argtypes = [vp, i, vp, vp, i, i, i, i, i, vp]
+        L.dash_pool_keys_append.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, vp]
         L.dash_block_entmax_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
         L.dash_block_entmax_workspace_bytes.restype = sz
         L.dash_block_entmax.argtypes = [vp, i, vp, i, i, i, i, i, i, i, i, f, f, f, vp, vp, vp,
                                         vp, sz, vp]
+        L.dash_block_entmax_ex.argtypes = [vp, i, vp, vp, i, i, i, i, i, i, i, i, f, f, f, i, vp,
+                                           vp, vp, vp, sz, vp]
         L.dash_sparse_attn_prefill.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i,
                                                f, vp]
         L.dash_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.dash_decode_workspace_bytes.restype = sz
         L.dash_sparse_attn_decode.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, f,
                                               vp, sz, vp]
-        for fn in ("dash_pool_keys", "dash_pool_keys_query", "dash_block_entmax",
-                   "dash_sparse_attn_prefill", "dash_sparse_attn_decode"):
+        L.dash_sparse_attn_decode_varlen.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i,
+                                                     i, i, f, vp, sz, vp]
+        for fn in ("dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append",
+                   "dash_block_entmax", "dash_block_entmax_ex", "dash_sparse_attn_prefill",
+                   "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen"):
             getattr(L, fn).restype = i
         _lib = L
     return _lib
@@ -141,6 +147,62 @@ def dash_block_entmax_workspace_bytes(dtype, batch, n_q, q_pos0, n_kv, h_q, h_kv
     code = DASH_BF16 if dtype == torch.bfloat16 else DASH_F32
     return int(lib().dash_block_entmax_workspace_bytes(code, batch, n_q, q_pos0, n_kv, h_q, h_kv,
                                                        head_dim, block))
+
+
+def dash_pool_keys_append(k_cache: torch.Tensor, ctx_lens: torch.Tensor, kbar: torch.Tensor,
+                          block: int, qbar: torch.Tensor | None = None) -> torch.Tensor:
+    """Streaming Stage 0: write the summary of the chunk each sequence's newest token completed
+    (ctx_lens int32 [B] a positive multiple of block) into kbar [B, n_cap // block, Hkv, D]."""
+    b, n_cap, hkv, d = k_cache.shape
+    if ctx_lens.dtype != torch.int32:
+        raise TypeError("ctx_lens must be int32")
+    dev = _dev(k_cache, ctx_lens, kbar, qbar)
+    _check(lib().dash_pool_keys_append(_ptr(k_cache), _dtype_code(k_cache), _ptr(qbar),
+                                       _ptr(ctx_lens), _ptr(kbar), b, n_cap, hkv, d, block,
+                                       _stream(dev)))
+    return kbar
+
+
+def _route_outputs(q, n_kv, block, hkv, mask, bias, tau, want_tau):
+    b, n_q, hq, _ = q.shape
+    nc = -(-n_kv // block)
+    nw = -(-nc // 32)
+    dev = q.device
+    if mask is None:
+        mask = torch.empty((b, n_q, hkv, nw), dtype=torch.int32, device=dev)
+    if bias is None:
+        bias = torch.empty((b, n_q, hkv, nc), dtype=torch.float32, device=dev)
+    if tau is None and want_tau:
+        tau = torch.empty((b, n_q, hq), dtype=torch.float32, device=dev)
+    return mask, bias, tau
+
+
+def dash_block_entmax_ex(q: torch.Tensor, kbar: torch.Tensor, *, n_kv: int, block: int,
+                         alpha: float, gamma: float, sigma: float, q_pos0: int = 0,
+                         h_kv: int | None = None, ctx_lens: torch.Tensor | None = None,
+                         window_blocks: int = 1, mask: torch.Tensor | None = None,
+                         bias: torch.Tensor | None = None, tau: torch.Tensor | None = None,
+                         want_tau: bool = True, workspace: torch.Tensor | None = None):
+    """Stage 1 with the attention window (window_blocks blocks always attended: the query's own
+    and the window_blocks - 1 before it) and, for decode (n_q = 1), per-sequence context lengths
+    ctx_lens int32 [B] in a cache of capacity n_kv. Outputs as dash_block_entmax."""
+    b, n_q, hq, d = q.shape
+    hkv = kbar.shape[2] if h_kv is None else h_kv
+    mask, bias, tau = _route_outputs(q, n_kv, block, hkv, mask, bias, tau, want_tau)
+    if ctx_lens is not None:
+        if ctx_lens.dtype != torch.int32:
+            raise TypeError("ctx_lens must be int32")
+        q_pos0 = n_kv - 1
+    need = dash_block_entmax_workspace_bytes(q.dtype, b, n_q, q_pos0, n_kv, hq, hkv, d, block)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dev = _dev(q, kbar, ctx_lens, mask, bias, tau, workspace)
+    _check(lib().dash_block_entmax_ex(
+        _ptr(q), _dtype_code(q), _ptr(kbar), _ptr(ctx_lens), b, n_q, q_pos0, n_kv, hq, hkv, d,
+        block, float(alpha), float(gamma), float(sigma), int(window_blocks), _ptr(mask),
+        _ptr(bias), _ptr(tau), _ptr(workspace), wsb, _stream(dev)))
+    return mask, bias, tau
 
 
 def dash_block_entmax(q: torch.Tensor, kbar: torch.Tensor, *, n_kv: int, block: int, alpha: float,
@@ -217,6 +279,33 @@ def dash_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     _check(lib().dash_sparse_attn_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(mask), _ptr(bias), _ptr(o),
         b, n_ctx, hq, hkv, d, block, float(scale), _ptr(workspace), wsb, _stream(dev)))
+    return o
+
+
+def dash_sparse_attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   ctx_lens: torch.Tensor, mask: torch.Tensor, bias: torch.Tensor,
+                                   *, block: int, scale: float | None = None,
+                                   o: torch.Tensor | None = None,
+                                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Stage 2 decode with per-sequence lengths ctx_lens int32 [B] in a cache of capacity
+    k_cache.shape[1]: q [B, Hq, D] (or [B, 1, Hq, D]) -> o of the same shape."""
+    b, n_cap, hkv, d = k_cache.shape
+    hq = q.shape[-2]
+    if ctx_lens.dtype != torch.int32:
+        raise TypeError("ctx_lens must be int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    need = dash_decode_workspace_bytes(b, n_cap, hq, hkv, d, block)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dev = _dev(q, k_cache, v_cache, ctx_lens, mask, bias, o, workspace)
+    _check(lib().dash_sparse_attn_decode_varlen(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(ctx_lens), _ptr(mask),
+        _ptr(bias), _ptr(o), b, n_cap, hq, hkv, d, block, float(scale), _ptr(workspace), wsb,
+        _stream(dev)))
     return o
 
 

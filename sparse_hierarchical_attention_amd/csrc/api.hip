@@ -67,6 +67,7 @@ dash::RouteParams route_params(int batch, int n_q, int q_pos0, int n_kv, int h_q
     p.g = h_q / h_kv; p.head_dim = head_dim; p.block = block; p.tc = n_kv / block;
     p.nc = ceil_div(n_kv, block); p.nw = ceil_div(p.nc, 32);
     p.alpha = alpha; p.gamma = gamma; p.inv_sigma = isinf(sigma) ? 0.0f : 1.0f / sigma;
+    p.win = 0; p.ctx_lens = nullptr;
     return p;
 }
 
@@ -76,8 +77,21 @@ dash::AttnParams attn_params(int batch, int n_q, int q_pos0, int n_kv, int h_q, 
     p.batch = batch; p.n_q = n_q; p.q_pos0 = q_pos0; p.n_kv = n_kv; p.h_q = h_q; p.h_kv = h_kv;
     p.g = h_q / h_kv; p.head_dim = head_dim; p.block = block;
     p.nc = ceil_div(n_kv, block); p.nw = ceil_div(p.nc, 32); p.scale = scale;
+    p.ctx_lens = nullptr;
     return p;
 }
+
+// the shared bodies of the entry points with and without per-sequence lengths (defined below)
+dash_status_t route_call(const char* fn, const void* q, dash_dtype_t dt, const float* kbar,
+                         const int32_t* ctx_lens, int batch, int n_q, int q_pos0, int n_kv,
+                         int h_q, int h_kv, int head_dim, int block, float alpha, float gamma,
+                         float sigma, int window_blocks, uint32_t* mask, float* bias, float* tau,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+dash_status_t decode_call(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                          dash_dtype_t dt, const int32_t* ctx_lens, const uint32_t* mask,
+                          const float* bias, void* o, int batch, int n_ctx, int h_q, int h_kv,
+                          int head_dim, int block, float scale, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace
 
@@ -119,6 +133,17 @@ dash_status_t dash_pool_keys_query(const void* k, dash_dtype_t dt, const float* 
                       "dash_pool_keys_query");
 }
 
+dash_status_t dash_pool_keys_append(const void* k_cache, dash_dtype_t dt, const float* qbar,
+                                    const int32_t* ctx_lens, float* kbar, int batch, int n_cap,
+                                    int h_kv, int head_dim, int block, hipStream_t stream) {
+    const char* fn = "dash_pool_keys_append";
+    dash_status_t s = check_shape(fn, dt, batch, n_cap, h_kv, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (!k_cache || !ctx_lens || (!kbar && n_cap / block > 0)) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    return hip_status(dash::launch_pool_append(k_cache, dt, qbar, ctx_lens, kbar, batch, n_cap, h_kv,
+                                               head_dim, block, stream), fn);
+}
+
 size_t dash_block_entmax_workspace_bytes(dash_dtype_t dt, int batch, int n_q, int q_pos0,
                                          int n_kv, int h_q, int h_kv, int head_dim, int block) {
     if (batch <= 0 || n_q <= 0 || n_kv <= 0 || h_q <= 0 || h_kv <= 0 || block <= 0 || h_q % h_kv)
@@ -132,9 +157,38 @@ dash_status_t dash_block_entmax(const void* q, dash_dtype_t dt, const float* kba
                                 int block, float alpha, float gamma, float sigma, uint32_t* mask,
                                 float* bias, float* tau, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
-    const char* fn = "dash_block_entmax";
+    return route_call("dash_block_entmax", q, dt, kbar, nullptr, batch, n_q, q_pos0, n_kv, h_q,
+                      h_kv, head_dim, block, alpha, gamma, sigma, 1, mask, bias, tau, workspace,
+                      workspace_bytes, stream);
+}
+
+dash_status_t dash_block_entmax_ex(const void* q, dash_dtype_t dt, const float* kbar,
+                                   const int32_t* ctx_lens, int batch, int n_q, int q_pos0,
+                                   int n_kv, int h_q, int h_kv, int head_dim, int block,
+                                   float alpha, float gamma, float sigma, int window_blocks,
+                                   uint32_t* mask, float* bias, float* tau, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    return route_call("dash_block_entmax_ex", q, dt, kbar, ctx_lens, batch, n_q, q_pos0, n_kv,
+                      h_q, h_kv, head_dim, block, alpha, gamma, sigma, window_blocks, mask, bias,
+                      tau, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+dash_status_t route_call(const char* fn, const void* q, dash_dtype_t dt, const float* kbar,
+                         const int32_t* ctx_lens, int batch, int n_q, int q_pos0, int n_kv,
+                         int h_q, int h_kv, int head_dim, int block, float alpha, float gamma,
+                         float sigma, int window_blocks, uint32_t* mask, float* bias, float* tau,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
     dash_status_t s = check_shape(fn, dt, batch, n_kv, h_q, h_kv, head_dim, block);
     if (s != DASH_OK) return s;
+    if (ctx_lens) {
+        if (n_q != 1) return fail(DASH_ERR_INVALID, "%s: per-sequence lengths need n_q = 1 (n_q=%d)", fn, n_q);
+        q_pos0 = n_kv - 1;  // unused on the device; keeps the range check below meaningful
+    }
+    if (window_blocks < 1) return fail(DASH_ERR_INVALID, "%s: window_blocks=%d must be >= 1", fn, window_blocks);
     if (n_q <= 0 || q_pos0 < 0 || (int64_t)q_pos0 + n_q > n_kv)
         return fail(DASH_ERR_INVALID, "%s: need n_q > 0 and 0 <= q_pos0, q_pos0 + n_q <= n_kv (n_q=%d q_pos0=%d n_kv=%d)",
                     fn, n_q, q_pos0, n_kv);
@@ -145,12 +199,18 @@ dash_status_t dash_block_entmax(const void* q, dash_dtype_t dt, const float* kba
         return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
     dash::RouteParams p = route_params(batch, n_q, q_pos0, n_kv, h_q, h_kv, head_dim, block, alpha,
                                        gamma, sigma);
+    p.win = window_blocks - 1;
+    p.ctx_lens = ctx_lens;
     const size_t need = dash::route_workspace_bytes(p, (int)dt);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace ? workspace_bytes : (size_t)0);
     return hip_status(dash::launch_block_entmax(q, dt, kbar, p, mask, bias, tau, workspace, stream), fn);
 }
+
+}  // namespace
+
+extern "C" {
 
 dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                        dash_dtype_t dt, const uint32_t* mask, const float* bias,
@@ -180,12 +240,39 @@ dash_status_t dash_sparse_attn_decode(const void* q, const void* k_cache, const 
                                       void* o, int batch, int n_ctx, int h_q, int h_kv,
                                       int head_dim, int block, float scale, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream) {
-    const char* fn = "dash_sparse_attn_decode";
+    return decode_call("dash_sparse_attn_decode", q, k_cache, v_cache, dt, nullptr, mask, bias, o,
+                       batch, n_ctx, h_q, h_kv, head_dim, block, scale, workspace, workspace_bytes,
+                       stream);
+}
+
+dash_status_t dash_sparse_attn_decode_varlen(const void* q, const void* k_cache,
+                                             const void* v_cache, dash_dtype_t dt,
+                                             const int32_t* ctx_lens, const uint32_t* mask,
+                                             const float* bias, void* o, int batch, int n_cap,
+                                             int h_q, int h_kv, int head_dim, int block,
+                                             float scale, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+    if (!ctx_lens) return fail(DASH_ERR_INVALID, "dash_sparse_attn_decode_varlen: null pointer");
+    return decode_call("dash_sparse_attn_decode_varlen", q, k_cache, v_cache, dt, ctx_lens, mask,
+                       bias, o, batch, n_cap, h_q, h_kv, head_dim, block, scale, workspace,
+                       workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+dash_status_t decode_call(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                          dash_dtype_t dt, const int32_t* ctx_lens, const uint32_t* mask,
+                          const float* bias, void* o, int batch, int n_ctx, int h_q, int h_kv,
+                          int head_dim, int block, float scale, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
     dash_status_t s = check_shape(fn, dt, batch, n_ctx, h_q, h_kv, head_dim, block);
     if (s != DASH_OK) return s;
     if (!(scale > 0.0f) || isinf(scale)) return fail(DASH_ERR_INVALID, "%s: scale=%g must be positive and finite", fn, scale);
     if (!q || !k_cache || !v_cache || !mask || !bias || !o) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
     dash::AttnParams p = attn_params(batch, 1, n_ctx - 1, n_ctx, h_q, h_kv, head_dim, block, scale);
+    p.ctx_lens = ctx_lens;
     const size_t need = dash::decode_workspace_bytes(p);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -193,4 +280,4 @@ dash_status_t dash_sparse_attn_decode(const void* q, const void* k_cache, const 
     return hip_status(dash::launch_attn_decode(q, k_cache, v_cache, dt, mask, bias, o, p, workspace, stream), fn);
 }
 
-}  // extern "C"
+}  // namespace

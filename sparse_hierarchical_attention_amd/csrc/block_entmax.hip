@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ q,
     const int row0 = blockIdx.y * kScoreTile, c0 = blockIdx.x * kScoreTile;
     const int rows_total = p.n_q * p.g;
     const int row_last = min(row0 + kScoreTile, rows_total) - 1;
-    const int m_last = min((p.q_pos0 + row_last / p.g) / p.block, p.tc);
+    const int m_last = route_cands(p, route_pos(p, b, row_last / p.g));
     if (c0 >= m_last) return;  // every row of this tile sees fewer chunks (uniform exit)
 
     // D is consumed in slices of 32: 64 x 32 tiles of Q and kbar in LDS (one 8-element load
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ q,
         const int row = row0 + ty + 16 * i;
         if (row >= rows_total) continue;
         const int t = row / p.g, gg = row % p.g;
-        const int m = min((p.q_pos0 + t) / p.block, p.tc);
+        const int m = route_cands(p, route_pos(p, b, t));
         float* xr = x + (((int64_t)b * p.n_q + t) * p.h_q + r * p.g + gg) * p.nc;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void score_one_kernel(const T* __restrict__ q,
     constexpr int NV = D / 16;  // float4 pieces per lane
     __shared__ __align__(16) float qs[16 * D];
     const int b = blockIdx.y / p.h_kv, r = blockIdx.y % p.h_kv;
-    const int m = min(p.q_pos0 / p.block, p.tc);  // complete chunks before the query's own
+    const int m = route_cands(p, route_pos(p, b, 0));  // complete chunks before the window
     const int tid = threadIdx.x;
     const int c = blockIdx.x * 64 + tid / 4;
     const int k = tid & 3;
@@ -158,9 +158,9 @@ __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ x,
                                                    float* __restrict__ tau_out, RouteParams p) {
     const int t = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
-    const int pos = p.q_pos0 + t;
+    const int pos = route_pos(p, b, t);
     const int cp = pos / p.block;
-    const int m = min(cp, p.tc);
+    const int m = route_cands(p, pos);
     const int64_t qrow = (int64_t)b * p.n_q + t;
     const float e = 1.0f / (p.alpha - 1.0f);
     float w[NPL];
@@ -196,9 +196,9 @@ __global__ __launch_bounds__(NPL >= 64 ? 256 : 1024) void route_group_kernel(con
     const int t = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     extern __shared__ float ps[];
-    const int pos = p.q_pos0 + t;
+    const int pos = route_pos(p, b, t);
     const int cp = pos / p.block;
-    const int m = min(cp, p.tc);
+    const int m = route_cands(p, pos);
     const int64_t qrow = (int64_t)b * p.n_q + t;
     const float e = 1.0f / (p.alpha - 1.0f);
     if (wave < p.g) {
@@ -309,8 +309,9 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(const float* __restr
     const int nwaves = blockDim.x >> 6;
     const int hh = wave / WPH, wq = wave % WPH;
     const int h = r * p.g + hh;
-    const int cp = p.q_pos0 / p.block;
-    const int m = min(cp, p.tc);
+    const int pos = route_pos(p, b, 0);
+    const int cp = pos / p.block;
+    const int m = route_cands(p, pos);
     const int ns = (m + L - 1) / L;
     const float e = 1.0f / (p.alpha - 1.0f);
 
@@ -422,13 +423,13 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(const float* __restr
         const float w = c < m ? wsum[c] * inv_g : 0.f;
         const bool sel = c < m && w > 0.f;
         if (sel) brow[c] = (__logf(w) - mu) * p.inv_sigma;
-        const uint64_t bal = __ballot(sel || c == cp);
+        const uint64_t bal = __ballot(sel || (c >= m && c <= cp));  // routed, or in the window
         if (lane == 0) {
             mrow[base / 32] = (uint32_t)bal;
             if (base / 32 + 1 < p.nw) mrow[base / 32 + 1] = (uint32_t)(bal >> 32);
         }
     }
-    if (tid == 0) brow[cp] = 0.f;
+    for (int c = m + tid; c <= cp; c += blockDim.x) brow[c] = 0.f;
 }
 
 // waves per head row of route_decode_kernel (16 waves at most), and its slots per lane

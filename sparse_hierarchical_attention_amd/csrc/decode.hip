@@ -102,8 +102,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
 
     const int s = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = p.n_kv;
-    const int pos = n - 1;
+    const int n = p.n_kv;  // cache capacity (the row stride of K and V)
+    const int pos = seq_pos(p.ctx_lens, n - 1, n, b, 0);
     const int cp = pos / p.block;
     const uint32_t* mrow = mask + ((int64_t)b * p.h_kv + r) * p.nw;
     const float* brow = bias + ((int64_t)b * p.h_kv + r) * p.nc;

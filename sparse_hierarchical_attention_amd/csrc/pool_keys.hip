@@ -13,11 +13,22 @@ namespace dash {
 
 constexpr int kPoolCols = kWave * 8;  // columns per workgroup
 
+// Streaming decode: the chunk that sequence b's newest token completed (its length clamped into
+// [0, cap] is a positive multiple of the chunk size), or -1 when that token left its chunk open.
+// A chunk's summary depends on its own keys only, so it is final from then on [DA §3.1].
+__device__ __forceinline__ int completed_chunk(const int* ctx_lens, int b, int cap, int block) {
+    const int n = min(max(ctx_lens[b], 0), cap);
+    return n > 0 && n % block == 0 ? n / block - 1 : -1;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void pool_mean_kernel(const T* __restrict__ k,
                                                         float* __restrict__ kbar, int n_kv,
-                                                        int cols, int block, int tc) {
-    const int c = blockIdx.y, b = blockIdx.z;
+                                                        int cols, int block, int tc,
+                                                        const int* __restrict__ ctx_lens) {
+    const int b = blockIdx.z;
+    const int c = ctx_lens ? completed_chunk(ctx_lens, b, n_kv, block) : (int)blockIdx.y;
+    if (c < 0) return;  // the whole workgroup
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int col = blockIdx.x * kPoolCols + lane * 8;
     __shared__ float part[4][8][kWave];
@@ -55,8 +66,11 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void pool_query_kernel(const T* __restrict__ k,
                                                         const float* __restrict__ qbar,
                                                         float* __restrict__ kbar, int n_kv,
-                                                        int h_kv, int block, int tc) {
-    const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+                                                        int h_kv, int block, int tc,
+                                                        const int* __restrict__ ctx_lens) {
+    const int r = blockIdx.y, b = blockIdx.z;
+    const int c = ctx_lens ? completed_chunk(ctx_lens, b, n_kv, block) : (int)blockIdx.x;
+    if (c < 0) return;  // the whole workgroup
     const int lane = threadIdx.x;
     __shared__ float qs[D];
     __shared__ float pw[128];
@@ -111,10 +125,10 @@ hipError_t launch_pool_mean(const void* k, int dt, float* kbar, int batch, int n
     dim3 grid(div_up(cols, kPoolCols), tc, batch);
     if (dt == kBF16)
         hipLaunchKernelGGL(pool_mean_kernel<bf16_t>, grid, dim3(256), 0, st,
-                           static_cast<const bf16_t*>(k), kbar, n_kv, cols, block, tc);
+                           static_cast<const bf16_t*>(k), kbar, n_kv, cols, block, tc, nullptr);
     else
         hipLaunchKernelGGL(pool_mean_kernel<float>, grid, dim3(256), 0, st,
-                           static_cast<const float*>(k), kbar, n_kv, cols, block, tc);
+                           static_cast<const float*>(k), kbar, n_kv, cols, block, tc, nullptr);
     return hipGetLastError();
 }
 
@@ -125,7 +139,38 @@ hipError_t launch_pool_query(const void* k, int dt, const float* qbar, float* kb
     dim3 grid(tc, h_kv, batch);
 #define DASH_POOLQ(T, DD)                                                                  \
     hipLaunchKernelGGL((pool_query_kernel<T, DD>), grid, dim3(64), 0, st,                  \
-                       static_cast<const T*>(k), qbar, kbar, n_kv, h_kv, block, tc)
+                       static_cast<const T*>(k), qbar, kbar, n_kv, h_kv, block, tc, nullptr)
+    if (dt == kBF16) {
+        if (head_dim == 64) DASH_POOLQ(bf16_t, 64); else DASH_POOLQ(bf16_t, 128);
+    } else {
+        if (head_dim == 64) DASH_POOLQ(float, 64); else DASH_POOLQ(float, 128);
+    }
+#undef DASH_POOLQ
+    return hipGetLastError();
+}
+
+// Summaries of the chunks completed by each sequence's newest token (streaming decode): one
+// workgroup per sequence (and column slab, or KV head), idle where no chunk completed.
+hipError_t launch_pool_append(const void* k, int dt, const float* qbar, const int* ctx_lens,
+                              float* kbar, int batch, int n_cap, int h_kv, int head_dim, int block,
+                              hipStream_t st) {
+    const int tc = n_cap / block;
+    if (tc == 0) return hipSuccess;
+    if (!qbar) {
+        const int cols = h_kv * head_dim;
+        dim3 grid(div_up(cols, kPoolCols), 1, batch);
+        if (dt == kBF16)
+            hipLaunchKernelGGL(pool_mean_kernel<bf16_t>, grid, dim3(256), 0, st,
+                               static_cast<const bf16_t*>(k), kbar, n_cap, cols, block, tc, ctx_lens);
+        else
+            hipLaunchKernelGGL(pool_mean_kernel<float>, grid, dim3(256), 0, st,
+                               static_cast<const float*>(k), kbar, n_cap, cols, block, tc, ctx_lens);
+        return hipGetLastError();
+    }
+    dim3 grid(1, h_kv, batch);
+#define DASH_POOLQ(T, DD)                                                                  \
+    hipLaunchKernelGGL((pool_query_kernel<T, DD>), grid, dim3(64), 0, st,                  \
+                       static_cast<const T*>(k), qbar, kbar, n_cap, h_kv, block, tc, ctx_lens)
     if (dt == kBF16) {
         if (head_dim == 64) DASH_POOLQ(bf16_t, 64); else DASH_POOLQ(bf16_t, 128);
     } else {

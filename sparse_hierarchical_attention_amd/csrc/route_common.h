@@ -31,7 +31,8 @@ __device__ __forceinline__ void load_row(const float* __restrict__ xr, int m, in
 
 // Mask words and bias of one (query, group) row from the group-averaged probabilities w held in
 // registers (chunk c in lane c % 64, slot c / 64): mu = mean log w over R = {c < m : w_c > 0},
-// d_c = (log w_c - mu) / sigma on R; the query's own chunk cp always gets its bit and d = 0.
+// d_c = (log w_c - mu) / sigma on R; the window's chunks m .. cp (the query's own chunk and the
+// blocks before it that are always attended) get their bits and d = 0.
 template <int NPL>
 __device__ __forceinline__ void write_route_row(const float (&w)[NPL], int m, int cp, int lane,
                                                 uint32_t* mrow, float* brow, const RouteParams& p) {
@@ -49,13 +50,13 @@ __device__ __forceinline__ void write_route_row(const float (&w)[NPL], int m, in
         const int c = 64 * i + lane;
         const bool sel = c < m && w[i] > 0.f;
         if (sel) brow[c] = (__logf(w[i]) - mu) * p.inv_sigma;
-        const uint64_t bal = __ballot(sel || c == cp);
+        const uint64_t bal = __ballot(sel || (c >= m && c <= cp));
         if (lane == 0) {
             mrow[2 * i] = (uint32_t)bal;
             if (2 * i + 1 < p.nw) mrow[2 * i + 1] = (uint32_t)(bal >> 32);
         }
     }
-    if (lane == 0) brow[cp] = 0.f;
+    for (int c = m + lane; c <= cp; c += 64) brow[c] = 0.f;
 }
 
 }  // namespace dash

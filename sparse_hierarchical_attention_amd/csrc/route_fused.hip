@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256) void split_kbar_kernel(const float* __restrict
 // The mask words and bias of one token's row from its group-summed probabilities wsum (entry c
 // in lane c % 16 of a 16-lane group, slot c / 16; every group holds the same row when g >= 4,
 // the rows of 4 / g tokens otherwise): w = wsum / g, mu = mean log w over R = {w > 0},
-// d = (log w - mu) / sigma on R, the query's own chunk cp always set with d = 0.
+// d = (log w - mu) / sigma on R, the window's chunks (the query's own chunk cp and the win
+// before it) always set with d = 0.
 template <int NSS, int GQ>
 __device__ __forceinline__ void route_write_token(float (&wsum)[NSS], int tok, int b, int r,
                                                   uint32_t* __restrict__ mask,
@@ -80,7 +81,9 @@ __device__ __forceinline__ void route_write_token(float (&wsum)[NSS], int tok, i
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4, li = lane & 15;
     const bool tvalid = tok < p.n_q;
-    const int cp = (p.q_pos0 + tok) / p.block;
+    const int pos = route_pos(p, b, tok);
+    const int cp = pos / p.block;
+    const int m = route_cands(p, pos);  // chunks m .. cp: the window, always attended with d = 0
     const float inv_g = 1.0f / (float)GQ;
     float lsum = 0.f, lcnt = 0.f;
 #pragma unroll
@@ -110,14 +113,14 @@ __device__ __forceinline__ void route_write_token(float (&wsum)[NSS], int tok, i
         if (writer && li == 0 && wd < p.nw) {
             uint32_t word = (uint32_t)((b0 >> (16 * grp)) & 0xffffu) |
                             ((uint32_t)((b1 >> (16 * grp)) & 0xffffu) << 16);
-            if (cp / 32 == wd) word |= 1u << (cp % 32);
-            mrow[wd] = word;
+            mrow[wd] = word | span_bits(wd, m, cp);
         }
     }
-    // words past the bucket: only the query's own chunk can be set there
+    // words past the bucket: only the window's chunks can be set there
     for (int wd = NSS / 2 + li; wd < p.nw; wd += 16)
-        if (writer) mrow[wd] = cp / 32 == wd ? 1u << (cp % 32) : 0u;
-    if (writer && li == 0) brow[cp] = 0.f;
+        if (writer) mrow[wd] = span_bits(wd, m, cp);
+    for (int c = m + li; c <= cp; c += 16)
+        if (writer) brow[c] = 0.f;
 }
 
 // One pass of the fused route's phase 2 (see route_fused_kernel): the four rows xr0 + k xstride,
@@ -133,7 +136,7 @@ __device__ __forceinline__ void route_pass(const float* __restrict__ xr0, int xs
     const int row = row0 + grp;
     const int tok = tile0 + row / GQ;
     const bool tvalid = tok < p.n_q;
-    const int m = tvalid ? min((p.q_pos0 + tok) / p.block, p.tc) : 0;
+    const int m = tvalid ? route_cands(p, route_pos(p, b, tok)) : 0;
     const float* xr = xr0 + grp * xstride;
     float xv[NSS];
 #pragma unroll
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
     const int b = gr / p.h_kv, r = gr % p.h_kv;
     const int tile0 = tile * T;
     const int tile_end = min(tile0 + T, p.n_q);
-    const int m_max = min((p.q_pos0 + tile_end - 1) / p.block, p.tc);
+    const int m_max = route_cands(p, route_pos(p, b, tile_end - 1));
     const int n_ct = div_up(m_max, 32);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
     else if (CMAX >= 512 && (NS_) <= 32) CALL(CMAX >= 512 ? 32 : 16);                           \
     else if (CMAX >= 1024) CALL(CMAX >= 1024 ? 64 : 16)
     auto slots_of = [&](int tok) {  // 16-lane slots of a token's row
-        return div_up(min((p.q_pos0 + min(tok, p.n_q - 1)) / p.block, p.tc), 16);
+        return div_up(route_cands(p, route_pos(p, b, min(tok, p.n_q - 1))), 16);
     };
     if constexpr (GQ <= 4) {
         for (int u = wave; u < ROWS / 4; u += NW) {

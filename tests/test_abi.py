@@ -100,3 +100,20 @@ def test_attention_rejects_bad_arguments(L):
                                      0, None) == 3
     assert L.dash_sparse_attn_decode(p, p, p, 1, p, p, p, 2, 4096, 8, 2, 128, 64, 0.0, None,
                                      0, None) == 1 and "scale" in err(L)
+
+
+def test_streaming_and_window_entry_points_reject_bad_arguments(L):
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation
+    # per-sequence lengths need one query per sequence
+    assert L.dash_block_entmax_ex(p, 1, p, p, 2, 2, 0, 4096, 8, 2, 128, 64, 1.5, 1.0, 1.0, 1,
+                                  p, p, None, p, 1 << 30, None) == 1 and "n_q = 1" in err(L)
+    assert L.dash_block_entmax_ex(p, 1, p, None, 1, 64, 0, 64, 4, 2, 128, 64, 1.5, 1.0, 1.0, 0,
+                                  p, p, None, p, 1 << 30, None) == 1 and "window" in err(L)
+    assert L.dash_block_entmax_ex(p, 1, p, None, 1, 64, 0, 64, 4, 2, 128, 64, 3.0, 1.0, 1.0, 2,
+                                  p, p, None, p, 1 << 30, None) == 1 and "alpha" in err(L)
+    assert L.dash_sparse_attn_decode_varlen(p, p, p, 1, None, p, p, p, 2, 4096, 8, 2, 128, 64,
+                                            0.1, p, 1 << 20, None) == 1 and "null" in err(L)
+    assert L.dash_sparse_attn_decode_varlen(p, p, p, 1, p, p, p, p, 2, 4096, 8, 2, 128, 64,
+                                            0.1, None, 0, None) == 3
+    assert L.dash_pool_keys_append(p, 1, None, None, p, 2, 4096, 2, 128, 64, None) == 1
+    assert L.dash_pool_keys_append(p, 1, None, p, p, 2, 4096, 2, 96, 64, None) == 2

@@ -142,6 +142,83 @@ def test_route_first_chunk_rows_attend_to_themselves_only(orc):
         assert np.all(st["mask"][t, :, 0] == 1) and np.all(np.isinf(st["tau"][t]))
 
 
+# ---------------------------------------------- the attention window [DA App. B.1.1]
+
+def test_window_of_one_block_is_the_default(orc):
+    w, inp = small_case(14)
+    kbar = orc.pool_keys(inp["k"], w.block)
+    a = orc.block_entmax(inp["q"], kbar, n_kv=w.n_kv, block=w.block, alpha=1.5, gamma=2.0, sigma=3.0)
+    b = orc.block_entmax(inp["q"], kbar, n_kv=w.n_kv, block=w.block, alpha=1.5, gamma=2.0, sigma=3.0,
+                         window=1)
+    for key in ("mask", "bias", "tau"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("window", [2, 3])
+def test_window_blocks_always_attended_and_not_routed(orc, window):
+    """The window's blocks (the query's own and window - 1 before it) carry their mask bit and
+    d = 0; routing sees only the complete chunks before them, and its threshold solves Eq. 2 on
+    exactly those candidates."""
+    w, inp = small_case(15)
+    kbar = orc.pool_keys(inp["k"], w.block)
+    alpha, sigma = 1.5, 3.0
+    st = orc.block_entmax(inp["q"], kbar, n_kv=w.n_kv, block=w.block, alpha=alpha, gamma=2.0,
+                          sigma=sigma, window=window)
+    gq = w.h_q // w.h_kv
+    for t in range(0, w.n_kv, 3):
+        ci = t // w.block
+        lo = max(0, ci - window + 1)
+        for h in range(w.h_q):
+            x = st["x"][t, h]
+            assert np.all(np.isnan(x[lo:]))                       # window and later: no score
+            if lo == 0:
+                assert np.isinf(st["tau"][t, h])
+                continue
+            assert not np.any(np.isnan(x[:lo]))
+            resid = np.sum(np.maximum(x[:lo] - st["tau"][t, h], 0.0) ** (1 / (alpha - 1))) - 1
+            assert abs(resid) < 1e-10                             # Eq. 2 on c < lo
+        for r in range(w.h_kv):
+            bits = np.array([(int(st["mask"][t, r, c // 32]) >> (c % 32)) & 1
+                             for c in range(-(-w.n_kv // w.block))])
+            assert bits[lo:ci + 1].all() and not bits[ci + 1:].any()
+            assert np.all(st["bias"][t, r, lo:ci + 1] == 0.0)
+            np.testing.assert_array_equal(bits[:lo], st["w"][t, r, :lo] > 0)
+            assert np.all(st["w"][t, r, lo:] == 0.0)
+
+
+@pytest.mark.parametrize("window", [2, 3])
+def test_window_attention_matches_brute_force_sdpa(orc, window):
+    """Stage 2 on a window's selection vs Eq. 1 with an explicit token-level mask and bias."""
+    w, inp = small_case(16)
+    q, k, v = (inp[x] for x in ("q", "k", "v"))
+    res = orc.forward(q, k, v, block=w.block, alpha=1.5, gamma=2.0, sigma=1.0, window=window)
+    gq = w.h_q // w.h_kv
+    scale = 1 / math.sqrt(w.head_dim)
+    qd, kd, vd = (x.double()[0] for x in (q, k, v))
+    for t in range(0, w.n_kv, 7):
+        for h in range(w.h_q):
+            r = h // gq
+            am = token_mask_matrix(res["mask"][t, r], res["bias"][t, r], t, w.block)
+            lo = max(0, t // w.block - window + 1)
+            assert np.all(am[lo * w.block:] == 0.0)               # the window, unbiased, in full
+            ref = sdpa_reference(qd[t:t + 1, h], kd[:t + 1, r], vd[:t + 1, r], am[None], scale)
+            np.testing.assert_allclose(res["o"][t, h], ref[0], atol=1e-12)
+
+
+def test_window_over_every_chunk_is_causal_sdpa(orc):
+    """A window reaching chunk 0 for every query leaves nothing to route: causal SDPA."""
+    w, inp = small_case(17, plant=False)
+    q, k, v = (inp[x] for x in ("q", "k", "v"))
+    res = orc.forward(q, k, v, block=w.block, alpha=1.5, gamma=2.0, sigma=1.0,
+                      window=w.n_kv // w.block + 1)
+    gq = w.h_q // w.h_kv
+    qd = q.double()[0].transpose(0, 1)[None]
+    kd = k.double()[0].transpose(0, 1).repeat_interleave(gq, 0)[None]
+    vd = v.double()[0].transpose(0, 1).repeat_interleave(gq, 0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, is_causal=True)[0]
+    np.testing.assert_allclose(res["o"], ref.transpose(0, 1).numpy(), atol=1e-12)
+
+
 # ------------------------------------------------------------------------------- Stage 2
 
 @pytest.mark.parametrize("sigma", [1.0, 10.0, 1e8])
