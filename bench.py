@@ -79,7 +79,7 @@ def decode_bytes(mask: torch.Tensor, w: wl.Workload) -> tuple[int, float]:
 KERNEL_SOURCES = {
     "sparse_attn_prefill": ["common.h", "kernels.h", "sparse_attn_dma.hip"],
     "decode_step": ["common.h", "kernels.h", "entmax.h", "route_common.h", "block_entmax.hip",
-                    "decode.hip"],
+                    "decode_common.h", "decode.hip"],
 }
 
 

@@ -226,77 +226,14 @@ __global__ __launch_bounds__(NPL >= 64 ? 256 : 1024) void route_group_kernel(con
                          bias + (qrow * p.h_kv + r) * p.nc, p);
 }
 
-// Reductions of the threshold solver over the WPH waves that hold one row, for a workgroup
-// whose waves all run the solver together (each reduction is one barrier). red: LDS scratch of
-// 2 x 16 x 6 floats, double-buffered so that one barrier per pass suffices. The loop of the
-// solver ends for the whole workgroup once every wave reported done at the start of a pass.
-template <int WPH>
-struct WaveSetReduce {
-    float* red;
-    int wave, lane, w0, nwaves;
-    int buf;
-    bool all_done;
-    __device__ float max(float v) {
-        v = wave_max(v);
-        if (lane == 0) red[wave * 6] = v;
-        __syncthreads();
-        float m = red[w0 * 6];
-#pragma unroll
-        for (int i = 1; i < WPH; ++i) m = fmaxf(m, red[(w0 + i) * 6]);
-        buf = 1;
-        all_done = false;
-        return m;
-    }
-    __device__ bool all(bool) { return all_done; }
-    __device__ void gather(float& k, float& p1, float& p2, float& tmin, float& tout, bool done) {
-        k = wave_sum(k);
-        p1 = wave_sum(p1);
-        p2 = wave_sum(p2);
-        tmin = wave_min(tmin);
-        tout = wave_max(tout);
-        float* rb = red + buf * 96;
-        if (lane == 0) {
-            rb[wave * 6 + 0] = k;
-            rb[wave * 6 + 1] = p1;
-            rb[wave * 6 + 2] = p2;
-            rb[wave * 6 + 3] = tmin;
-            rb[wave * 6 + 4] = tout;
-            rb[wave * 6 + 5] = done ? 1.f : 0.f;
-        }
-        __syncthreads();
-        k = rb[w0 * 6];
-        p1 = rb[w0 * 6 + 1];
-        p2 = rb[w0 * 6 + 2];
-        tmin = rb[w0 * 6 + 3];
-        tout = rb[w0 * 6 + 4];
-#pragma unroll
-        for (int i = 1; i < WPH; ++i) {
-            k += rb[(w0 + i) * 6];
-            p1 += rb[(w0 + i) * 6 + 1];
-            p2 += rb[(w0 + i) * 6 + 2];
-            tmin = fminf(tmin, rb[(w0 + i) * 6 + 3]);
-            tout = fmaxf(tout, rb[(w0 + i) * 6 + 4]);
-        }
-        bool ad = true;
-        for (int i = 0; i < nwaves; ++i) ad = ad && rb[i * 6 + 5] != 0.f;
-        all_done = ad;
-        buf ^= 1;
-    }
-};
-
-constexpr int kDecCand = 256;  // packed candidates per head row
-
-// One query per sequence (decode), one workgroup per (sequence, group): the g heads' rows are
-// each spread over WPH waves (entry c in lane c % 64 of the head's wave (c / 64) % WPH, slot
-// c / (64 WPH)), which solve the head's threshold together; the heads' probabilities are added
-// in head order in LDS, and all waves then write the mask words and the bias.
+// One query per sequence (decode): one workgroup per (sequence, group), scores from the
+// workspace (see decode_route_group).
 template <int NS, int KIND, int WPH>
 __global__ __launch_bounds__(1024) void route_decode_kernel(const float* __restrict__ x,
                                                             uint32_t* __restrict__ mask,
                                                             float* __restrict__ bias,
                                                             float* __restrict__ tau_out,
                                                             RouteParams p) {
-    constexpr int L = 64 * WPH;  // lanes per row
     __shared__ float red[2 * 16 * 6];
     __shared__ float stat_s[16];
     __shared__ int stat_n[16];
@@ -305,131 +242,15 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(const float* __restr
     __shared__ float cand[16 * kDecCand];
     extern __shared__ float wsum[];  // group sum of probabilities, one per chunk
     const int r = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
-    const int hh = wave / WPH, wq = wave % WPH;
-    const int h = r * p.g + hh;
     const int pos = route_pos(p, b, 0);
-    const int cp = pos / p.block;
-    const int m = route_cands(p, pos);
-    const int ns = (m + L - 1) / L;
-    const float e = 1.0f / (p.alpha - 1.0f);
-
-    // the row, loads unconditional (clamped into the row) so that all are in flight together
-    const float* xr = x + ((int64_t)b * p.h_q + h) * p.nc;
-    const int last = m > 0 ? m - 1 : 0;
-    float xv[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) xv[i] = xr[min(i * L + wq * 64 + lane, last)];
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-        if (i * L + wq * 64 + lane >= m) xv[i] = -INFINITY;
-
-    // tau never falls below max x - 1, so only entries above it can enter the support. When no
-    // head has more than kDecCand of them, they are packed into LDS and each head's first wave
-    // solves on its packed list alone; otherwise the head's waves solve on the whole row.
-    WaveSetReduce<WPH> rd{red, wave, lane, hh * WPH, nwaves, 0, false};
-    float xm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) xm = fmaxf(xm, xv[i]);
-    const float lo = rd.max(xm) - 1.0f;
-    int ncand = 0;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) ncand += __popcll(__ballot(xv[i] > lo));
-    if (lane == 0) cand_n[wave] = ncand;
-    __syncthreads();
-    int before = 0, head_n = 0, most = 0;
-    for (int w = 0; w < nwaves; ++w) {
-        const int cw = cand_n[w];
-        if (w / WPH == hh) {
-            head_n += cw;
-            before += w < wave ? cw : 0;
-        }
-        if (w % WPH == WPH - 1) {
-            int hn = 0;
-            for (int v = w - WPH + 1; v <= w; ++v) hn += cand_n[v];
-            most = max(most, hn);
-        }
-    }
-    float tau;
-    if (most <= kDecCand) {
-        const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            const bool in = xv[i] > lo;
-            const uint64_t bal = __ballot(in);
-            if (in) cand[hh * kDecCand + before + __popcll(bal & below)] = xv[i];
-            before += __popcll(bal);
-        }
-        __syncthreads();
-        if (wq == 0) {
-            float cv[kDecCand / 64];
-#pragma unroll
-            for (int i = 0; i < kDecCand / 64; ++i)
-                cv[i] = 64 * i + lane < head_n ? cand[hh * kDecCand + 64 * i + lane] : -INFINITY;
-            const float t = solve_tau_exact<kDecCand / 64, KIND, 64>(cv, (head_n + 63) / 64, head_n, p.alpha);
-            if (lane == 0) tau_h[hh] = t;
-        }
-        __syncthreads();
-        tau = tau_h[hh];
-    } else {
-        tau = solve_tau_core<NS, KIND>(xv, ns, m, p.alpha, rd);
-    }
-    if (tau_out && wq == 0 && lane == 0) tau_out[(int64_t)b * p.h_q + h] = tau;
-
-    for (int g0 = 0; g0 < p.g; ++g0) {
-        if (hh == g0) {
-#pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                const int c = i * L + wq * 64 + lane;
-                if (c < m) {
-                    const float pv = pow_e<KIND>(xv[i] - tau, e);
-                    wsum[c] = g0 == 0 ? pv : wsum[c] + pv;
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    // mu = mean of log w over R, in a fixed order (waves, then lanes by DPP)
-    const float inv_g = 1.0f / (float)p.g;
-    float sl = 0.f;
-    int cnt = 0;
-    for (int c = tid; c < m; c += blockDim.x) {
-        const float w = wsum[c] * inv_g;
-        if (w > 0.f) {
-            sl += __logf(w);
-            ++cnt;
-        }
-    }
-    sl = wave_sum(sl);
-    cnt = wave_sum_int(cnt);
-    if (lane == 0) {
-        stat_s[wave] = sl;
-        stat_n[wave] = cnt;
-    }
-    __syncthreads();
-    float tot = 0.f;
-    int n_r = 0;
-    for (int i = 0; i < nwaves; ++i) {
-        tot += stat_s[i];
-        n_r += stat_n[i];
-    }
-    const float mu = n_r > 0 ? tot / (float)n_r : 0.f;
-    uint32_t* mrow = mask + ((int64_t)b * p.h_kv + r) * p.nw;
-    float* brow = bias + ((int64_t)b * p.h_kv + r) * p.nc;
-    for (int base = wave * 64; base < p.nw * 32; base += nwaves * 64) {
-        const int c = base + lane;
-        const float w = c < m ? wsum[c] * inv_g : 0.f;
-        const bool sel = c < m && w > 0.f;
-        if (sel) brow[c] = (__logf(w) - mu) * p.inv_sigma;
-        const uint64_t bal = __ballot(sel || (c >= m && c <= cp));  // routed, or in the window
-        if (lane == 0) {
-            mrow[base / 32] = (uint32_t)bal;
-            if (base / 32 + 1 < p.nw) mrow[base / 32 + 1] = (uint32_t)(bal >> 32);
-        }
-    }
-    for (int c = m + tid; c <= cp; c += blockDim.x) brow[c] = 0.f;
+    const DecodeRouteLds lds{red, stat_s, stat_n, cand_n, tau_h, cand, wsum};
+    const float* xg = x + ((int64_t)b * p.h_q + (int64_t)r * p.g) * p.nc;
+    decode_route_group<NS, KIND, WPH>([&](int hh) { return xg + (int64_t)hh * p.nc; },
+                                      route_cands(p, pos), pos / p.block, p, lds,
+                                      mask + ((int64_t)b * p.h_kv + r) * p.nw,
+                                      bias + ((int64_t)b * p.h_kv + r) * p.nc,
+                                      tau_out ? tau_out + (int64_t)b * p.h_q + r * p.g : nullptr,
+                                      nullptr, nullptr);
 }
 
 // waves per head row of route_decode_kernel (16 waves at most), and its slots per lane
@@ -513,6 +334,23 @@ static void launch_route(bool group, const float* x, uint32_t* mask, float* bias
     }
 }
 
+// one query per sequence: a coalesced stream over the summaries into x [B, H_q, Nc]
+hipError_t launch_score_one(const void* q, int dt, const float* kbar, float* x,
+                            const RouteParams& p, hipStream_t st) {
+    const float coef = (p.alpha - 1.0f) * p.gamma / sqrtf((float)p.head_dim);
+    dim3 grid(div_up(p.tc, 64), p.batch * p.h_kv);
+#define DASH_SCORE1(T, DD)                                                                 \
+    hipLaunchKernelGGL((score_one_kernel<T, DD>), grid, dim3(256), 0, st,                  \
+                       static_cast<const T*>(q), kbar, x, p, coef)
+    if (dt == kBF16) {
+        if (p.head_dim == 64) DASH_SCORE1(bf16_t, 64); else DASH_SCORE1(bf16_t, 128);
+    } else {
+        if (p.head_dim == 64) DASH_SCORE1(float, 64); else DASH_SCORE1(float, 128);
+    }
+#undef DASH_SCORE1
+    return hipGetLastError();
+}
+
 hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const RouteParams& p,
                                uint32_t* mask, float* bias, float* tau, void* ws,
                                hipStream_t st) {
@@ -523,17 +361,7 @@ hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const R
     const bool one = p.n_q == 1;
     if (p.tc > 0) {
         if (one) {
-            // one query per sequence: a coalesced stream over the summaries
-            dim3 grid(div_up(p.tc, 64), p.batch * p.h_kv);
-#define DASH_SCORE1(T, DD)                                                                 \
-            hipLaunchKernelGGL((score_one_kernel<T, DD>), grid, dim3(256), 0, st,          \
-                               static_cast<const T*>(q), kbar, x, p, coef)
-            if (dt == kBF16) {
-                if (p.head_dim == 64) DASH_SCORE1(bf16_t, 64); else DASH_SCORE1(bf16_t, 128);
-            } else {
-                if (p.head_dim == 64) DASH_SCORE1(float, 64); else DASH_SCORE1(float, 128);
-            }
-#undef DASH_SCORE1
+            launch_score_one(q, dt, kbar, x, p, st);
         } else {
             dim3 grid(div_up(p.tc, kScoreTile), div_up(p.n_q * p.g, kScoreTile), p.batch * p.h_kv);
 #define DASH_SCORE(T, DD)                                                                    \

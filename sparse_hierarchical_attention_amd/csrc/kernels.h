@@ -39,6 +39,9 @@ hipError_t launch_route_fused(const void* q, const float* kbar, uint32_t* mask, 
 hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const RouteParams& p,
                                uint32_t* mask, float* bias, float* tau, void* ws,
                                hipStream_t st);
+hipError_t launch_score_one(const void* q, int dt, const float* kbar, float* x,
+                            const RouteParams& p, hipStream_t st);
+
 
 // ---- Stage 2 (sparse_attn.hip)
 struct AttnParams {

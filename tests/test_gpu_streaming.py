@@ -102,7 +102,8 @@ def _check_varlen_rows(gpu_mask, gpu_bias, gpu_tau, gpu_o, refs, lens, block, hk
         gm = gpu_mask[b:b + 1, :, :nw_b]
         assert not np.any(gpu_mask[b, :, nw_b:nw_cap]), "bits past the sequence"
         gbias = gpu_bias[b:b + 1, :, :nc_b]
-        rep = parity.compare_stage1(gm, gbias, gpu_tau[b:b + 1], ref, n_kv=n_b, block=block,
+        rep = parity.compare_stage1(gm, gbias, None if gpu_tau is None else gpu_tau[b:b + 1],
+                                    ref, n_kv=n_b, block=block,
                                     h_kv=hkv, q_pos=np.array([n_b - 1]), alpha=alpha, sigma=sigma)
         parity.compare_output(gpu_o[b:b + 1], ref["o"], "bf16", exclude_rows=rep["row_flip"],
                               cond_row=rep["cond_row"], vmax=vmax)
