@@ -85,13 +85,19 @@ __device__ __forceinline__ void route_write_token(float (&wsum)[NSS], int tok, i
     const int cp = pos / p.block;
     const int m = route_cands(p, pos);  // chunks m .. cp: the window, always attended with d = 0
     const float inv_g = 1.0f / (float)GQ;
+    // log w on R (0 elsewhere), kept for the bias when the row is short enough to hold it in
+    // registers, else computed again there
+    constexpr bool kKeepLog = NSS <= 16;
+    float lw[kKeepLog ? NSS : 1];
+    auto logw = [&](int sl) { return wsum[sl] > 0.f ? __logf(wsum[sl]) : 0.f; };
     float lsum = 0.f, lcnt = 0.f;
 #pragma unroll
     for (int sl = 0; sl < NSS; ++sl) {
         wsum[sl] *= inv_g;
-        const bool in = wsum[sl] > 0.f;
-        lsum += in ? __logf(wsum[sl]) : 0.f;
-        lcnt += in ? 1.f : 0.f;
+        const float l = logw(sl);
+        if (kKeepLog) lw[kKeepLog ? sl : 0] = l;
+        lsum += l;
+        lcnt += wsum[sl] > 0.f ? 1.f : 0.f;
     }
     lsum = row16_sum(lsum);
     lcnt = row16_sum(lcnt);
@@ -101,21 +107,47 @@ __device__ __forceinline__ void route_write_token(float (&wsum)[NSS], int tok, i
     const int64_t qrow = (int64_t)b * p.n_q + tok;
     uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
     float* brow = bias + (qrow * p.h_kv + r) * p.nc;
+    if (GQ >= 4) {
+        // every group holds the token's row: group k stores the bias of slots k, k + 4, ...
 #pragma unroll
-    for (int sl = 0; sl < NSS; ++sl) {
-        const int c = 16 * sl + li;
-        if (writer && wsum[sl] > 0.f) brow[c] = (__logf(wsum[sl]) - mu) * p.inv_sigma;
+        for (int s0 = 0; s0 < NSS; s0 += 4) {
+            float w = wsum[s0];
+#pragma unroll
+            for (int j = 1; j < 4; ++j)
+                if (s0 + j < NSS && grp == j) w = wsum[s0 + j];
+            float l;
+            if (kKeepLog) {
+                l = lw[kKeepLog ? s0 : 0];
+#pragma unroll
+                for (int j = 1; j < 4; ++j)
+                    if (s0 + j < NSS && grp == j) l = lw[kKeepLog ? s0 + j : 0];
+            } else {
+                l = w > 0.f ? __logf(w) : 0.f;
+            }
+            if (tvalid && s0 + grp < NSS && w > 0.f) brow[16 * (s0 + grp) + li] = (l - mu) * p.inv_sigma;
+        }
+    } else {
+#pragma unroll
+        for (int sl = 0; sl < NSS; ++sl)
+            if (writer && wsum[sl] > 0.f)
+                brow[16 * sl + li] = ((kKeepLog ? lw[kKeepLog ? sl : 0] : logw(sl)) - mu) * p.inv_sigma;
     }
+    // mask words of the bucket, gathered so that lane li of a group holds words li and li + 16
+    uint32_t wlo = 0u, whi = 0u;
 #pragma unroll
     for (int wd = 0; wd < NSS / 2; ++wd) {
         const uint64_t b0 = __ballot(wsum[2 * wd] > 0.f);
         const uint64_t b1 = __ballot(wsum[2 * wd + 1] > 0.f);
-        if (writer && li == 0 && wd < p.nw) {
-            uint32_t word = (uint32_t)((b0 >> (16 * grp)) & 0xffffu) |
-                            ((uint32_t)((b1 >> (16 * grp)) & 0xffffu) << 16);
-            mrow[wd] = word | span_bits(wd, m, cp);
+        const uint32_t word = (uint32_t)((b0 >> (16 * grp)) & 0xffffu) |
+                              ((uint32_t)((b1 >> (16 * grp)) & 0xffffu) << 16);
+        if (li == (wd & 15)) {
+            if (wd < 16) wlo = word;
+            else whi = word;
         }
     }
+    if (writer && li < NSS / 2 && li < p.nw) mrow[li] = wlo | span_bits(li, m, cp);
+    if (NSS / 2 > 16 && writer && li + 16 < NSS / 2 && li + 16 < p.nw)
+        mrow[li + 16] = whi | span_bits(li + 16, m, cp);
     // words past the bucket: only the window's chunks can be set there
     for (int wd = NSS / 2 + li; wd < p.nw; wd += 16)
         if (writer) mrow[wd] = span_bits(wd, m, cp);
@@ -203,7 +235,7 @@ __device__ __forceinline__ void route_finish_token(const float* __restrict__ xt,
     route_write_token<NSS, GQ>(wsum, tok, b, r, mask, bias, p);
 }
 
-// 16 waves per CU (four per SIMD): NW waves per workgroup, 16 / NW workgroups per CU. NR MFMA
+// NW waves per workgroup, at least 16 / NW waves per SIMD (the register budget follows). NR MFMA
 // N-tiles of 32 query rows share every summary fragment a wave loads.
 template <int D, int GQ, int MT, int NW, int NR, int KIND>
 __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
@@ -355,9 +387,9 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
 #undef DASH_BUCKETS
 }
 
-// (MT, NW) with NW * MT * 32 >= tc chunks: up to 1024 chunks in 16 waves
+// (MT, NW) with NW * MT * 32 >= tc chunks: up to 1024 chunks (8 waves of 4 tiles)
 bool route_fused_supported(const RouteParams& p, int dt) {
-    return dt == kBF16 && p.tc <= 1024 && p.n_q > 1 && p.nw <= 2 * (p.tc <= 512 ? 8 : 16);
+    return dt == kBF16 && p.tc <= 1024 && p.n_q > 1 && p.nw <= 32;
 }
 
 template <int D, int GQ, int MT, int NW, int NR>
@@ -376,14 +408,15 @@ static void launch_fused_shape(const void* q, const bf16_t* kbar, uint32_t* mask
 #undef DASH_FUSED
 }
 
-// (MT, NW, NR) per row length: 16 waves per CU, and as many query rows per workgroup as the LDS
-// of their score rows allows (each summary fragment is loaded once per workgroup)
+// (MT, NW, NR) per row length: 32 query rows per workgroup (the LDS of their score rows), 4 to 8
+// waves. Past 512 chunks eight waves of four tiles each: 32 rows give phase 2 no more than 8
+// units, and eight waves leave each one 256 registers for the 64-slot rows.
 template <int D, int GQ>
 static void launch_fused_g(const void* q, const bf16_t* kbar, uint32_t* mask, float* bias,
                            float* tau, const RouteParams& p, float coef, hipStream_t st) {
     if (p.tc <= 256) launch_fused_shape<D, GQ, 2, 4, 1>(q, kbar, mask, bias, tau, p, coef, st);
     else if (p.tc <= 512) launch_fused_shape<D, GQ, 2, 8, 1>(q, kbar, mask, bias, tau, p, coef, st);
-    else launch_fused_shape<D, GQ, 2, 16, 1>(q, kbar, mask, bias, tau, p, coef, st);
+    else launch_fused_shape<D, GQ, 4, 8, 1>(q, kbar, mask, bias, tau, p, coef, st);
 }
 
 template <int D>
