@@ -295,9 +295,24 @@ static void launch_route_decode(const float* x, uint32_t* mask, float* bias, flo
     }
 }
 
+// Many queries off the fused path score through the workspace in slabs of query rows, so that it
+// never holds more than kRouteSlabBytes (a 256K-token prefill would otherwise need 64 GiB).
+constexpr size_t kRouteSlabBytes = (size_t)512 << 20;
+
+static size_t score_row_bytes(const RouteParams& p) { return (size_t)p.h_q * p.nc * sizeof(float); }
+
+// query rows per slab (of one sequence), or 0 when the whole call fits one workspace
+static int route_slab_rows(const RouteParams& p) {
+    if (p.n_q == 1 || (size_t)p.batch * p.n_q * score_row_bytes(p) <= kRouteSlabBytes) return 0;
+    const size_t rows = kRouteSlabBytes / score_row_bytes(p);
+    return (int)(rows < 1 ? 1 : (rows < (size_t)p.n_q ? rows : (size_t)p.n_q));
+}
+
 size_t route_workspace_bytes(const RouteParams& p, int dt) {
     if (route_fused_supported(p, dt)) return route_fused_workspace_bytes(p);  // scores stay on chip
-    return (size_t)p.batch * p.n_q * p.h_q * p.nc * sizeof(float);
+    const int slab = route_slab_rows(p);
+    if (slab > 0) return (size_t)slab * score_row_bytes(p);
+    return (size_t)p.batch * p.n_q * score_row_bytes(p);
 }
 
 template <int NPL>
@@ -355,6 +370,25 @@ hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const R
                                uint32_t* mask, float* bias, float* tau, void* ws,
                                hipStream_t st) {
     if (route_fused_supported(p, dt)) return launch_route_fused(q, kbar, mask, bias, tau, p, ws, st);
+    const int slab = route_slab_rows(p);
+    if (slab > 0) {
+        // one sequence and up to `slab` query rows at a time through the workspace
+        const size_t qe = dt == kBF16 ? sizeof(bf16_t) : sizeof(float);
+        for (int b = 0; b < p.batch; ++b)
+            for (int t0 = 0; t0 < p.n_q; t0 += slab) {
+                RouteParams ps = p;
+                ps.batch = 1;
+                ps.n_q = p.n_q - t0 < slab ? p.n_q - t0 : slab;
+                ps.q_pos0 = p.q_pos0 + t0;
+                const int64_t row = (int64_t)b * p.n_q + t0;
+                const hipError_t e = launch_block_entmax(
+                    static_cast<const char*>(q) + row * p.h_q * p.head_dim * qe, dt,
+                    kbar + (int64_t)b * p.tc * p.h_kv * p.head_dim, ps, mask + row * p.h_kv * p.nw,
+                    bias + row * p.h_kv * p.nc, tau ? tau + row * p.h_q : nullptr, ws, st);
+                if (e != hipSuccess) return e;
+            }
+        return hipSuccess;
+    }
     float* x = static_cast<float*>(ws);
     const float coef = (p.alpha - 1.0f) * p.gamma / sqrtf((float)p.head_dim);
     const size_t group_lds = (size_t)p.g * slots_for(p.nc) * 64 * sizeof(float);

@@ -78,6 +78,18 @@ def test_sweep_16k(dash, orc, alpha, block, gamma):
     rep, _ = prefill_parity(dash, orc, w, 1.0, sample_rows(w.n_q, w.block, 64, seed=62))
 
 
+def test_prefill_slabs_across_sequences(dash, orc):
+    """Two fp32 sequences of 16K whose score rows (2 GiB) exceed the workspace: Stage 1 runs in
+    four slabs of query rows, two per sequence; sampled rows of both against the oracle."""
+    w = wl.Workload("prefill fp32 2 x 16K, 32q/8kv heads, D 128, block 32", 2, 16384, 32, 8, 128, 32,
+                    1.5, 0.5, 1.0, dtype="f32", plant="span", plant_args=dict(span=16, per_span=4),
+                    seed=65)
+    assert dash.dash_block_entmax_workspace_bytes(torch.float32, 2, w.n_q, 0, w.n_kv, 32, 8, 128, 32) == 512 << 20
+    rows = sample_rows(w.n_q, w.block, 24, seed=66, batch=2)
+    rows = np.union1d(rows, [8191, 8192, 16383, 16384, 16385, 24575, 24576])  # slab edges
+    prefill_parity(dash, orc, w, w.sigma, rows)
+
+
 def test_prefill_256k(dash, orc):
     w = wl.PREFILL_256K
     prefill_parity(dash, orc, w, w.sigma, sample_rows(w.n_q, w.block, 48, seed=63))
