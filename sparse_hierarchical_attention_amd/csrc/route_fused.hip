@@ -13,6 +13,8 @@
 // workspace path (entmax.h, route_common.h): the g heads in turn, the GQA mean, mask and bias.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "entmax.h"
 #include "kernels.h"
@@ -22,6 +24,9 @@ namespace dash {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kLongRows = 16;   // query rows per workgroup of route_long_kernel
+constexpr int kLongMax = 2048;  // chunks route_long_kernel holds per row
 
 // The fp32 summaries as three bf16 terms, hi = bf16(kbar), mid = bf16(kbar - hi),
 // lo = bf16(kbar - hi - mid), each rounded to nearest even (together about 24 mantissa bits),
@@ -387,9 +392,11 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
 #undef DASH_BUCKETS
 }
 
-// (MT, NW) with NW * MT * 32 >= tc chunks: up to 1024 chunks (8 waves of 4 tiles)
+// (MT, NW) with NW * MT * 32 >= tc chunks: up to 1024 chunks (8 waves of 4 tiles); 1025 to 2048
+// chunks in route_long_kernel
 bool route_fused_supported(const RouteParams& p, int dt) {
-    return dt == kBF16 && p.tc <= 1024 && p.n_q > 1 && p.nw <= 32;
+    if (dt != kBF16 || p.n_q <= 1) return false;
+    return p.tc <= 1024 ? p.nw <= 32 : p.tc <= kLongMax;
 }
 
 template <int D, int GQ, int MT, int NW, int NR>
@@ -419,9 +426,227 @@ static void launch_fused_g(const void* q, const bf16_t* kbar, uint32_t* mask, fl
     else launch_fused_shape<D, GQ, 4, 8, 1>(q, kbar, mask, bias, tau, p, coef, st);
 }
 
+// Rows of 1025 to 2048 chunks. 32 score rows of that length do not fit the LDS, so a workgroup
+// of 16 waves owns 16 query rows (16 / g tokens times the g heads) of one (sequence b, KV group r)
+// and their score rows take 132 KiB:
+//   phase 1: X^T = Kbar Q^T on v_mfma_f32_32x32x16_bf16 as in route_fused_kernel, the 16 rows
+//            filling half of the N-tile (the other half multiplies zeros); wave w takes the
+//            chunk tiles w, w + 16, ..., two at a time, and writes their scores to LDS;
+//   phase 2: wave w solves row w's threshold with the row over the whole wave (entry c in lane
+//            c % 64, slot c / 64) and leaves the row's probabilities in its LDS row;
+//   phase 3: per token the waves split the chunks, 128 each: the GQA mean, mu (summed over the
+//            waves in order), the mask words and the bias.
+template <int D, int GQ, int KIND>
+__global__ __launch_bounds__(1024) void route_long_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ planes, uint32_t* __restrict__ mask,
+    float* __restrict__ bias, float* __restrict__ tau_out, RouteParams p, int n_tiles,
+    float coef) {
+    constexpr int NW = 16;
+    constexpr int T = kLongRows / GQ;     // tokens per workgroup
+    constexpr int XS = kLongMax + 17;     // LDS row stride of the scores
+    constexpr int QS = D + 8;             // LDS row stride of Q (elements)
+    __shared__ __align__(16) float xs[kLongRows * XS];
+    __shared__ __align__(16) bf16_t qs[kLongRows * QS];
+    __shared__ float st_s[NW];
+    __shared__ float st_n[NW];
+
+    const int bh = p.batch * p.h_kv;
+    const int x = blockIdx.x;
+    const int gr = bh % 8 == 0 ? (x % 8) + 8 * ((x / 8) % (bh / 8)) : x % bh;
+    const int tile = n_tiles - 1 - x / bh;
+    const int b = gr / p.h_kv, r = gr % p.h_kv;
+    const int tile0 = tile * T;
+    const int tile_end = min(tile0 + T, p.n_q);
+    const int m_max = route_cands(p, route_pos(p, b, tile_end - 1));
+    const int n_ct = div_up(m_max, 32);
+    const int ct_n = div_up(p.tc, 32);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 31, G = lane >> 5;
+
+    // ---- phase 1
+    for (int idx = tid; idx < kLongRows * (D / 8); idx += NW * 64) {
+        const int row = idx / (D / 8), d8 = idx % (D / 8);
+        const int t = tile0 + row / GQ;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (t < p.n_q)
+            u = *reinterpret_cast<const uint4*>(
+                q + (((int64_t)b * p.n_q + t) * p.h_q + r * GQ + row % GQ) * D + 8 * d8);
+        *reinterpret_cast<uint4*>(&qs[row * QS + 8 * d8]) = u;
+    }
+    __syncthreads();
+    for (int c0 = wave; c0 < n_ct; c0 += 2 * NW) {
+        const bool two = c0 + NW < n_ct;
+        f32x16_t X[2] = {f32x16_t{}, f32x16_t{}};
+        const uint4* src[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            src[i] = reinterpret_cast<const uint4*>(planes) +
+                     ((int64_t)(b * p.h_kv + r) * ct_n + min(c0 + NW * i, ct_n - 1)) * (D / 16) * 3 * 64 + lane;
+        uint4 cur[2][3], nxt[2][3];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) cur[i][pl] = src[i][pl * 64];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            if (ks + 1 < D / 16) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int pl = 0; pl < 3; ++pl) nxt[i][pl] = src[i][((ks + 1) * 3 + pl) * 64];
+            }
+            bf16x8_t qf = bf16x8_t{};
+            if (j < kLongRows) qf = *reinterpret_cast<const bf16x8_t*>(&qs[j * QS + 16 * ks + 8 * G]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (i == 1 && !two) break;
+#pragma unroll
+                for (int pl = 2; pl >= 0; --pl)  // lo, mid, hi: the small terms first
+                    X[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, cur[i][pl]), qf, X[i], 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) cur[i][pl] = nxt[i][pl];
+        }
+        // lane (j, G) holds row j, chunks 32 ct + 8 (rr / 4) + 4 G + rr % 4
+        if (j < kLongRows) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (i == 1 && !two) break;
+                const int ct = c0 + NW * i;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+                    xs[j * XS + 32 * ct + 8 * (rr >> 2) + 4 * G + (rr & 3)] = coef * X[i][rr];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: wave w owns row w
+    {
+        const int row = wave;
+        const int tok = tile0 + row / GQ;
+        const bool tvalid = tok < p.n_q;
+        const int m = tvalid ? route_cands(p, route_pos(p, b, tok)) : 0;
+        const int ns = div_up(m, 64);
+        float* xr = xs + row * XS;
+        const float e = 1.0f / (p.alpha - 1.0f);
+        auto solve = [&](auto nsc) __attribute__((always_inline)) {
+            constexpr int NS = decltype(nsc)::value;
+            float xv[NS];
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int c = 64 * i + lane;
+                xv[i] = c < m ? xr[c] : -INFINITY;
+            }
+            const float tau = solve_tau_exact<NS, KIND, 64>(xv, ns, m, p.alpha);
+            if (tau_out && tvalid && lane == 0)
+                tau_out[((int64_t)b * p.n_q + tok) * p.h_q + r * GQ + row % GQ] = tau;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int c = 64 * i + lane;
+                if (c < m) xr[c] = pow_e<KIND>(xv[i] - tau, e);
+            }
+        };
+        if (ns <= 8) solve(std::integral_constant<int, 8>{});
+        else if (ns <= 16) solve(std::integral_constant<int, 16>{});
+        else solve(std::integral_constant<int, 32>{});
+    }
+    __syncthreads();
+
+    // ---- phase 3: per token, chunks 128 w .. 128 w + 127 in wave w
+    const float inv_g = 1.0f / (float)GQ;
+    for (int t = 0; t < T; ++t) {
+        const int tok = tile0 + t;
+        const bool tvalid = tok < p.n_q;
+        const int pos = route_pos(p, b, min(tok, p.n_q - 1));
+        const int cp = pos / p.block;
+        const int m = route_cands(p, pos);
+        float w[2], lw[2];
+        float lsum = 0.f, lcnt = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = 128 * wave + 64 * i + lane;
+            float sum = 0.f;
+            if (c < m) {
+#pragma unroll
+                for (int h = 0; h < GQ; ++h) sum += xs[(t * GQ + h) * XS + c];
+            }
+            w[i] = sum * inv_g;
+            lw[i] = w[i] > 0.f ? __logf(w[i]) : 0.f;
+            lsum += lw[i];
+            lcnt += w[i] > 0.f ? 1.f : 0.f;
+        }
+        lsum = wave_sum(lsum);
+        lcnt = wave_sum(lcnt);
+        if (lane == 0) {
+            st_s[wave] = lsum;
+            st_n[wave] = lcnt;
+        }
+        __syncthreads();
+        float tot = 0.f, cnt = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            tot += st_s[i];
+            cnt += st_n[i];
+        }
+        const float mu = cnt > 0.f ? tot / cnt : 0.f;
+        const int64_t qrow = (int64_t)b * p.n_q + tok;
+        uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
+        float* brow = bias + (qrow * p.h_kv + r) * p.nc;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = 128 * wave + 64 * i + lane;
+            const bool sel = c < m && w[i] > 0.f;
+            if (tvalid && sel) brow[c] = (lw[i] - mu) * p.inv_sigma;
+            const uint64_t bal = __ballot(sel || (c >= m && c <= cp));
+            const int wd = (128 * wave + 64 * i) / 32;
+            if (tvalid && lane == 0 && wd < p.nw) {
+                mrow[wd] = (uint32_t)bal;
+                if (wd + 1 < p.nw) mrow[wd + 1] = (uint32_t)(bal >> 32);
+            }
+        }
+        // a word past the 2048 chunks holds the window's bits only
+        for (int wd = kLongMax / 32 + tid; wd < p.nw; wd += NW * 64)
+            if (tvalid) mrow[wd] = span_bits(wd, m, cp);
+        for (int c = m + tid; c <= cp; c += NW * 64)
+            if (tvalid) brow[c] = 0.f;
+        __syncthreads();  // st_s / st_n are read again for the next token
+    }
+}
+
+template <int D, int GQ>
+static void launch_long_g(const void* q, const bf16_t* kbar, uint32_t* mask, float* bias,
+                          float* tau, const RouteParams& p, float coef, hipStream_t st) {
+    constexpr int T = kLongRows / GQ;
+    const int n_tiles = div_up(p.n_q, T);
+    dim3 grid(p.batch * p.h_kv * n_tiles), block(1024);
+    const int kind = pow_kind(p.alpha);
+#define DASH_LONG(K)                                                                        \
+    hipLaunchKernelGGL((route_long_kernel<D, GQ, K>), grid, block, 0, st,                  \
+                       static_cast<const bf16_t*>(q), kbar, mask, bias, tau, p, n_tiles, coef)
+    if (kind == kPowOne) DASH_LONG(kPowOne);
+    else if (kind == kPowTwo) DASH_LONG(kPowTwo);
+    else DASH_LONG(kPowGeneral);
+#undef DASH_LONG
+}
+
 template <int D>
 static void launch_fused_d(const void* q, const bf16_t* kbar, uint32_t* mask, float* bias,
                            float* tau, const RouteParams& p, float coef, hipStream_t st) {
+    if (p.tc > 1024) {
+        switch (p.g) {
+            case 1: launch_long_g<D, 1>(q, kbar, mask, bias, tau, p, coef, st); break;
+            case 2: launch_long_g<D, 2>(q, kbar, mask, bias, tau, p, coef, st); break;
+            case 4: launch_long_g<D, 4>(q, kbar, mask, bias, tau, p, coef, st); break;
+            case 8: launch_long_g<D, 8>(q, kbar, mask, bias, tau, p, coef, st); break;
+            default: launch_long_g<D, 16>(q, kbar, mask, bias, tau, p, coef, st); break;
+        }
+        return;
+    }
     switch (p.g) {
         case 1: launch_fused_g<D, 1>(q, kbar, mask, bias, tau, p, coef, st); break;
         case 2: launch_fused_g<D, 2>(q, kbar, mask, bias, tau, p, coef, st); break;

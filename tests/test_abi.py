@@ -85,9 +85,13 @@ def test_block_entmax_rejects_bad_arguments(L):
     assert call(dt=0, wsb=need - 1) == 3 and "workspace" in err(L)
     need = L.dash_block_entmax_workspace_bytes(1, 2, 1, 4095, 4096, 8, 2, 128, 64)
     assert need == 2 * 8 * 64 * 4  # decode scores through the workspace
-    # a 256K prefill off the fused path scores in slabs of query rows: 512 MiB, not 64 GiB
+    # a 256K prefill off the fused path (fp32) scores in slabs of query rows: 512 MiB, not 64 GiB
     assert L.dash_block_entmax_workspace_bytes(0, 1, 262144, 0, 262144, 32, 8, 128, 128) == 512 << 20
-    assert L.dash_block_entmax_workspace_bytes(1, 1, 262144, 0, 262144, 32, 8, 128, 128) == 512 << 20
+    # in bf16 its 2048-chunk rows stay on chip; the workspace holds the split summaries
+    assert L.dash_block_entmax_workspace_bytes(1, 1, 262144, 0, 262144, 32, 8, 128, 128) == \
+        1 * 8 * 64 * 32 * 3 * 128 * 2
+    # past 2048 chunks bf16 leaves the fused path too
+    assert L.dash_block_entmax_workspace_bytes(1, 1, 262144, 0, 262144, 32, 8, 128, 64) == 512 << 20
 
 
 def test_attention_rejects_bad_arguments(L):

@@ -78,6 +78,17 @@ def test_sweep_16k(dash, orc, alpha, block, gamma):
     rep, _ = prefill_parity(dash, orc, w, 1.0, sample_rows(w.n_q, w.block, 64, seed=62))
 
 
+@pytest.mark.parametrize("n,hq,hkv,block", [(40000, 32, 8, 32), (36000, 32, 2, 32), (34000, 8, 8, 32),
+                                           (34000, 16, 2, 32), (2048 * 32 + 17, 8, 2, 32)])
+def test_prefill_rows_past_1024_chunks(dash, orc, n, hq, hkv, block):
+    """bf16 prefill whose rows reach 1025 to 2048 chunks (the long-row route), groups of 1 to 16
+    and a ragged tail whose 2049th chunk slot spills into a 65th mask word."""
+    w = wl.Workload(f"prefill {n} tokens, {hq}q/{hkv}kv heads, D 128, block {block}", 1, n, hq, hkv,
+                    128, block, 1.5, 0.5, 1.0, plant="span", plant_args=dict(span=16, per_span=4),
+                    seed=67)
+    prefill_parity(dash, orc, w, w.sigma, sample_rows(w.n_q, w.block, 40, seed=68))
+
+
 def test_prefill_slabs_across_sequences(dash, orc):
     """Two fp32 sequences of 16K whose score rows (2 GiB) exceed the workspace: Stage 1 runs in
     four slabs of query rows, two per sequence; sampled rows of both against the oracle."""
