@@ -22,7 +22,7 @@ _SRC = os.path.join(_HERE, "dash_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -58,6 +58,8 @@ def lib():
                                       vp, vp]
         L.orc_sparse_attn_prior.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, d, d, vp,
                                             i64, vp]
+        L.orc_backward.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, d, d, d, i, d, vp, vp, vp,
+                                   vp]
         L.orc_num_threads.restype = i
         _lib = L
     return _lib
@@ -79,10 +81,14 @@ def _host(a):
             return t.view(torch.int16).numpy().view(np.uint16), BF16
         if t.dtype == torch.float32:
             return t.numpy(), F32
+        if t.dtype == torch.float64:
+            return t.numpy(), F64
         raise TypeError(f"unsupported dtype {t.dtype}")
     a = np.ascontiguousarray(a)
     if a.dtype == np.float32:
         return a, F32
+    if a.dtype == np.float64:
+        return a, F64
     if a.dtype == np.uint16:
         return a, BF16
     raise TypeError(f"unsupported dtype {a.dtype}")
@@ -226,3 +232,30 @@ def forward(q, k, v, *, block: int, alpha: float, gamma: float, sigma: float,
     o, lse = sparse_attn(q, k, v, st1["mask"], st1["bias"], block=block, scale=scale,
                          q_pos0=q_pos0, rows=rows)
     return dict(kbar=kbar, o=o, lse=lse, **st1)
+
+
+def backward(q, k, v, dout, *, block: int, alpha: float, gamma: float, sigma: float,
+             window: int = 1, scale: float | None = None) -> dict:
+    """Gradients of the prefill forward (pool, route, attend; every query row) for dL/do = dout
+    [B, n, Hq, D]: dict(dq, dk, dv, dbias) in float64 (see orc_backward)."""
+    qa, dt = _host(q)
+    ka, dtk = _host(k)
+    va, dtv = _host(v)
+    if not (dt == dtk == dtv):
+        raise TypeError("q, k, v must share a dtype")
+    b, n, hq, d = qa.shape
+    hkv = ka.shape[2]
+    do = np.ascontiguousarray(np.asarray(dout, dtype=np.float64))
+    if do.shape != qa.shape:
+        raise ValueError("dout must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nc = math.ceil(n / block)
+    dq = np.zeros((b, n, hq, d))
+    dk = np.zeros((b, n, hkv, d))
+    dv = np.zeros((b, n, hkv, d))
+    dbias = np.zeros((b, n, hkv, nc))
+    _check(lib().orc_backward(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(do), b, n, hq, hkv, d, block,
+                              alpha, gamma, sigma, int(window), scale, _ptr(dq), _ptr(dk), _ptr(dv),
+                              _ptr(dbias)), "backward")
+    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias)

@@ -16,6 +16,7 @@
 #endif
 
 double orc_load(const void* base, int dtype, int64_t i) {
+    if (dtype == ORC_F64) return ((const double*)base)[i];
     if (dtype == ORC_F32) return (double)((const float*)base)[i];
     /* bf16 is the upper half of an IEEE binary32 pattern: widen, then convert exactly. */
     uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
@@ -434,4 +435,154 @@ int orc_sparse_attn_prior(const void* q, const void* k, const void* v, int dtype
         free(z);
     }
     return 0;
+}
+
+/* ------------------------------------------------ gradients [DA §3.2-3.4, App. A; §3.5 training] */
+
+static double dot_d(const void* a, int dtype, int64_t ia, const void* b, int64_t ib, int d) {
+    double s = 0.0;
+    for (int e = 0; e < d; ++e) s += orc_load(a, dtype, ia + e) * orc_load(b, dtype, ib + e);
+    return s;
+}
+
+int orc_backward(const void* q, const void* k, const void* v, int dtype, const double* dout,
+                 int batch, int n, int h_q, int h_kv, int head_dim, int block, double alpha,
+                 double gamma, double sigma, int window, double scale, double* dq, double* dk,
+                 double* dv, double* dbias) {
+    if (check_attn_args(q, k, v, batch, n, 0, n, h_q, h_kv, head_dim, block) || !dout || !dq ||
+        !dk || !dv || window < 1)
+        return -1;
+    if (!(alpha > 1.0 && alpha <= 2.0) || !(gamma > 0.0) || !(sigma > 0.0)) return -1;
+    const int g = h_q / h_kv, tc = n / block;
+    const int nc = (int)div_ceil(n, block), nw = (int)div_ceil(nc, 32);
+    const int D = head_dim;
+    const int64_t R = (int64_t)batch * n;
+    double* kbar = calloc((size_t)batch * (tc > 0 ? tc : 1) * h_kv * D, sizeof(double));
+    uint32_t* mask = calloc((size_t)R * h_kv * nw, sizeof(uint32_t));
+    double* bias = calloc((size_t)R * h_kv * nc, sizeof(double));
+    double* tau = calloc((size_t)R * h_q, sizeof(double));
+    double* x = calloc((size_t)R * h_q * nc, sizeof(double));
+    double* w = calloc((size_t)R * h_kv * nc, sizeof(double));
+    double* o = calloc((size_t)R * h_q * D, sizeof(double));
+    double* lse = calloc((size_t)R * h_q, sizeof(double));
+    double* dd = calloc((size_t)R * h_kv * nc, sizeof(double));
+    double* dw = calloc((size_t)R * h_kv * nc, sizeof(double));
+    double* dkbar = calloc((size_t)batch * (tc > 0 ? tc : 1) * h_kv * D, sizeof(double));
+    int rc = -1;
+    if (!kbar || !mask || !bias || !tau || !x || !w || !o || !lse || !dd || !dw || !dkbar) goto done;
+    /* the forward pass, for the quantities the gradients need */
+    if (tc > 0 && orc_pool_keys(k, dtype, batch, n, h_kv, D, block, kbar)) goto done;
+    if (orc_block_entmax(q, dtype, kbar, batch, n, 0, n, h_q, h_kv, D, block, alpha, gamma, sigma,
+                         window, NULL, 0, mask, bias, tau, x, w))
+        goto done;
+    if (orc_sparse_attn(q, k, v, dtype, mask, bias, batch, n, 0, n, h_q, h_kv, D, block, scale,
+                        NULL, 0, o, lse))
+        goto done;
+    memset(dq, 0, sizeof(double) * R * h_q * D);
+    memset(dk, 0, sizeof(double) * R * h_kv * D);
+    memset(dv, 0, sizeof(double) * R * h_kv * D);
+
+    /* Stage 2 [DA Prop. 1]: with p_j = exp(scale <q, k_j> + d_c(j) - lse) over the row's tokens,
+     * dp_j = <dout, v_j>, ds_j = p_j (dp_j - <dout, o>); dq = scale sum ds_j k_j,
+     * dk_j += scale ds_j q, dv_j += p_j dout, and dL/dd_c = sum of ds_j over chunk c's tokens for the
+     * routed chunks (the window's chunks carry the constant d = 0). */
+    for (int b = 0; b < batch; ++b)
+        for (int t = 0; t < n; ++t)
+            for (int h = 0; h < h_q; ++h) {
+                const int r = h / g, ci = t / block;
+                const int64_t row = (int64_t)b * n + t;
+                const int64_t qi = (row * h_q + h) * D;
+                const uint32_t* mw = mask + (row * h_kv + r) * nw;
+                const double* bo = bias + (row * h_kv + r) * nc;
+                double dsum = 0.0;
+                for (int e = 0; e < D; ++e) dsum += dout[qi + e] * o[qi + e];
+                for (int j = 0; j <= t; ++j) {
+                    const int c = j / block;
+                    const int attended = c == ci || ((mw[c / 32] >> (c % 32)) & 1u);
+                    if (!attended) continue;
+                    const int64_t kj = (((int64_t)b * n + j) * h_kv + r) * D;
+                    const double dval = c == ci ? 0.0 : bo[c];
+                    const double pj = exp(scale * dot_d(q, dtype, qi, k, kj, D) + dval - lse[row * h_q + h]);
+                    double dp = 0.0;
+                    for (int e = 0; e < D; ++e) dp += dout[qi + e] * orc_load(v, dtype, kj + e);
+                    const double ds = pj * (dp - dsum);
+                    for (int e = 0; e < D; ++e) {
+                        dq[qi + e] += scale * ds * orc_load(k, dtype, kj + e);
+                        dk[kj + e] += scale * ds * orc_load(q, dtype, qi + e);
+                        dv[kj + e] += pj * dout[qi + e];
+                    }
+                    if (c != ci && w[(row * h_kv + r) * nc + c] > 0.0) dd[(row * h_kv + r) * nc + c] += ds;
+                }
+            }
+
+    /* d -> w [DA Prop. 1]: d_c = (log w_c - mu) / sigma on R with mu the mean of log w over R, so
+     * dL/dlog w_c = (dd_c - mean_R dd) / sigma and dL/dw_c = that / w_c (c in R; 0 elsewhere). */
+    if (!isinf(sigma))
+        for (int64_t row = 0; row < R; ++row)
+            for (int r = 0; r < h_kv; ++r) {
+                const double* wr = w + (row * h_kv + r) * nc;
+                const double* ddr = dd + (row * h_kv + r) * nc;
+                double s = 0.0;
+                int nr = 0;
+                for (int c = 0; c < nc; ++c)
+                    if (wr[c] > 0.0) {
+                        s += ddr[c];
+                        ++nr;
+                    }
+                if (nr == 0) continue;
+                for (int c = 0; c < nc; ++c)
+                    if (wr[c] > 0.0) dw[(row * h_kv + r) * nc + c] = (ddr[c] - s / nr) / sigma / wr[c];
+            }
+
+    /* w -> p_h -> x_h [DA §3.2, Eq. 2; App. A]: w is the mean of the group's heads, so each head
+     * receives dp = dw / g; on the support of p = [x - tau]_+^(1/(alpha-1)), with u = p^(2-alpha),
+     * the entmax Jacobian gives dx = u (dp - sum(u dp) / sum(u)) / (alpha - 1), 0 off the support.
+     * x = coef <q, kbar> with coef = (alpha - 1) gamma / sqrt(D) [Eq. 4]. */
+    {
+        const double coef = (alpha - 1.0) * gamma / sqrt((double)D);
+        const double e = 1.0 / (alpha - 1.0);
+        for (int b = 0; b < batch; ++b)
+            for (int t = 0; t < n; ++t)
+                for (int h = 0; h < h_q; ++h) {
+                    const int r = h / g;
+                    const int64_t row = (int64_t)b * n + t;
+                    const double* xr = x + (row * h_q + h) * nc;
+                    const double th = tau[row * h_q + h];
+                    if (isinf(th)) continue; /* no candidate chunk */
+                    double su = 0.0, sud = 0.0;
+                    for (int c = 0; c < nc && !isnan(xr[c]); ++c)
+                        if (xr[c] > th) {
+                            const double u = pow(pow(xr[c] - th, e), 2.0 - alpha);
+                            su += u;
+                            sud += u * dw[(row * h_kv + r) * nc + c] / g;
+                        }
+                    if (su <= 0.0) continue;
+                    const int64_t qi = (row * h_q + h) * D;
+                    for (int c = 0; c < nc && !isnan(xr[c]); ++c) {
+                        if (!(xr[c] > th)) continue;
+                        const double u = pow(pow(xr[c] - th, e), 2.0 - alpha);
+                        const double dx = u * (dw[(row * h_kv + r) * nc + c] / g - sud / su) / (alpha - 1.0);
+                        const int64_t kb = (((int64_t)b * tc + c) * h_kv + r) * D;
+                        for (int f = 0; f < D; ++f) {
+                            dq[qi + f] += coef * dx * kbar[kb + f];
+                            dkbar[kb + f] += coef * dx * orc_load(q, dtype, qi + f);
+                        }
+                    }
+                }
+    }
+
+    /* kbar -> k [DA Eq. 3 with the summary query at zero]: the mean of the chunk's keys */
+    for (int b = 0; b < batch; ++b)
+        for (int c = 0; c < tc; ++c)
+            for (int r = 0; r < h_kv; ++r)
+                for (int t = c * block; t < (c + 1) * block; ++t)
+                    for (int f = 0; f < D; ++f)
+                        dk[(((int64_t)b * n + t) * h_kv + r) * D + f] +=
+                            dkbar[(((int64_t)b * tc + c) * h_kv + r) * D + f] / block;
+    if (dbias) memcpy(dbias, dd, sizeof(double) * R * h_kv * nc);
+    rc = 0;
+done:
+    free(kbar); free(mask); free(bias); free(tau); free(x); free(w); free(o); free(lse);
+    free(dd); free(dw); free(dkbar);
+    return rc;
 }

@@ -43,9 +43,9 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
 
-/* Value i of an fp32 or bf16 array, exactly, in double. */
+/* Value i of an fp32, bf16 or fp64 array, exactly, in double. */
 double orc_load(const void* base, int dtype, int64_t i);
 
 /* Stage 0 with the learned summary query at zero: Eq. 3 then weighs every token of a chunk
@@ -93,6 +93,18 @@ int orc_sparse_attn_prior(const void* q, const void* k, const void* v, int dtype
                           int batch, int n_q, int q_pos0, int n_kv, int h_q, int h_kv,
                           int head_dim, int block, double scale, double sigma, const int64_t* rows,
                           int64_t n_rows, double* o);
+
+/* Gradients of the whole forward pass (Stage 0 mean pooling, Stage 1 routing, Stage 2 bias-form
+ * attention) for prefill (every query row, q_pos0 = 0), given dout = dL/do [B, n, H_q, D]:
+ * dq [B, n, H_q, D], dk, dv [B, n, H_kv, D] and, when dbias is not NULL, dL/dd for every routed
+ * chunk [B, n, H_kv, Nc] (0 elsewhere). The selection (the support of each entmax and the routed
+ * set R) is piecewise constant, so no gradient flows through which chunks are selected; within a
+ * fixed support the chain is d -> log w (mu couples the routed chunks) -> w (the GQA mean) -> each
+ * head's entmax (its Jacobian) -> the chunk scores -> q and the summaries -> k (mean pooling). */
+int orc_backward(const void* q, const void* k, const void* v, int dtype, const double* dout,
+                 int batch, int n, int h_q, int h_kv, int head_dim, int block, double alpha,
+                 double gamma, double sigma, int window, double scale, double* dq, double* dk,
+                 double* dv, double* dbias);
 
 /* Number of OpenMP threads the oracle's row loops use. */
 int orc_num_threads(void);

@@ -1,0 +1,100 @@
+"""Pins of the oracle's gradients of the forward pass ("DashAttention", arXiv 2605.18753v1:
+§3.2-3.4 and App. A give the forward; its gradients follow by the chain rule through a fixed
+selection). Each pin is independent of the backward code: central differences of the oracle's own
+forward in float64, and torch autograd of plain causal attention where the routing cannot move."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+torch.set_default_dtype(torch.float64)
+
+
+def case(seed, n=96, hq=4, hkv=2, d=8, block=8):
+    """Random inputs whose rows route several chunks with unequal weights, so that the bias and
+    the gradient through the routing are far from zero."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, n, hq, d))
+    k = rng.standard_normal((1, n, hkv, d))
+    v = rng.standard_normal((1, n, hkv, d))
+    dout = rng.standard_normal((1, n, hq, d))
+    return q, k, v, dout
+
+
+def loss(orc, q, k, v, dout, **kw):
+    res = orc.forward(q, k, v, **kw)
+    return float((res["o"] * dout.reshape(res["o"].shape)).sum()), res["mask"]
+
+
+@pytest.mark.parametrize("alpha,gamma,window", [(1.5, 8.0, 1), (2.0, 4.0, 1), (1.25, 8.0, 1),
+                                                (1.5, 8.0, 2)])
+def test_gradients_match_central_differences(orc, alpha, gamma, window):
+    kw = dict(block=8, alpha=alpha, gamma=gamma, sigma=2.0, window=window)
+    q, k, v, dout = case(11)
+    g = orc.backward(q, k, v, dout, **kw)
+    base = orc.forward(q, k, v, **kw)
+    # rows route several chunks with unequal weights: the bias, and the gradient through it, live
+    assert (base["w"] > 0).sum(axis=2).max() >= 3 and np.ptp(base["bias"]) > 1.0
+    rng = np.random.default_rng(7)
+    eps = 1e-6
+    checked = 0
+    for name, arr, grad in (("q", q, g["dq"]), ("k", k, g["dk"]), ("v", v, g["dv"])):
+        idx = rng.choice(arr.size, size=40, replace=False)
+        for i in idx:
+            plus, minus = arr.copy(), arr.copy()
+            plus.flat[i] += eps
+            minus.flat[i] -= eps
+            args = {"q": q, "k": k, "v": v}
+            lp, mp = loss(orc, **{**args, name: plus}, dout=dout, **kw)
+            lm, mm = loss(orc, **{**args, name: minus}, dout=dout, **kw)
+            if not (np.array_equal(mp, base["mask"]) and np.array_equal(mm, base["mask"])):
+                continue  # the step moved the selection: no derivative there
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad.flat[i]) <= 1e-5 * max(1.0, abs(fd)), (name, i, fd, grad.flat[i])
+            checked += 1
+    assert checked >= 100
+
+
+def test_routing_gradient_is_not_negligible(orc):
+    """The case above exercises the chain through the routing: with sigma = inf (constant bias)
+    the gradients differ by a large margin."""
+    q, k, v, dout = case(11)
+    kw = dict(block=8, alpha=1.5, gamma=8.0, window=1)
+    a = orc.backward(q, k, v, dout, sigma=2.0, **kw)
+    b = orc.backward(q, k, v, dout, sigma=math.inf, **kw)
+    assert np.abs(a["dq"] - b["dq"]).max() > 0.1 * np.abs(a["dq"]).max()
+    assert np.abs(a["dk"] - b["dk"]).max() > 0.1 * np.abs(a["dk"]).max()
+
+
+def causal_sdpa_grads(q, k, v, dout):
+    """Gradients of plain causal SDPA (Eq. 1) by torch autograd, K/V shared by each query group."""
+    g = q.shape[2] // k.shape[2]
+    qt = torch.tensor(q[0]).transpose(0, 1).requires_grad_()
+    kt = torch.tensor(k[0]).transpose(0, 1).requires_grad_()
+    vt = torch.tensor(v[0]).transpose(0, 1).requires_grad_()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt[None], kt.repeat_interleave(g, 0)[None], vt.repeat_interleave(g, 0)[None], is_causal=True)[0]
+    o.backward(torch.tensor(dout[0]).transpose(0, 1))
+    return (qt.grad.transpose(0, 1).numpy()[None], kt.grad.transpose(0, 1).numpy()[None],
+            vt.grad.transpose(0, 1).numpy()[None])
+
+
+def test_dense_routing_without_bias_is_causal_sdpa(orc):
+    """alpha -> 1 routes every chunk and sigma = inf removes the bias: the forward is causal SDPA,
+    and no gradient flows through the routing."""
+    q, k, v, dout = case(4, n=48)
+    g = orc.backward(q, k, v, dout, block=8, alpha=1.0 + 1e-5, gamma=1.0, sigma=math.inf)
+    dq, dk, dv = causal_sdpa_grads(q, k, v, dout)
+    for a, b in ((g["dq"], dq), (g["dk"], dk), (g["dv"], dv)):
+        np.testing.assert_allclose(a, b, atol=1e-10)
+
+
+def test_window_over_every_chunk_is_causal_sdpa(orc):
+    """A window reaching chunk 0 for every query routes nothing: causal SDPA and its gradients."""
+    q, k, v, dout = case(5, n=48)
+    g = orc.backward(q, k, v, dout, block=8, alpha=1.5, gamma=3.0, sigma=1.0, window=7)
+    dq, dk, dv = causal_sdpa_grads(q, k, v, dout)
+    for a, b in ((g["dq"], dq), (g["dk"], dk), (g["dv"], dv)):
+        np.testing.assert_allclose(a, b, atol=1e-10)
+    assert np.all(g["dbias"] == 0.0)
