@@ -60,6 +60,8 @@ def lib():
                                             i64, vp]
         L.orc_backward.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, d, d, d, i, d, vp, vp, vp,
                                    vp]
+        L.orc_sparse_attn_backward.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, d, vp,
+                                               vp, vp, vp]
         L.orc_num_threads.restype = i
         _lib = L
     return _lib
@@ -258,4 +260,29 @@ def backward(q, k, v, dout, *, block: int, alpha: float, gamma: float, sigma: fl
     _check(lib().orc_backward(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(do), b, n, hq, hkv, d, block,
                               alpha, gamma, sigma, int(window), scale, _ptr(dq), _ptr(dk), _ptr(dv),
                               _ptr(dbias)), "backward")
+    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias)
+
+
+def sparse_attn_backward(q, k, v, mask, bias, dout, *, block: int, scale: float | None = None) -> dict:
+    """Stage 2 gradients for prefill with the selection held fixed: mask [B, n, Hkv, W] uint32 and
+    bias [B, n, Hkv, Nc] as Stage 1 writes them; dout [B, n, Hq, D]. Returns dict(dq, dk, dv,
+    dbias) in float64 (dbias [B, n, Hkv, Nc], 0 off the routed chunks)."""
+    qa, dt = _host(q)
+    ka, _ = _host(k)
+    va, _ = _host(v)
+    b, n, hq, d = qa.shape
+    hkv = ka.shape[2]
+    nc = math.ceil(n / block)
+    m = np.ascontiguousarray(np.asarray(mask).view(np.uint32).reshape(b * n, hkv, -1))
+    bi = np.ascontiguousarray(np.asarray(bias, dtype=np.float64).reshape(b * n, hkv, nc))
+    do = np.ascontiguousarray(np.asarray(dout, dtype=np.float64))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = np.zeros((b, n, hq, d))
+    dk = np.zeros((b, n, hkv, d))
+    dv = np.zeros((b, n, hkv, d))
+    dbias = np.zeros((b, n, hkv, nc))
+    _check(lib().orc_sparse_attn_backward(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(m), _ptr(bi),
+                                          _ptr(do), b, n, hq, hkv, d, block, scale, _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(dbias)), "sparse_attn_backward")
     return dict(dq=dq, dk=dk, dv=dv, dbias=dbias)

@@ -445,6 +445,71 @@ static double dot_d(const void* a, int dtype, int64_t ia, const void* b, int64_t
     return s;
 }
 
+int orc_sparse_attn_backward(const void* q, const void* k, const void* v, int dtype,
+                             const uint32_t* mask, const double* bias, const double* dout,
+                             int batch, int n, int h_q, int h_kv, int head_dim, int block,
+                             double scale, double* dq, double* dk, double* dv, double* dbias) {
+    if (check_attn_args(q, k, v, batch, n, 0, n, h_q, h_kv, head_dim, block) || !mask || !bias ||
+        !dout || !dq || !dk || !dv)
+        return -1;
+    const int g = h_q / h_kv, D = head_dim;
+    const int nc = (int)div_ceil(n, block), nw = (int)div_ceil(nc, 32);
+    const int64_t R = (int64_t)batch * n;
+    double* o = calloc((size_t)R * h_q * D, sizeof(double));
+    double* lse = calloc((size_t)R * h_q, sizeof(double));
+    if (!o || !lse) {
+        free(o);
+        free(lse);
+        return -1;
+    }
+    if (orc_sparse_attn(q, k, v, dtype, mask, bias, batch, n, 0, n, h_q, h_kv, D, block, scale,
+                        NULL, 0, o, lse)) {
+        free(o);
+        free(lse);
+        return -1;
+    }
+    memset(dq, 0, sizeof(double) * R * h_q * D);
+    memset(dk, 0, sizeof(double) * R * h_kv * D);
+    memset(dv, 0, sizeof(double) * R * h_kv * D);
+    if (dbias) memset(dbias, 0, sizeof(double) * R * h_kv * nc);
+    /* Stage 2 [DA Prop. 1]: with p_j = exp(scale <q, k_j> + d_c(j) - lse) over the row's tokens,
+     * dp_j = <dout, v_j>, ds_j = p_j (dp_j - <dout, o>); dq = scale sum ds_j k_j,
+     * dk_j += scale ds_j q, dv_j += p_j dout, and dL/dd_c = sum of ds_j over chunk c's tokens for the
+     * routed chunks (the window's chunks carry the constant d = 0). */
+    for (int b = 0; b < batch; ++b)
+        for (int t = 0; t < n; ++t)
+            for (int h = 0; h < h_q; ++h) {
+                const int r = h / g, ci = t / block;
+                const int64_t row = (int64_t)b * n + t;
+                const int64_t qi = (row * h_q + h) * D;
+                const uint32_t* mw = mask + (row * h_kv + r) * nw;
+                const double* bo = bias + (row * h_kv + r) * nc;
+                double dsum = 0.0;
+                for (int e = 0; e < D; ++e) dsum += dout[qi + e] * o[qi + e];
+                for (int j = 0; j <= t; ++j) {
+                    const int c = j / block;
+                    const int attended = c == ci || ((mw[c / 32] >> (c % 32)) & 1u);
+                    if (!attended) continue;
+                    const int64_t kj = (((int64_t)b * n + j) * h_kv + r) * D;
+                    const double dval = c == ci ? 0.0 : bo[c];
+                    const double pj = exp(scale * dot_d(q, dtype, qi, k, kj, D) + dval - lse[row * h_q + h]);
+                    double dp = 0.0;
+                    for (int e = 0; e < D; ++e) dp += dout[qi + e] * orc_load(v, dtype, kj + e);
+                    const double ds = pj * (dp - dsum);
+                    for (int e = 0; e < D; ++e) {
+                        dq[qi + e] += scale * ds * orc_load(k, dtype, kj + e);
+                        dk[kj + e] += scale * ds * orc_load(q, dtype, qi + e);
+                        dv[kj + e] += pj * dout[qi + e];
+                    }
+                    if (dbias && c != ci) dbias[(row * h_kv + r) * nc + c] += ds;
+                }
+            }
+
+    free(o);
+    free(lse);
+    return 0;
+}
+
 int orc_backward(const void* q, const void* k, const void* v, int dtype, const double* dout,
                  int batch, int n, int h_q, int h_kv, int head_dim, int block, double alpha,
                  double gamma, double sigma, int window, double scale, double* dq, double* dk,
@@ -478,42 +543,12 @@ int orc_backward(const void* q, const void* k, const void* v, int dtype, const d
     if (orc_sparse_attn(q, k, v, dtype, mask, bias, batch, n, 0, n, h_q, h_kv, D, block, scale,
                         NULL, 0, o, lse))
         goto done;
-    memset(dq, 0, sizeof(double) * R * h_q * D);
-    memset(dk, 0, sizeof(double) * R * h_kv * D);
-    memset(dv, 0, sizeof(double) * R * h_kv * D);
-
-    /* Stage 2 [DA Prop. 1]: with p_j = exp(scale <q, k_j> + d_c(j) - lse) over the row's tokens,
-     * dp_j = <dout, v_j>, ds_j = p_j (dp_j - <dout, o>); dq = scale sum ds_j k_j,
-     * dk_j += scale ds_j q, dv_j += p_j dout, and dL/dd_c = sum of ds_j over chunk c's tokens for the
-     * routed chunks (the window's chunks carry the constant d = 0). */
-    for (int b = 0; b < batch; ++b)
-        for (int t = 0; t < n; ++t)
-            for (int h = 0; h < h_q; ++h) {
-                const int r = h / g, ci = t / block;
-                const int64_t row = (int64_t)b * n + t;
-                const int64_t qi = (row * h_q + h) * D;
-                const uint32_t* mw = mask + (row * h_kv + r) * nw;
-                const double* bo = bias + (row * h_kv + r) * nc;
-                double dsum = 0.0;
-                for (int e = 0; e < D; ++e) dsum += dout[qi + e] * o[qi + e];
-                for (int j = 0; j <= t; ++j) {
-                    const int c = j / block;
-                    const int attended = c == ci || ((mw[c / 32] >> (c % 32)) & 1u);
-                    if (!attended) continue;
-                    const int64_t kj = (((int64_t)b * n + j) * h_kv + r) * D;
-                    const double dval = c == ci ? 0.0 : bo[c];
-                    const double pj = exp(scale * dot_d(q, dtype, qi, k, kj, D) + dval - lse[row * h_q + h]);
-                    double dp = 0.0;
-                    for (int e = 0; e < D; ++e) dp += dout[qi + e] * orc_load(v, dtype, kj + e);
-                    const double ds = pj * (dp - dsum);
-                    for (int e = 0; e < D; ++e) {
-                        dq[qi + e] += scale * ds * orc_load(k, dtype, kj + e);
-                        dk[kj + e] += scale * ds * orc_load(q, dtype, qi + e);
-                        dv[kj + e] += pj * dout[qi + e];
-                    }
-                    if (c != ci && w[(row * h_kv + r) * nc + c] > 0.0) dd[(row * h_kv + r) * nc + c] += ds;
-                }
-            }
+    if (orc_sparse_attn_backward(q, k, v, dtype, mask, bias, dout, batch, n, h_q, h_kv, D, block,
+                                 scale, dq, dk, dv, dd))
+        goto done;
+    /* only the routed chunks' d depends on w (the window's chunks carry the constant d = 0) */
+    for (int64_t i = 0; i < R * h_kv * nc; ++i)
+        if (!(w[i] > 0.0)) dd[i] = 0.0;
 
     /* d -> w [DA Prop. 1]: d_c = (log w_c - mu) / sigma on R with mu the mean of log w over R, so
      * dL/dlog w_c = (dd_c - mean_R dd) / sigma and dL/dw_c = that / w_c (c in R; 0 elsewhere). */

@@ -94,6 +94,14 @@ int orc_sparse_attn_prior(const void* q, const void* k, const void* v, int dtype
                           int head_dim, int block, double scale, double sigma, const int64_t* rows,
                           int64_t n_rows, double* o);
 
+/* Gradients of Stage 2 alone (bias form, Prop. 1) for prefill, every query row, with the mask and
+ * the bias held fixed: dq [B, n, H_q, D], dk, dv [B, n, H_kv, D] and, when dbias is not NULL,
+ * dL/dd [B, n, H_kv, Nc] for every chunk below the query's own whose mask bit is set (0 elsewhere). */
+int orc_sparse_attn_backward(const void* q, const void* k, const void* v, int dtype,
+                             const uint32_t* mask, const double* bias, const double* dout,
+                             int batch, int n, int h_q, int h_kv, int head_dim, int block,
+                             double scale, double* dq, double* dk, double* dv, double* dbias);
+
 /* Gradients of the whole forward pass (Stage 0 mean pooling, Stage 1 routing, Stage 2 bias-form
  * attention) for prefill (every query row, q_pos0 = 0), given dout = dL/do [B, n, H_q, D]:
  * dq [B, n, H_q, D], dk, dv [B, n, H_kv, D] and, when dbias is not NULL, dL/dd for every routed

@@ -98,3 +98,42 @@ def test_window_over_every_chunk_is_causal_sdpa(orc):
     for a, b in ((g["dq"], dq), (g["dk"], dk), (g["dv"], dv)):
         np.testing.assert_allclose(a, b, atol=1e-10)
     assert np.all(g["dbias"] == 0.0)
+
+
+def test_stage2_gradients_match_central_differences(orc):
+    """Stage 2 alone with a fixed selection and bias: central differences of the bias-form
+    attention for q, k, v and the bias entries."""
+    q, k, v, dout = case(12)
+    kw = dict(block=8, alpha=1.5, gamma=8.0, sigma=0.5)
+    st = orc.forward(q, k, v, **kw)
+    mask, bias = st["mask"], st["bias"]
+    g = orc.sparse_attn_backward(q, k, v, mask, bias, dout, block=8)
+
+    def loss(q_, k_, v_, bias_):
+        o, _ = orc.sparse_attn(q_, k_, v_, mask, bias_, block=8)
+        return float((o * dout.reshape(o.shape)).sum())
+
+    rng = np.random.default_rng(8)
+    eps = 1e-6
+    for name, arr, grad in (("q", q, g["dq"]), ("k", k, g["dk"]), ("v", v, g["dv"])):
+        for i in rng.choice(arr.size, size=30, replace=False):
+            plus, minus = arr.copy(), arr.copy()
+            plus.flat[i] += eps
+            minus.flat[i] -= eps
+            args = dict(q_=q, k_=k, v_=v, bias_=bias)
+            fd = (loss(**{**args, name + "_": plus}) - loss(**{**args, name + "_": minus})) / (2 * eps)
+            assert abs(fd - grad.flat[i]) <= 1e-5 * max(1.0, abs(fd)), (name, i)
+    # the bias: only routed chunks below the query's own chunk move the output
+    nc = bias.shape[-1]
+    bits = ((mask[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(mask.shape[:2] + (-1,))[..., :nc]
+    rows, heads, chunks = np.nonzero(bits)
+    own = chunks == (rows // 8)
+    pick = rng.choice(np.flatnonzero(~own), size=30, replace=False)
+    for j in pick:
+        rr, hh, cc = rows[j], heads[j], chunks[j]
+        plus, minus = bias.copy(), bias.copy()
+        plus[rr, hh, cc] += eps
+        minus[rr, hh, cc] -= eps
+        fd = (loss(q, k, v, plus) - loss(q, k, v, minus)) / (2 * eps)
+        assert abs(fd - g["dbias"].reshape(bias.shape)[rr, hh, cc]) <= 1e-5 * max(1.0, abs(fd))
+    assert np.all(g["dbias"].reshape(bias.shape)[rows[own], heads[own], chunks[own]] == 0.0)
