@@ -177,6 +177,30 @@ dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void*
                                        int head_dim, int block, float scale, hipStream_t stream);
 
 /*
+ * Stage 2 backward for prefill [DA Prop. 1, differentiated], the selection held fixed: with the
+ * forward's lse, p_j = exp(scale <q, k_j> + d_c(j) - lse) over the keys the row attends to,
+ * dp_j = <dout, v_j> and ds_j = p_j (dp_j - <dout, o>), it writes
+ *   dq = scale sum_j ds_j k_j,  dk_j = scale sum ds_j q,  dv_j = sum p_j dout  (over every row
+ *   and query head of the group that attends key j), and
+ *   dbias[c] = sum of ds_j over chunk c's keys and the group's heads, for the chunks c below the
+ *   row's own whose mask bit is set (the gradient of the loss with respect to the routing bias
+ *   d_c); every other entry of dbias is 0 (the own chunk, and the window chunks Stage 1 marks
+ *   with d = 0, are included as the forward used them).
+ *   q, o, dout [B, n, H_q, D] (dt); k, v [B, n, H_kv, D] (dt); lse [B, n, H_q] fp32, mask and
+ *   bias as given to dash_sparse_attn_prefill, o and lse as it returned them.
+ *   dq [B, n, H_q, D], dk, dv [B, n, H_kv, D], dbias [B, n, H_kv, Nc]: fp32, fully written
+ *   (dbias may be NULL: not computed). workspace: device scratch of
+ *   dash_sparse_attn_backward_workspace_bytes(B, n, H_q) bytes (rowsum(dout * o) per row).
+ * Each output element is written by one thread, in a fixed order: the result is deterministic.
+ */
+size_t dash_sparse_attn_backward_workspace_bytes(int batch, int n, int h_q);
+dash_status_t dash_sparse_attn_prefill_backward(
+    const void* q, const void* k, const void* v, const void* o, const float* lse,
+    const void* dout, dash_dtype_t dt, const uint32_t* mask, const float* bias, float* dq,
+    float* dk, float* dv, float* dbias, int batch, int n, int h_q, int h_kv, int head_dim,
+    int block, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Stage 2, decode [DA §3.5, split-KV variant]: the Stage 2 output of one new query per sequence
  * at position n_ctx - 1 of its cache. The selected chunks are split over many workgroups; their
  * partial (max, sum, output) triples are merged in a fixed order, so the result is deterministic.

@@ -62,6 +62,8 @@ def lib():
                                    vp]
         L.orc_sparse_attn_backward.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, d, vp,
                                                vp, vp, vp]
+        L.orc_sparse_attn_backward_rows.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, d,
+                                                    vp, ctypes.c_int64, vp, vp]
         L.orc_num_threads.restype = i
         _lib = L
     return _lib
@@ -286,3 +288,31 @@ def sparse_attn_backward(q, k, v, mask, bias, dout, *, block: int, scale: float 
                                           _ptr(do), b, n, hq, hkv, d, block, scale, _ptr(dq),
                                           _ptr(dk), _ptr(dv), _ptr(dbias)), "sparse_attn_backward")
     return dict(dq=dq, dk=dk, dv=dv, dbias=dbias)
+
+
+def sparse_attn_backward_rows(q, k, v, mask, bias, dout, rows, *, block: int,
+                              scale: float | None = None) -> dict:
+    """dq and dL/dd of the listed rows (rho = b * n + t) only, the selection held fixed: mask
+    [R, Hkv, W], bias [R, Hkv, Nc] and dout [R, Hq, D] hold the listed rows in list order.
+    Returns dict(dq [R, Hq, D], dbias [R, Hkv, Nc]) in float64."""
+    qa, dt = _host(q)
+    ka, _ = _host(k)
+    va, _ = _host(v)
+    b, n, hq, d = qa.shape
+    hkv = ka.shape[2]
+    nc = math.ceil(n / block)
+    r, nr = _rows(rows, b * n)
+    if r is None or nr == 0:
+        raise ValueError("rows must list at least one row")
+    m = np.ascontiguousarray(np.asarray(mask).view(np.uint32).reshape(nr, hkv, -1))
+    bi = np.ascontiguousarray(np.asarray(bias, dtype=np.float64).reshape(nr, hkv, nc))
+    do = np.ascontiguousarray(np.asarray(dout, dtype=np.float64).reshape(nr, hq, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = np.zeros((nr, hq, d))
+    dbias = np.zeros((nr, hkv, nc))
+    _check(lib().orc_sparse_attn_backward_rows(_ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(m),
+                                               _ptr(bi), _ptr(do), b, n, hq, hkv, d, block, scale,
+                                               _ptr(r), nr, _ptr(dq), _ptr(dbias)),
+           "sparse_attn_backward_rows")
+    return dict(dq=dq, dbias=dbias)

@@ -41,7 +41,7 @@ int orc_pool_keys(const void* k, int dtype, int batch, int n_kv, int h_kv, int h
                   double* kbar) {
     if (!k || !kbar || batch <= 0 || n_kv <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0)
         return -1;
-    const int tc = n_kv / block; /* complete chunks only [DA App. G, Alg. 1, line 1] */
+    const int tc = n_kv / block; /* complete chunks only [DA App. G, Alg. 1] */
 #pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < batch; ++b)
         for (int c = 0; c < tc; ++c)
@@ -303,7 +303,7 @@ int orc_sparse_attn(const void* q, const void* k, const void* v, int dtype, cons
         const int pos = q_pos0 + t;
         const int ci = pos / block;
         /* attended tokens: every token of each routed chunk c < c_i, then the causal prefix
-         * c_i*B .. pos of the query's own chunk [DA Prop. 1; Alg. 3, lines 5-8] */
+         * c_i*B .. pos of the query's own chunk [DA Prop. 1; Alg. 3] */
         int* tok = malloc(sizeof(int) * (pos + 1));
         double* lg = malloc(sizeof(double) * (pos + 1));
         for (int h = 0; h < h_q; ++h) {
@@ -445,6 +445,46 @@ static double dot_d(const void* a, int dtype, int64_t ia, const void* b, int64_t
     return s;
 }
 
+/* Stage 2 gradients of one query row (sequence b, position t), every head, the selection held
+ * fixed [DA Prop. 1, differentiated]: with p_j = exp(scale <q, k_j> + d_c(j) - lse) over the
+ * row's tokens, dp_j = <dout, v_j> and ds_j = p_j (dp_j - <dout, o>), it adds
+ * dq = scale sum ds_j k_j, dk_j += scale ds_j q, dv_j += p_j dout, and dL/dd_c = sum of ds_j over
+ * chunk c's tokens for the routed chunks c < c_i (the own chunk carries the constant d = 0).
+ * mw / bo: the row's mask words and bias for each KV head (h_kv * nw, h_kv * nc); dout, o:
+ * [h_q, D]; lse [h_q]; dq [h_q, D]; dk, dv [B, n, h_kv, D] or NULL; dbias [h_kv, nc] or NULL. */
+static void row_backward(const void* q, const void* k, const void* v, int dtype,
+                         const uint32_t* mw, const double* bo, const double* dout,
+                         const double* o, const double* lse, int b, int t, int n, int h_q,
+                         int h_kv, int D, int block, double scale, double* dq, double* dk,
+                         double* dv, double* dbias) {
+    const int g = h_q / h_kv, ci = t / block;
+    const int nc = (int)div_ceil(n, block), nw = (int)div_ceil(nc, 32);
+    const int64_t row = (int64_t)b * n + t;
+    for (int h = 0; h < h_q; ++h) {
+        const int r = h / g;
+        const int64_t qi = (row * h_q + h) * D;
+        const double* dh = dout + (int64_t)h * D;
+        double dsum = 0.0;
+        for (int e = 0; e < D; ++e) dsum += dh[e] * o[(int64_t)h * D + e];
+        for (int j = 0; j <= t; ++j) {
+            const int c = j / block;
+            if (c != ci && !mask_bit(mw + (int64_t)r * nw, c)) continue;
+            const int64_t kj = (((int64_t)b * n + j) * h_kv + r) * D;
+            const double dval = c == ci ? 0.0 : bo[(int64_t)r * nc + c];
+            const double pj = exp(scale * dot_d(q, dtype, qi, k, kj, D) + dval - lse[h]);
+            double dp = 0.0;
+            for (int e = 0; e < D; ++e) dp += dh[e] * orc_load(v, dtype, kj + e);
+            const double ds = pj * (dp - dsum);
+            for (int e = 0; e < D; ++e) {
+                dq[(int64_t)h * D + e] += scale * ds * orc_load(k, dtype, kj + e);
+                if (dk) dk[kj + e] += scale * ds * orc_load(q, dtype, qi + e);
+                if (dv) dv[kj + e] += pj * dh[e];
+            }
+            if (dbias && c != ci) dbias[(int64_t)r * nc + c] += ds;
+        }
+    }
+}
+
 int orc_sparse_attn_backward(const void* q, const void* k, const void* v, int dtype,
                              const uint32_t* mask, const double* bias, const double* dout,
                              int batch, int n, int h_q, int h_kv, int head_dim, int block,
@@ -452,7 +492,7 @@ int orc_sparse_attn_backward(const void* q, const void* k, const void* v, int dt
     if (check_attn_args(q, k, v, batch, n, 0, n, h_q, h_kv, head_dim, block) || !mask || !bias ||
         !dout || !dq || !dk || !dv)
         return -1;
-    const int g = h_q / h_kv, D = head_dim;
+    const int D = head_dim;
     const int nc = (int)div_ceil(n, block), nw = (int)div_ceil(nc, 32);
     const int64_t R = (int64_t)batch * n;
     double* o = calloc((size_t)R * h_q * D, sizeof(double));
@@ -472,42 +512,50 @@ int orc_sparse_attn_backward(const void* q, const void* k, const void* v, int dt
     memset(dk, 0, sizeof(double) * R * h_kv * D);
     memset(dv, 0, sizeof(double) * R * h_kv * D);
     if (dbias) memset(dbias, 0, sizeof(double) * R * h_kv * nc);
-    /* Stage 2 [DA Prop. 1]: with p_j = exp(scale <q, k_j> + d_c(j) - lse) over the row's tokens,
-     * dp_j = <dout, v_j>, ds_j = p_j (dp_j - <dout, o>); dq = scale sum ds_j k_j,
-     * dk_j += scale ds_j q, dv_j += p_j dout, and dL/dd_c = sum of ds_j over chunk c's tokens for the
-     * routed chunks (the window's chunks carry the constant d = 0). */
-    for (int b = 0; b < batch; ++b)
-        for (int t = 0; t < n; ++t)
-            for (int h = 0; h < h_q; ++h) {
-                const int r = h / g, ci = t / block;
-                const int64_t row = (int64_t)b * n + t;
-                const int64_t qi = (row * h_q + h) * D;
-                const uint32_t* mw = mask + (row * h_kv + r) * nw;
-                const double* bo = bias + (row * h_kv + r) * nc;
-                double dsum = 0.0;
-                for (int e = 0; e < D; ++e) dsum += dout[qi + e] * o[qi + e];
-                for (int j = 0; j <= t; ++j) {
-                    const int c = j / block;
-                    const int attended = c == ci || ((mw[c / 32] >> (c % 32)) & 1u);
-                    if (!attended) continue;
-                    const int64_t kj = (((int64_t)b * n + j) * h_kv + r) * D;
-                    const double dval = c == ci ? 0.0 : bo[c];
-                    const double pj = exp(scale * dot_d(q, dtype, qi, k, kj, D) + dval - lse[row * h_q + h]);
-                    double dp = 0.0;
-                    for (int e = 0; e < D; ++e) dp += dout[qi + e] * orc_load(v, dtype, kj + e);
-                    const double ds = pj * (dp - dsum);
-                    for (int e = 0; e < D; ++e) {
-                        dq[qi + e] += scale * ds * orc_load(k, dtype, kj + e);
-                        dk[kj + e] += scale * ds * orc_load(q, dtype, qi + e);
-                        dv[kj + e] += pj * dout[qi + e];
-                    }
-                    if (dbias && c != ci) dbias[(row * h_kv + r) * nc + c] += ds;
-                }
-            }
-
+    for (int64_t row = 0; row < R; ++row)
+        row_backward(q, k, v, dtype, mask + row * h_kv * nw, bias + row * h_kv * nc,
+                     dout + row * h_q * D, o + row * h_q * D, lse + row * h_q, (int)(row / n),
+                     (int)(row % n), n, h_q, h_kv, D, block, scale, dq + row * h_q * D, dk, dv,
+                     dbias ? dbias + row * h_kv * nc : NULL);
     free(o);
     free(lse);
     return 0;
+}
+
+/* dq and dL/dd of the listed rows only (rows[i] = b * n + t, increasing or not): mask, bias,
+ * dout, dq and dbias hold one entry per listed row, in list order. */
+int orc_sparse_attn_backward_rows(const void* q, const void* k, const void* v, int dtype,
+                                  const uint32_t* mask, const double* bias, const double* dout,
+                                  int batch, int n, int h_q, int h_kv, int head_dim, int block,
+                                  double scale, const int64_t* rows, int64_t n_rows, double* dq,
+                                  double* dbias) {
+    if (check_attn_args(q, k, v, batch, n, 0, n, h_q, h_kv, head_dim, block) || !mask || !bias ||
+        !dout || !dq || !rows || n_rows <= 0)
+        return -1;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= (int64_t)batch * n) return -1;
+    const int D = head_dim;
+    const int nc = (int)div_ceil(n, block), nw = (int)div_ceil(nc, 32);
+    double* o = calloc((size_t)n_rows * h_q * D, sizeof(double));
+    double* lse = calloc((size_t)n_rows * h_q, sizeof(double));
+    int rc = -1;
+    if (!o || !lse) goto done;
+    if (orc_sparse_attn(q, k, v, dtype, mask, bias, batch, n, 0, n, h_q, h_kv, D, block, scale,
+                        rows, n_rows, o, lse))
+        goto done;
+    memset(dq, 0, sizeof(double) * n_rows * h_q * D);
+    if (dbias) memset(dbias, 0, sizeof(double) * n_rows * h_kv * nc);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i)
+        row_backward(q, k, v, dtype, mask + i * h_kv * nw, bias + i * h_kv * nc,
+                     dout + i * h_q * D, o + i * h_q * D, lse + i * h_q, (int)(rows[i] / n),
+                     (int)(rows[i] % n), n, h_q, h_kv, D, block, scale, dq + i * h_q * D, NULL,
+                     NULL, dbias ? dbias + i * h_kv * nc : NULL);
+    rc = 0;
+done:
+    free(o);
+    free(lse);
+    return rc;
 }
 
 int orc_backward(const void* q, const void* k, const void* v, int dtype, const double* dout,

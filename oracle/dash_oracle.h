@@ -102,6 +102,14 @@ int orc_sparse_attn_backward(const void* q, const void* k, const void* v, int dt
                              int batch, int n, int h_q, int h_kv, int head_dim, int block,
                              double scale, double* dq, double* dk, double* dv, double* dbias);
 
+/* dq and dL/dd of the listed query rows only (rows[i] = b * n + t); mask [R, H_kv, W], bias
+ * [R, H_kv, Nc], dout and dq [R, H_q, D], dbias [R, H_kv, Nc] hold one entry per listed row. */
+int orc_sparse_attn_backward_rows(const void* q, const void* k, const void* v, int dtype,
+                                  const uint32_t* mask, const double* bias, const double* dout,
+                                  int batch, int n, int h_q, int h_kv, int head_dim, int block,
+                                  double scale, const int64_t* rows, int64_t n_rows, double* dq,
+                                  double* dbias);
+
 /* Gradients of the whole forward pass (Stage 0 mean pooling, Stage 1 routing, Stage 2 bias-form
  * attention) for prefill (every query row, q_pos0 = 0), given dout = dL/do [B, n, H_q, D]:
  * dq [B, n, H_q, D], dk, dv [B, n, H_kv, D] and, when dbias is not NULL, dL/dd for every routed

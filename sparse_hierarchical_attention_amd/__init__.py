@@ -21,6 +21,7 @@ __all__ = [
     "dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append", "dash_block_entmax",
     "dash_block_entmax_ex", "dash_block_entmax_workspace_bytes", "dash_sparse_attn_prefill",
     "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
+    "dash_sparse_attn_backward_workspace_bytes", "dash_sparse_attn_prefill_backward",
     "dash_version", "forward", "decode_step",
 ]
 
@@ -71,9 +72,14 @@ def lib():
                                               vp, sz, vp]
         L.dash_sparse_attn_decode_varlen.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i,
                                                      i, i, f, vp, sz, vp]
+        L.dash_sparse_attn_backward_workspace_bytes.argtypes = [i, i, i]
+        L.dash_sparse_attn_backward_workspace_bytes.restype = sz
+        L.dash_sparse_attn_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp, vp, vp,
+                                                        vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         for fn in ("dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append",
                    "dash_block_entmax", "dash_block_entmax_ex", "dash_sparse_attn_prefill",
-                   "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen"):
+                   "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
+                   "dash_sparse_attn_prefill_backward"):
             getattr(L, fn).restype = i
         _lib = L
     return _lib
@@ -254,6 +260,39 @@ def dash_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(mask), _ptr(bias), _ptr(o), _ptr(lse),
         b, n, hq, hkv, d, block, float(scale), _stream(dev)))
     return o, lse
+
+
+def dash_sparse_attn_backward_workspace_bytes(batch, n, h_q) -> int:
+    return int(lib().dash_sparse_attn_backward_workspace_bytes(batch, n, h_q))
+
+
+def dash_sparse_attn_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                      o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                                      mask: torch.Tensor, bias: torch.Tensor, *, block: int,
+                                      scale: float | None = None, want_dbias: bool = True,
+                                      workspace: torch.Tensor | None = None):
+    """Stage 2 prefill gradients with the selection held fixed: o, lse from
+    dash_sparse_attn_prefill, dout like o (q's dtype). -> (dq, dk, dv, dbias or None), fp32."""
+    b, n, hq, d = q.shape
+    hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dout.dtype != q.dtype or o.dtype != q.dtype:
+        raise TypeError("o and dout must have q's dtype")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((b, n, hq, d), **f32)
+    dk = torch.empty((b, n, hkv, d), **f32)
+    dv = torch.empty((b, n, hkv, d), **f32)
+    dbias = torch.empty(bias.shape, **f32) if want_dbias else None
+    need = dash_sparse_attn_backward_workspace_bytes(b, n, hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dev = _dev(q, k, v, o, lse, dout, mask, bias, workspace)
+    _check(lib().dash_sparse_attn_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _dtype_code(q), _ptr(mask),
+        _ptr(bias), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), b, n, hq, hkv, d, block,
+        float(scale), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return dq, dk, dv, dbias
 
 
 def dash_decode_workspace_bytes(batch, n_ctx, h_q, h_kv, head_dim, block) -> int:

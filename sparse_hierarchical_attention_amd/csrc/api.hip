@@ -228,6 +228,31 @@ dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void*
     return hip_status(dash::launch_attn_prefill(q, k, v, dt, mask, bias, o, lse, p, stream), fn);
 }
 
+size_t dash_sparse_attn_backward_workspace_bytes(int batch, int n, int h_q) {
+    if (batch <= 0 || n <= 0 || h_q <= 0) return 0;
+    return (size_t)batch * n * h_q * sizeof(float);
+}
+
+dash_status_t dash_sparse_attn_prefill_backward(
+    const void* q, const void* k, const void* v, const void* o, const float* lse,
+    const void* dout, dash_dtype_t dt, const uint32_t* mask, const float* bias, float* dq,
+    float* dk, float* dv, float* dbias, int batch, int n, int h_q, int h_kv, int head_dim,
+    int block, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "dash_sparse_attn_prefill_backward";
+    dash_status_t s = check_shape(fn, dt, batch, n, h_q, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (!(scale > 0.0f) || isinf(scale)) return fail(DASH_ERR_INVALID, "%s: scale=%g must be positive and finite", fn, scale);
+    if (!q || !k || !v || !o || !lse || !dout || !mask || !bias || !dq || !dk || !dv)
+        return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    dash::AttnParams p = attn_params(batch, n, 0, n, h_q, h_kv, head_dim, block, scale);
+    const size_t need = dash::attn_backward_workspace_bytes(p);
+    if (!workspace || workspace_bytes < need)
+        return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(dash::launch_attn_backward(q, k, v, o, lse, dout, dt, mask, bias, dq, dk, dv,
+                                                 dbias, p, workspace, stream), fn);
+}
+
 size_t dash_decode_workspace_bytes(int batch, int n_ctx, int h_q, int h_kv, int head_dim,
                                    int block) {
     if (batch <= 0 || n_ctx <= 0 || h_q <= 0 || h_kv <= 0 || block <= 0 || h_q % h_kv) return 0;

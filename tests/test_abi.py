@@ -124,3 +124,26 @@ def test_streaming_and_window_entry_points_reject_bad_arguments(L):
                                             0.1, None, 0, None) == 3
     assert L.dash_pool_keys_append(p, 1, None, None, p, 2, 4096, 2, 128, 64, None) == 1
     assert L.dash_pool_keys_append(p, 1, None, p, p, 2, 4096, 2, 96, 64, None) == 2
+
+
+def test_backward_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation
+    need = L.dash_sparse_attn_backward_workspace_bytes(2, 300, 8)
+    assert need == 2 * 300 * 8 * 4
+    assert L.dash_sparse_attn_backward_workspace_bytes(0, 300, 8) == 0
+    args = [p] * 6 + [1] + [p] * 6
+    assert L.dash_sparse_attn_prefill_backward(*args, 2, 300, 8, 2, 128, 32, 0.1, p, need - 1,
+                                               None) == 3
+    assert L.dash_sparse_attn_prefill_backward(*args, 2, 300, 8, 2, 128, 32, 0.0, p, need,
+                                               None) == 1 and "scale" in err(L)
+    assert L.dash_sparse_attn_prefill_backward(*args, 2, 300, 8, 3, 128, 32, 0.1, p, need,
+                                               None) == 1
+    assert L.dash_sparse_attn_prefill_backward(*args, 2, 300, 8, 2, 96, 32, 0.1, p, need,
+                                               None) == 2
+    nulls = [p] * 5 + [None] + [1] + [p] * 6
+    assert L.dash_sparse_attn_prefill_backward(*nulls, 2, 300, 8, 2, 128, 32, 0.1, p, need,
+                                               None) == 1 and "null" in err(L)
+    # dbias may be NULL: validation passes up to the (absent) workspace
+    no_dbias = [p] * 6 + [1] + [p] * 5 + [None]
+    assert L.dash_sparse_attn_prefill_backward(*no_dbias, 2, 300, 8, 2, 128, 32, 0.1, None, 0,
+                                               None) == 3

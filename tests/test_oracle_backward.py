@@ -137,3 +137,22 @@ def test_stage2_gradients_match_central_differences(orc):
         fd = (loss(q, k, v, plus) - loss(q, k, v, minus)) / (2 * eps)
         assert abs(fd - g["dbias"].reshape(bias.shape)[rr, hh, cc]) <= 1e-5 * max(1.0, abs(fd))
     assert np.all(g["dbias"].reshape(bias.shape)[rows[own], heads[own], chunks[own]] == 0.0)
+
+
+def test_stage2_row_gradients_match_the_full_pass(orc):
+    """The row-subset form (dq and dL/dd of listed rows, used to check sampled rows of long
+    sequences) against the full pass on a batch of two with a ragged tail, rows listed out of
+    order."""
+    q, k, v, dout = case(13, n=45)
+    q, k, v, dout = (np.concatenate([a, a[:, ::-1].copy()], axis=0) for a in (q, k, v, dout))
+    kw = dict(block=8, alpha=1.5, gamma=8.0, sigma=0.5)
+    st = orc.forward(q, k, v, **kw)
+    mask, bias = st["mask"], st["bias"]
+    full = orc.sparse_attn_backward(q, k, v, mask, bias, dout, block=8)
+    rows = np.array([89, 3, 44, 45, 0, 60, 17])
+    part = orc.sparse_attn_backward_rows(q, k, v, mask[rows], bias[rows],
+                                         dout.reshape(-1, 4, 8)[rows], rows, block=8)
+    np.testing.assert_allclose(part["dq"], full["dq"].reshape(-1, 4, 8)[rows], rtol=1e-12,
+                               atol=1e-12)
+    np.testing.assert_allclose(part["dbias"], full["dbias"].reshape(90, 2, -1)[rows], rtol=1e-12,
+                               atol=1e-12)

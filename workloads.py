@@ -181,6 +181,11 @@ def table5_workload(n: int, decode: bool) -> Workload:
                     seed=6 + (1 if decode else 0))
 
 
+def output_gradient(shape, seed: int, dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
+    """A seeded upstream gradient dL/dO ~ N(0, 1) of the given shape, rounded to dtype."""
+    return _randn(tuple(shape), np.random.SeedSequence(seed), device).to(dtype)
+
+
 def random_selection(batch: int, n_q: int, q_pos0: int, n_kv: int, h_kv: int, block: int,
                      sparsity: float, seed: int, device="cpu", bias_std: float = 0.0,
                      slab: int = 4096) -> tuple[torch.Tensor, torch.Tensor]:
