@@ -179,26 +179,56 @@ dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void*
 /*
  * Stage 2 backward for prefill [DA Prop. 1, differentiated], the selection held fixed: with the
  * forward's lse, p_j = exp(scale <q, k_j> + d_c(j) - lse) over the keys the row attends to,
- * dp_j = <dout, v_j> and ds_j = p_j (dp_j - <dout, o>), it writes
+ * dp_j = <dout, v_j> and ds_j = p_j (dp_j - <dout, o>), where <dout, o> = sum_j p_j dp_j is
+ * summed in fp32 from the probabilities (the output o itself is not needed), it writes
  *   dq = scale sum_j ds_j k_j,  dk_j = scale sum ds_j q,  dv_j = sum p_j dout  (over every row
  *   and query head of the group that attends key j), and
  *   dbias[c] = sum of ds_j over chunk c's keys and the group's heads, for the chunks c below the
  *   row's own whose mask bit is set (the gradient of the loss with respect to the routing bias
  *   d_c); every other entry of dbias is 0 (the own chunk, and the window chunks Stage 1 marks
  *   with d = 0, are included as the forward used them).
- *   q, o, dout [B, n, H_q, D] (dt); k, v [B, n, H_kv, D] (dt); lse [B, n, H_q] fp32, mask and
- *   bias as given to dash_sparse_attn_prefill, o and lse as it returned them.
+ *   q, dout [B, n, H_q, D] (dt); k, v [B, n, H_kv, D] (dt); lse [B, n, H_q] fp32 as
+ *   dash_sparse_attn_prefill returned it for the same mask and bias.
  *   dq [B, n, H_q, D], dk, dv [B, n, H_kv, D], dbias [B, n, H_kv, Nc]: fp32, fully written
  *   (dbias may be NULL: not computed). workspace: device scratch of
- *   dash_sparse_attn_backward_workspace_bytes(B, n, H_q) bytes (rowsum(dout * o) per row).
+ *   dash_sparse_attn_backward_workspace_bytes(B, n, H_q) bytes (<dout, o> per row and head).
  * Each output element is written by one thread, in a fixed order: the result is deterministic.
  */
 size_t dash_sparse_attn_backward_workspace_bytes(int batch, int n, int h_q);
 dash_status_t dash_sparse_attn_prefill_backward(
-    const void* q, const void* k, const void* v, const void* o, const float* lse,
-    const void* dout, dash_dtype_t dt, const uint32_t* mask, const float* bias, float* dq,
+    const void* q, const void* k, const void* v, const float* lse, const void* dout,
+    dash_dtype_t dt, const uint32_t* mask, const float* bias, float* dq,
     float* dk, float* dv, float* dbias, int batch, int n, int h_q, int h_kv, int head_dim,
     int block, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Stage 1 and Stage 0 backward for prefill [DA §3.1 Eq. 3, §3.2 Eq. 4, Prop. 1; App. A for the
+ * entmax Jacobian], the selection held fixed (each head's support and the routed set R are
+ * piecewise constant in the inputs, so no gradient flows through which chunks are selected).
+ * From dbias = dL/dd of dash_sparse_attn_prefill_backward it ADDS to dq and dk:
+ *   dlogw_c = (dd_c - mean over R of dd) / sigma on R = {c < m : mask bit set} (the routed
+ *   chunks; the window's chunks carry the constant d = 0), dw_c = dlogw_c / w_c, each head of the
+ *   group receives dp = dw / g, the entmax Jacobian gives dx = u (dp - sum(u dp) / sum(u)) /
+ *   (alpha - 1) with u = p^(2 - alpha) on the head's support, and with x = coef <q, kbar>,
+ *   coef = (alpha - 1) gamma / sqrt(D):  dq += coef sum_c dx_c kbar_c;  dkbar_c = coef sum over
+ *   rows and heads of dx_c q;  dk_j += dkbar_c / Bc for the keys j of each complete chunk c.
+ * p and w are recomputed from q, kbar and tau (the forward's threshold); a routed chunk whose
+ * recomputed w is 0 contributes nothing.
+ *   q [B, n, H_q, D] (dt); kbar [B, Tc, H_kv, D] fp32 from dash_pool_keys (mean pooling);
+ *   tau [B, n, H_q], mask [B, n, H_kv, W] from dash_block_entmax(_ex) on the same q, kbar, alpha,
+ *   gamma, sigma, window_blocks; dbias [B, n, H_kv, Nc] fp32; dq [B, n, H_q, D] and dk
+ *   [B, n, H_kv, D] fp32, read and updated in place. workspace: device scratch of
+ *   dash_block_entmax_backward_workspace_bytes(B, n, H_q, H_kv) bytes.
+ * Deterministic: every element is updated by one thread in a fixed order.
+ */
+size_t dash_block_entmax_backward_workspace_bytes(int batch, int n, int h_q, int h_kv);
+dash_status_t dash_block_entmax_backward(const void* q, dash_dtype_t dt, const float* kbar,
+                                         const float* tau, const uint32_t* mask,
+                                         const float* dbias, float* dq, float* dk, int batch,
+                                         int n, int h_q, int h_kv, int head_dim, int block,
+                                         float alpha, float gamma, float sigma,
+                                         int window_blocks, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Stage 2, decode [DA §3.5, split-KV variant]: the Stage 2 output of one new query per sequence

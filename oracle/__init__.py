@@ -64,6 +64,8 @@ def lib():
                                                vp, vp, vp]
         L.orc_sparse_attn_backward_rows.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, d,
                                                     vp, ctypes.c_int64, vp, vp]
+        L.orc_block_entmax_backward.argtypes = [vp, i, vp, vp, i, i, i, i, i, i, d, d, d, i, vp,
+                                                ctypes.c_int64, vp, vp]
         L.orc_num_threads.restype = i
         _lib = L
     return _lib
@@ -98,8 +100,8 @@ def _host(a):
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
-def _ptr(a: np.ndarray):
-    return a.ctypes.data_as(ctypes.c_void_p)
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
 def _check(rc: int, name: str):
@@ -316,3 +318,24 @@ def sparse_attn_backward_rows(q, k, v, mask, bias, dout, rows, *, block: int,
                                                _ptr(r), nr, _ptr(dq), _ptr(dbias)),
            "sparse_attn_backward_rows")
     return dict(dq=dq, dbias=dbias)
+
+
+def block_entmax_backward(q, kbar, dd, *, n_kv: int, block: int, alpha: float, gamma: float,
+                          sigma: float, window: int = 1, rows=None, want_dkbar: bool = False):
+    """Routing gradients for prefill with the selection held fixed: dd = dL/dd [R, Hkv, Nc] of
+    the listed rows (all rows when rows is None). Returns dict(dq [R, Hq, D]: the routing part of
+    dq, dkbar [B, Tc, Hkv, D] or None) in float64."""
+    qa, dt = _host(q)
+    kb = np.ascontiguousarray(np.asarray(kbar, dtype=np.float64))
+    b, n, hq, d = qa.shape
+    hkv = kb.shape[2]
+    nc = math.ceil(n_kv / block)
+    r, nr = _rows(rows, b * n)
+    ddv = np.ascontiguousarray(np.asarray(dd, dtype=np.float64).reshape(nr, hkv, nc))
+    dq = np.zeros((nr, hq, d))
+    dkbar = np.zeros(kb.shape) if want_dkbar else None
+    _check(lib().orc_block_entmax_backward(
+        _ptr(qa), dt, _ptr(kb), _ptr(ddv), b, n, hq, hkv, d, block, alpha, gamma, sigma,
+        int(window), None if r is None else _ptr(r), nr, _ptr(dq), _ptr(dkbar)),
+        "block_entmax_backward")
+    return dict(dq=dq, dkbar=dkbar)

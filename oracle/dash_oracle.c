@@ -558,53 +558,43 @@ done:
     return rc;
 }
 
-int orc_backward(const void* q, const void* k, const void* v, int dtype, const double* dout,
-                 int batch, int n, int h_q, int h_kv, int head_dim, int block, double alpha,
-                 double gamma, double sigma, int window, double scale, double* dq, double* dk,
-                 double* dv, double* dbias) {
-    if (check_attn_args(q, k, v, batch, n, 0, n, h_q, h_kv, head_dim, block) || !dout || !dq ||
-        !dk || !dv || window < 1)
+int orc_block_entmax_backward(const void* q, int dtype, const double* kbar, const double* dd,
+                              int batch, int n, int h_q, int h_kv, int head_dim, int block,
+                              double alpha, double gamma, double sigma, int window,
+                              const int64_t* rows, int64_t n_rows, double* dq, double* dkbar) {
+    if (!q || !dd || !dq || window < 1) return -1;
+    if (batch <= 0 || n <= 0 || h_q <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0 ||
+        h_q % h_kv != 0)
         return -1;
     if (!(alpha > 1.0 && alpha <= 2.0) || !(gamma > 0.0) || !(sigma > 0.0)) return -1;
-    const int g = h_q / h_kv, tc = n / block;
+    const int g = h_q / h_kv, tc = n / block, D = head_dim;
     const int nc = (int)div_ceil(n, block), nw = (int)div_ceil(nc, 32);
-    const int D = head_dim;
-    const int64_t R = (int64_t)batch * n;
-    double* kbar = calloc((size_t)batch * (tc > 0 ? tc : 1) * h_kv * D, sizeof(double));
-    uint32_t* mask = calloc((size_t)R * h_kv * nw, sizeof(uint32_t));
-    double* bias = calloc((size_t)R * h_kv * nc, sizeof(double));
-    double* tau = calloc((size_t)R * h_q, sizeof(double));
-    double* x = calloc((size_t)R * h_q * nc, sizeof(double));
-    double* w = calloc((size_t)R * h_kv * nc, sizeof(double));
-    double* o = calloc((size_t)R * h_q * D, sizeof(double));
-    double* lse = calloc((size_t)R * h_q, sizeof(double));
-    double* dd = calloc((size_t)R * h_kv * nc, sizeof(double));
-    double* dw = calloc((size_t)R * h_kv * nc, sizeof(double));
-    double* dkbar = calloc((size_t)batch * (tc > 0 ? tc : 1) * h_kv * D, sizeof(double));
+    if (tc > 0 && !kbar) return -1;
+    if (!rows) n_rows = (int64_t)batch * n;
+    for (int64_t i = 0; rows && i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= (int64_t)batch * n) return -1;
+    uint32_t* mask = calloc((size_t)n_rows * h_kv * nw, sizeof(uint32_t));
+    double* bias = calloc((size_t)n_rows * h_kv * nc, sizeof(double));
+    double* tau = calloc((size_t)n_rows * h_q, sizeof(double));
+    double* x = calloc((size_t)n_rows * h_q * nc, sizeof(double));
+    double* w = calloc((size_t)n_rows * h_kv * nc, sizeof(double));
+    double* dw = calloc((size_t)n_rows * h_kv * nc, sizeof(double));
     int rc = -1;
-    if (!kbar || !mask || !bias || !tau || !x || !w || !o || !lse || !dd || !dw || !dkbar) goto done;
-    /* the forward pass, for the quantities the gradients need */
-    if (tc > 0 && orc_pool_keys(k, dtype, batch, n, h_kv, D, block, kbar)) goto done;
-    if (orc_block_entmax(q, dtype, kbar, batch, n, 0, n, h_q, h_kv, D, block, alpha, gamma, sigma,
-                         window, NULL, 0, mask, bias, tau, x, w))
+    if (!mask || !bias || !tau || !x || !w || !dw) goto done;
+    /* the routing of the listed rows, for x, tau and w */
+    if (tc > 0 && orc_block_entmax(q, dtype, kbar, batch, n, 0, n, h_q, h_kv, D, block, alpha,
+                                   gamma, sigma, window, rows, n_rows, mask, bias, tau, x, w))
         goto done;
-    if (orc_sparse_attn(q, k, v, dtype, mask, bias, batch, n, 0, n, h_q, h_kv, D, block, scale,
-                        NULL, 0, o, lse))
-        goto done;
-    if (orc_sparse_attn_backward(q, k, v, dtype, mask, bias, dout, batch, n, h_q, h_kv, D, block,
-                                 scale, dq, dk, dv, dd))
-        goto done;
-    /* only the routed chunks' d depends on w (the window's chunks carry the constant d = 0) */
-    for (int64_t i = 0; i < R * h_kv * nc; ++i)
-        if (!(w[i] > 0.0)) dd[i] = 0.0;
+    memset(dq, 0, sizeof(double) * n_rows * h_q * D);
 
-    /* d -> w [DA Prop. 1]: d_c = (log w_c - mu) / sigma on R with mu the mean of log w over R, so
+    /* d -> w [DA Prop. 1]: d_c = (log w_c - mu) / sigma on R = {c : w_c > 0} (the window's
+     * chunks carry the constant d = 0 and have no w) with mu the mean of log w over R, so
      * dL/dlog w_c = (dd_c - mean_R dd) / sigma and dL/dw_c = that / w_c (c in R; 0 elsewhere). */
-    if (!isinf(sigma))
-        for (int64_t row = 0; row < R; ++row)
+    if (tc > 0 && !isinf(sigma))
+        for (int64_t kk = 0; kk < n_rows; ++kk)
             for (int r = 0; r < h_kv; ++r) {
-                const double* wr = w + (row * h_kv + r) * nc;
-                const double* ddr = dd + (row * h_kv + r) * nc;
+                const double* wr = w + (kk * h_kv + r) * nc;
+                const double* ddr = dd + (kk * h_kv + r) * nc;
                 double s = 0.0;
                 int nr = 0;
                 for (int c = 0; c < nc; ++c)
@@ -614,46 +604,92 @@ int orc_backward(const void* q, const void* k, const void* v, int dtype, const d
                     }
                 if (nr == 0) continue;
                 for (int c = 0; c < nc; ++c)
-                    if (wr[c] > 0.0) dw[(row * h_kv + r) * nc + c] = (ddr[c] - s / nr) / sigma / wr[c];
+                    if (wr[c] > 0.0) dw[(kk * h_kv + r) * nc + c] = (ddr[c] - s / nr) / sigma / wr[c];
             }
 
     /* w -> p_h -> x_h [DA §3.2, Eq. 2; App. A]: w is the mean of the group's heads, so each head
      * receives dp = dw / g; on the support of p = [x - tau]_+^(1/(alpha-1)), with u = p^(2-alpha),
      * the entmax Jacobian gives dx = u (dp - sum(u dp) / sum(u)) / (alpha - 1), 0 off the support.
      * x = coef <q, kbar> with coef = (alpha - 1) gamma / sqrt(D) [Eq. 4]. */
-    {
+    if (tc > 0) {
         const double coef = (alpha - 1.0) * gamma / sqrt((double)D);
         const double e = 1.0 / (alpha - 1.0);
-        for (int b = 0; b < batch; ++b)
-            for (int t = 0; t < n; ++t)
-                for (int h = 0; h < h_q; ++h) {
-                    const int r = h / g;
-                    const int64_t row = (int64_t)b * n + t;
-                    const double* xr = x + (row * h_q + h) * nc;
-                    const double th = tau[row * h_q + h];
-                    if (isinf(th)) continue; /* no candidate chunk */
-                    double su = 0.0, sud = 0.0;
-                    for (int c = 0; c < nc && !isnan(xr[c]); ++c)
-                        if (xr[c] > th) {
-                            const double u = pow(pow(xr[c] - th, e), 2.0 - alpha);
-                            su += u;
-                            sud += u * dw[(row * h_kv + r) * nc + c] / g;
-                        }
-                    if (su <= 0.0) continue;
-                    const int64_t qi = (row * h_q + h) * D;
-                    for (int c = 0; c < nc && !isnan(xr[c]); ++c) {
-                        if (!(xr[c] > th)) continue;
+        for (int64_t kk = 0; kk < n_rows; ++kk) {
+            const int64_t rho = rows ? rows[kk] : kk;
+            const int b = (int)(rho / n);
+            for (int h = 0; h < h_q; ++h) {
+                const int r = h / g;
+                const double* xr = x + (kk * h_q + h) * nc;
+                const double th = tau[kk * h_q + h];
+                if (isinf(th)) continue; /* no candidate chunk */
+                double su = 0.0, sud = 0.0;
+                for (int c = 0; c < nc && !isnan(xr[c]); ++c)
+                    if (xr[c] > th) {
                         const double u = pow(pow(xr[c] - th, e), 2.0 - alpha);
-                        const double dx = u * (dw[(row * h_kv + r) * nc + c] / g - sud / su) / (alpha - 1.0);
-                        const int64_t kb = (((int64_t)b * tc + c) * h_kv + r) * D;
-                        for (int f = 0; f < D; ++f) {
-                            dq[qi + f] += coef * dx * kbar[kb + f];
-                            dkbar[kb + f] += coef * dx * orc_load(q, dtype, qi + f);
-                        }
+                        su += u;
+                        sud += u * dw[(kk * h_kv + r) * nc + c] / g;
+                    }
+                if (su <= 0.0) continue;
+                const int64_t qi = (rho * h_q + h) * D;
+                for (int c = 0; c < nc && !isnan(xr[c]); ++c) {
+                    if (!(xr[c] > th)) continue;
+                    const double u = pow(pow(xr[c] - th, e), 2.0 - alpha);
+                    const double dx = u * (dw[(kk * h_kv + r) * nc + c] / g - sud / su) / (alpha - 1.0);
+                    const int64_t kb = (((int64_t)b * tc + c) * h_kv + r) * D;
+                    for (int f = 0; f < D; ++f) {
+                        dq[(kk * h_q + h) * D + f] += coef * dx * kbar[kb + f];
+                        if (dkbar) dkbar[kb + f] += coef * dx * orc_load(q, dtype, qi + f);
                     }
                 }
+            }
+        }
     }
+    rc = 0;
+done:
+    free(mask); free(bias); free(tau); free(x); free(w); free(dw);
+    return rc;
+}
 
+int orc_backward(const void* q, const void* k, const void* v, int dtype, const double* dout,
+                 int batch, int n, int h_q, int h_kv, int head_dim, int block, double alpha,
+                 double gamma, double sigma, int window, double scale, double* dq, double* dk,
+                 double* dv, double* dbias) {
+    if (check_attn_args(q, k, v, batch, n, 0, n, h_q, h_kv, head_dim, block) || !dout || !dq ||
+        !dk || !dv || window < 1)
+        return -1;
+    if (!(alpha > 1.0 && alpha <= 2.0) || !(gamma > 0.0) || !(sigma > 0.0)) return -1;
+    const int tc = n / block;
+    const int nc = (int)div_ceil(n, block), nw = (int)div_ceil(nc, 32);
+    const int D = head_dim;
+    const int64_t R = (int64_t)batch * n;
+    double* kbar = calloc((size_t)batch * (tc > 0 ? tc : 1) * h_kv * D, sizeof(double));
+    uint32_t* mask = calloc((size_t)R * h_kv * nw, sizeof(uint32_t));
+    double* bias = calloc((size_t)R * h_kv * nc, sizeof(double));
+    double* tau = calloc((size_t)R * h_q, sizeof(double));
+    double* x = calloc((size_t)R * h_q * nc, sizeof(double));
+    double* w = calloc((size_t)R * h_kv * nc, sizeof(double));
+    double* dd = calloc((size_t)R * h_kv * nc, sizeof(double));
+    double* dqr = calloc((size_t)R * h_q * D, sizeof(double));
+    double* dkbar = calloc((size_t)batch * (tc > 0 ? tc : 1) * h_kv * D, sizeof(double));
+    int rc = -1;
+    if (!kbar || !mask || !bias || !tau || !x || !w || !dd || !dqr || !dkbar) goto done;
+    /* the forward pass's selection */
+    if (tc > 0 && orc_pool_keys(k, dtype, batch, n, h_kv, D, block, kbar)) goto done;
+    if (orc_block_entmax(q, dtype, kbar, batch, n, 0, n, h_q, h_kv, D, block, alpha, gamma, sigma,
+                         window, NULL, 0, mask, bias, tau, x, w))
+        goto done;
+    /* Stage 2 with the selection held fixed: dq, dk, dv and dL/dd */
+    if (orc_sparse_attn_backward(q, k, v, dtype, mask, bias, dout, batch, n, h_q, h_kv, D, block,
+                                 scale, dq, dk, dv, dd))
+        goto done;
+    /* only the routed chunks' d depends on w (the window's chunks carry the constant d = 0) */
+    for (int64_t i = 0; i < R * h_kv * nc; ++i)
+        if (!(w[i] > 0.0)) dd[i] = 0.0;
+    /* Stage 1: d -> w -> p -> x -> q and kbar */
+    if (orc_block_entmax_backward(q, dtype, kbar, dd, batch, n, h_q, h_kv, D, block, alpha, gamma,
+                                  sigma, window, NULL, 0, dqr, dkbar))
+        goto done;
+    for (int64_t i = 0; i < R * h_q * D; ++i) dq[i] += dqr[i];
     /* kbar -> k [DA Eq. 3 with the summary query at zero]: the mean of the chunk's keys */
     for (int b = 0; b < batch; ++b)
         for (int c = 0; c < tc; ++c)
@@ -665,7 +701,7 @@ int orc_backward(const void* q, const void* k, const void* v, int dtype, const d
     if (dbias) memcpy(dbias, dd, sizeof(double) * R * h_kv * nc);
     rc = 0;
 done:
-    free(kbar); free(mask); free(bias); free(tau); free(x); free(w); free(o); free(lse);
-    free(dd); free(dw); free(dkbar);
+    free(kbar); free(mask); free(bias); free(tau); free(x); free(w); free(dd); free(dqr);
+    free(dkbar);
     return rc;
 }

@@ -110,6 +110,17 @@ int orc_sparse_attn_backward_rows(const void* q, const void* k, const void* v, i
                                   double scale, const int64_t* rows, int64_t n_rows, double* dq,
                                   double* dbias);
 
+/* Gradients of Stage 1 (the routing) for prefill, the selection held fixed: from dd = dL/dd of
+ * the listed rows (rows[i] = b * n + t; every row when rows is NULL) [R, H_kv, Nc], the chain
+ * d -> log w (mu couples the routed chunks) -> w (the GQA mean) -> each head's entmax (its
+ * Jacobian on the support) -> x = coef <q, kbar>. Writes the routing part of dq for the listed
+ * rows [R, H_q, D] and, when dkbar is not NULL, adds coef * sum of dx q into dkbar [B, Tc, H_kv, D].
+ * kbar [B, Tc, H_kv, D] are the mean-pooled summaries the forward routed with. */
+int orc_block_entmax_backward(const void* q, int dtype, const double* kbar, const double* dd,
+                              int batch, int n, int h_q, int h_kv, int head_dim, int block,
+                              double alpha, double gamma, double sigma, int window,
+                              const int64_t* rows, int64_t n_rows, double* dq, double* dkbar);
+
 /* Gradients of the whole forward pass (Stage 0 mean pooling, Stage 1 routing, Stage 2 bias-form
  * attention) for prefill (every query row, q_pos0 = 0), given dout = dL/do [B, n, H_q, D]:
  * dq [B, n, H_q, D], dk, dv [B, n, H_kv, D] and, when dbias is not NULL, dL/dd for every routed

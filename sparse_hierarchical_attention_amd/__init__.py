@@ -22,7 +22,8 @@ __all__ = [
     "dash_block_entmax_ex", "dash_block_entmax_workspace_bytes", "dash_sparse_attn_prefill",
     "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
     "dash_sparse_attn_backward_workspace_bytes", "dash_sparse_attn_prefill_backward",
-    "dash_version", "forward", "decode_step",
+    "dash_block_entmax_backward_workspace_bytes", "dash_block_entmax_backward",
+    "dash_version", "backward", "forward", "decode_step",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -74,8 +75,13 @@ def lib():
                                                      i, i, f, vp, sz, vp]
         L.dash_sparse_attn_backward_workspace_bytes.argtypes = [i, i, i]
         L.dash_sparse_attn_backward_workspace_bytes.restype = sz
-        L.dash_sparse_attn_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp, vp, vp,
-                                                        vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        L.dash_sparse_attn_prefill_backward.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp,
+                                                        vp, i, i, i, i, i, i, f, vp, sz, vp]
+        L.dash_block_entmax_backward_workspace_bytes.argtypes = [i, i, i, i]
+        L.dash_block_entmax_backward_workspace_bytes.restype = sz
+        L.dash_block_entmax_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                                 f, f, f, i, vp, sz, vp]
+        L.dash_block_entmax_backward.restype = i
         for fn in ("dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append",
                    "dash_block_entmax", "dash_block_entmax_ex", "dash_sparse_attn_prefill",
                    "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
@@ -267,18 +273,18 @@ def dash_sparse_attn_backward_workspace_bytes(batch, n, h_q) -> int:
 
 
 def dash_sparse_attn_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                                      o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
-                                      mask: torch.Tensor, bias: torch.Tensor, *, block: int,
+                                      lse: torch.Tensor, dout: torch.Tensor, mask: torch.Tensor,
+                                      bias: torch.Tensor, *, block: int,
                                       scale: float | None = None, want_dbias: bool = True,
                                       workspace: torch.Tensor | None = None):
-    """Stage 2 prefill gradients with the selection held fixed: o, lse from
-    dash_sparse_attn_prefill, dout like o (q's dtype). -> (dq, dk, dv, dbias or None), fp32."""
+    """Stage 2 prefill gradients with the selection held fixed: lse from
+    dash_sparse_attn_prefill, dout in q's dtype. -> (dq, dk, dv, dbias or None), fp32."""
     b, n, hq, d = q.shape
     hkv = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if dout.dtype != q.dtype or o.dtype != q.dtype:
-        raise TypeError("o and dout must have q's dtype")
+    if dout.dtype != q.dtype:
+        raise TypeError("dout must have q's dtype")
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty((b, n, hq, d), **f32)
     dk = torch.empty((b, n, hkv, d), **f32)
@@ -287,12 +293,37 @@ def dash_sparse_attn_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch
     need = dash_sparse_attn_backward_workspace_bytes(b, n, hq)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dev = _dev(q, k, v, o, lse, dout, mask, bias, workspace)
+    dev = _dev(q, k, v, lse, dout, mask, bias, workspace)
     _check(lib().dash_sparse_attn_prefill_backward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _dtype_code(q), _ptr(mask),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _dtype_code(q), _ptr(mask),
         _ptr(bias), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), b, n, hq, hkv, d, block,
         float(scale), _ptr(workspace), workspace.numel(), _stream(dev)))
     return dq, dk, dv, dbias
+
+
+def dash_block_entmax_backward_workspace_bytes(batch, n, h_q, h_kv) -> int:
+    return int(lib().dash_block_entmax_backward_workspace_bytes(batch, n, h_q, h_kv))
+
+
+def dash_block_entmax_backward(q: torch.Tensor, kbar: torch.Tensor, tau: torch.Tensor,
+                               mask: torch.Tensor, dbias: torch.Tensor, dq: torch.Tensor,
+                               dk: torch.Tensor, *, block: int, alpha: float, gamma: float,
+                               sigma: float, window_blocks: int = 1,
+                               workspace: torch.Tensor | None = None) -> None:
+    """Routing and pooling gradients for prefill, added in place to dq [B, n, Hq, D] and dk
+    [B, n, Hkv, D] (fp32), from dbias = dL/dd of dash_sparse_attn_prefill_backward."""
+    b, n, hq, d = q.shape
+    hkv = dk.shape[2]
+    if dq.dtype != torch.float32 or dk.dtype != torch.float32:
+        raise TypeError("dq and dk must be float32")
+    need = dash_block_entmax_backward_workspace_bytes(b, n, hq, hkv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dev = _dev(q, kbar, tau, mask, dbias, dq, dk, workspace)
+    _check(lib().dash_block_entmax_backward(
+        _ptr(q), _dtype_code(q), _ptr(kbar), _ptr(tau), _ptr(mask), _ptr(dbias), _ptr(dq),
+        _ptr(dk), b, n, hq, hkv, d, block, float(alpha), float(gamma), float(sigma),
+        int(window_blocks), _ptr(workspace), workspace.numel(), _stream(dev)))
 
 
 def dash_decode_workspace_bytes(batch, n_ctx, h_q, h_kv, head_dim, block) -> int:
@@ -349,14 +380,33 @@ def dash_sparse_attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cac
 
 
 def forward(q, k, v, *, block: int, alpha: float, gamma: float, sigma: float,
-            scale: float | None = None):
+            scale: float | None = None, window: int = 1):
     """Whole prefill forward: pool -> route -> sparse attention. Returns a dict of every
-    intermediate (kbar, mask, bias, tau, o, lse)."""
+    intermediate (kbar, mask, bias, tau, o, lse). window: blocks always attended (the query's
+    own and window - 1 before it)."""
     kbar = dash_pool_keys(k, block)
-    mask, bias, tau = dash_block_entmax(q, kbar, n_kv=k.shape[1], block=block, alpha=alpha,
-                                        gamma=gamma, sigma=sigma, h_kv=k.shape[2])
+    if window == 1:
+        mask, bias, tau = dash_block_entmax(q, kbar, n_kv=k.shape[1], block=block, alpha=alpha,
+                                            gamma=gamma, sigma=sigma, h_kv=k.shape[2])
+    else:
+        mask, bias, tau = dash_block_entmax_ex(q, kbar, n_kv=k.shape[1], block=block,
+                                               alpha=alpha, gamma=gamma, sigma=sigma,
+                                               h_kv=k.shape[2], window_blocks=window)
     o, lse = dash_sparse_attn_prefill(q, k, v, mask, bias, block=block, scale=scale)
     return dict(kbar=kbar, mask=mask, bias=bias, tau=tau, o=o, lse=lse)
+
+
+def backward(q, k, v, dout, fwd: dict, *, block: int, alpha: float, gamma: float, sigma: float,
+             scale: float | None = None, window: int = 1) -> dict:
+    """Gradients of the prefill forward (pool, route, attend) for dL/do = dout, given the dict
+    that forward() returned with the same arguments: dict(dq, dk, dv, dbias), fp32. The
+    selection is held fixed (no gradient flows through which chunks are selected)."""
+    dq, dk, dv, dbias = dash_sparse_attn_prefill_backward(q, k, v, fwd["lse"], dout, fwd["mask"],
+                                                          fwd["bias"], block=block, scale=scale)
+    dash_block_entmax_backward(q, fwd["kbar"], fwd["tau"], fwd["mask"], dbias, dq, dk,
+                               block=block, alpha=alpha, gamma=gamma, sigma=sigma,
+                               window_blocks=window)
+    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias)
 
 
 def decode_step(q, k_cache, v_cache, kbar, *, block: int, alpha: float, gamma: float,

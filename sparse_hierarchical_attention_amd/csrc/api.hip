@@ -234,23 +234,55 @@ size_t dash_sparse_attn_backward_workspace_bytes(int batch, int n, int h_q) {
 }
 
 dash_status_t dash_sparse_attn_prefill_backward(
-    const void* q, const void* k, const void* v, const void* o, const float* lse,
-    const void* dout, dash_dtype_t dt, const uint32_t* mask, const float* bias, float* dq,
+    const void* q, const void* k, const void* v, const float* lse, const void* dout,
+    dash_dtype_t dt, const uint32_t* mask, const float* bias, float* dq,
     float* dk, float* dv, float* dbias, int batch, int n, int h_q, int h_kv, int head_dim,
     int block, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const char* fn = "dash_sparse_attn_prefill_backward";
     dash_status_t s = check_shape(fn, dt, batch, n, h_q, h_kv, head_dim, block);
     if (s != DASH_OK) return s;
     if (!(scale > 0.0f) || isinf(scale)) return fail(DASH_ERR_INVALID, "%s: scale=%g must be positive and finite", fn, scale);
-    if (!q || !k || !v || !o || !lse || !dout || !mask || !bias || !dq || !dk || !dv)
+    if (!q || !k || !v || !lse || !dout || !mask || !bias || !dq || !dk || !dv)
         return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
     dash::AttnParams p = attn_params(batch, n, 0, n, h_q, h_kv, head_dim, block, scale);
     const size_t need = dash::attn_backward_workspace_bytes(p);
     if (!workspace || workspace_bytes < need)
         return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace ? workspace_bytes : (size_t)0);
-    return hip_status(dash::launch_attn_backward(q, k, v, o, lse, dout, dt, mask, bias, dq, dk, dv,
+    return hip_status(dash::launch_attn_backward(q, k, v, lse, dout, dt, mask, bias, dq, dk, dv,
                                                  dbias, p, workspace, stream), fn);
+}
+
+size_t dash_block_entmax_backward_workspace_bytes(int batch, int n, int h_q, int h_kv) {
+    if (batch <= 0 || n <= 0 || h_q <= 0 || h_kv <= 0) return 0;
+    return (size_t)batch * n * (h_q + h_kv) * sizeof(float);
+}
+
+dash_status_t dash_block_entmax_backward(const void* q, dash_dtype_t dt, const float* kbar,
+                                         const float* tau, const uint32_t* mask,
+                                         const float* dbias, float* dq, float* dk, int batch,
+                                         int n, int h_q, int h_kv, int head_dim, int block,
+                                         float alpha, float gamma, float sigma,
+                                         int window_blocks, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "dash_block_entmax_backward";
+    dash_status_t s = check_shape(fn, dt, batch, n, h_q, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (window_blocks < 1) return fail(DASH_ERR_INVALID, "%s: window_blocks=%d must be >= 1", fn, window_blocks);
+    if (!(alpha > 1.0f && alpha <= 2.0f)) return fail(DASH_ERR_INVALID, "%s: alpha=%g not in (1, 2]", fn, alpha);
+    if (!(gamma > 0.0f) || isinf(gamma)) return fail(DASH_ERR_INVALID, "%s: gamma=%g must be positive and finite", fn, gamma);
+    if (!(sigma > 0.0f)) return fail(DASH_ERR_INVALID, "%s: sigma=%g must be positive (or +inf)", fn, sigma);
+    if (!q || (!kbar && n / block > 0) || !tau || !mask || !dbias || !dq || !dk)
+        return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    dash::RouteParams p = route_params(batch, n, 0, n, h_q, h_kv, head_dim, block, alpha, gamma,
+                                       sigma);
+    p.win = window_blocks - 1;
+    const size_t need = dash::route_backward_workspace_bytes(p);
+    if (!workspace || workspace_bytes < need)
+        return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(dash::launch_route_backward(q, (int)dt, kbar, tau, mask, dbias, dq, dk, p,
+                                                  workspace, stream), fn);
 }
 
 size_t dash_decode_workspace_bytes(int batch, int n_ctx, int h_q, int h_kv, int head_dim,

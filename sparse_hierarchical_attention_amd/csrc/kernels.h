@@ -41,6 +41,10 @@ hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const R
                                hipStream_t st);
 hipError_t launch_score_one(const void* q, int dt, const float* kbar, float* x,
                             const RouteParams& p, hipStream_t st);
+size_t route_backward_workspace_bytes(const RouteParams& p);
+hipError_t launch_route_backward(const void* q, int dt, const float* kbar, const float* tau,
+                                 const uint32_t* mask, const float* dbias, float* dq, float* dk,
+                                 const RouteParams& p, void* ws, hipStream_t st);
 
 
 // ---- Stage 2 (sparse_attn.hip)
@@ -83,8 +87,8 @@ hipError_t launch_attn_decode(const void* q, const void* k, const void* v, int d
                               const uint32_t* mask, const float* bias, void* o,
                               const AttnParams& p, void* ws, hipStream_t st);
 size_t attn_backward_workspace_bytes(const AttnParams& p);
-hipError_t launch_attn_backward(const void* q, const void* k, const void* v, const void* o,
-                                const float* lse, const void* dout, int dt, const uint32_t* mask,
+hipError_t launch_attn_backward(const void* q, const void* k, const void* v, const float* lse,
+                                const void* dout, int dt, const uint32_t* mask,
                                 const float* bias, float* dq, float* dk, float* dv, float* dbias,
                                 const AttnParams& p, void* ws, hipStream_t st);
 

@@ -131,7 +131,7 @@ def test_backward_rejects_bad_arguments(L):
     need = L.dash_sparse_attn_backward_workspace_bytes(2, 300, 8)
     assert need == 2 * 300 * 8 * 4
     assert L.dash_sparse_attn_backward_workspace_bytes(0, 300, 8) == 0
-    args = [p] * 6 + [1] + [p] * 6
+    args = [p] * 5 + [1] + [p] * 6
     assert L.dash_sparse_attn_prefill_backward(*args, 2, 300, 8, 2, 128, 32, 0.1, p, need - 1,
                                                None) == 3
     assert L.dash_sparse_attn_prefill_backward(*args, 2, 300, 8, 2, 128, 32, 0.0, p, need,
@@ -140,10 +140,10 @@ def test_backward_rejects_bad_arguments(L):
                                                None) == 1
     assert L.dash_sparse_attn_prefill_backward(*args, 2, 300, 8, 2, 96, 32, 0.1, p, need,
                                                None) == 2
-    nulls = [p] * 5 + [None] + [1] + [p] * 6
+    nulls = [p] * 4 + [None] + [1] + [p] * 6
     assert L.dash_sparse_attn_prefill_backward(*nulls, 2, 300, 8, 2, 128, 32, 0.1, p, need,
                                                None) == 1 and "null" in err(L)
     # dbias may be NULL: validation passes up to the (absent) workspace
-    no_dbias = [p] * 6 + [1] + [p] * 5 + [None]
+    no_dbias = [p] * 5 + [1] + [p] * 5 + [None]
     assert L.dash_sparse_attn_prefill_backward(*no_dbias, 2, 300, 8, 2, 128, 32, 0.1, None, 0,
                                                None) == 3

@@ -156,3 +156,24 @@ def test_stage2_row_gradients_match_the_full_pass(orc):
                                atol=1e-12)
     np.testing.assert_allclose(part["dbias"], full["dbias"].reshape(90, 2, -1)[rows], rtol=1e-12,
                                atol=1e-12)
+
+
+def test_routing_gradient_rows_match_the_full_chain(orc):
+    """The routing part on its own (listed rows, and every row with dkbar) against the full
+    chain minus the Stage 2 part, with a window of two blocks."""
+    q, k, v, dout = case(14, n=80)
+    kw = dict(block=8, alpha=1.5, gamma=8.0, sigma=0.5, window=2)
+    full = orc.backward(q, k, v, dout, **kw)
+    st = orc.forward(q, k, v, **kw)
+    s2 = orc.sparse_attn_backward(q, k, v, st["mask"], st["bias"], dout, block=8)
+    dd = s2["dbias"].reshape(st["w"].shape)
+    rk = dict(n_kv=80, block=8, alpha=1.5, gamma=8.0, sigma=0.5, window=2)
+    rows = np.array([79, 40, 17, 63, 5])
+    part = orc.block_entmax_backward(q, st["kbar"], dd[rows], rows=rows, **rk)
+    route_dq = (full["dq"] - s2["dq"]).reshape(80, 4, 8)
+    np.testing.assert_allclose(part["dq"], route_dq[rows], rtol=1e-10, atol=1e-12)
+    assert np.abs(route_dq).max() > 1e-3  # the routing part is present
+    every = orc.block_entmax_backward(q, st["kbar"], dd, want_dkbar=True, **rk)
+    np.testing.assert_allclose(every["dq"], route_dq, rtol=1e-10, atol=1e-12)
+    dk_route = np.repeat(every["dkbar"], 8, axis=1) / 8  # mean pooling: each key gets dkbar / Bc
+    np.testing.assert_allclose(dk_route, full["dk"] - s2["dk"], rtol=1e-10, atol=1e-12)
