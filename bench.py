@@ -33,6 +33,9 @@ import workloads as wl  # noqa: E402
 METRIC = "prefill eff. TFLOP/s @32K + decode tok/s @128K; % of MFMA / HBM roofline"
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+# vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 4 flops (a packed bf16 dot2 or a packed
+# fp32 FMA per lane and cycle)
+VALU_PEAK_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -267,6 +270,56 @@ def random_mask_sweep(dash, dev, reps: int):
               file=sys.stderr, flush=True)
 
 
+def backward_leg(dash, pre, wp: wl.Workload, args) -> dict:
+    """Gradients of the 32K prefill (Stage 2 with the selection held fixed, then the routing and
+    pooling chain) for a seeded dL/do, timed with HIP events over `steps` passes after `warmup`
+    untimed ones. The forward that produces the selection, lse and tau runs once, untimed.
+    Algorithmic work of Stage 2: the five products of attention's backward (S = QK^T, dP = dO V^T,
+    dV = P^T dO, dQ = dS K, dK = dS^T Q), 2 D flops each per selected (query head, key) pair."""
+    q, k, v = pre["q"], pre["k"], pre["v"]
+    kw = dict(block=wp.block, alpha=wp.alpha, gamma=wp.gamma, sigma=wp.sigma)
+    fwd = dash.forward(q, k, v, **kw)
+    dout = wl.output_gradient(q.shape, 77, q.dtype, q.device)
+    hq, hkv, d = wp.h_q, wp.h_kv, wp.head_dim
+    ws2 = torch.empty(dash.dash_sparse_attn_backward_workspace_bytes(1, wp.n_q, hq),
+                      dtype=torch.uint8, device=q.device)
+    wsr = torch.empty(dash.dash_block_entmax_backward_workspace_bytes(1, wp.n_q, hq, hkv),
+                      dtype=torch.uint8, device=q.device)
+    timer = Timer()
+
+    def one(t):
+        s, e = t.span("bwd_attn") if t else (None, None)
+        s and s.record()
+        dq, dk, dv, dbias = dash.dash_sparse_attn_prefill_backward(
+            q, k, v, fwd["lse"], dout, fwd["mask"], fwd["bias"], block=wp.block, workspace=ws2)
+        e and e.record()
+        s, e = t.span("bwd_route") if t else (None, None)
+        s and s.record()
+        dash.dash_block_entmax_backward(q, fwd["kbar"], fwd["tau"], fwd["mask"], dbias, dq, dk,
+                                        workspace=wsr, **kw)
+        e and e.record()
+
+    print(f"[bench] backward: warmup {args.warmup}, timing {args.steps}", file=sys.stderr,
+          flush=True)
+    for _ in range(args.warmup):
+        one(None)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        one(timer)
+    torch.cuda.synchronize()
+    pairs, _ = selected_pairs_prefill(fwd["mask"], wp)
+    flops = 10.0 * d * pairs
+    t_attn, t_route = timer.mean_ms("bwd_attn"), timer.mean_ms("bwd_route")
+    tf = flops / (t_attn * 1e-3) / 1e12
+    return {
+        "ms": {"attn": round(t_attn, 3), "route": round(t_route, 3)},
+        "algorithmic_tflop": round(flops / 1e12, 4),
+        "tflops": round(flops / ((t_attn + t_route) * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "alu", "achieved": round(tf, 3), "peak": VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / VALU_PEAK_TFLOPS, 4), "traffic": None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +331,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB `steps` times: the "
                          "reference for scaling HBM byte counters; no JSON line is printed")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward leg (gradients of the 32K prefill, timed on their own "
+                         "after the step)")
     ap.add_argument("--random-mask-sweep", action="store_true",
                     help="run the pages' random-selection efficiency sweep instead of the step "
                          "(Hq 32, Hkv 2, N 16-96K, three sparsities); one JSON line per point")
@@ -386,6 +442,7 @@ def main():
     if args.only:
         print(f"[bench] {args.only} only: {ms_step:.3f} ms per step", file=sys.stderr, flush=True)
         return
+    backward = None if args.no_backward else backward_leg(dash, pre, wp, args)
 
     pairs, frac = selected_pairs_prefill(mask, wp)
     flops = 4.0 * wp.head_dim * pairs
@@ -444,6 +501,7 @@ def main():
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None,
+        "backward": backward,
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

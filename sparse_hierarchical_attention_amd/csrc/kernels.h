@@ -87,6 +87,10 @@ hipError_t launch_attn_decode(const void* q, const void* k, const void* v, int d
                               const uint32_t* mask, const float* bias, void* o,
                               const AttnParams& p, void* ws, hipStream_t st);
 size_t attn_backward_workspace_bytes(const AttnParams& p);
+hipError_t launch_attn_backward_mfma(const void* q, const void* k, const void* v,
+                                     const float* lse, const void* dout, const uint32_t* mask,
+                                     const float* bias, float* dq, float* dk, float* dv,
+                                     float* dbias, const AttnParams& p, void* ws, hipStream_t st);
 hipError_t launch_attn_backward(const void* q, const void* k, const void* v, const float* lse,
                                 const void* dout, int dt, const uint32_t* mask,
                                 const float* bias, float* dq, float* dk, float* dv, float* dbias,

@@ -7,6 +7,7 @@
 // downstream multiplies dL/dd by 1 / w, which is large near the edge of a head's support.
 //   dL/dd_c = sum of ds_j over chunk c's keys and the group's heads (the chunks below the query's
 //   own whose mask bit is set).
+// These VALU kernels serve fp32 inputs; bf16 runs on the matrix cores (sparse_attn_bwd_mfma.hip).
 // Two kernels, each output element written by one wave (no atomics, deterministic):
 //   attn_bwd_dq_kernel, row-parallel: one wave per (token, KV group, set of four heads) walks the
 //     token's selection in units of kDecUnit keys (the decode path's per-lane layout: a 16-byte
@@ -350,17 +351,15 @@ static void launch_bwd_d(const void* q, const void* k, const void* v,
     }
 }
 
-hipError_t launch_attn_backward(const void* q, const void* k, const void* v, const float* lse, const void* dout, int dt, const uint32_t* mask,
+hipError_t launch_attn_backward(const void* q, const void* k, const void* v, const float* lse,
+                                const void* dout, int dt, const uint32_t* mask,
                                 const float* bias, float* dq, float* dk, float* dv, float* dbias,
                                 const AttnParams& p, void* ws, hipStream_t st) {
+    // bf16 runs on the matrix cores (sparse_attn_bwd_mfma.hip); fp32 here
+    if (dt == kBF16) return launch_attn_backward_mfma(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, p, ws, st);
     float* drow = static_cast<float*>(ws);
-    if (dt == kBF16) {
-        if (p.head_dim == 64) launch_bwd_d<bf16_t, 64>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, drow, p, st);
-        else launch_bwd_d<bf16_t, 128>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, drow, p, st);
-    } else {
-        if (p.head_dim == 64) launch_bwd_d<float, 64>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, drow, p, st);
-        else launch_bwd_d<float, 128>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, drow, p, st);
-    }
+    if (p.head_dim == 64) launch_bwd_d<float, 64>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, drow, p, st);
+    else launch_bwd_d<float, 128>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, drow, p, st);
     return hipGetLastError();
 }
 

@@ -1,0 +1,490 @@
+// Stage 2 backward for prefill on bf16 MFMA ("DashAttention", arXiv 2605.18753v1, §3.4 Prop. 1,
+// differentiated with the selection held fixed), gfx950. The same gradients as the VALU kernels
+// of sparse_attn_bwd.hip:
+//   p_j = exp(scale <q, k_j> + d_c(j) - lse), dp_j = <dO, v_j>, ds_j = p_j (dp_j - Delta),
+//   Delta = sum_j p_j dp_j (summed in fp32 from the probabilities, not from the stored O),
+//   dQ = scale sum_j ds_j k_j, dK_j = scale sum ds_j q, dV_j = sum p_j dO, dL/dd_c = sum of ds_j
+//   over chunk c's keys and the group's heads.
+// The score and dP products accumulate exact bf16 products in fp32, so p, dp, ds, Delta and
+// dL/dd carry fp32 rounding only; the products that take p or ds as an operand (dV, dK, dQ)
+// round them to bf16, as attention's forward rounds p for P V.
+//
+// attn_bwd_dq_mfma_kernel, row-parallel, one workgroup (4 waves) per 128 rows of one (sequence,
+// KV group): T = 128 / g consecutive tokens times the g heads, as the forward kernel tiles them.
+// It walks the union of its tokens' selected chunks twice, K and V tiles of up to 64 keys staged
+// through LDS (double-buffered):
+//   pass 1: S^T = K Q^T and dP^T = V dO^T (v_mfma_f32_32x32x16_bf16, Q and dO rows held as B
+//           operands), p from the stored lse, Delta += p dp;
+//   pass 2: the same products, ds = p (dp - Delta), dL/dd per (token, chunk) summed over the
+//           chunk's keys and the token's heads, and dQ^T += K^T dS^T with K^T read through
+//           transposing LDS loads (ds_read_b64_tr_b16), dS^T straight from the accumulator.
+// attn_bwd_dkv_mfma_kernel, column-parallel, one workgroup per (sequence, KV group, chunk), one
+// wave per 32 keys holding its keys and values as B operands: the tokens that attend the chunk
+// (its own, causally, and later ones whose mask bit is set) are listed in order, their rows
+// (token x head) gathered into LDS 32 at a time, and per tile
+//   S = Q K^T, dP = dO V^T, p, ds = p (dp - Delta), dV^T += dO^T P, dK^T += Q^T dS,
+// with dO^T and Q^T read through transposing LDS loads and P, dS from the accumulators.
+// Each output element is written once, by one lane: deterministic, no atomics.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dash {
+
+namespace {
+
+typedef __bf16 bw_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short bw_i16x4 __attribute__((ext_vector_type(4)));
+typedef float bw_f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) bw_i16x4 bw_lds_i16x4;
+
+constexpr int kBwRows = 128;     // rows (token x head) per workgroup of the dq kernel
+constexpr int kBwThreads = 256;
+constexpr int kBwMaxWords = 256;  // 8192 chunks
+constexpr float kBwLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ bw_i16x4 bw_read_tr16(const bf16_t* ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (bw_lds_i16x4*)(__attribute__((address_space(3))) void*)(ptr));
+}
+
+// A operand (32 dims x 16 rows) of X^T += Y^T Z for Y stored row-major in LDS (stride LS): the
+// transposing loads give lane l dimension 32 dt + (l % 32) of the rows 16 ks + 4 G + {0..3} and
+// + 8, the order in which the accumulator-derived B operand holds its rows.
+template <int LS>
+__device__ __forceinline__ bw_bf16x8 tr_operand(const bf16_t* base, int ks, int dt, int lane) {
+    const int grp = lane >> 4, kl = lane & 15;
+    const int r = 4 * (grp >> 1) + (kl >> 2);
+    const int d = 16 * (grp & 1) + 4 * (kl & 3);
+    const bf16_t* ptr = base + (16 * ks + r) * LS + 32 * dt + d;
+    const bw_i16x4 lo = bw_read_tr16(ptr);
+    const bw_i16x4 hi = bw_read_tr16(ptr + 8 * LS);
+    return __builtin_bit_cast(bw_bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace
+
+template <int D, int BLK, int GQ>
+__global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ lse, const bf16_t* __restrict__ dout,
+    const uint32_t* __restrict__ mask, const float* __restrict__ bias, float* __restrict__ dq,
+    float* __restrict__ dbias, float* __restrict__ delta, AttnParams p, int n_tiles) {
+    constexpr int T = kBwRows / GQ;          // tokens per workgroup
+    constexpr int KT = BLK < 64 ? BLK : 64;  // keys per LDS tile
+    constexpr int NSUB = BLK / KT;
+    constexpr int LS = D + 16;               // K / V row stride in LDS (elements)
+    constexpr int MT = KT / 32;              // 32-key M-tiles
+    constexpr int DT = D / 32;               // 32-dim M-tiles of dQ^T
+    constexpr int LOADS = KT * (D / 8) / kBwThreads;
+    static_assert(LOADS >= 1, "tile too small");
+    __shared__ __align__(16) bf16_t Ks[2][KT * LS];
+    __shared__ __align__(16) bf16_t Vs[2][KT * LS];
+    __shared__ uint32_t uni[kBwMaxWords];
+
+    int gr;
+    {
+        const int bh = p.batch * p.h_kv, x = blockIdx.x;
+        gr = bh % 8 == 0 ? (x % 8) + 8 * ((x / 8) % (bh / 8)) : x % bh;
+    }
+    const int tile = n_tiles - 1 - blockIdx.x / (p.batch * p.h_kv);
+    const int b = gr / p.h_kv, r = gr % p.h_kv;
+    const int n = p.n_kv;
+    const int tile0 = tile * T;
+    const int tile_end = min(tile0 + T, n);
+    const int c_first = tile0 / BLK, c_last = (tile_end - 1) / BLK;
+    const int nwt = c_last / 32 + 1;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 31, G = lane >> 5;
+    const int row = wave * 32 + j;
+    const int tok = row / GQ, hl = row % GQ;
+    const int pos = tile0 + tok;
+    const bool valid = pos < n;
+    const int cpos = pos / BLK;
+    const int64_t qrow = (int64_t)b * n + pos;
+    const uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
+    const float* brow = bias + (qrow * p.h_kv + r) * p.nc;
+
+    // dL/dd entries no selected chunk writes: chunks at or past each token's own, and unselected
+    if (dbias) {
+        for (int idx = tid; idx < T * p.nc; idx += kBwThreads) {
+            const int t = idx / p.nc, c = idx % p.nc;
+            const int ps = tile0 + t;
+            if (ps >= n) continue;
+            const int64_t rr = ((int64_t)b * n + ps) * p.h_kv + r;
+            if (c >= ps / BLK || !((mask[rr * p.nw + (c >> 5)] >> (c & 31)) & 1u)) dbias[rr * p.nc + c] = 0.f;
+        }
+    }
+    // union of the tile tokens' selections (bits past a token's own chunk ignored)
+    for (int w = tid; w < nwt; w += kBwThreads) uni[w] = 0u;
+    __syncthreads();
+    for (int idx = tid; idx < T * nwt; idx += kBwThreads) {
+        const int t = idx / nwt, w = idx % nwt;
+        const int ps = tile0 + t;
+        if (ps >= n) continue;
+        const int hi = ps / BLK - 32 * w;
+        if (hi < 0) continue;
+        uint32_t word = mask[(((int64_t)b * n + ps) * p.h_kv + r) * p.nw + w];
+        if (hi < 31) word &= (2u << hi) - 1u;
+        if (hi < 32) word |= 1u << hi;
+        if (word) atomicOr(&uni[w], word);
+    }
+    __syncthreads();
+    auto next_chunk = [&](int c) -> int {
+        int w = (c + 1) >> 5;
+        if (w >= nwt) return -1;
+        uint32_t word = uni[w] & (~0u << ((c + 1) & 31));
+        while (true) {
+            if (word) return 32 * w + __builtin_ctz(word);
+            if (++w >= nwt) return -1;
+            word = uni[w];
+        }
+    };
+
+    // this wave's Q and dO rows as B operands (k-slot order shared with the K / V row reads)
+    bw_bf16x8 qf[D / 16], df[D / 16];
+    {
+        const int64_t off = (qrow * p.h_q + r * GQ + hl) * D + 8 * G;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const uint4 uq = valid ? *reinterpret_cast<const uint4*>(q + off + 16 * s) : make_uint4(0, 0, 0, 0);
+            const uint4 ud = valid ? *reinterpret_cast<const uint4*>(dout + off + 16 * s) : make_uint4(0, 0, 0, 0);
+            qf[s] = __builtin_bit_cast(bw_bf16x8, uq);
+            df[s] = __builtin_bit_cast(bw_bf16x8, ud);
+        }
+    }
+    const float lse2 = valid ? lse[qrow * p.h_q + r * GQ + hl] * kBwLog2e : 0.f;
+    const float qk_scale = p.scale * kBwLog2e;
+    const int64_t kv_row_stride = (int64_t)p.h_kv * D;
+    const bf16_t* kbase = k + (int64_t)b * n * kv_row_stride + (int64_t)r * D;
+    const bf16_t* vbase = v + (int64_t)b * n * kv_row_stride + (int64_t)r * D;
+
+    uint4 pk[LOADS], pv[LOADS];
+    auto fetch = [&](int c, int sub) {
+        const int key0 = c * BLK + sub * KT;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int e = tid + i * kBwThreads;
+            const int kk = e / (D / 8), d8 = e % (D / 8);
+            const int key = key0 + kk;
+            pk[i] = make_uint4(0, 0, 0, 0);
+            pv[i] = make_uint4(0, 0, 0, 0);
+            if (key < n) {
+                pk[i] = *reinterpret_cast<const uint4*>(kbase + key * kv_row_stride + 8 * d8);
+                pv[i] = *reinterpret_cast<const uint4*>(vbase + key * kv_row_stride + 8 * d8);
+            }
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int e = tid + i * kBwThreads;
+            const int kk = e / (D / 8), d8 = e % (D / 8);
+            *reinterpret_cast<uint4*>(&Ks[buf][kk * LS + 8 * d8]) = pk[i];
+            *reinterpret_cast<uint4*>(&Vs[buf][kk * LS + 8 * d8]) = pv[i];
+        }
+    };
+
+    float dsum = 0.f;   // pass 1: this lane's part of Delta
+    float Delta = 0.f;  // pass 2: the row's Delta
+    float dbpart = 0.f; // pass 2: this lane's part of dL/dd of the current chunk
+    bw_f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = bw_f32x16{};
+
+    for (int pass = 0; pass < 2; ++pass) {
+        int c = next_chunk(-1), sub = 0;  // every tile has at least its own chunk
+        fetch(c, 0);
+        stash(0);
+        __syncthreads();
+        for (int buf = 0; c >= 0; buf ^= 1) {
+            const int key0 = c * BLK + sub * KT;
+            const int c_nx = sub + 1 < NSUB ? c : next_chunk(c);
+            const int sub_nx = sub + 1 < NSUB ? sub + 1 : 0;
+            if (c_nx >= 0) fetch(c_nx, sub_nx);
+            bool sel = false;
+            if (valid && c <= cpos) sel = c == cpos || ((mrow[c >> 5] >> (c & 31)) & 1u);
+            const float off = sel ? (c == cpos ? 0.f : brow[c] * kBwLog2e) - lse2 : -INFINITY;
+            const bool causal = c >= c_first;
+
+            // per 32-key M-tile: S^T = K Q^T, dP^T = V dO^T, then p (and in pass 2 ds and the
+            // two 16-key k-steps of dQ^T += K^T dS^T that this M-tile feeds)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const bw_bf16x8 a = *reinterpret_cast<const bw_bf16x8*>(&Ks[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+                    const bw_bf16x8 av = *reinterpret_cast<const bw_bf16x8*>(&Vs[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, df[ks], dp, 0, 0, 0);
+                }
+                // p = exp(scale s + d - lse) on the row's selected, causal keys; 0 elsewhere
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    float pe = __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, off));
+                    if (causal) {
+                        const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
+                        pe = key > pos ? 0.f : pe;
+                    }
+                    s[rr] = pe;
+                }
+                if (pass == 0) {
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) dsum = fmaf(s[rr], dp[rr], dsum);
+                } else {
+                    bw_bf16x8 dsf[2];
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) {
+                        const float ds = s[rr] * (dp[rr] - Delta);
+                        dbpart += ds;
+                        dsf[rr >> 3][rr & 7] = (__bf16)ds;
+                    }
+                    // dQ^T += K^T dS^T over k-steps 2 mt and 2 mt + 1
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) {
+                            const bw_bf16x8 a = tr_operand<LS>(Ks[buf], 2 * mt + h2, dt, lane);
+                            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[h2], acc[dt], 0, 0, 0);
+                        }
+                }
+            }
+            if (pass == 1) {
+                if (sub == NSUB - 1) {
+                    // dL/dd of chunk c: the row's keys (both lane halves), then the token's heads
+                    float tot = dbpart + __shfl_xor(dbpart, 32, kWave);
+#pragma unroll
+                    for (int x = 1; x < GQ; x <<= 1) tot += __shfl_xor(tot, x, kWave);
+                    if (dbias && sel && c != cpos && G == 0 && hl == 0)
+                        dbias[(qrow * p.h_kv + r) * p.nc + c] = tot;
+                    dbpart = 0.f;
+                }
+            }
+            if (c_nx >= 0) stash(buf ^ 1);
+            __syncthreads();
+            c = c_nx;
+            sub = sub_nx;
+        }
+        if (pass == 0) Delta = dsum + __shfl_xor(dsum, 32, kWave);
+    }
+
+    if (!valid) return;
+    if (G == 0) delta[qrow * p.h_q + r * GQ + hl] = Delta;
+    float* orow = dq + (qrow * p.h_q + r * GQ + hl) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const int d0 = 32 * dt + 8 * qd + 4 * G;
+            *reinterpret_cast<float4*>(orow + d0) =
+                make_float4(acc[dt][4 * qd] * p.scale, acc[dt][4 * qd + 1] * p.scale,
+                            acc[dt][4 * qd + 2] * p.scale, acc[dt][4 * qd + 3] * p.scale);
+        }
+}
+
+template <int D, int BLK, int GQ>
+__global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ lse, const bf16_t* __restrict__ dout,
+    const uint32_t* __restrict__ mask, const float* __restrict__ bias,
+    const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
+    AttnParams p) {
+    constexpr int NTH = 2 * BLK;             // one wave per 32 keys
+    constexpr int NWV = NTH / 64;
+    constexpr int LS = D + 16;               // row stride of the gathered Q / dO rows in LDS
+    constexpr int RT = 32;                   // rows (token x head) per tile
+    constexpr int TPT = RT / GQ;             // tokens per tile
+    constexpr int DT = D / 32;
+    constexpr int PIECES = RT * (D / 8);     // 16-byte pieces per tensor and tile
+    __shared__ __align__(16) bf16_t Qs[RT * LS];
+    __shared__ __align__(16) bf16_t Ds[RT * LS];
+    __shared__ float meta[4][RT];             // lse * log2(e) - d log2(e), Delta, token, valid
+    __shared__ int list[NTH];
+    __shared__ int wtot[NWV];
+
+    const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 31, G = lane >> 5;
+    const int n = p.n_kv;
+    const int key = c * BLK + 32 * wave + j;  // this lane's key (B operand column)
+    const bool key_ok = key < n;
+    const int64_t kv_row_stride = (int64_t)p.h_kv * D;
+
+    // the wave's keys and values as B operands: lane (j, G) holds dims 16 ks + 8 G .. + 7
+    bw_bf16x8 kf[D / 16], vf[D / 16];
+    {
+        const int64_t off = ((int64_t)b * n + (key_ok ? key : 0)) * kv_row_stride + (int64_t)r * D + 8 * G;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const uint4 uk = key_ok ? *reinterpret_cast<const uint4*>(k + off + 16 * s) : make_uint4(0, 0, 0, 0);
+            const uint4 uv = key_ok ? *reinterpret_cast<const uint4*>(v + off + 16 * s) : make_uint4(0, 0, 0, 0);
+            kf[s] = __builtin_bit_cast(bw_bf16x8, uk);
+            vf[s] = __builtin_bit_cast(bw_bf16x8, uv);
+        }
+    }
+    bw_f32x16 acck[DT], accv[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        acck[dt] = bw_f32x16{};
+        accv[dt] = bw_f32x16{};
+    }
+    const float qk_scale = p.scale * kBwLog2e;
+
+    for (int t0 = c * BLK; t0 < n; t0 += NTH) {
+        // ordered list of this block's tokens that attend chunk c
+        const int t = t0 + tid;
+        bool att = false;
+        if (t < n) {
+            const int ct = t / BLK;
+            att = ct == c || (ct > c && ((mask[(((int64_t)b * n + t) * p.h_kv + r) * p.nw + (c >> 5)] >> (c & 31)) & 1u));
+        }
+        const uint64_t bal = __ballot(att);
+        if (lane == 0) wtot[wave] = __popcll(bal);
+        __syncthreads();
+        int before = 0, total = 0;
+        for (int w2 = 0; w2 < NWV; ++w2) {
+            before += w2 < wave ? wtot[w2] : 0;
+            total += wtot[w2];
+        }
+        if (att) list[before + __popcll(bal & ((1ull << lane) - 1ull))] = t;
+        __syncthreads();
+
+        for (int tl0 = 0; tl0 < total; tl0 += TPT) {
+            // gather the tile's rows: row m = token (tl0 + m / g) x head m % g
+            for (int e = tid; e < PIECES; e += NTH) {
+                const int m = e / (D / 8), d8 = e % (D / 8);
+                const int tl = tl0 + m / GQ;
+                uint4 uq = make_uint4(0, 0, 0, 0), ud = make_uint4(0, 0, 0, 0);
+                if (tl < total) {
+                    const int64_t off = ((((int64_t)b * n + list[tl]) * p.h_q) + r * GQ + m % GQ) * D + 8 * d8;
+                    uq = *reinterpret_cast<const uint4*>(q + off);
+                    ud = *reinterpret_cast<const uint4*>(dout + off);
+                }
+                *reinterpret_cast<uint4*>(&Qs[m * LS + 8 * d8]) = uq;
+                *reinterpret_cast<uint4*>(&Ds[m * LS + 8 * d8]) = ud;
+            }
+            if (tid < RT) {
+                const int m = tid, tl = tl0 + m / GQ;
+                float base = 0.f, dl = 0.f, tokf = -1.f, ok = 0.f;
+                if (tl < total) {
+                    const int tt = list[tl];
+                    const int64_t qr = (int64_t)b * n + tt;
+                    const int h = r * GQ + m % GQ;
+                    const float dd = tt / BLK == c ? 0.f : bias[(qr * p.h_kv + r) * p.nc + c];
+                    base = (lse[qr * p.h_q + h] - dd) * kBwLog2e;
+                    dl = delta[qr * p.h_q + h];
+                    tokf = (float)tt;
+                    ok = 1.f;
+                }
+                meta[0][m] = base;
+                meta[1][m] = dl;
+                meta[2][m] = tokf;
+                meta[3][m] = ok;
+            }
+            __syncthreads();
+
+            // S = Q K^T and dP = dO V^T: lane (j, G) holds key j and rows 8 (rr / 4) + 4 G + rr % 4
+            bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const bw_bf16x8 aq = *reinterpret_cast<const bw_bf16x8*>(&Qs[j * LS + 16 * ks + 8 * G]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s, 0, 0, 0);
+                const bw_bf16x8 ad = *reinterpret_cast<const bw_bf16x8*>(&Ds[j * LS + 16 * ks + 8 * G]);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], dp, 0, 0, 0);
+            }
+            bw_bf16x8 pf[2], dsf[2];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int m = 8 * (rr >> 2) + 4 * G + (rr & 3);
+                const bool ok = meta[3][m] != 0.f && key_ok && (float)key <= meta[2][m];
+                const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, -meta[0][m])) : 0.f;
+                const float ds = pe * (dp[rr] - meta[1][m]);
+                pf[rr >> 3][rr & 7] = (__bf16)pe;
+                dsf[rr >> 3][rr & 7] = (__bf16)ds;
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bw_bf16x8 ad = tr_operand<LS>(Ds, kb, dt, lane);
+                    accv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pf[kb], accv[dt], 0, 0, 0);
+                    const bw_bf16x8 aq = tr_operand<LS>(Qs, kb, dt, lane);
+                    acck[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[kb], acck[dt], 0, 0, 0);
+                }
+            __syncthreads();  // Qs, Ds and meta are refilled by the next tile
+        }
+    }
+    if (!key_ok) return;
+    const int64_t obase = (((int64_t)b * n + key) * p.h_kv + r) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const int d0 = 32 * dt + 8 * qd + 4 * G;
+            *reinterpret_cast<float4*>(dk + obase + d0) =
+                make_float4(acck[dt][4 * qd] * p.scale, acck[dt][4 * qd + 1] * p.scale,
+                            acck[dt][4 * qd + 2] * p.scale, acck[dt][4 * qd + 3] * p.scale);
+            *reinterpret_cast<float4*>(dv + obase + d0) =
+                make_float4(accv[dt][4 * qd], accv[dt][4 * qd + 1], accv[dt][4 * qd + 2],
+                            accv[dt][4 * qd + 3]);
+        }
+}
+
+template <int D, int BLK, int GQ>
+static void launch_bwd_mfma_g(const void* q, const void* k, const void* v, const float* lse,
+                              const void* dout, const uint32_t* mask, const float* bias,
+                              float* dq, float* dk, float* dv, float* dbias, float* delta,
+                              const AttnParams& p, hipStream_t st) {
+    const int T = kBwRows / GQ;
+    const int n_tiles = div_up(p.n_kv, T);
+    hipLaunchKernelGGL((attn_bwd_dq_mfma_kernel<D, BLK, GQ>), dim3(p.batch * p.h_kv * n_tiles),
+                       dim3(kBwThreads), 0, st, static_cast<const bf16_t*>(q),
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse,
+                       static_cast<const bf16_t*>(dout), mask, bias, dq, dbias, delta, p, n_tiles);
+    hipLaunchKernelGGL((attn_bwd_dkv_mfma_kernel<D, BLK, GQ>), dim3(p.nc, p.h_kv, p.batch),
+                       dim3(2 * BLK), 0, st, static_cast<const bf16_t*>(q),
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse,
+                       static_cast<const bf16_t*>(dout), mask, bias, delta, dk, dv, p);
+}
+
+template <int D, int BLK>
+static void launch_bwd_mfma_b(const void* q, const void* k, const void* v, const float* lse,
+                              const void* dout, const uint32_t* mask, const float* bias,
+                              float* dq, float* dk, float* dv, float* dbias, float* delta,
+                              const AttnParams& p, hipStream_t st) {
+    switch (p.g) {
+        case 1: launch_bwd_mfma_g<D, BLK, 1>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st); break;
+        case 2: launch_bwd_mfma_g<D, BLK, 2>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st); break;
+        case 4: launch_bwd_mfma_g<D, BLK, 4>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st); break;
+        case 8: launch_bwd_mfma_g<D, BLK, 8>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st); break;
+        default: launch_bwd_mfma_g<D, BLK, 16>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st); break;
+    }
+}
+
+template <int D>
+static void launch_bwd_mfma_d(const void* q, const void* k, const void* v, const float* lse,
+                              const void* dout, const uint32_t* mask, const float* bias,
+                              float* dq, float* dk, float* dv, float* dbias, float* delta,
+                              const AttnParams& p, hipStream_t st) {
+    if (p.block == 32) launch_bwd_mfma_b<D, 32>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st);
+    else if (p.block == 64) launch_bwd_mfma_b<D, 64>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st);
+    else launch_bwd_mfma_b<D, 128>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st);
+}
+
+hipError_t launch_attn_backward_mfma(const void* q, const void* k, const void* v,
+                                     const float* lse, const void* dout, const uint32_t* mask,
+                                     const float* bias, float* dq, float* dk, float* dv,
+                                     float* dbias, const AttnParams& p, void* ws,
+                                     hipStream_t st) {
+    float* delta = static_cast<float*>(ws);
+    if (p.head_dim == 64) launch_bwd_mfma_d<64>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st);
+    else launch_bwd_mfma_d<128>(q, k, v, lse, dout, mask, bias, dq, dk, dv, dbias, delta, p, st);
+    return hipGetLastError();
+}
+
+}  // namespace dash

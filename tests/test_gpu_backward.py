@@ -2,10 +2,12 @@
 on seeded random inputs: Stage 2 on random selections, and the whole chain (pool, route, attend).
 
 Tolerance: the gradients have no fixed scale, so each tensor's error is measured against its
-largest reference magnitude. They are computed and written in fp32 from inputs that fp32 reads
-exactly (bf16 or fp32), so the bar is 1e-4 of that magnitude for both input types; the routing
-part is loosened by its condition (the rounding of x - tau relative to x - tau, see
-_row_condition) times 1e-6, and rows whose condition exceeds 1e4 are left out."""
+largest (max) and mean (mean) reference magnitude. fp32 inputs run in fp32 throughout: 1e-4.
+bf16 inputs run on the matrix cores, whose dV, dK and dQ products take p and ds rounded to bf16
+(2^-9), as the forward's P V does: the forward's bf16 bars, 2e-2 (max) and 1e-2 (mean). dL/dd
+sums ds in fp32 and keeps 1e-4 for both. The routing part is loosened by its condition (the
+rounding of x - tau relative to x - tau, see _row_condition) times 1e-6, and rows whose condition
+exceeds 1e4 are left out."""
 from __future__ import annotations
 
 import numpy as np
@@ -26,6 +28,13 @@ def dash():
     return d
 
 
+def _bars(name, dtype):
+    """(max, mean) bars for a gradient tensor."""
+    if dtype == "f32" or name.startswith("dbias"):
+        return 1e-4, 1e-4
+    return 2e-2, 1e-2
+
+
 def _compare(name, gpu, ref, dtype):
     gpu = np.asarray(gpu, dtype=np.float64)
     scale = float(np.abs(ref).max())
@@ -36,7 +45,8 @@ def _compare(name, gpu, ref, dtype):
     max_rel = float(err.max()) / scale
     mean_rel = float(err.mean()) / float(np.abs(ref).mean())
     print(f"{name}: max {max_rel:.2e} mean {mean_rel:.2e} (scale {scale:.3g})", flush=True)
-    assert max_rel <= 1e-4 and mean_rel <= 1e-4, (name, max_rel, mean_rel)
+    bmax, bmean = _bars(name, dtype)
+    assert max_rel <= bmax and mean_rel <= bmean, (name, max_rel, mean_rel)
 
 
 def run_backward(dash, orc, w: wl.Workload, sparsity: float, seed: int, want_dbias=True):
@@ -149,7 +159,7 @@ def test_backward_prefill_32k(dash, orc):
     dk_h = parity.to_host(dk).astype(np.float64)
     err_k = float(np.abs(dk_h.sum(axis=(0, 1))).max()) / float(np.abs(dk_h).sum(axis=(0, 1)).max())
     print(f"sum rules: dv {err_v:.2e}, dk {err_k:.2e} (of the summed magnitudes)", flush=True)
-    assert err_v <= 1e-5 and err_k <= 1e-5
+    assert err_v <= 1e-3 and err_k <= 1e-3  # bf16 rounding of p and ds in the dV, dK products
 
 
 # ------------------------------------------------------------- the whole chain: pool, route, attend
@@ -183,7 +193,7 @@ def _row_condition(st, q, w: wl.Workload) -> np.ndarray:
 
 
 def _compare_cond(name, gpu, ref, dtype, cond):
-    base_max = 1e-4
+    base_max, base_mean = _bars(name, dtype)
     gpu = np.asarray(gpu, dtype=np.float64)
     scale = float(np.abs(ref).max())
     if scale == 0.0:
@@ -195,7 +205,7 @@ def _compare_cond(name, gpu, ref, dtype, cond):
     tol = base_max + 1e-6 * cond  # rounding of x - tau, scaled by the condition (at most 1e4)
     print(f"{name}: max {max_rel:.2e} (tol {tol:.1e}) mean {mean_rel:.2e} (scale {scale:.3g})",
           flush=True)
-    assert max_rel <= tol and mean_rel <= tol, (name, max_rel, mean_rel, tol)
+    assert max_rel <= tol and mean_rel <= base_mean + 1e-6 * cond, (name, max_rel, mean_rel, tol)
 
 
 def _as_gpu_selection(st, w):
