@@ -300,6 +300,8 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
     constexpr int TPT = RT / GQ;             // tokens per tile
     constexpr int DT = D / 32;
     constexpr int PIECES = RT * (D / 8);     // 16-byte pieces per tensor and tile
+    constexpr int NP = PIECES / NTH;         // of them per thread
+    static_assert(PIECES % NTH == 0 && NTH >= RT, "tile does not split over the threads");
     __shared__ __align__(16) bf16_t Qs[RT * LS];
     __shared__ __align__(16) bf16_t Ds[RT * LS];
     __shared__ float meta[4][RT];             // lse * log2(e) - d log2(e), Delta, token, valid
@@ -353,39 +355,59 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
         if (att) list[before + __popcll(bal & ((1ull << lane) - 1ull))] = t;
         __syncthreads();
 
-        for (int tl0 = 0; tl0 < total; tl0 += TPT) {
-            // gather the tile's rows: row m = token (tl0 + m / g) x head m % g
-            for (int e = tid; e < PIECES; e += NTH) {
+        // the rows of a tile (row m = token tl0 + m / g, head m % g) go global -> registers ->
+        // LDS; the next tile's loads are issued before the current tile's products
+        uint4 gq[NP], gd[NP];
+        float g_base = 0.f, g_dl = 0.f, g_tok = -1.f, g_ok = 0.f;
+        auto gather = [&](int tl0) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int e = tid + i * NTH;
                 const int m = e / (D / 8), d8 = e % (D / 8);
                 const int tl = tl0 + m / GQ;
-                uint4 uq = make_uint4(0, 0, 0, 0), ud = make_uint4(0, 0, 0, 0);
+                gq[i] = make_uint4(0, 0, 0, 0);
+                gd[i] = make_uint4(0, 0, 0, 0);
                 if (tl < total) {
                     const int64_t off = ((((int64_t)b * n + list[tl]) * p.h_q) + r * GQ + m % GQ) * D + 8 * d8;
-                    uq = *reinterpret_cast<const uint4*>(q + off);
-                    ud = *reinterpret_cast<const uint4*>(dout + off);
+                    gq[i] = *reinterpret_cast<const uint4*>(q + off);
+                    gd[i] = *reinterpret_cast<const uint4*>(dout + off);
                 }
-                *reinterpret_cast<uint4*>(&Qs[m * LS + 8 * d8]) = uq;
-                *reinterpret_cast<uint4*>(&Ds[m * LS + 8 * d8]) = ud;
             }
             if (tid < RT) {
                 const int m = tid, tl = tl0 + m / GQ;
-                float base = 0.f, dl = 0.f, tokf = -1.f, ok = 0.f;
+                g_base = 0.f, g_dl = 0.f, g_tok = -1.f, g_ok = 0.f;
                 if (tl < total) {
                     const int tt = list[tl];
                     const int64_t qr = (int64_t)b * n + tt;
                     const int h = r * GQ + m % GQ;
                     const float dd = tt / BLK == c ? 0.f : bias[(qr * p.h_kv + r) * p.nc + c];
-                    base = (lse[qr * p.h_q + h] - dd) * kBwLog2e;
-                    dl = delta[qr * p.h_q + h];
-                    tokf = (float)tt;
-                    ok = 1.f;
+                    g_base = (lse[qr * p.h_q + h] - dd) * kBwLog2e;
+                    g_dl = delta[qr * p.h_q + h];
+                    g_tok = (float)tt;
+                    g_ok = 1.f;
                 }
-                meta[0][m] = base;
-                meta[1][m] = dl;
-                meta[2][m] = tokf;
-                meta[3][m] = ok;
             }
+        };
+        auto put = [&]() {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int e = tid + i * NTH;
+                const int m = e / (D / 8), d8 = e % (D / 8);
+                *reinterpret_cast<uint4*>(&Qs[m * LS + 8 * d8]) = gq[i];
+                *reinterpret_cast<uint4*>(&Ds[m * LS + 8 * d8]) = gd[i];
+            }
+            if (tid < RT) {
+                meta[0][tid] = g_base;
+                meta[1][tid] = g_dl;
+                meta[2][tid] = g_tok;
+                meta[3][tid] = g_ok;
+            }
+        };
+        if (total > 0) gather(0);
+        for (int tl0 = 0; tl0 < total; tl0 += TPT) {
+            put();
             __syncthreads();
+            if (tl0 + TPT < total) gather(tl0 + TPT);
 
             // S = Q K^T and dP = dO V^T: lane (j, G) holds key j and rows 8 (rr / 4) + 4 G + rr % 4
             bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
