@@ -19,7 +19,8 @@
 //           chunk's keys and the token's heads, and dQ^T += K^T dS^T with K^T read through
 //           transposing LDS loads (ds_read_b64_tr_b16), dS^T straight from the accumulator.
 // attn_bwd_dkv_mfma_kernel, column-parallel, one workgroup per (sequence, KV group, chunk), one
-// wave per 32 keys holding its keys and values as B operands: the tokens that attend the chunk
+// wave per 32 keys holding its keys and values as B operands, the chunks of one (sequence, group)
+// on one XCD: the tokens that attend the chunk
 // (its own, causally, and later ones whose mask bit is set) are listed in order, their rows
 // (token x head) gathered into LDS 32 at a time, and per tile
 //   S = Q K^T, dP = dO V^T, p, ds = p (dp - Delta), dV^T += dO^T P, dK^T += Q^T dS,
@@ -296,7 +297,8 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
     constexpr int NTH = 2 * BLK;             // one wave per 32 keys
     constexpr int NWV = NTH / 64;
     constexpr int LS = D + 16;               // row stride of the gathered Q / dO rows in LDS
-    constexpr int RT = 32;                   // rows (token x head) per tile
+    constexpr int RT = BLK >= 64 ? 64 : 32;  // rows (token x head) per tile
+    constexpr int RM = RT / 32;              // 32-row M-tiles per tile
     constexpr int TPT = RT / GQ;             // tokens per tile
     constexpr int DT = D / 32;
     constexpr int PIECES = RT * (D / 8);     // 16-byte pieces per tensor and tile
@@ -308,7 +310,21 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
     __shared__ int list[NTH];
     __shared__ int wtot[NWV];
 
-    const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+    // XCD-aware order: workgroups are dealt to the eight XCDs round-robin, so index x runs on
+    // XCD x % 8; all chunks of one (sequence, KV group) are given to one XCD, in increasing
+    // order, so the workgroups streaming the same query rows share that XCD's L2
+    int c, gr;
+    {
+        const int bh = p.batch * p.h_kv, x = blockIdx.x;
+        if (bh % 8 == 0) {
+            gr = (x % 8) + 8 * ((x / 8) / p.nc);
+            c = (x / 8) % p.nc;
+        } else {
+            gr = x / p.nc;
+            c = x % p.nc;
+        }
+    }
+    const int b = gr / p.h_kv, r = gr % p.h_kv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, G = lane >> 5;
     const int n = p.n_kv;
@@ -336,7 +352,12 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
     }
     const float qk_scale = p.scale * kBwLog2e;
 
-    for (int t0 = c * BLK; t0 < n; t0 += NTH) {
+    // the tokens from chunk c on, in blocks of NTH taken from the last block down: workgroups of
+    // the same (sequence, group) start together at the end of the sequence and walk down in step,
+    // so the query rows they gather are read from HBM once and shared through the L2
+    const int nblk = div_up(n - c * BLK, NTH);
+    for (int bi = nblk - 1; bi >= 0; --bi) {
+        const int t0 = c * BLK + bi * NTH;
         // ordered list of this block's tokens that attend chunk c
         const int t = t0 + tid;
         bool att = false;
@@ -409,35 +430,39 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
             __syncthreads();
             if (tl0 + TPT < total) gather(tl0 + TPT);
 
-            // S = Q K^T and dP = dO V^T: lane (j, G) holds key j and rows 8 (rr / 4) + 4 G + rr % 4
-            bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
+            // per 32-row M-tile: S = Q K^T and dP = dO V^T (lane (j, G) holds key j and rows
+            // 32 rm + 8 (rr / 4) + 4 G + rr % 4), p and ds, then the two 16-row k-steps of
+            // dV^T += dO^T P and dK^T += Q^T dS that these rows feed
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const bw_bf16x8 aq = *reinterpret_cast<const bw_bf16x8*>(&Qs[j * LS + 16 * ks + 8 * G]);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s, 0, 0, 0);
-                const bw_bf16x8 ad = *reinterpret_cast<const bw_bf16x8*>(&Ds[j * LS + 16 * ks + 8 * G]);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], dp, 0, 0, 0);
-            }
-            bw_bf16x8 pf[2], dsf[2];
+            for (int rm = 0; rm < RM; ++rm) {
+                bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int m = 8 * (rr >> 2) + 4 * G + (rr & 3);
-                const bool ok = meta[3][m] != 0.f && key_ok && (float)key <= meta[2][m];
-                const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, -meta[0][m])) : 0.f;
-                const float ds = pe * (dp[rr] - meta[1][m]);
-                pf[rr >> 3][rr & 7] = (__bf16)pe;
-                dsf[rr >> 3][rr & 7] = (__bf16)ds;
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const bw_bf16x8 ad = tr_operand<LS>(Ds, kb, dt, lane);
-                    accv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pf[kb], accv[dt], 0, 0, 0);
-                    const bw_bf16x8 aq = tr_operand<LS>(Qs, kb, dt, lane);
-                    acck[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[kb], acck[dt], 0, 0, 0);
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const bw_bf16x8 aq = *reinterpret_cast<const bw_bf16x8*>(&Qs[(32 * rm + j) * LS + 16 * ks + 8 * G]);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s, 0, 0, 0);
+                    const bw_bf16x8 ad = *reinterpret_cast<const bw_bf16x8*>(&Ds[(32 * rm + j) * LS + 16 * ks + 8 * G]);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], dp, 0, 0, 0);
                 }
+                bw_bf16x8 pf[2], dsf[2];
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int m = 32 * rm + 8 * (rr >> 2) + 4 * G + (rr & 3);
+                    const bool ok = meta[3][m] != 0.f && key_ok && (float)key <= meta[2][m];
+                    const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, -meta[0][m])) : 0.f;
+                    const float ds = pe * (dp[rr] - meta[1][m]);
+                    pf[rr >> 3][rr & 7] = (__bf16)pe;
+                    dsf[rr >> 3][rr & 7] = (__bf16)ds;
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const bw_bf16x8 ad = tr_operand<LS>(Ds, 2 * rm + kb, dt, lane);
+                        accv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pf[kb], accv[dt], 0, 0, 0);
+                        const bw_bf16x8 aq = tr_operand<LS>(Qs, 2 * rm + kb, dt, lane);
+                        acck[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[kb], acck[dt], 0, 0, 0);
+                    }
+            }
             __syncthreads();  // Qs, Ds and meta are refilled by the next tile
         }
     }
@@ -468,7 +493,7 @@ static void launch_bwd_mfma_g(const void* q, const void* k, const void* v, const
                        dim3(kBwThreads), 0, st, static_cast<const bf16_t*>(q),
                        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse,
                        static_cast<const bf16_t*>(dout), mask, bias, dq, dbias, delta, p, n_tiles);
-    hipLaunchKernelGGL((attn_bwd_dkv_mfma_kernel<D, BLK, GQ>), dim3(p.nc, p.h_kv, p.batch),
+    hipLaunchKernelGGL((attn_bwd_dkv_mfma_kernel<D, BLK, GQ>), dim3(p.nc * p.h_kv * p.batch),
                        dim3(2 * BLK), 0, st, static_cast<const bf16_t*>(q),
                        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse,
                        static_cast<const bf16_t*>(dout), mask, bias, delta, dk, dv, p);
