@@ -122,6 +122,13 @@ def _dev(*ts: torch.Tensor) -> torch.device:
     return dev
 
 
+def _f32(**ts):
+    """Raise unless every given tensor (None skipped) is float32."""
+    for name, t in ts.items():
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32 (got {t.dtype})")
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -132,6 +139,7 @@ def _stream(dev: torch.device):
 
 def dash_pool_keys(k: torch.Tensor, block: int, kbar: torch.Tensor | None = None) -> torch.Tensor:
     """Stage 0 (mean pooling): k [B, n, Hkv, D] -> kbar [B, n // block, Hkv, D] fp32."""
+    _f32(kbar=kbar)
     b, n, hkv, d = k.shape
     if kbar is None:
         kbar = torch.empty((b, n // block, hkv, d), dtype=torch.float32, device=k.device)
@@ -144,6 +152,7 @@ def dash_pool_keys(k: torch.Tensor, block: int, kbar: torch.Tensor | None = None
 def dash_pool_keys_query(k: torch.Tensor, qbar: torch.Tensor, block: int,
                          kbar: torch.Tensor | None = None) -> torch.Tensor:
     """Stage 0 with a learned summary query qbar [Hkv, D] fp32 (Eq. 3)."""
+    _f32(qbar=qbar, kbar=kbar)
     b, n, hkv, d = k.shape
     if kbar is None:
         kbar = torch.empty((b, n // block, hkv, d), dtype=torch.float32, device=k.device)
@@ -165,6 +174,7 @@ def dash_pool_keys_append(k_cache: torch.Tensor, ctx_lens: torch.Tensor, kbar: t
                           block: int, qbar: torch.Tensor | None = None) -> torch.Tensor:
     """Streaming Stage 0: write the summary of the chunk each sequence's newest token completed
     (ctx_lens int32 [B] a positive multiple of block) into kbar [B, n_cap // block, Hkv, D]."""
+    _f32(kbar=kbar, qbar=qbar)
     b, n_cap, hkv, d = k_cache.shape
     if ctx_lens.dtype != torch.int32:
         raise TypeError("ctx_lens must be int32")
@@ -198,6 +208,7 @@ def dash_block_entmax_ex(q: torch.Tensor, kbar: torch.Tensor, *, n_kv: int, bloc
     """Stage 1 with the attention window (window_blocks blocks always attended: the query's own
     and the window_blocks - 1 before it) and, for decode (n_q = 1), per-sequence context lengths
     ctx_lens int32 [B] in a cache of capacity n_kv. Outputs as dash_block_entmax."""
+    _f32(kbar=kbar, bias=bias, tau=tau)
     b, n_q, hq, d = q.shape
     hkv = kbar.shape[2] if h_kv is None else h_kv
     mask, bias, tau = _route_outputs(q, n_kv, block, hkv, mask, bias, tau, want_tau)
@@ -225,6 +236,7 @@ def dash_block_entmax(q: torch.Tensor, kbar: torch.Tensor, *, n_kv: int, block: 
     """Stage 1: q [B, n_q, Hq, D], kbar [B, Tc, Hkv, D] fp32 ->
     mask int32 [B, n_q, Hkv, W] (uint32 bit patterns), bias fp32 [B, n_q, Hkv, Nc],
     tau fp32 [B, n_q, Hq] (None unless want_tau)."""
+    _f32(kbar=kbar, bias=bias, tau=tau)
     b, n_q, hq, d = q.shape
     hkv = kbar.shape[2] if h_kv is None else h_kv
     nc = -(-n_kv // block)
@@ -253,6 +265,7 @@ def dash_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              scale: float | None = None, o: torch.Tensor | None = None,
                              lse: torch.Tensor | None = None, want_lse: bool = True):
     """Stage 2 prefill: -> (o [B, n, Hq, D] in q's dtype, lse fp32 [B, n, Hq] or None)."""
+    _f32(bias=bias, lse=lse)
     b, n, hq, d = q.shape
     hkv = k.shape[2]
     if scale is None:
@@ -279,6 +292,7 @@ def dash_sparse_attn_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch
                                       workspace: torch.Tensor | None = None):
     """Stage 2 prefill gradients with the selection held fixed: lse from
     dash_sparse_attn_prefill, dout in q's dtype. -> (dq, dk, dv, dbias or None), fp32."""
+    _f32(lse=lse, bias=bias)
     b, n, hq, d = q.shape
     hkv = k.shape[2]
     if scale is None:
@@ -312,10 +326,9 @@ def dash_block_entmax_backward(q: torch.Tensor, kbar: torch.Tensor, tau: torch.T
                                workspace: torch.Tensor | None = None) -> None:
     """Routing and pooling gradients for prefill, added in place to dq [B, n, Hq, D] and dk
     [B, n, Hkv, D] (fp32), from dbias = dL/dd of dash_sparse_attn_prefill_backward."""
+    _f32(kbar=kbar, tau=tau, dbias=dbias, dq=dq, dk=dk)
     b, n, hq, d = q.shape
     hkv = dk.shape[2]
-    if dq.dtype != torch.float32 or dk.dtype != torch.float32:
-        raise TypeError("dq and dk must be float32")
     need = dash_block_entmax_backward_workspace_bytes(b, n, hq, hkv)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -335,6 +348,7 @@ def dash_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
                             scale: float | None = None, o: torch.Tensor | None = None,
                             workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Stage 2 decode: q [B, Hq, D] (or [B, 1, Hq, D]) -> o of the same shape."""
+    _f32(bias=bias)
     b, n_ctx, hkv, d = k_cache.shape
     hq = q.shape[-2]
     if scale is None:
@@ -359,6 +373,7 @@ def dash_sparse_attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cac
                                    workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Stage 2 decode with per-sequence lengths ctx_lens int32 [B] in a cache of capacity
     k_cache.shape[1]: q [B, Hq, D] (or [B, 1, Hq, D]) -> o of the same shape."""
+    _f32(bias=bias)
     b, n_cap, hkv, d = k_cache.shape
     hq = q.shape[-2]
     if ctx_lens.dtype != torch.int32:

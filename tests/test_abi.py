@@ -147,3 +147,15 @@ def test_backward_rejects_bad_arguments(L):
     no_dbias = [p] * 5 + [1] + [p] * 5 + [None]
     assert L.dash_sparse_attn_prefill_backward(*no_dbias, 2, 300, 8, 2, 128, 32, 0.1, None, 0,
                                                None) == 3
+
+
+def test_binding_rejects_non_fp32_side_inputs():
+    """The binding checks the fp32 operands' dtype before anything reaches the library (a float64
+    buffer passed as float * would be read as garbage)."""
+    import torch
+    import sparse_hierarchical_attention_amd as d
+    k = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(TypeError, match="qbar"):
+        d.dash_pool_keys_query(k, torch.zeros(1, 64, dtype=torch.float64), 64)
+    with pytest.raises(TypeError, match="kbar"):
+        d.dash_pool_keys(k, 64, kbar=torch.zeros(1, 1, 1, 64, dtype=torch.float64))

@@ -8,8 +8,6 @@ import numpy as np
 import pytest
 import torch
 
-torch.set_default_dtype(torch.float64)
-
 
 def case(seed, n=96, hq=4, hkv=2, d=8, block=8):
     """Random inputs whose rows route several chunks with unequal weights, so that the bias and
@@ -70,12 +68,13 @@ def test_routing_gradient_is_not_negligible(orc):
 def causal_sdpa_grads(q, k, v, dout):
     """Gradients of plain causal SDPA (Eq. 1) by torch autograd, K/V shared by each query group."""
     g = q.shape[2] // k.shape[2]
-    qt = torch.tensor(q[0]).transpose(0, 1).requires_grad_()
-    kt = torch.tensor(k[0]).transpose(0, 1).requires_grad_()
-    vt = torch.tensor(v[0]).transpose(0, 1).requires_grad_()
+    f64 = dict(dtype=torch.float64)
+    qt = torch.tensor(q[0], **f64).transpose(0, 1).requires_grad_()
+    kt = torch.tensor(k[0], **f64).transpose(0, 1).requires_grad_()
+    vt = torch.tensor(v[0], **f64).transpose(0, 1).requires_grad_()
     o = torch.nn.functional.scaled_dot_product_attention(
         qt[None], kt.repeat_interleave(g, 0)[None], vt.repeat_interleave(g, 0)[None], is_causal=True)[0]
-    o.backward(torch.tensor(dout[0]).transpose(0, 1))
+    o.backward(torch.tensor(dout[0], **f64).transpose(0, 1))
     return (qt.grad.transpose(0, 1).numpy()[None], kt.grad.transpose(0, 1).numpy()[None],
             vt.grad.transpose(0, 1).numpy()[None])
 
