@@ -75,6 +75,124 @@ def decode_bytes(mask: torch.Tensor, w: wl.Workload) -> tuple[int, float]:
     return int(kbar_bytes + kv_bytes + qo_bytes), float(routed / (w.batch * w.h_kv))
 
 
+def decode_bytes_varlen(mask: torch.Tensor, lens: np.ndarray, w: wl.Workload) -> int:
+    """decode_bytes for one new token per sequence at position lens[b] - 1 of a cache of capacity
+    w.n_kv: the summaries of the complete chunks before each token's chunk, the routed K and V
+    chunks, the token's own chunk up to it, and q / o."""
+    m = mask.cpu().numpy().view(np.uint32)                  # [B, 1, Hkv, W]
+    bits = popcount32(m).sum(axis=-1).astype(np.int64)[:, 0]  # [B, Hkv] routed + own
+    pos = lens.astype(np.int64) - 1
+    cp = pos // w.block
+    kbar_bytes = int((np.minimum(cp, w.n_kv // w.block) * w.h_kv * w.head_dim * 4).sum())
+    routed = int((bits - 1).sum())
+    diag = int(((pos - cp * w.block + 1) * w.h_kv).sum())
+    kv_bytes = (routed * w.block + diag) * w.head_dim * 2 * 2
+    qo_bytes = 2 * w.batch * w.h_q * w.head_dim * 2
+    return kbar_bytes + kv_bytes + qo_bytes
+
+
+def decode_graph(step):
+    """step() captured once in a HIP graph (after a warm run on a side stream of default priority);
+    every buffer it touches is allocated beforehand."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    return g
+
+
+def extras_leg(dash, pre, dec, wp: wl.Workload, wd: wl.Workload, reps: int) -> dict:
+    """The learned summary query (Stage 0 as the local attention of a learned q per KV head) over
+    the 32K prefill keys and the 16 x 128K decode cache, and the streaming paths: a decode step
+    with per-sequence lengths (seeded, ragged over the cache's second half) and the 32K prefill
+    with a window of two blocks. Each timed with HIP events over `reps` calls after one warm call."""
+    dev = pre["q"].device
+    out = {}
+    k, kd = pre["k"], dec["k"]
+    qbar = wl.summary_query(wp.h_kv, wp.head_dim, 91, dev)
+    pool = {}
+    for name, kk, blk in (("prefill_32k", k, wp.block), ("decode_cache_16x128k", kd, wd.block)):
+        kb = torch.empty((kk.shape[0], kk.shape[1] // blk, kk.shape[2], kk.shape[3]),
+                         dtype=torch.float32, device=dev)
+        t = _time_ms(lambda: dash.dash_pool_keys_query(kk, qbar, blk, kbar=kb), reps)
+        nbytes = kk.numel() * kk.element_size() + kb.numel() * 4
+        gbs = nbytes / (t * 1e-3) / 1e9
+        pool[name] = {"ms": round(t, 4), "algorithmic_bytes": nbytes, "gb_per_s": round(gbs, 1),
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS,
+                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBPS, 4)}}
+    out["learned_summary_query"] = pool
+
+    # decode with a length per sequence: append the newest token's completed chunk (if any),
+    # route with the lengths, split attention with the lengths
+    qd, vd = dec["q"], dec["v"]
+    lens = wl.ragged_lengths(wd.batch, wd.n_kv, 92, dev)
+    kbar_d = dash.dash_pool_keys(kd, wd.block)
+    ncd = -(-wd.n_kv // wd.block)
+    mask_d = torch.empty((wd.batch, 1, wd.h_kv, -(-ncd // 32)), dtype=torch.int32, device=dev)
+    bias_d = torch.empty((wd.batch, 1, wd.h_kv, ncd), dtype=torch.float32, device=dev)
+    o_d = torch.empty_like(qd)
+    wsb = dash.dash_block_entmax_workspace_bytes(qd.dtype, wd.batch, 1, wd.n_kv - 1, wd.n_kv,
+                                                 wd.h_q, wd.h_kv, wd.head_dim, wd.block)
+    rws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    awb = dash.dash_decode_workspace_bytes(wd.batch, wd.n_kv, wd.h_q, wd.h_kv, wd.head_dim, wd.block)
+    aws = torch.empty(awb, dtype=torch.uint8, device=dev) if awb else None
+
+    def varlen_step():
+        dash.dash_pool_keys_append(kd, lens, kbar_d, wd.block)
+        dash.dash_block_entmax_ex(qd, kbar_d, n_kv=wd.n_kv, block=wd.block, alpha=wd.alpha,
+                                  gamma=wd.gamma, sigma=wd.sigma, h_kv=wd.h_kv, ctx_lens=lens,
+                                  mask=mask_d, bias=bias_d, want_tau=False, workspace=rws)
+        dash.dash_sparse_attn_decode_varlen(qd, kd, vd, lens, mask_d, bias_d, block=wd.block,
+                                            o=o_d, workspace=aws)
+
+    t_eager = _time_ms(varlen_step, reps)
+    # the step's three calls cost more host time than the GPU spends on them, so it is also
+    # captured once in a HIP graph and replayed (no allocation or memset inside the step)
+    t = _time_ms(decode_graph(varlen_step).replay, reps)
+    nbytes = decode_bytes_varlen(mask_d, lens.cpu().numpy(), wd)
+    gbs = nbytes / (t * 1e-3) / 1e9
+    out["varlen_decode"] = {
+        "lengths": "uniform over [64K, 128K] per sequence", "us_per_step": round(t * 1e3, 2),
+        "us_per_step_eager": round(t_eager * 1e3, 2), "tok_per_s": round(wd.batch / (t * 1e-3), 1),
+        "algorithmic_bytes": nbytes, "gb_per_s": round(gbs, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBPS, 4)}}
+
+    # prefill with a window of two blocks (the own block and the one before it always attended)
+    q, v = pre["q"], pre["v"]
+    kbar = dash.dash_pool_keys(k, wp.block)
+    nc = -(-wp.n_kv // wp.block)
+    mask = torch.empty((1, wp.n_q, wp.h_kv, -(-nc // 32)), dtype=torch.int32, device=dev)
+    bias = torch.empty((1, wp.n_q, wp.h_kv, nc), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, wp.n_q, wp.h_q), dtype=torch.float32, device=dev)
+    wsb = dash.dash_block_entmax_workspace_bytes(q.dtype, 1, wp.n_q, 0, wp.n_kv, wp.h_q, wp.h_kv,
+                                                 wp.head_dim, wp.block)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    t_pool = _time_ms(lambda: dash.dash_pool_keys(k, wp.block, kbar=kbar), reps)
+    t_route = _time_ms(lambda: dash.dash_block_entmax_ex(
+        q, kbar, n_kv=wp.n_kv, block=wp.block, alpha=wp.alpha, gamma=wp.gamma, sigma=wp.sigma,
+        h_kv=wp.h_kv, window_blocks=2, mask=mask, bias=bias, want_tau=False, workspace=ws), reps)
+    t_attn = _time_ms(lambda: dash.dash_sparse_attn_prefill(q, k, v, mask, bias, block=wp.block,
+                                                            o=o, lse=lse), reps)
+    pairs, frac = selected_pairs_prefill(mask, wp)
+    flops = 4.0 * wp.head_dim * pairs
+    at = flops / (t_attn * 1e-3) / 1e12
+    out["window2_prefill"] = {
+        "ms": {"pool": round(t_pool, 4), "entmax": round(t_route, 4), "attn": round(t_attn, 4)},
+        "selected_pairs": pairs, "selected_fraction_of_candidates": round(frac, 4),
+        "end_to_end_tflops": round(flops / ((t_pool + t_route + t_attn) * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "mfma", "achieved": round(at, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(at / MFMA_BF16_PEAK_TFLOPS, 4)}}
+    return out
+
+
 # Sources each measured launch is built from: a counter summary taken on other sources is stale.
 KERNEL_SOURCES = {
     "sparse_attn_prefill": ["common.h", "kernels.h", "sparse_attn_dma.hip"],
@@ -333,6 +451,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward leg (gradients of the 32K prefill, timed on their own "
                          "after the step)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the learned-summary-query and streaming legs (timed on their own "
+                         "after the step)")
     ap.add_argument("--random-mask-sweep", action="store_true",
                     help="run the pages' random-selection efficiency sweep instead of the step "
                          "(Hq 32, Hkv 2, N 16-96K, three sparsities); one JSON line per point")
@@ -442,6 +563,7 @@ def main():
         print(f"[bench] {args.only} only: {ms_step:.3f} ms per step", file=sys.stderr, flush=True)
         return
     backward = None if args.no_backward else backward_leg(dash, pre, wp, args)
+    extras = None if args.no_extras else extras_leg(dash, pre, dec, wp, wd, max(1, args.steps))
 
     pairs, frac = selected_pairs_prefill(mask, wp)
     flops = 4.0 * wp.head_dim * pairs
@@ -450,6 +572,8 @@ def main():
     pre_tflops = flops / (t_pre * 1e-3) / 1e12
     attn_tflops = flops / (t_attn * 1e-3) / 1e12
     dbytes, mean_routed = decode_bytes(mask_d, wd)
+    t_dec_graph = _time_ms(decode_graph(lambda: decode_step(lambda name: (None, None))).replay,
+                           args.steps)
     t_dec = timer.mean_ms("decode")
     t_dec_attn = timer.mean_ms("decode_attn")
     dec_gbps = dbytes / (t_dec * 1e-3) / 1e9
@@ -488,6 +612,7 @@ def main():
         "decode": {
             "tok_per_s": round(wd.batch / (t_dec * 1e-3), 1),
             "us_per_step": round(t_dec * 1e3, 2),
+            "us_per_step_graph": round(t_dec_graph * 1e3, 2),
             "us_attn": round(t_dec_attn * 1e3, 2),
             "algorithmic_bytes": dbytes,
             "mean_routed_chunks": round(mean_routed, 3),
@@ -501,6 +626,7 @@ def main():
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None,
         "backward": backward,
+        "extras": extras,
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -186,6 +186,19 @@ def output_gradient(shape, seed: int, dtype=torch.bfloat16, device="cpu") -> tor
     return _randn(tuple(shape), np.random.SeedSequence(seed), device).to(dtype)
 
 
+def summary_query(h_kv: int, head_dim: int, seed: int, device="cpu", scale: float = 0.3) -> torch.Tensor:
+    """A seeded learned summary query qbar [Hkv, D] fp32 ~ N(0, scale^2) for Stage 0's local
+    attention over each chunk."""
+    return _randn((h_kv, head_dim), np.random.SeedSequence(seed), device) * scale
+
+
+def ragged_lengths(batch: int, n_cap: int, seed: int, device="cpu") -> torch.Tensor:
+    """Seeded per-sequence context lengths int32 [B], uniform over [n_cap / 2, n_cap]."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    lens = rng.integers(n_cap // 2, n_cap + 1, size=batch)
+    return torch.from_numpy(lens.astype(np.int32)).to(device)
+
+
 def random_selection(batch: int, n_q: int, q_pos0: int, n_kv: int, h_kv: int, block: int,
                      sparsity: float, seed: int, device="cpu", bias_std: float = 0.0,
                      slab: int = 4096) -> tuple[torch.Tensor, torch.Tensor]:
