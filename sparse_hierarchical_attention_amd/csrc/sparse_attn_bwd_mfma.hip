@@ -215,13 +215,18 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
             // two 16-key k-steps of dQ^T += K^T dS^T that this M-tile feeds)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
+                // the M-tile's K and V rows are read before the products (the reads overlap)
+                bw_bf16x8 ka[D / 16], va[D / 16];
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    ka[ks] = *reinterpret_cast<const bw_bf16x8*>(&Ks[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
+                    va[ks] = *reinterpret_cast<const bw_bf16x8*>(&Vs[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
+                }
                 bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks) {
-                    const bw_bf16x8 a = *reinterpret_cast<const bw_bf16x8*>(&Ks[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-                    const bw_bf16x8 av = *reinterpret_cast<const bw_bf16x8*>(&Vs[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, df[ks], dp, 0, 0, 0);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
                 }
                 // p = exp(scale s + d - lse) on the row's selected, causal keys; 0 elsewhere
 #pragma unroll
@@ -237,6 +242,11 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr) dsum = fmaf(s[rr], dp[rr], dsum);
                 } else {
+                    bw_bf16x8 ktr[2][DT];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) ktr[h2][dt] = tr_operand<LS>(Ks[buf], 2 * mt + h2, dt, lane);
                     bw_bf16x8 dsf[2];
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr) {
@@ -248,10 +258,8 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) {
-                            const bw_bf16x8 a = tr_operand<LS>(Ks[buf], 2 * mt + h2, dt, lane);
-                            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[h2], acc[dt], 0, 0, 0);
-                        }
+                        for (int dt = 0; dt < DT; ++dt)
+                            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr[h2][dt], dsf[h2], acc[dt], 0, 0, 0);
                 }
             }
             if (pass == 1) {
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
     static_assert(PIECES % NTH == 0 && NTH >= RT, "tile does not split over the threads");
     __shared__ __align__(16) bf16_t Qs[RT * LS];
     __shared__ __align__(16) bf16_t Ds[RT * LS];
-    __shared__ float meta[4][RT];             // lse * log2(e) - d log2(e), Delta, token, valid
+    __shared__ float4 meta[RT];               // per row: lse log2(e) - d log2(e), Delta, token, valid
     __shared__ int list[NTH];
     __shared__ int wtot[NWV];
 
@@ -381,17 +389,27 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
         uint4 gq[NP], gd[NP];
         float g_base = 0.f, g_dl = 0.f, g_tok = -1.f, g_ok = 0.f;
         auto gather = [&](int tl0) {
+            // rows past the list read its first token (tl0 < total) and are zeroed after: no
+            // branches, so every load is issued back to back
+            int tok[NP];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int tl = tl0 + (tid + i * NTH) / (D / 8) / GQ;
+                tok[i] = list[tl < total ? tl : 0];
+            }
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
                 const int e = tid + i * NTH;
                 const int m = e / (D / 8), d8 = e % (D / 8);
-                const int tl = tl0 + m / GQ;
-                gq[i] = make_uint4(0, 0, 0, 0);
-                gd[i] = make_uint4(0, 0, 0, 0);
-                if (tl < total) {
-                    const int64_t off = ((((int64_t)b * n + list[tl]) * p.h_q) + r * GQ + m % GQ) * D + 8 * d8;
-                    gq[i] = *reinterpret_cast<const uint4*>(q + off);
-                    gd[i] = *reinterpret_cast<const uint4*>(dout + off);
+                const int64_t off = ((((int64_t)b * n + tok[i]) * p.h_q) + r * GQ + m % GQ) * D + 8 * d8;
+                gq[i] = *reinterpret_cast<const uint4*>(q + off);
+                gd[i] = *reinterpret_cast<const uint4*>(dout + off);
+            }
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                if (tl0 + (tid + i * NTH) / (D / 8) / GQ >= total) {
+                    gq[i] = make_uint4(0, 0, 0, 0);
+                    gd[i] = make_uint4(0, 0, 0, 0);
                 }
             }
             if (tid < RT) {
@@ -418,10 +436,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
                 *reinterpret_cast<uint4*>(&Ds[m * LS + 8 * d8]) = gd[i];
             }
             if (tid < RT) {
-                meta[0][tid] = g_base;
-                meta[1][tid] = g_dl;
-                meta[2][tid] = g_tok;
-                meta[3][tid] = g_ok;
+                meta[tid] = make_float4(g_base, g_dl, g_tok, g_ok);
             }
         };
         if (total > 0) gather(0);
@@ -435,21 +450,38 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
             // dV^T += dO^T P and dK^T += Q^T dS that these rows feed
 #pragma unroll
             for (int rm = 0; rm < RM; ++rm) {
+                // every LDS operand of this M-tile is read before the products that use it, so
+                // that the reads overlap one another instead of each waiting in turn
+                bw_bf16x8 aq[D / 16], ad[D / 16];
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    aq[ks] = *reinterpret_cast<const bw_bf16x8*>(&Qs[(32 * rm + j) * LS + 16 * ks + 8 * G]);
+                    ad[ks] = *reinterpret_cast<const bw_bf16x8*>(&Ds[(32 * rm + j) * LS + 16 * ks + 8 * G]);
+                }
+                float4 mrow[16];
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) mrow[rr] = meta[32 * rm + 8 * (rr >> 2) + 4 * G + (rr & 3)];
                 bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks) {
-                    const bw_bf16x8 aq = *reinterpret_cast<const bw_bf16x8*>(&Qs[(32 * rm + j) * LS + 16 * ks + 8 * G]);
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s, 0, 0, 0);
-                    const bw_bf16x8 ad = *reinterpret_cast<const bw_bf16x8*>(&Ds[(32 * rm + j) * LS + 16 * ks + 8 * G]);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], dp, 0, 0, 0);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], kf[ks], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[ks], vf[ks], dp, 0, 0, 0);
                 }
+                bw_bf16x8 trd[2][DT], trq[2][DT];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        trd[kb][dt] = tr_operand<LS>(Ds, 2 * rm + kb, dt, lane);
+                        trq[kb][dt] = tr_operand<LS>(Qs, 2 * rm + kb, dt, lane);
+                    }
                 bw_bf16x8 pf[2], dsf[2];
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
-                    const int m = 32 * rm + 8 * (rr >> 2) + 4 * G + (rr & 3);
-                    const bool ok = meta[3][m] != 0.f && key_ok && (float)key <= meta[2][m];
-                    const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, -meta[0][m])) : 0.f;
-                    const float ds = pe * (dp[rr] - meta[1][m]);
+                    const float4 mr = mrow[rr];  // (base, Delta, token, valid)
+                    const bool ok = mr.w != 0.f && key_ok && (float)key <= mr.z;
+                    const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, -mr.x)) : 0.f;
+                    const float ds = pe * (dp[rr] - mr.y);
                     pf[rr >> 3][rr & 7] = (__bf16)pe;
                     dsf[rr >> 3][rr & 7] = (__bf16)ds;
                 }
@@ -457,10 +489,8 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
-                        const bw_bf16x8 ad = tr_operand<LS>(Ds, 2 * rm + kb, dt, lane);
-                        accv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, pf[kb], accv[dt], 0, 0, 0);
-                        const bw_bf16x8 aq = tr_operand<LS>(Qs, 2 * rm + kb, dt, lane);
-                        acck[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[kb], acck[dt], 0, 0, 0);
+                        accv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trd[kb][dt], pf[kb], accv[dt], 0, 0, 0);
+                        acck[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trq[kb][dt], dsf[kb], acck[dt], 0, 0, 0);
                     }
             }
             __syncthreads();  // Qs, Ds and meta are refilled by the next tile
