@@ -32,6 +32,8 @@ namespace {
 constexpr int kRbThreads = 256;  // threads per workgroup (four waves)
 constexpr int kRbWaves = kRbThreads / 64;
 constexpr int kRbMaxChunks = 8192;
+constexpr int kColThreads = 512;  // threads per workgroup of the column kernel (eight waves)
+constexpr int kColWaves = kColThreads / 64;
 
 // [t]_+^(e - 1) = p^(2 - alpha) on the support (t = x - tau > 0), 0 off it.
 template <int KIND>
@@ -279,18 +281,31 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_row_kernel(
 }
 
 template <typename T, int D, int GQ, int KIND>
-__global__ __launch_bounds__(kRbThreads) void route_bwd_col_kernel(
+__global__ __launch_bounds__(kColThreads) void route_bwd_col_kernel(
     const T* __restrict__ q, const float* __restrict__ kbar, const float* __restrict__ tau,
     const uint32_t* __restrict__ mask, const float* __restrict__ dbias,
     const float* __restrict__ mean_ws, const float* __restrict__ rho_ws, float* __restrict__ dk,
     RouteParams p) {
     constexpr int LPK = D / 4;
     constexpr int RPW = 64 / LPK;
-    constexpr int kScan = kRbThreads;  // rows examined per block of the scan
+    constexpr int kScan = kColThreads;  // rows examined per block of the scan
     __shared__ int list[kScan];
-    __shared__ int wtot[kRbWaves];
-    __shared__ float dkred[kRbWaves][D];
-    const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+    __shared__ int wtot[kColWaves];
+    __shared__ float dkred[kColWaves][D];
+    // XCD-aware order (index x runs on XCD x % 8): all chunks of one (sequence, group) on one
+    // XCD, so that the workgroups gathering the same query rows share its L2
+    int c, gr;
+    {
+        const int bh = p.batch * p.h_kv, x = blockIdx.x;
+        if (bh % 8 == 0) {
+            gr = (x % 8) + 8 * ((x / 8) / p.tc);
+            c = (x / 8) % p.tc;
+        } else {
+            gr = x / p.tc;
+            c = x % p.tc;
+        }
+    }
+    const int b = gr / p.h_kv, r = gr % p.h_kv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int seg = lane / LPK, li = lane % LPK;
     const float coef = (p.alpha - 1.0f) * p.gamma / sqrtf((float)D);
@@ -301,8 +316,12 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_col_kernel(
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 
     // rows whose routing candidates reach chunk c: c < route_cands(pos), i.e. pos / Bc > c + win
+    // the rows from t_first on, in blocks taken from the last one down: the workgroups of one
+    // (sequence, group) start together at the end of the sequence and walk down in step
     const int t_first = max(0, (c + p.win + 1) * p.block - p.q_pos0);
-    for (int t0 = t_first; t0 < p.n_q; t0 += kScan) {
+    const int nblk = t_first < p.n_q ? div_up(p.n_q - t_first, kScan) : 0;
+    for (int bi = nblk - 1; bi >= 0; --bi) {
+        const int t0 = t_first + bi * kScan;
         const int t = t0 + tid;
         bool sel = false;
         if (t < p.n_q) {
@@ -315,13 +334,13 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_col_kernel(
         __syncthreads();
         int before = 0, total = 0;
 #pragma unroll
-        for (int i = 0; i < kRbWaves; ++i) {
+        for (int i = 0; i < kColWaves; ++i) {
             before += i < wave ? wtot[i] : 0;
             total += wtot[i];
         }
         if (sel) list[before + __popcll(bal & ((1ull << lane) - 1ull))] = t;
         __syncthreads();
-        for (int j0 = wave * RPW; j0 < total; j0 += kRbWaves * RPW) {
+        for (int j0 = wave * RPW; j0 < total; j0 += kColWaves * RPW) {
             const int j = j0 + seg;
             const bool valid = j < total;
             const int tt = list[valid ? j : 0];
@@ -357,11 +376,11 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_col_kernel(
     __syncthreads();
     // dk_j += coef dkbar_c / Bc for the chunk's keys (complete chunk: Bc keys)
     const float f = coef / (float)p.block;
-    for (int idx = tid; idx < p.block * D; idx += kRbThreads) {
+    for (int idx = tid; idx < p.block * D; idx += kColThreads) {
         const int j = idx / D, d = idx % D;
         float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < kRbWaves; ++i) s += dkred[i][d];
+        for (int i = 0; i < kColWaves; ++i) s += dkred[i][d];
         dk[(((int64_t)b * p.n_kv + (int64_t)c * p.block + j) * p.h_kv + r) * D + d] += f * s;
     }
 }
@@ -378,8 +397,8 @@ static void launch_rb_k(const void* q, const float* kbar, const float* tau, cons
                        dim3(kRbThreads), 0, st, static_cast<const T*>(q), kbar, tau, mask, dbias,
                        dq, mean_ws, rho_ws, p);
     if (p.tc > 0)
-        hipLaunchKernelGGL((route_bwd_col_kernel<T, D, GQ, KIND>), dim3(p.tc, p.h_kv, p.batch),
-                           dim3(kRbThreads), 0, st, static_cast<const T*>(q), kbar, tau, mask,
+        hipLaunchKernelGGL((route_bwd_col_kernel<T, D, GQ, KIND>), dim3(p.tc * p.h_kv * p.batch),
+                           dim3(kColThreads), 0, st, static_cast<const T*>(q), kbar, tau, mask,
                            dbias, mean_ws, rho_ws, dk, p);
 }
 
