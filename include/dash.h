@@ -177,6 +177,23 @@ dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void*
                                        int head_dim, int block, float scale, hipStream_t stream);
 
 /*
+ * Stage 2 for a block of query rows [DA §3.4 Prop. 1]: as dash_sparse_attn_prefill for the rows
+ * at positions q_pos0 .. q_pos0 + n_q - 1 of each sequence of n_kv tokens (0 <= q_pos0,
+ * q_pos0 + n_q <= n_kv). q, o [B, n_q, H_q, D], lse [B, n_q, H_q], mask and bias [B, n_q, ...]
+ * hold those rows (as dash_block_entmax writes them for the same n_q and q_pos0); k, v
+ * [B, n_kv, H_kv, D]. The query at position p attends its routed chunks and the keys of its own
+ * chunk up to p. Splitting the rows into blocks gives each row the output of one call over all
+ * rows up to the last bit (the row tiling decides whether an exponent is one fused multiply-add or
+ * two), so a caller can route one block while attending the previous one.
+ */
+dash_status_t dash_sparse_attn_prefill_ex(const void* q, const void* k, const void* v,
+                                          dash_dtype_t dt, const uint32_t* mask,
+                                          const float* bias, void* o, float* lse, int batch,
+                                          int n_q, int q_pos0, int n_kv, int h_q, int h_kv,
+                                          int head_dim, int block, float scale,
+                                          hipStream_t stream);
+
+/*
  * Stage 2 backward for prefill [DA Prop. 1, differentiated], the selection held fixed: with the
  * forward's lse, p_j = exp(scale <q, k_j> + d_c(j) - lse) over the keys the row attends to,
  * dp_j = <dout, v_j> and ds_j = p_j (dp_j - <dout, o>), where <dout, o> = sum_j p_j dp_j is

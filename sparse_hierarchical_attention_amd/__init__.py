@@ -20,6 +20,7 @@ __all__ = [
     "DashError", "lib", "library_path",
     "dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append", "dash_block_entmax",
     "dash_block_entmax_ex", "dash_block_entmax_workspace_bytes", "dash_sparse_attn_prefill",
+    "dash_sparse_attn_prefill_ex",
     "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
     "dash_sparse_attn_backward_workspace_bytes", "dash_sparse_attn_prefill_backward",
     "dash_block_entmax_backward_workspace_bytes", "dash_block_entmax_backward",
@@ -67,6 +68,8 @@ def lib():
                                            vp, vp, vp, sz, vp]
         L.dash_sparse_attn_prefill.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i,
                                                f, vp]
+        L.dash_sparse_attn_prefill_ex.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i,
+                                                  i, i, f, vp]
         L.dash_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.dash_decode_workspace_bytes.restype = sz
         L.dash_sparse_attn_decode.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, f,
@@ -84,7 +87,7 @@ def lib():
         L.dash_block_entmax_backward.restype = i
         for fn in ("dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append",
                    "dash_block_entmax", "dash_block_entmax_ex", "dash_sparse_attn_prefill",
-                   "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
+                   "dash_sparse_attn_prefill_ex", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
                    "dash_sparse_attn_prefill_backward"):
             getattr(L, fn).restype = i
         _lib = L
@@ -263,21 +266,24 @@ def dash_block_entmax(q: torch.Tensor, kbar: torch.Tensor, *, n_kv: int, block: 
 def dash_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              mask: torch.Tensor, bias: torch.Tensor, *, block: int,
                              scale: float | None = None, o: torch.Tensor | None = None,
-                             lse: torch.Tensor | None = None, want_lse: bool = True):
-    """Stage 2 prefill: -> (o [B, n, Hq, D] in q's dtype, lse fp32 [B, n, Hq] or None)."""
+                             lse: torch.Tensor | None = None, want_lse: bool = True,
+                             q_pos0: int = 0):
+    """Stage 2 prefill: -> (o [B, n_q, Hq, D] in q's dtype, lse fp32 [B, n_q, Hq] or None).
+    q holds the rows at positions q_pos0 .. q_pos0 + n_q - 1 of sequences of k.shape[1] tokens
+    (all of them by default); mask and bias hold the same rows."""
     _f32(bias=bias, lse=lse)
-    b, n, hq, d = q.shape
-    hkv = k.shape[2]
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:
-        lse = torch.empty((b, n, hq), dtype=torch.float32, device=q.device)
+        lse = torch.empty((b, n_q, hq), dtype=torch.float32, device=q.device)
     dev = _dev(q, k, v, mask, bias, o, lse)
-    _check(lib().dash_sparse_attn_prefill(
+    _check(lib().dash_sparse_attn_prefill_ex(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(mask), _ptr(bias), _ptr(o), _ptr(lse),
-        b, n, hq, hkv, d, block, float(scale), _stream(dev)))
+        b, n_q, int(q_pos0), n_kv, hq, hkv, d, block, float(scale), _stream(dev)))
     return o, lse
 
 

@@ -82,6 +82,25 @@ dash::AttnParams attn_params(int batch, int n_q, int q_pos0, int n_kv, int h_q, 
 }
 
 // the shared bodies of the entry points with and without per-sequence lengths (defined below)
+// Stage 2 prefill over rows q_pos0 .. q_pos0 + n_q - 1 of each sequence (all rows: 0, n_kv).
+dash_status_t prefill_call(const char* fn, const void* q, const void* k, const void* v,
+                           dash_dtype_t dt, const uint32_t* mask, const float* bias, void* o,
+                           float* lse, int batch, int n_q, int q_pos0, int n_kv, int h_q,
+                           int h_kv, int head_dim, int block, float scale, hipStream_t stream) {
+    dash_status_t s = check_shape(fn, dt, batch, n_kv, h_q, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (n_q <= 0 || q_pos0 < 0 || (int64_t)q_pos0 + n_q > n_kv)
+        return fail(DASH_ERR_INVALID, "%s: need n_q > 0 and 0 <= q_pos0, q_pos0 + n_q <= n_kv (n_q=%d q_pos0=%d n_kv=%d)",
+                    fn, n_q, q_pos0, n_kv);
+    if (!(scale > 0.0f) || isinf(scale)) return fail(DASH_ERR_INVALID, "%s: scale=%g must be positive and finite", fn, scale);
+    if (!q || !k || !v || !mask || !bias || !o) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    // bf16 head dim 128 addresses one sequence's keys (and values) with 32-bit byte offsets
+    if (dt == DASH_BF16 && head_dim == 128 && (int64_t)n_kv * h_kv * head_dim * 2 > INT32_MAX)
+        return fail(DASH_ERR_UNSUPPORTED, "%s: one sequence's keys (n * h_kv * head_dim bf16) exceed 2 GiB", fn);
+    dash::AttnParams p = attn_params(batch, n_q, q_pos0, n_kv, h_q, h_kv, head_dim, block, scale);
+    return hip_status(dash::launch_attn_prefill(q, k, v, dt, mask, bias, o, lse, p, stream), fn);
+}
+
 dash_status_t route_call(const char* fn, const void* q, dash_dtype_t dt, const float* kbar,
                          const int32_t* ctx_lens, int batch, int n_q, int q_pos0, int n_kv,
                          int h_q, int h_kv, int head_dim, int block, float alpha, float gamma,
@@ -212,20 +231,22 @@ dash_status_t route_call(const char* fn, const void* q, dash_dtype_t dt, const f
 
 extern "C" {
 
+dash_status_t dash_sparse_attn_prefill_ex(const void* q, const void* k, const void* v,
+                                          dash_dtype_t dt, const uint32_t* mask,
+                                          const float* bias, void* o, float* lse, int batch,
+                                          int n_q, int q_pos0, int n_kv, int h_q, int h_kv,
+                                          int head_dim, int block, float scale,
+                                          hipStream_t stream) {
+    return prefill_call("dash_sparse_attn_prefill_ex", q, k, v, dt, mask, bias, o, lse, batch, n_q,
+                        q_pos0, n_kv, h_q, h_kv, head_dim, block, scale, stream);
+}
+
 dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                        dash_dtype_t dt, const uint32_t* mask, const float* bias,
                                        void* o, float* lse, int batch, int n, int h_q, int h_kv,
                                        int head_dim, int block, float scale, hipStream_t stream) {
-    const char* fn = "dash_sparse_attn_prefill";
-    dash_status_t s = check_shape(fn, dt, batch, n, h_q, h_kv, head_dim, block);
-    if (s != DASH_OK) return s;
-    if (!(scale > 0.0f) || isinf(scale)) return fail(DASH_ERR_INVALID, "%s: scale=%g must be positive and finite", fn, scale);
-    if (!q || !k || !v || !mask || !bias || !o) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
-    // bf16 head dim 128 addresses one sequence's keys (and values) with 32-bit byte offsets
-    if (dt == DASH_BF16 && head_dim == 128 && (int64_t)n * h_kv * head_dim * 2 > INT32_MAX)
-        return fail(DASH_ERR_UNSUPPORTED, "%s: one sequence's keys (n * h_kv * head_dim bf16) exceed 2 GiB", fn);
-    dash::AttnParams p = attn_params(batch, n, 0, n, h_q, h_kv, head_dim, block, scale);
-    return hip_status(dash::launch_attn_prefill(q, k, v, dt, mask, bias, o, lse, p, stream), fn);
+    return prefill_call("dash_sparse_attn_prefill", q, k, v, dt, mask, bias, o, lse, batch, n, 0, n,
+                        h_q, h_kv, head_dim, block, scale, stream);
 }
 
 size_t dash_sparse_attn_backward_workspace_bytes(int batch, int n, int h_q) {

@@ -94,9 +94,9 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
     const int tile = n_tiles - 1 - blockIdx.x / (p.batch * p.h_kv);
     const int b = gr / p.h_kv, r = gr % p.h_kv;
     const int n = p.n_kv;
-    const int tile0 = tile * T;
-    const int tile_end = min(tile0 + T, n);
-    const int c_first = tile0 / BLK, c_last = (tile_end - 1) / BLK;
+    const int tile0 = tile * T;                        // first row of the tile among the n_q rows
+    const int tile_end = min(tile0 + T, p.n_q);
+    const int c_first = (p.q_pos0 + tile0) / BLK, c_last = (p.q_pos0 + tile_end - 1) / BLK;
     const int nwt = c_last / 32 + 1;
 
     const int tid = threadIdx.x;
@@ -104,11 +104,12 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
     const int j = lane & 31, G = lane >> 5;
     const int row = wave * 32 + j;
     const int tok = row / GQ, hl = row % GQ;
-    const int pos = tile0 + tok;
-    const bool valid = pos < n;
+    const int rowi = tile0 + tok;                       // the row among the n_q rows
+    const int pos = p.q_pos0 + rowi;                    // its token position
+    const bool valid = rowi < p.n_q;
     const int cpos = pos / BLK;
-    const int64_t qrow = (int64_t)b * p.n_q + pos;
-    const int64_t qrow_c = (int64_t)b * p.n_q + min(pos, n - 1);  // rows past the end read row n - 1
+    const int64_t qrow = (int64_t)b * p.n_q + rowi;
+    const int64_t qrow_c = (int64_t)b * p.n_q + min(rowi, p.n_q - 1);  // rows past the end read the last
     const uint32_t* mrow = mask + (qrow_c * p.h_kv + r) * p.nw;
     const float* brow = bias + (qrow_c * p.h_kv + r) * p.nc;
 
@@ -118,8 +119,8 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
     for (int idx = tid; idx < T * nwt; idx += kThreads) {
         const int t = idx / nwt, w = idx % nwt;
         const int ps = tile0 + t;
-        if (ps >= n) continue;
-        const int hi = ps / BLK - 32 * w;
+        if (ps >= p.n_q) continue;
+        const int hi = (p.q_pos0 + ps) / BLK - 32 * w;
         if (hi < 0) continue;
         uint32_t word = mask[(((int64_t)b * p.n_q + ps) * p.h_kv + r) * p.nw + w];
         if (hi < 31) word &= (2u << hi) - 1u;
@@ -377,7 +378,7 @@ static void launch_dma_blk(const void* q, const void* k, const void* v, const ui
                            const float* bias, void* o, float* lse, const AttnParams& p,
                            hipStream_t st) {
     const int T = kRows / p.g;
-    const int n_tiles = div_up(p.n_kv, T);
+    const int n_tiles = div_up(p.n_q, T);
     dim3 grid(p.batch * p.h_kv * n_tiles);
 #define DASH_DMA(GG)                                                                        \
     hipLaunchKernelGGL((attn_dma_kernel<BLK, GG>), grid, dim3(kThreads), 0, st,             \

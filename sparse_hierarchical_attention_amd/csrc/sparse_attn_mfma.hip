@@ -74,9 +74,9 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
     const int tile = n_tiles - 1 - blockIdx.x / (p.batch * p.h_kv);
     const int b = gr / p.h_kv, r = gr % p.h_kv;
     const int n = p.n_kv;
-    const int tile0 = tile * T;
-    const int tile_end = min(tile0 + T, n);
-    const int c_first = tile0 / BLK, c_last = (tile_end - 1) / BLK;
+    const int tile0 = tile * T;                        // first row of the tile among the n_q rows
+    const int tile_end = min(tile0 + T, p.n_q);
+    const int c_first = (p.q_pos0 + tile0) / BLK, c_last = (p.q_pos0 + tile_end - 1) / BLK;
     const int nwt = c_last / 32 + 1;
 
     const int tid = threadIdx.x;
@@ -84,10 +84,11 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
     const int j = lane & 31, G = lane >> 5;
     const int row = wave * 32 + j;
     const int tok = row / GQ, hl = row % GQ;
-    const int pos = tile0 + tok;
-    const bool valid = pos < n;
+    const int rowi = tile0 + tok;                       // the row among the n_q rows
+    const int pos = p.q_pos0 + rowi;                    // its token position
+    const bool valid = rowi < p.n_q;
     const int cpos = pos / BLK;
-    const int64_t qrow = (int64_t)b * p.n_q + pos;
+    const int64_t qrow = (int64_t)b * p.n_q + rowi;
     const uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
     const float* brow = bias + (qrow * p.h_kv + r) * p.nc;
 
@@ -97,8 +98,8 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
     for (int idx = tid; idx < T * nwt; idx += kMfmaThreads) {
         const int t = idx / nwt, w = idx % nwt;
         const int ps = tile0 + t;
-        if (ps >= n) continue;
-        const int hi = ps / BLK - 32 * w;
+        if (ps >= p.n_q) continue;
+        const int hi = (p.q_pos0 + ps) / BLK - 32 * w;
         if (hi < 0) continue;
         uint32_t word = mask[(((int64_t)b * p.n_q + ps) * p.h_kv + r) * p.nw + w];
         if (hi < 31) word &= (2u << hi) - 1u;
@@ -297,7 +298,7 @@ static void launch_mfma_blk(const void* q, const void* k, const void* v, const u
                             const float* bias, void* o, float* lse, const AttnParams& p,
                             hipStream_t st) {
     const int T = kMfmaRows / p.g;
-    const int n_tiles = div_up(p.n_kv, T);
+    const int n_tiles = div_up(p.n_q, T);
     dim3 grid(p.batch * p.h_kv * n_tiles);
 #define DASH_MFMA(GG)                                                                       \
     hipLaunchKernelGGL((attn_mfma_kernel<D, BLK, GG>), grid, dim3(kMfmaThreads), 0, st,     \
