@@ -62,6 +62,18 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const bf16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)(p));
 }
 
+// lanes l and l ^ 32 hold the two halves of one query row's keys; v_permlane32_swap hands each
+// lane its partner's value without a trip through LDS (every lane gets the same pair, so the
+// result is the same in both halves)
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace
 
 template <int BLK, int GQ>
@@ -223,7 +235,6 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
         dma(Kn, Vn, c_ld, c_nx >= 0 ? sub_nx : sub);
         // a wave none of whose rows selected the chunk has nothing to add (every score -inf)
         if (__any(sel)) {
-            const float sc = sel ? qk_scale : 0.f;
             const float off = sel ? (c == cpos ? 0.f : dcur * kLog2e) : -INFINITY;
             const bool causal = c >= c_first;  // some row's own chunk: mask keys past each row
 
@@ -255,31 +266,23 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
                 }
             }
             __builtin_amdgcn_s_setprio(0);
-            // row maximum of x = s * sc + off (sc >= 0)
-            float xmax;
+            // keys past the row's own position score -inf; x = s * scale log2(e) + off is then -inf
+            // too (scale > 0), as it is for every key of a row that did not select the chunk
             if (causal) {
     #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
     #pragma unroll
                     for (int rr = 0; rr < 16; ++rr) {
                         const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
-                        const float x = fmaf(s[mt][rr], sc, off);
-                        s[mt][rr] = key > pos ? -INFINITY : x;
+                        if (key > pos) s[mt][rr] = -INFINITY;
                     }
-                xmax = -INFINITY;
-    #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-    #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) xmax = fmaxf(xmax, s[mt][rr]);
-            } else {
-                float smax = -INFINITY;
-    #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-    #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) smax = fmaxf(smax, s[mt][rr]);
-                xmax = sel ? fmaf(smax, sc, off) : -INFINITY;
             }
-            xmax = fmaxf(xmax, __shfl_xor(xmax, 32, kWave));
+            float smax = -INFINITY;
+    #pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+    #pragma unroll
+                for (int rr = 0; rr < 16; ++rr) smax = fmaxf(smax, s[mt][rr]);
+            const float xmax = fmaf(halves_max(smax), qk_scale, off);
             // raise the running maximum only when needed (rare once a row has seen its peak)
             const bool raise = xmax > m_used + kLazyMax;
             if (__any(raise)) {
@@ -290,30 +293,18 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
                 for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
                 m_used = m_new;
             }
-            const float m_ref = m_used == -INFINITY ? 0.f : m_used;
-            float rsum = 0.f;
+            // p = exp2(x - m) as one FMA and exp2; the row sum stays per lane (this half's keys)
+            // until the end, since both halves scale it by the same factors
+            const float off_m = off - (m_used == -INFINITY ? 0.f : m_used);
             bf16x8 pf[KSTEP];
-            if (causal) {
     #pragma unroll
-                for (int ks = 0; ks < KSTEP; ++ks)
+            for (int ks = 0; ks < KSTEP; ++ks)
     #pragma unroll
-                    for (int vv = 0; vv < 8; ++vv) {
-                        const float pe = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + vv] - m_ref);
-                        rsum += pe;
-                        pf[ks][vv] = (__bf16)pe;
-                    }
-            } else {
-                const float off_m = off - m_ref;
-    #pragma unroll
-                for (int ks = 0; ks < KSTEP; ++ks)
-    #pragma unroll
-                    for (int vv = 0; vv < 8; ++vv) {
-                        const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + vv], sc, off_m));
-                        rsum += pe;
-                        pf[ks][vv] = (__bf16)pe;
-                    }
-            }
-            l_run += rsum + __shfl_xor(rsum, 32, kWave);
+                for (int vv = 0; vv < 8; ++vv) {
+                    const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + vv], qk_scale, off_m));
+                    l_run += pe;
+                    pf[ks][vv] = (__bf16)pe;
+                }
 
             // O^T += V^T P^T, V^T through transposing reads issued one k-step ahead of their MFMAs
             __builtin_amdgcn_s_setprio(1);
@@ -356,6 +347,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
         if (c < 0) break;
     }
 
+    l_run = halves_sum(l_run);
     if (!valid) return;
     const float inv_l = 1.0f / l_run;
     bf16_t* orow = o + (qrow * p.h_q + r * GQ + hl) * kD;
