@@ -170,7 +170,13 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
 
     // LDS element offsets of this lane's reads: K piece 2 ks + G of row j (+ 32 mt rows), and the
     // transposing V reads of rows v_key (+ 8) at dims 32 dt + v_dim (+ 16 ks rows)
-    const int kl_base = (j % NB) * kKBlock + (j / NB) * kD + 8 * G;   // + mt (32 / NB) kD + 16 ks
+    // K rows in odd slots of a block hold their 16-byte pieces in the order piece ^ 8, so that the
+    // 16 rows one 16-lane group reads (two slots of eight blocks) cover all 64 banks: reads of
+    // pieces 0-7 (k-steps 0-3) start at kl_lo, pieces 8-15 at kl_hi, each plus a constant offset
+    static_assert(NB == 8 && MT == 1, "tiles of 32 keys");
+    const int kl_base = (j % NB) * kKBlock + (j / NB) * kD + 8 * G;   // + 16 ks
+    const int k_odd = (j / NB) & 1;
+    const int kl_lo = kl_base + 64 * k_odd, kl_hi = kl_base - 64 * k_odd;
     int vl_base[2];                                                    // + ks (16 / NB) kD + 32 dt
     {
         const int grp = lane >> 4, kl = lane & 15;
@@ -193,18 +199,20 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
     const uint32_t span = (uint32_t)((n - 1) * kv_row_stride + kD) * 2u;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, (int)span, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, (int)span, 0x00020000);
-    uint32_t loff[NLD];
+    uint32_t loff[NLD], loff_k[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
         const int rr = NLD * wave + i + NB * (lane >> 4);
         loff[i] = rr * row_bytes + (uint32_t)((lane & 15) * 16);
+        // K: the slot's pieces swizzled (lane >> 4 is the row's slot in its block)
+        loff_k[i] = rr * row_bytes + (uint32_t)(((lane & 15) ^ (8 * ((lane >> 4) & 1))) * 16);
     }
     auto dma = [&](bf16_t* Kd, bf16_t* Vd, int c, int sub) __attribute__((always_inline)) {
         const uint32_t soff = (uint32_t)(c * BLK + sub * KT) * row_bytes;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int blk = NLD * wave + i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(Kd + blk * kKBlock), 16, loff[i], soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(Kd + blk * kKBlock), 16, loff_k[i], soff, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(Vd + blk * kVBlock), 16, loff[i], soff, 0, 0);
         }
     };
@@ -253,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
                 auto kread = [&](int ks, bf16x8 (&dst)[MT]) __attribute__((always_inline)) {
     #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        dst[mt] = *reinterpret_cast<const bf16x8*>(Kc + kl_base + mt * (32 / NB) * kD + 16 * ks);
+                        dst[mt] = *reinterpret_cast<const bf16x8*>(Kc + (ks < 4 ? kl_lo : kl_hi) + 16 * ks);
                 };
                 kread(0, ka[0]);
                 kread(1, ka[1]);
