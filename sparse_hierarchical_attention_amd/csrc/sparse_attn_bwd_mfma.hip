@@ -106,8 +106,16 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
     const bool valid = pos < n;
     const int cpos = pos / BLK;
     const int64_t qrow = (int64_t)b * n + pos;
-    const uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
-    const float* brow = bias + (qrow * p.h_kv + r) * p.nc;
+    const int64_t qrow_c = (int64_t)b * n + min(pos, n - 1);  // rows past the end read the last
+    const uint32_t* mrow = mask + (qrow_c * p.h_kv + r) * p.nw;
+    const float* brow = bias + (qrow_c * p.h_kv + r) * p.nc;
+    // this row's mask word and bias for a chunk, loaded without a branch (chunk clamped into
+    // range) one tile ahead of their use, so that they have landed by then
+    auto row_view = [&](int cc, uint32_t& mw, float& dv) {
+        const int cq = valid ? min(cc, cpos) : 0;
+        mw = mrow[cq >> 5];
+        dv = brow[cq];
+    };
 
     // dL/dd entries no selected chunk writes: chunks at or past each token's own, and unselected
     if (dbias) {
@@ -198,6 +206,9 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
 
     for (int pass = 0; pass < 2; ++pass) {
         int c = next_chunk(-1), sub = 0;  // every tile has at least its own chunk
+        uint32_t mw;
+        float dv;
+        row_view(c, mw, dv);
         fetch(c, 0);
         stash(0);
         __syncthreads();
@@ -206,60 +217,64 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
             const int c_nx = sub + 1 < NSUB ? c : next_chunk(c);
             const int sub_nx = sub + 1 < NSUB ? sub + 1 : 0;
             if (c_nx >= 0) fetch(c_nx, sub_nx);
-            bool sel = false;
-            if (valid && c <= cpos) sel = c == cpos || ((mrow[c >> 5] >> (c & 31)) & 1u);
-            const float off = sel ? (c == cpos ? 0.f : brow[c] * kBwLog2e) - lse2 : -INFINITY;
+            uint32_t mw_nx;
+            float dv_nx;
+            row_view(c_nx >= 0 ? c_nx : c, mw_nx, dv_nx);
+            const bool sel = valid && c <= cpos && (c == cpos || ((mw >> (c & 31)) & 1u));
+            const float off = sel ? (c == cpos ? 0.f : dv * kBwLog2e) - lse2 : -INFINITY;
             const bool causal = c >= c_first;
-
-            // per 32-key M-tile: S^T = K Q^T, dP^T = V dO^T, then p (and in pass 2 ds and the
-            // two 16-key k-steps of dQ^T += K^T dS^T that this M-tile feeds)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                // the M-tile's K and V rows are read before the products (the reads overlap)
-                bw_bf16x8 ka[D / 16], va[D / 16];
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    ka[ks] = *reinterpret_cast<const bw_bf16x8*>(&Ks[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
-                    va[ks] = *reinterpret_cast<const bw_bf16x8*>(&Vs[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
-                }
-                bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
-                }
-                // p = exp(scale s + d - lse) on the row's selected, causal keys; 0 elsewhere
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    float pe = __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, off));
-                    if (causal) {
-                        const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
-                        pe = key > pos ? 0.f : pe;
+            // a wave none of whose rows selected the tile adds nothing (p = 0 on every key)
+            if (__any(sel)) {
+                // per 32-key M-tile: S^T = K Q^T, dP^T = V dO^T, then p (and in pass 2 ds and the
+                // two 16-key k-steps of dQ^T += K^T dS^T that this M-tile feeds)
+    #pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    // the M-tile's K and V rows are read before the products (the reads overlap)
+                    bw_bf16x8 ka[D / 16], va[D / 16];
+    #pragma unroll
+                    for (int ks = 0; ks < D / 16; ++ks) {
+                        ka[ks] = *reinterpret_cast<const bw_bf16x8*>(&Ks[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
+                        va[ks] = *reinterpret_cast<const bw_bf16x8*>(&Vs[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
                     }
-                    s[rr] = pe;
-                }
-                if (pass == 0) {
-#pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) dsum = fmaf(s[rr], dp[rr], dsum);
-                } else {
-                    bw_bf16x8 ktr[2][DT];
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) ktr[h2][dt] = tr_operand<LS>(Ks[buf], 2 * mt + h2, dt, lane);
-                    bw_bf16x8 dsf[2];
-#pragma unroll
+                    bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
+    #pragma unroll
+                    for (int ks = 0; ks < D / 16; ++ks) {
+                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
+                    }
+                    // p = exp(scale s + d - lse) on the row's selected, causal keys; 0 elsewhere
+    #pragma unroll
                     for (int rr = 0; rr < 16; ++rr) {
-                        const float ds = s[rr] * (dp[rr] - Delta);
-                        dbpart += ds;
-                        dsf[rr >> 3][rr & 7] = (__bf16)ds;
+                        float pe = __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, off));
+                        if (causal) {
+                            const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
+                            pe = key > pos ? 0.f : pe;
+                        }
+                        s[rr] = pe;
                     }
-                    // dQ^T += K^T dS^T over k-steps 2 mt and 2 mt + 1
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt)
-                            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr[h2][dt], dsf[h2], acc[dt], 0, 0, 0);
+                    if (pass == 0) {
+    #pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) dsum = fmaf(s[rr], dp[rr], dsum);
+                    } else {
+                        bw_bf16x8 ktr[2][DT];
+    #pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2)
+    #pragma unroll
+                            for (int dt = 0; dt < DT; ++dt) ktr[h2][dt] = tr_operand<LS>(Ks[buf], 2 * mt + h2, dt, lane);
+                        bw_bf16x8 dsf[2];
+    #pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) {
+                            const float ds = s[rr] * (dp[rr] - Delta);
+                            dbpart += ds;
+                            dsf[rr >> 3][rr & 7] = (__bf16)ds;
+                        }
+                        // dQ^T += K^T dS^T over k-steps 2 mt and 2 mt + 1
+    #pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2)
+    #pragma unroll
+                            for (int dt = 0; dt < DT; ++dt)
+                                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr[h2][dt], dsf[h2], acc[dt], 0, 0, 0);
+                    }
                 }
             }
             if (pass == 1) {
@@ -277,6 +292,8 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
             __syncthreads();
             c = c_nx;
             sub = sub_nx;
+            mw = mw_nx;
+            dv = dv_nx;
         }
         if (pass == 0) Delta = dsum + __shfl_xor(dsum, 32, kWave);
     }
