@@ -198,6 +198,7 @@ KERNEL_SOURCES = {
     "sparse_attn_prefill": ["common.h", "kernels.h", "sparse_attn_dma.hip"],
     "decode_step": ["common.h", "kernels.h", "entmax.h", "route_common.h", "block_entmax.hip",
                     "decode_common.h", "decode.hip"],
+    "sparse_attn_backward": ["common.h", "kernels.h", "sparse_attn_bwd_mfma.hip"],
 }
 
 
@@ -433,7 +434,7 @@ def backward_leg(dash, pre, wp: wl.Workload, args) -> dict:
         "tflops": round(flops / ((t_attn + t_route) * 1e-3) / 1e12, 3),
         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic("sparse_attn_backward")},
     }
 
 
