@@ -5,16 +5,18 @@
 // consecutive tokens times the g heads of the group, row = token * g + head. All rows share the
 // group's chunk selection per token, so the workgroup walks the union of its tokens' selected
 // chunks (their own diagonal chunks included) and masks, per row, the chunks its token did not
-// select. Chunks are cut into tiles of up to 32 keys, which keeps a workgroup at 35 KiB of LDS and
-// 167 VGPRs, so that three workgroups (three waves per SIMD) share a CU.
+// select. Chunks are cut into tiles of 32 keys, which keeps a workgroup at 35 KiB of LDS and
+// 156 VGPRs, so that three workgroups (three waves per SIMD) share a CU.
 //
 // Tiles reach LDS through buffer_load_dwordx4 ... lds: each wave instruction writes 1 KiB (lane i
 // at byte 16 i) straight into LDS, so the next tile streams in while the current one is multiplied,
 // with no registers held and nothing for the compiler to reorder. A tile's rows are stored in
 // NB = KT / 4 blocks of four 256-byte rows (row r in block r % NB at slot r / NB, one load
-// instruction per block); K blocks are 1040 bytes apart and V blocks 1088, so that the K reads
-// of a 16-lane group (16 rows, one piece) and the transposing V reads of a 32-lane group (4 rows,
-// 8 dims each) fall on distinct banks, and every read is a lane base plus a constant offset. Two
+// instruction per block). The LDS has 64 banks and serves a 128-bit read 16 lanes per cycle and a
+// 64-bit read 32 lanes per cycle. K blocks are 1040 bytes apart and the K rows of odd slots hold
+// their 16-byte pieces in the order piece ^ 8, so the K reads of a 16-lane group (16 rows of two
+// slots, one piece) cover the 64 banks; V blocks are 1088 bytes apart, so the transposing V reads
+// of a 32-lane group (4 rows, 8 dims each) do too. Every read is a lane base plus a constant. Two
 // buffers each for K and V are separate LDS objects and the tile loop is unrolled by two, so
 // the compiler sees that the reads of one buffer never wait for the loads into the other.
 //
@@ -29,7 +31,7 @@
 // only raised when a tile's maximum exceeds it by more than 8 (so exp2(x - m) <= 256 and the
 // output, normalised by the sum taken against the same m, is unchanged); p = exp2(x - m) is a
 // single FMA and exp2 per score. A row whose token did not select the chunk has x = -inf; the
-// query's own chunk is causally masked.
+// query's own chunk is causally masked on the raw scores, so every tile takes the same code.
 #include <math.h>
 
 #include "common.h"
