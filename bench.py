@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -203,11 +204,15 @@ KERNEL_SOURCES = {
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of the code (comments and whitespace dropped) of the sources a kernel is built from."""
     csrc = os.path.join(ROOT, "sparse_hierarchical_attention_amd", "csrc")
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(f.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
