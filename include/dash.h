@@ -33,6 +33,8 @@
  *                nothing and keeps no pointer after a call returns.
  *   Asynchrony:  every call enqueues its kernels on `stream` and returns without waiting.
  *                Calls are thread-safe; the only state is the thread-local error string.
+ *   Sizes:       batch, lengths and head counts are at least 1; an empty call (a zero size) is
+ *                DASH_ERR_INVALID, not a silent no-op.
  *   Errors:      arguments are validated before anything is launched. Invalid arguments give
  *                DASH_ERR_INVALID, valid but unimplemented shapes DASH_ERR_UNSUPPORTED, a short
  *                workspace DASH_ERR_WORKSPACE, a failed launch DASH_ERR_HIP; nothing is launched

@@ -109,6 +109,21 @@ def test_attention_rejects_bad_arguments(L):
                                      0, None) == 1 and "scale" in err(L)
 
 
+def test_empty_calls_are_invalid(L):
+    # a zero batch, sequence length or row count is rejected before any launch (no silent no-op)
+    p = ctypes.c_void_p(16)
+    assert L.dash_sparse_attn_prefill(p, p, p, 1, p, p, p, None, 0, 64, 4, 2, 128, 64, 0.1, None) == 1
+    assert "positive" in err(L)
+    assert L.dash_sparse_attn_prefill(p, p, p, 1, p, p, p, None, 1, 0, 4, 2, 128, 64, 0.1, None) == 1
+    assert L.dash_sparse_attn_prefill_ex(p, p, p, 1, p, p, p, None, 1, 0, 0, 64, 4, 2, 128, 64,
+                                         0.1, None) == 1
+    assert L.dash_sparse_attn_decode(p, p, p, 1, p, p, p, 0, 4096, 8, 2, 128, 64, 0.1, p,
+                                     1 << 30, None) == 1
+    assert L.dash_block_entmax(p, 1, p, 1, 0, 0, 64, 4, 2, 128, 64, 1.5, 1.0, 1.0, p, p, None, p,
+                               1 << 40, None) == 1
+    assert L.dash_pool_keys(p, 1, p, 1, 0, 2, 128, 64, None) == 1
+
+
 def test_streaming_and_window_entry_points_reject_bad_arguments(L):
     p = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation
     # per-sequence lengths need one query per sequence
