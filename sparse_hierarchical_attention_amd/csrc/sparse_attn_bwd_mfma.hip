@@ -75,7 +75,10 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
     constexpr int T = kBwRows / GQ;          // tokens per workgroup
     constexpr int KT = BLK < 64 ? BLK : 64;  // keys per LDS tile
     constexpr int NSUB = BLK / KT;
-    constexpr int LS = D + 16;               // K / V row stride in LDS (elements)
+    // K / V row stride in LDS (elements): the LDS has 64 banks and serves a 128-bit read 16 lanes
+    // per cycle; at D + 24 the 16 rows a lane group reads fall on distinct banks (at D + 16 two
+    // rows shared each bank), and the transposing reads stay two-way as before
+    constexpr int LS = D + 24;
     constexpr int MT = KT / 32;              // 32-key M-tiles
     constexpr int DT = D / 32;               // 32-dim M-tiles of dQ^T
     constexpr int LOADS = KT * (D / 8) / kBwThreads;
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
     AttnParams p) {
     constexpr int NTH = 2 * BLK;             // one wave per 32 keys
     constexpr int NWV = NTH / 64;
-    constexpr int LS = D + 16;               // row stride of the gathered Q / dO rows in LDS
+    constexpr int LS = D + 24;               // row stride of the gathered Q / dO rows (as in the dq kernel)
     constexpr int RT = BLK >= 64 ? 64 : 32;  // rows (token x head) per tile
     constexpr int RM = RT / 32;              // 32-row M-tiles per tile
     constexpr int TPT = RT / GQ;             // tokens per tile
