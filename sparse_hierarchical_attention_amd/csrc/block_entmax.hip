@@ -395,7 +395,8 @@ hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const R
     const bool one = p.n_q == 1;
     if (p.tc > 0) {
         if (one) {
-            launch_score_one(q, dt, kbar, x, p, st);
+            const hipError_t e = launch_score_one(q, dt, kbar, x, p, st);
+            if (e != hipSuccess) return e;
         } else {
             dim3 grid(div_up(p.tc, kScoreTile), div_up(p.n_q * p.g, kScoreTile), p.batch * p.h_kv);
 #define DASH_SCORE(T, DD)                                                                    \

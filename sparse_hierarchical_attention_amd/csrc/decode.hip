@@ -37,7 +37,7 @@ __host__ __device__ constexpr int dec_workgroups(int g, int slots = kDecodeMaxSl
 
 // units of the (sequence, group)'s selection: its chunks below the own chunk cp whose bit is set
 // (whole chunks) and the own chunk (all of its units counted; those past the query are empty)
-__device__ __forceinline__ int dec_units(const uint32_t* mrow, int cp, int block) {
+__device__ __forceinline__ int dec_units(const uint32_t* mrow, int cp) {
     int total = 0;
     for (int wd = threadIdx.x; wd <= cp / 32; wd += blockDim.x) {
         uint32_t word = mrow[wd];
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const uint32_t* __re
     const int n = p.n_kv;
     const int cp = seq_pos(p.ctx_lens, n - 1, n, b, 0) / p.block;
     const int upc = (p.block + kDecUnit - 1) / kDecUnit;
-    const int units = wave_sum_int(dec_units(mask + ((int64_t)b * p.h_kv + r) * p.nw, cp, p.block)) * upc;
+    const int units = wave_sum_int(dec_units(mask + ((int64_t)b * p.h_kv + r) * p.nw, cp)) * upc;
     const int np = dec_slots(units) * WPS / 4;  // workgroups that wrote a partial, in order
     const int nmax = dec_workgroups(p.g);
     const float* base = ws + (((int64_t)b * p.h_kv + r) * nmax * p.g + hh) * (D + 4);
