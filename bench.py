@@ -298,7 +298,8 @@ def _time_ms(fn, reps: int, warm: int = 1) -> float:
 
 def _sdpa_ms(q, k, v, causal: bool, reps: int):
     """torch's fused scaled-dot-product attention (flash or memory-efficient kernel only, never
-    the math path) on [B, H, n, D] views, or None where this build offers neither for the shape."""
+    the math path) on [B, H, n, D] views, or None where the installed torch offers neither for the
+    shape."""
     from torch.nn.attention import SDPBackend, sdpa_kernel
     import torch.nn.functional as F
     qt, kt, vt = (x.transpose(1, 2) for x in (q, k, v))
@@ -318,7 +319,7 @@ def random_mask_sweep(dash, dev, reps: int):
     given a random selection at sparsity s in place of the router's (Stages 0 and 1 still run
     in full, their cost does not depend on s). Prints one JSON line per (mode, N) with each
     stage's time, the speedup over dense causal attention through the same Stage 2 kernel (every
-    chunk selected) and over torch's fused attention kernel, where this build has one."""
+    chunk selected) and over torch's fused attention kernel, where the installed torch has one."""
     rows = []
     for n in wl.TABLE5_CONTEXTS:
         for decode in (False, True):
@@ -465,7 +466,7 @@ def main():
                          "(Hq 32, Hkv 2, N 16-96K, three sparsities); one JSON line per point")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(the path runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 

@@ -1,7 +1,7 @@
 """Comparison helpers for GPU-vs-oracle parity (tolerances as the method's checks demand).
 
 Support sets: identical except for chunks within 1e-4 (x-units) of some head's threshold,
-judged on the oracle's values. tau: |diff| <= 1e-5 * max(1, |tau|) (fp32 resolves tau only
+as decided on the oracle's values. tau: |diff| <= 1e-5 * max(1, |tau|) (fp32 resolves tau only
 relative to its size; large routing scales put tau near 100).
 
 Bias d = (log w_c - mu) / sigma, on chunks in both supports of rows whose supports match:
