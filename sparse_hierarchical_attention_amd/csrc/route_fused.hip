@@ -354,13 +354,21 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void route_fused_kernel(
     // of a row sits in lane c % 16 of its group, slot c / 16. For g <= 4 a unit is one pass over
     // 4 / g tokens or one token; for g > 4 it is one pass over four heads of a token, and the
     // token's passes, spread over the waves, leave partial sums in LDS that one wave then adds.
-    // The slot count is a compile-time bucket (the unit's longest row, rounded up to 4, 8, 16,
-    // ...) so that every slot loop unrolls; slots past a row hold -inf.
+    // The slot count is a compile-time bucket (the unit's longest row, rounded up to a multiple of
+    // 4 slots up to 32, of 8 up to 64) so that every slot loop unrolls and a row pays for at most
+    // a few slots it does not have; slots past a row hold -inf.
 #define DASH_BUCKETS(NS_, CALL)                                                                 \
     if ((NS_) <= 4) CALL(4);                                                                    \
     else if ((NS_) <= 8) CALL(8);                                                               \
+    else if ((NS_) <= 12) CALL(12);                                                             \
     else if ((NS_) <= 16) CALL(16);                                                             \
+    else if (CMAX >= 512 && (NS_) <= 20) CALL(CMAX >= 512 ? 20 : 16);                           \
+    else if (CMAX >= 512 && (NS_) <= 24) CALL(CMAX >= 512 ? 24 : 16);                           \
+    else if (CMAX >= 512 && (NS_) <= 28) CALL(CMAX >= 512 ? 28 : 16);                           \
     else if (CMAX >= 512 && (NS_) <= 32) CALL(CMAX >= 512 ? 32 : 16);                           \
+    else if (CMAX >= 1024 && (NS_) <= 40) CALL(CMAX >= 1024 ? 40 : 16);                         \
+    else if (CMAX >= 1024 && (NS_) <= 48) CALL(CMAX >= 1024 ? 48 : 16);                         \
+    else if (CMAX >= 1024 && (NS_) <= 56) CALL(CMAX >= 1024 ? 56 : 16);                         \
     else if (CMAX >= 1024) CALL(CMAX >= 1024 ? 64 : 16)
     auto slots_of = [&](int tok) {  // 16-lane slots of a token's row
         return div_up(route_cands(p, route_pos(p, b, min(tok, p.n_q - 1))), 16);
