@@ -185,9 +185,9 @@ dash_status_t dash_sparse_attn_prefill(const void* q, const void* k, const void*
  * hold those rows (as dash_block_entmax writes them for the same n_q and q_pos0); k, v
  * [B, n_kv, H_kv, D]. The query at position p attends its routed chunks and the keys of its own
  * chunk up to p. Splitting the rows into blocks gives each row the output of one call over all
- * rows for the same mask and bias: bit for bit for bf16 at D = 128, up to the last bit otherwise
- * (there the row tiling decides whether an exponent is one fused multiply-add or two), so a caller
- * can route one block while attending the previous one.
+ * rows for the same mask and bias: bit for bit for bf16, up to the last bit for fp32 (there the
+ * row tiling decides whether an exponent is one fused multiply-add or two), so a caller can route
+ * one block while attending the previous one.
  */
 dash_status_t dash_sparse_attn_prefill_ex(const void* q, const void* k, const void* v,
                                           dash_dtype_t dt, const uint32_t* mask,

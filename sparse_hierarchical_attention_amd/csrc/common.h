@@ -64,6 +64,16 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f<0x143, 0xc>(0.f, v);
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+// Lanes l and l ^ 32 of a wave: v_permlane32_swap hands each lane its partner's value without a
+// trip through LDS; every lane gets the same pair, so the result is the same in both halves.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_f<0xb1, 0xf>(-INFINITY, v));
     v = fmaxf(v, dpp_f<0x4e, 0xf>(-INFINITY, v));

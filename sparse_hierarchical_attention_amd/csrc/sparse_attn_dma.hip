@@ -64,18 +64,6 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const bf16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)(p));
 }
 
-// lanes l and l ^ 32 hold the two halves of one query row's keys; v_permlane32_swap hands each
-// lane its partner's value without a trip through LDS (every lane gets the same pair, so the
-// result is the same in both halves)
-__device__ __forceinline__ float halves_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 }  // namespace
 
 template <int BLK, int GQ>

@@ -20,7 +20,7 @@
 // only raised when a tile's maximum exceeds it by more than 8 (so exp2(x - m) <= 256 and the
 // output, normalised by the sum taken against the same m, is unchanged); p = exp2(x - m) is a
 // single FMA and exp2 per score. A row whose token did not select the chunk has x = -inf; the
-// query's own chunk is causally masked.
+// query's own chunk is causally masked on the raw scores, so every tile takes the same code.
 #include <math.h>
 
 #include "common.h"
@@ -185,7 +185,6 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
         // this row's view of the chunk
         bool sel = false;
         if (valid && c <= cpos) sel = c == cpos || ((mrow[c >> 5] >> (c & 31)) & 1u);
-        const float sc = sel ? qk_scale : 0.f;
         const float off = sel ? (c == cpos ? 0.f : brow[c] * kLog2e) : -INFINITY;
         const bool causal = c >= c_first;  // some row's own chunk: mask keys past each row
 
@@ -200,31 +199,23 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mt], 0, 0, 0);
             }
         }
-        // row maximum of x = s * sc + off (sc >= 0)
-        float xmax;
+        // keys past the row's own position score -inf; x = s * scale log2(e) + off is then -inf
+        // too (scale > 0), as it is for every key of a row that did not select the chunk
         if (causal) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
                     const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
-                    const float x = fmaf(s[mt][rr], sc, off);
-                    s[mt][rr] = key > pos ? -INFINITY : x;
+                    if (key > pos) s[mt][rr] = -INFINITY;
                 }
-            xmax = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) xmax = fmaxf(xmax, s[mt][rr]);
-        } else {
-            float smax = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) smax = fmaxf(smax, s[mt][rr]);
-            xmax = sel ? fmaf(smax, sc, off) : -INFINITY;
         }
-        xmax = fmaxf(xmax, __shfl_xor(xmax, 32, kWave));
+        float smax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) smax = fmaxf(smax, s[mt][rr]);
+        const float xmax = fmaf(halves_max(smax), qk_scale, off);
         // raise the running maximum only when needed (rare once a row has seen its peak)
         const bool raise = xmax > m_used + kLazyMax;
         if (__any(raise)) {
@@ -235,30 +226,18 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
             for (int dt = 0; dt < DT; ++dt) acc[dt] *= corr;
             m_used = m_new;
         }
-        const float m_ref = m_used == -INFINITY ? 0.f : m_used;
-        float rsum = 0.f;
+        // p = exp2(x - m) as one FMA and exp2; the row sum stays per lane (this half's keys) until
+        // the end, since both halves scale it by the same factors
+        const float off_m = off - (m_used == -INFINITY ? 0.f : m_used);
         bf16x8 pf[KSTEP];
-        if (causal) {
 #pragma unroll
-            for (int ks = 0; ks < KSTEP; ++ks)
+        for (int ks = 0; ks < KSTEP; ++ks)
 #pragma unroll
-                for (int vv = 0; vv < 8; ++vv) {
-                    const float pe = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + vv] - m_ref);
-                    rsum += pe;
-                    pf[ks][vv] = (__bf16)pe;
-                }
-        } else {
-            const float off_m = off - m_ref;
-#pragma unroll
-            for (int ks = 0; ks < KSTEP; ++ks)
-#pragma unroll
-                for (int vv = 0; vv < 8; ++vv) {
-                    const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + vv], sc, off_m));
-                    rsum += pe;
-                    pf[ks][vv] = (__bf16)pe;
-                }
-        }
-        l_run += rsum + __shfl_xor(rsum, 32, kWave);
+            for (int vv = 0; vv < 8; ++vv) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + vv], qk_scale, off_m));
+                l_run += pe;
+                pf[ks][vv] = (__bf16)pe;
+            }
 
         // O^T += V^T P^T, V^T from the stored rows through transposing reads
 #pragma unroll
@@ -277,6 +256,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
         sub = sub_nx;
     }
 
+    l_run = halves_sum(l_run);
     if (!valid) return;
     const float inv_l = 1.0f / l_run;
     bf16_t* orow = o + (qrow * p.h_q + r * GQ + hl) * D;

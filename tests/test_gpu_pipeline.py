@@ -48,7 +48,7 @@ def test_row_blocks_match_one_call(dash, dtype, d, block, hq, hkv):
         ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -20
         assert d_o <= ulp * ref_o.abs().max().item(), (t0, t1, d_o)
         assert d_l <= 1e-5, (t0, t1, d_l)
-        if dtype == "bf16" and d == 128:
+        if dtype == "bf16":
             # Stage 2 alone on the single call's own mask and bias rows: one softmax path for every
             # tile, so a row's result does not depend on the row tiling
             o2, l2 = dash.dash_sparse_attn_prefill(qs, k, v, mask[:, t0:t1].contiguous(),
