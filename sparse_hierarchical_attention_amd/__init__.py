@@ -281,9 +281,14 @@ def dash_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if lse is None and want_lse:
         lse = torch.empty((b, n_q, hq), dtype=torch.float32, device=q.device)
     dev = _dev(q, k, v, mask, bias, o, lse)
-    _check(lib().dash_sparse_attn_prefill_ex(
-        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(mask), _ptr(bias), _ptr(o), _ptr(lse),
-        b, n_q, int(q_pos0), n_kv, hq, hkv, d, block, float(scale), _stream(dev)))
+    if q_pos0 == 0 and n_q == n_kv:  # whole sequences: the plain entry point
+        _check(lib().dash_sparse_attn_prefill(
+            _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(mask), _ptr(bias), _ptr(o),
+            _ptr(lse), b, n_kv, hq, hkv, d, block, float(scale), _stream(dev)))
+    else:
+        _check(lib().dash_sparse_attn_prefill_ex(
+            _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(mask), _ptr(bias), _ptr(o),
+            _ptr(lse), b, n_q, int(q_pos0), n_kv, hq, hkv, d, block, float(scale), _stream(dev)))
     return o, lse
 
 

@@ -30,8 +30,17 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
+def _headers_mtime() -> float:
+    hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    hs += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    return max([os.path.getmtime(h) for h in hs] + [os.path.getmtime(__file__)])
+
+
+def _compile(src: str, force: bool = True) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    if (not force and os.path.exists(obj)
+            and os.path.getmtime(obj) > max(os.path.getmtime(src), _headers_mtime())):
+        return obj
     cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -39,11 +48,12 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, force: bool = True) -> str:
+    """Compile every source (force=False: only those older than their object file) and link."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s_: _compile(s_, force), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,5 +66,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, force="--incremental" not in sys.argv)
     sys.exit(0)

@@ -182,9 +182,10 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
     // one tile (chunk c, 32-key part sub) into K / V buffers: wave w fills blocks
     // NLD w .. NLD (w + 1) - 1, one instruction each; lane i fetches piece i % 16 of the block's
     // row i / 16, i.e. tile row b + NB (i / 16). The loads go through buffer descriptors over this
-    // (sequence, KV head)'s rows: each lane's byte offset within a tile is fixed, the tile's start
-    // is one scalar offset, and rows past the sequence fall outside the descriptor's range and
-    // read as zero (every query masks them causally).
+    // (sequence, KV head)'s rows. The whole byte offset (the tile's start plus the lane's fixed
+    // offset within a tile) goes in the per-lane offset, the one the descriptor's range check
+    // covers (the scalar offset is outside it), so rows past the sequence read as zero and never
+    // touch the next sequence or memory past the tensor (every query masks them causally).
     const uint32_t row_bytes = (uint32_t)kv_row_stride * 2u;
     const uint32_t span = (uint32_t)((n - 1) * kv_row_stride + kD) * 2u;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, (int)span, 0x00020000);
@@ -202,8 +203,8 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int blk = NLD * wave + i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(Kd + blk * kKBlock), 16, loff_k[i], soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(Vd + blk * kVBlock), 16, loff[i], soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(Kd + blk * kKBlock), 16, loff_k[i] + soff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(Vd + blk * kVBlock), 16, loff[i] + soff, 0, 0, 0);
         }
     };
 

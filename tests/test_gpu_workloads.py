@@ -39,18 +39,18 @@ def prefill_parity(dash, orc, w: wl.Workload, sigma: float, rows: np.ndarray):
     res = dash.forward(q, k, v, block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=sigma)
     torch.cuda.synchronize()
     log(f"oracle on {len(rows)} rows")
-    ref = orc.forward(q.cpu(), k.cpu(), v.cpu(), block=w.block, alpha=w.alpha, gamma=w.gamma,
-                      sigma=sigma, rows=rows)
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    ref = orc.forward(qh, kh, vh, block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=sigma,
+                      rows=rows)
     np.testing.assert_allclose(res["kbar"].cpu().numpy(), ref["kbar"], rtol=1e-6, atol=1e-6)
-    rep = parity.compare_stage1(flat_rows(res["mask"], rows), flat_rows(res["bias"], rows),
-                                flat_rows(res["tau"], rows), ref, n_kv=w.n_kv, block=w.block,
-                                h_kv=w.h_kv, q_pos=rows % w.n_q, alpha=w.alpha, sigma=sigma)
-    assert rep["rows_with_flips"] <= max(2, 0.02 * len(rows)), rep
-    out = parity.compare_output(flat_rows(res["o"], rows), ref["o"], w.dtype,
-                                exclude_rows=rep["row_flip"], gpu_lse=flat_rows(res["lse"], rows),
-                                ref_lse=ref["lse"], cond_row=rep["cond_row"],
-                                vmax=float(v.abs().max()))
-    log(f"support {rep['support_frac']:.4f} flips {rep['flips']} out {out}")
+    rep = parity.check_forward(orc, qh, kh, vh, ref, mask=flat_rows(res["mask"], rows),
+                               bias=flat_rows(res["bias"], rows), tau=flat_rows(res["tau"], rows),
+                               o=flat_rows(res["o"], rows), lse=flat_rows(res["lse"], rows),
+                               rows=rows, n_kv=w.n_kv, block=w.block, h_kv=w.h_kv,
+                               q_pos=rows % w.n_q, alpha=w.alpha, sigma=sigma, dtype=w.dtype,
+                               vmax=float(v.abs().max()))
+    out = rep["e2e"]
+    log(f"support {rep['support_frac']:.4f} flips {rep['flips']} own {rep['own']} e2e {out}")
     return rep, out
 
 
@@ -118,19 +118,21 @@ def test_decode_128k(dash, orc, sigma):
     torch.cuda.synchronize()
     for b in (0, 7, 15):  # the oracle regenerates nothing: it reads these sequences' inputs
         log(f"oracle on sequence {b}")
-        ref = orc.forward(q[b:b + 1].cpu(), k[b:b + 1].cpu(), v[b:b + 1].cpu(), block=w.block,
-                          alpha=w.alpha, gamma=w.gamma, sigma=sigma, q_pos0=w.n_kv - 1)
+        qh, kh, vh = q[b:b + 1].cpu(), k[b:b + 1].cpu(), v[b:b + 1].cpu()
+        ref = orc.forward(qh, kh, vh, block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=sigma,
+                          q_pos0=w.n_kv - 1)
         np.testing.assert_allclose(kbar[b:b + 1].cpu().numpy(), ref["kbar"], rtol=1e-6, atol=1e-6)
-        rep = parity.compare_stage1(parity.to_host(mask[b]), parity.to_host(bias[b]), None, ref,
-                                    n_kv=w.n_kv, block=w.block, h_kv=w.h_kv,
-                                    q_pos=np.array([w.n_kv - 1]), alpha=w.alpha, sigma=sigma)
+        parity.check_forward(orc, qh, kh, vh, ref, mask=parity.to_host(mask[b]),
+                             bias=parity.to_host(bias[b]), tau=None, o=parity.to_host(o[b]),
+                             rows=np.array([0]), n_kv=w.n_kv, block=w.block, h_kv=w.h_kv,
+                             q_pos=np.array([w.n_kv - 1]), q_pos0=w.n_kv - 1, alpha=w.alpha,
+                             sigma=sigma, dtype="bf16", vmax=float(v[b].abs().max()),
+                             max_flip_frac=1.0)
         # the planted chunks are what the router finds
         routed = parity.bits(ref["mask"], -(-w.n_kv // w.block))[0]
         for r in range(w.h_kv):
             sel = set(np.flatnonzero(routed[r][:-1]).tolist())
             assert set(inp["planted"][b][r].tolist()) <= sel
-        parity.compare_output(parity.to_host(o[b]), ref["o"], "bf16", exclude_rows=rep["row_flip"],
-                              cond_row=rep["cond_row"], vmax=float(v[b].abs().max()))
 
 
 # ------------------------------------------- the pages' efficiency sweep: injected random selection
