@@ -140,11 +140,21 @@ def extras_leg(dash, pre, dec, wp: wl.Workload, wd: wl.Workload, reps: int) -> d
     o_d = torch.empty_like(qd)
     wsb = dash.dash_block_entmax_workspace_bytes(qd.dtype, wd.batch, 1, wd.n_kv - 1, wd.n_kv,
                                                  wd.h_q, wd.h_kv, wd.head_dim, wd.block)
-    rws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    rws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
     awb = dash.dash_decode_workspace_bytes(wd.batch, wd.n_kv, wd.h_q, wd.h_kv, wd.head_dim, wd.block)
-    aws = torch.empty(awb, dtype=torch.uint8, device=dev) if awb else None
+    aws = torch.zeros(awb, dtype=torch.uint8, device=dev) if awb else None
+
+    sws = torch.zeros(dash.dash_decode_step_workspace_bytes(wd.batch, wd.n_kv, wd.h_q, wd.h_kv,
+                                                            wd.head_dim, wd.block),
+                      dtype=torch.uint8, device=dev)
 
     def varlen_step():
+        dash.dash_pool_keys_append(kd, lens, kbar_d, wd.block)
+        dash.dash_decode_step(qd, kd, vd, kbar_d, block=wd.block, alpha=wd.alpha, gamma=wd.gamma,
+                              sigma=wd.sigma, ctx_lens=lens, mask=mask_d, bias=bias_d, o=o_d,
+                              workspace=sws)
+
+    def varlen_two_calls():
         dash.dash_pool_keys_append(kd, lens, kbar_d, wd.block)
         dash.dash_block_entmax_ex(qd, kbar_d, n_kv=wd.n_kv, block=wd.block, alpha=wd.alpha,
                                   gamma=wd.gamma, sigma=wd.sigma, h_kv=wd.h_kv, ctx_lens=lens,
@@ -152,6 +162,7 @@ def extras_leg(dash, pre, dec, wp: wl.Workload, wd: wl.Workload, reps: int) -> d
         dash.dash_sparse_attn_decode_varlen(qd, kd, vd, lens, mask_d, bias_d, block=wd.block,
                                             o=o_d, workspace=aws)
 
+    t_two = _time_ms(decode_graph(varlen_two_calls).replay, reps)
     t_eager = _time_ms(varlen_step, reps)
     # the step's three calls cost more host time than the GPU spends on them, so it is also
     # captured once in a HIP graph and replayed (no allocation or memset inside the step)
@@ -160,7 +171,8 @@ def extras_leg(dash, pre, dec, wp: wl.Workload, wd: wl.Workload, reps: int) -> d
     gbs = nbytes / (t * 1e-3) / 1e9
     out["varlen_decode"] = {
         "lengths": "uniform over [64K, 128K] per sequence", "us_per_step": round(t * 1e3, 2),
-        "us_per_step_eager": round(t_eager * 1e3, 2), "tok_per_s": round(wd.batch / (t * 1e-3), 1),
+        "us_per_step_eager": round(t_eager * 1e3, 2),
+        "us_per_step_two_calls": round(t_two * 1e3, 2), "tok_per_s": round(wd.batch / (t * 1e-3), 1),
         "algorithmic_bytes": nbytes, "gb_per_s": round(gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBPS, 4)}}
@@ -241,8 +253,8 @@ class Timer:
         self.spans.setdefault(name, []).append((s, e))
         return s, e
 
-    def mean_ms(self, name):
-        return float(np.mean([s.elapsed_time(e) for s, e in self.spans[name]]))
+    def median_ms(self, name):
+        return float(np.median([s.elapsed_time(e) for s, e in self.spans[name]]))
 
 
 def cpu_baseline(pre_inp, dec_inp, wp: wl.Workload, wd: wl.Workload, pre_pairs_per_row: float):
@@ -334,7 +346,7 @@ def random_mask_sweep(dash, dev, reps: int):
             bias = torch.empty((w.batch, w.n_q, w.h_kv, nc), dtype=torch.float32, device=dev)
             wsb = dash.dash_block_entmax_workspace_bytes(q.dtype, w.batch, w.n_q, w.q_pos0, n,
                                                          w.h_q, w.h_kv, w.head_dim, w.block)
-            ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=dev) if wsb else None
             o = torch.empty_like(q)
             lse = torch.empty((w.batch, w.n_q, w.h_q), dtype=torch.float32, device=dev)
             t_pool = 0.0 if decode else _time_ms(lambda: dash.dash_pool_keys(k, w.block, kbar=kbar), reps)
@@ -344,7 +356,7 @@ def random_mask_sweep(dash, dev, reps: int):
             del ws
             if decode:
                 awb = dash.dash_decode_workspace_bytes(w.batch, n, w.h_q, w.h_kv, w.head_dim, w.block)
-                aws = torch.empty(awb, dtype=torch.uint8, device=dev) if awb else None
+                aws = torch.zeros(awb, dtype=torch.uint8, device=dev) if awb else None
 
                 def stage2(m, bi):
                     dash.dash_sparse_attn_decode(q, k, v, m, bi, block=w.block, o=o, workspace=aws)
@@ -432,7 +444,7 @@ def backward_leg(dash, pre, wp: wl.Workload, args) -> dict:
     torch.cuda.synchronize()
     pairs, _ = selected_pairs_prefill(fwd["mask"], wp)
     flops = 10.0 * d * pairs
-    t_attn, t_route = timer.mean_ms("bwd_attn"), timer.mean_ms("bwd_route")
+    t_attn, t_route = timer.median_ms("bwd_attn"), timer.median_ms("bwd_route")
     tf = flops / (t_attn * 1e-3) / 1e12
     return {
         "ms": {"attn": round(t_attn, 3), "route": round(t_route, 3)},
@@ -447,8 +459,10 @@ def backward_leg(dash, pre, wp: wl.Workload, args) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=200,
+                    help="decode steps timed on their own (median), each from a cold cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one half of the step (for profiling); no JSON line is printed")
@@ -511,10 +525,15 @@ def main():
     o_d = torch.empty_like(qd)
     wsd_b = dash.dash_block_entmax_workspace_bytes(qd.dtype, wd.batch, 1, wd.n_kv - 1, wd.n_kv,
                                                    wd.h_q, wd.h_kv, wd.head_dim, wd.block)
-    route_ws_d = torch.empty(max(wsd_b, 1), dtype=torch.uint8, device=dev)
+    route_ws_d = torch.zeros(max(wsd_b, 1), dtype=torch.uint8, device=dev)
     attn_ws_b = dash.dash_decode_workspace_bytes(wd.batch, wd.n_kv, wd.h_q, wd.h_kv, wd.head_dim,
                                                  wd.block)
-    attn_ws_d = torch.empty(attn_ws_b, dtype=torch.uint8, device=dev) if attn_ws_b else None
+    attn_ws_d = torch.zeros(attn_ws_b, dtype=torch.uint8, device=dev) if attn_ws_b else None
+    step_ws_d = torch.zeros(dash.dash_decode_step_workspace_bytes(wd.batch, wd.n_kv, wd.h_q, wd.h_kv,
+                                                                  wd.head_dim, wd.block),
+                            dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB: more than the MALL
+    flush_sum = torch.empty((), dtype=torch.float32, device=dev)
 
     def step(timer: Timer | None):
         def ev(name):
@@ -543,15 +562,31 @@ def main():
     def decode_step(ev):
         s, e = ev("decode")
         s and s.record()
+        dash.dash_decode_step(qd, kd, vd, kbar_d, block=wd.block, alpha=wd.alpha, gamma=wd.gamma,
+                              sigma=wd.sigma, mask=mask_d, bias=bias_d, o=o_d,
+                              workspace=step_ws_d)
+        e and e.record()
+
+    def decode_two_calls():
         dash.dash_block_entmax(qd, kbar_d, n_kv=wd.n_kv, block=wd.block, alpha=wd.alpha,
                                gamma=wd.gamma, sigma=wd.sigma, q_pos0=wd.n_kv - 1, mask=mask_d,
                                bias=bias_d, want_tau=False, workspace=route_ws_d)
-        s2, e2 = ev("decode_attn")
-        s2 and s2.record()
         dash.dash_sparse_attn_decode(qd, kd, vd, mask_d, bias_d, block=wd.block, o=o_d,
                                      workspace=attn_ws_d)
-        e2 and e2.record()
-        e and e.record()
+
+    def decode_cold(fn, n):
+        """Median HIP-event time of fn() over n runs, each after a 1 GiB read (outside the
+        events) that leaves none of the step's data in the L2 caches or the 256 MB MALL, and no
+        dirty lines to write back either."""
+        t = Timer()
+        for i in range(n):
+            torch.sum(flush, dim=0, out=flush_sum)
+            s_ev, e_ev = t.span("x")
+            s_ev.record()
+            fn()
+            e_ev.record()
+        torch.cuda.synchronize()
+        return t.median_ms("x")
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -574,25 +609,22 @@ def main():
 
     pairs, frac = selected_pairs_prefill(mask, wp)
     flops = 4.0 * wp.head_dim * pairs
-    t_pool, t_ent, t_attn = timer.mean_ms("pool"), timer.mean_ms("entmax"), timer.mean_ms("attn")
+    t_pool, t_ent, t_attn = timer.median_ms("pool"), timer.median_ms("entmax"), timer.median_ms("attn")
     t_pre = t_pool + t_ent + t_attn
     pre_tflops = flops / (t_pre * 1e-3) / 1e12
     attn_tflops = flops / (t_attn * 1e-3) / 1e12
     dbytes, mean_routed = decode_bytes(mask_d, wd)
-    # the decode step as a server runs it, captured once in a HIP graph and replayed, timed in the
-    # same place of the step as the eager one (right after a prefill, so from a cold cache)
+    # the decode step on its own, from a cold cache, as the median of --decode-steps runs: the
+    # fused step (headline), the same step as a HIP graph replay, and the two separate calls
+    print(f"[bench] decode: {args.decode_steps} cold steps each way", file=sys.stderr, flush=True)
+    n_dec = max(1, args.decode_steps)
+    t_dec = decode_cold(lambda: decode_step(lambda name: (None, None)), n_dec)
     dec_graph = decode_graph(lambda: decode_step(lambda name: (None, None)))
-    gtimer = Timer()
-    for i in range(args.warmup + args.steps):
-        prefill_step(lambda name: (None, None))
-        s_ev, e_ev = gtimer.span("decode") if i >= args.warmup else (None, None)
-        s_ev and s_ev.record()
-        dec_graph.replay()
-        e_ev and e_ev.record()
+    t_dec_graph = decode_cold(dec_graph.replay, n_dec)
+    t_dec_two = decode_cold(decode_two_calls, n_dec)
+    decode_step(lambda name: (None, None))  # leave the step's own mask in mask_d
     torch.cuda.synchronize()
-    t_dec_graph = gtimer.mean_ms("decode")
-    t_dec = timer.mean_ms("decode")
-    t_dec_attn = timer.mean_ms("decode_attn")
+    t_dec_in_step = timer.median_ms("decode")
     dec_gbps = dbytes / (t_dec * 1e-3) / 1e9
     traffic = measured_traffic("sparse_attn_prefill")
     dec_traffic = measured_traffic("decode_step")
@@ -630,7 +662,9 @@ def main():
             "tok_per_s": round(wd.batch / (t_dec * 1e-3), 1),
             "us_per_step": round(t_dec * 1e3, 2),
             "us_per_step_graph": round(t_dec_graph * 1e3, 2),
-            "us_attn": round(t_dec_attn * 1e3, 2),
+            "us_per_step_two_calls": round(t_dec_two * 1e3, 2),
+            "us_per_step_after_prefill": round(t_dec_in_step * 1e3, 2),
+            "timing": f"median of {n_dec} steps, each after a 1 GiB read (cold L2 and MALL)",
             "algorithmic_bytes": dbytes,
             "mean_routed_chunks": round(mean_routed, 3),
             "gb_per_s": round(dec_gbps, 1),

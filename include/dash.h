@@ -131,7 +131,8 @@ dash_status_t dash_pool_keys_append(const void* k_cache, dash_dtype_t dt, const 
  * workspace holds the summaries split into three bf16 terms (6 bytes per summary element, Tc
  * rounded up to a multiple of 32). Other calls (fp32, decode, longer rows) first score into `workspace`, fp32
  * [B, n_q, H_q, Nc]. dash_block_entmax_workspace_bytes() gives the bytes a call needs (0 if
- * none); the workspace may be NULL when it is 0. The workspace holds nothing between calls.
+ * none); the workspace may be NULL when it is 0.
+ * The workspace holds nothing between calls.
  */
 size_t dash_block_entmax_workspace_bytes(dash_dtype_t dt, int batch, int n_q, int q_pos0,
                                          int n_kv, int h_q, int h_kv, int head_dim, int block);
@@ -253,10 +254,15 @@ dash_status_t dash_block_entmax_backward(const void* q, dash_dtype_t dt, const f
 /*
  * Stage 2, decode [DA §3.5, split-KV variant]: the Stage 2 output of one new query per sequence
  * at position n_ctx - 1 of its cache. The selected chunks are split over many workgroups; their
- * partial (max, sum, output) triples are merged in a fixed order, so the result is deterministic.
+ * partial (max, sum, output) triples are merged in a fixed order by the last of them to finish,
+ * so the result is deterministic and the call is one launch.
  *   q, o [B, H_q, D] (dt);  k_cache, v_cache [B, n_ctx, H_kv, D] (dt);
  *   mask [B, 1, H_kv, W], bias [B, 1, H_kv, Nc] from dash_block_entmax(n_q = 1,
- *   q_pos0 = n_ctx - 1).  workspace: device scratch of dash_decode_workspace_bytes() bytes.
+ *   q_pos0 = n_ctx - 1).  workspace: device scratch of dash_decode_workspace_bytes() bytes: the
+ *   one ticket counter per (sequence, group) (the first ceil(4 B H_kv / 256) * 256 bytes), then the
+ *   partial triples; the counters must be zero when a call starts, and every call leaves them
+ *   zero. Zero the workspace once when it is allocated. Two calls in flight at once on one
+ *   workspace race.
  */
 size_t dash_decode_workspace_bytes(int batch, int n_ctx, int h_q, int h_kv, int head_dim,
                                    int block);
@@ -281,6 +287,31 @@ dash_status_t dash_sparse_attn_decode_varlen(const void* q, const void* k_cache,
                                              int h_q, int h_kv, int head_dim, int block,
                                              float scale, void* workspace,
                                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One whole decode step [DA §3.2 Alg. 2 and §3.4-3.5, one new query per sequence]: Stage 1
+ * routing against the cached summaries and Stage 2 split attention, exactly
+ * dash_block_entmax_ex(n_q = 1) followed by dash_sparse_attn_decode(_varlen) with the same
+ * arguments, in one call with one workspace (convenient to capture in a graph).
+ *   q, o [B, H_q, D] (dt); k_cache, v_cache [B, n_ctx, H_kv, D] (dt); kbar [B, floor(n_ctx / Bc),
+ *   H_kv, D] fp32 (the summaries of the complete chunks); ctx_lens: NULL (every query at
+ *   n_ctx - 1) or device int32 [B] (query b at ctx_lens[b] - 1, n_ctx the capacity), as
+ *   dash_block_entmax_ex; alpha, gamma, sigma, window_blocks as dash_block_entmax_ex; scale as
+ *   dash_sparse_attn_decode.
+ *   mask [B, 1, H_kv, W], bias [B, 1, H_kv, Nc]: written as dash_block_entmax_ex writes them.
+ *   workspace: dash_decode_step_workspace_bytes() bytes: dash_sparse_attn_decode's workspace
+ *   (ticket counters first) followed by dash_block_entmax's. The ticket counters must be zero
+ *   when a call starts and every call leaves them zero: zero the workspace once when it is
+ *   allocated. Two calls in flight at once on one workspace race.
+ */
+size_t dash_decode_step_workspace_bytes(int batch, int n_ctx, int h_q, int h_kv, int head_dim,
+                                        int block);
+dash_status_t dash_decode_step(const void* q, const void* k_cache, const void* v_cache,
+                               dash_dtype_t dt, const float* kbar, const int32_t* ctx_lens,
+                               int batch, int n_ctx, int h_q, int h_kv, int head_dim, int block,
+                               float alpha, float gamma, float sigma, int window_blocks,
+                               float scale, uint32_t* mask, float* bias, void* o, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ __all__ = [
     "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
     "dash_sparse_attn_backward_workspace_bytes", "dash_sparse_attn_prefill_backward",
     "dash_block_entmax_backward_workspace_bytes", "dash_block_entmax_backward",
+    "dash_decode_step_workspace_bytes", "dash_decode_step",
     "dash_version", "backward", "forward", "decode_step",
 ]
 
@@ -85,6 +86,11 @@ def lib():
         L.dash_block_entmax_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
                                                  f, f, f, i, vp, sz, vp]
         L.dash_block_entmax_backward.restype = i
+        L.dash_decode_step_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.dash_decode_step_workspace_bytes.restype = sz
+        L.dash_decode_step.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, f, f, f, i, f, vp,
+                                       vp, vp, vp, sz, vp]
+        L.dash_decode_step.restype = i
         for fn in ("dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append",
                    "dash_block_entmax", "dash_block_entmax_ex", "dash_sparse_attn_prefill",
                    "dash_sparse_attn_prefill_ex", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
@@ -221,7 +227,7 @@ def dash_block_entmax_ex(q: torch.Tensor, kbar: torch.Tensor, *, n_kv: int, bloc
         q_pos0 = n_kv - 1
     need = dash_block_entmax_workspace_bytes(q.dtype, b, n_q, q_pos0, n_kv, hq, hkv, d, block)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dev = _dev(q, kbar, ctx_lens, mask, bias, tau, workspace)
     _check(lib().dash_block_entmax_ex(
@@ -253,7 +259,7 @@ def dash_block_entmax(q: torch.Tensor, kbar: torch.Tensor, *, n_kv: int, block: 
         tau = torch.empty((b, n_q, hq), dtype=torch.float32, device=dev)
     need = dash_block_entmax_workspace_bytes(q.dtype, b, n_q, q_pos0, n_kv, hq, hkv, d, block)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dev = _dev(q, kbar, mask, bias, tau, workspace)
     _check(lib().dash_block_entmax(
@@ -368,7 +374,7 @@ def dash_sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         o = torch.empty_like(q)
     need = dash_decode_workspace_bytes(b, n_ctx, hq, hkv, d, block)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dev = _dev(q, k_cache, v_cache, mask, bias, o, workspace)
     _check(lib().dash_sparse_attn_decode(
@@ -395,7 +401,7 @@ def dash_sparse_attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cac
         o = torch.empty_like(q)
     need = dash_decode_workspace_bytes(b, n_cap, hq, hkv, d, block)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dev = _dev(q, k_cache, v_cache, ctx_lens, mask, bias, o, workspace)
     _check(lib().dash_sparse_attn_decode_varlen(
@@ -435,11 +441,58 @@ def backward(q, k, v, dout, fwd: dict, *, block: int, alpha: float, gamma: float
     return dict(dq=dq, dk=dk, dv=dv, dbias=dbias)
 
 
+def dash_decode_step_workspace_bytes(batch, n_ctx, h_q, h_kv, head_dim, block) -> int:
+    return int(lib().dash_decode_step_workspace_bytes(batch, n_ctx, h_q, h_kv, head_dim, block))
+
+
+def dash_decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     kbar: torch.Tensor, *, block: int, alpha: float, gamma: float, sigma: float,
+                     ctx_lens: torch.Tensor | None = None, window_blocks: int = 1,
+                     scale: float | None = None, mask: torch.Tensor | None = None,
+                     bias: torch.Tensor | None = None, o: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None):
+    """One decode step (Stage 1 routing and Stage 2 attention, one call) for a new token per
+    sequence whose key/value are already in the cache: q [B, Hq, D] (or [B, 1, Hq, D]) ->
+    (o, mask, bias).
+    ctx_lens int32 [B] gives per-sequence lengths in a cache of capacity k_cache.shape[1]. A
+    workspace passed in must be zero-filled when allocated (it keeps its ticket counters zero)."""
+    _f32(kbar=kbar, bias=bias)
+    b, n_ctx, hkv, d = k_cache.shape
+    hq = q.shape[-2]
+    if ctx_lens is not None and ctx_lens.dtype != torch.int32:
+        raise TypeError("ctx_lens must be int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nc = -(-n_ctx // block)
+    if mask is None:
+        mask = torch.empty((b, 1, hkv, -(-nc // 32)), dtype=torch.int32, device=q.device)
+    if bias is None:
+        bias = torch.empty((b, 1, hkv, nc), dtype=torch.float32, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    need = dash_decode_step_workspace_bytes(b, n_ctx, hq, hkv, d, block)
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    dev = _dev(q, k_cache, v_cache, kbar, ctx_lens, mask, bias, o, workspace)
+    _check(lib().dash_decode_step(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(kbar), _ptr(ctx_lens), b,
+        n_ctx, hq, hkv, d, block, float(alpha), float(gamma), float(sigma), int(window_blocks),
+        float(scale), _ptr(mask), _ptr(bias), _ptr(o), _ptr(workspace), wsb, _stream(dev)))
+    return o, mask, bias
+
+
 def decode_step(q, k_cache, v_cache, kbar, *, block: int, alpha: float, gamma: float,
-                sigma: float, scale: float | None = None, route_ws=None, attn_ws=None):
+                sigma: float, scale: float | None = None, route_ws=None, attn_ws=None,
+                fused: bool = True, workspace=None):
     """One decode step for a new token per sequence whose key/value are already in the cache:
-    route with the cached summaries, then the split sparse attention. q [B, 1, Hq, D]."""
+    route with the cached summaries, then the split sparse attention. q [B, 1, Hq, D].
+    fused: one dash_decode_step call (workspace), else dash_block_entmax and
+    dash_sparse_attn_decode (route_ws, attn_ws). Returns (o, mask, bias)."""
     n_ctx = k_cache.shape[1]
+    if fused:
+        return dash_decode_step(q, k_cache, v_cache, kbar, block=block, alpha=alpha, gamma=gamma,
+                                sigma=sigma, scale=scale, workspace=workspace)
     mask, bias, _ = dash_block_entmax(q, kbar, n_kv=n_ctx, block=block, alpha=alpha, gamma=gamma,
                                       sigma=sigma, q_pos0=n_ctx - 1, h_kv=k_cache.shape[2],
                                       want_tau=False, workspace=route_ws)

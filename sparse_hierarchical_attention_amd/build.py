@@ -30,16 +30,28 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _headers_mtime() -> float:
-    hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
-    hs += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
-    return max([os.path.getmtime(h) for h in hs] + [os.path.getmtime(__file__)])
+def _deps_mtime(src: str) -> float:
+    """Newest modification time of src and the local headers it includes, transitively."""
+    seen, todo, newest = set(), [src], os.path.getmtime(__file__)
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(f):
+            continue
+        seen.add(f)
+        newest = max(newest, os.path.getmtime(f))
+        with open(f, encoding="utf-8") as fh:
+            for line in fh:
+                line = line.strip()
+                if line.startswith("#include \""):
+                    name = line.split('"')[1]
+                    todo += [os.path.join(CSRC, name), os.path.join(INCLUDE, name)]
+    return newest
 
 
 def _compile(src: str, force: bool = True) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     if (not force and os.path.exists(obj)
-            and os.path.getmtime(obj) > max(os.path.getmtime(src), _headers_mtime())):
+            and os.path.getmtime(obj) > _deps_mtime(src)):
         return obj
     cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -111,6 +111,13 @@ dash_status_t decode_call(const char* fn, const void* q, const void* k_cache, co
                           const float* bias, void* o, int batch, int n_ctx, int h_q, int h_kv,
                           int head_dim, int block, float scale, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+dash_status_t decode_step_call(const char* fn, const void* q, const void* k_cache,
+                               const void* v_cache, dash_dtype_t dt, const float* kbar,
+                               const int32_t* ctx_lens, int batch, int n_ctx, int h_q, int h_kv,
+                               int head_dim, int block, float alpha, float gamma, float sigma,
+                               int window_blocks, float scale, uint32_t* mask, float* bias,
+                               void* o, void* workspace, size_t workspace_bytes, bool use_scratch,
+                               hipStream_t stream);
 
 }  // namespace
 
@@ -356,6 +363,65 @@ dash_status_t decode_call(const char* fn, const void* q, const void* k_cache, co
         return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace ? workspace_bytes : (size_t)0);
     return hip_status(dash::launch_attn_decode(q, k_cache, v_cache, dt, mask, bias, o, p, workspace, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dash_decode_step_workspace_bytes(int batch, int n_ctx, int h_q, int h_kv, int head_dim,
+                                        int block) {
+    if (batch <= 0 || n_ctx <= 0 || h_q <= 0 || h_kv <= 0 || block <= 0 || h_q % h_kv) return 0;
+    const dash::RouteParams rp = route_params(batch, 1, n_ctx - 1, n_ctx, h_q, h_kv, head_dim,
+                                              block, 1.5f, 1.0f, 1.0f);
+    const dash::AttnParams p = attn_params(batch, 1, n_ctx - 1, n_ctx, h_q, h_kv, head_dim, block, 1.0f);
+    return dash::decode_step_workspace_bytes(rp, p);
+}
+
+dash_status_t dash_decode_step(const void* q, const void* k_cache, const void* v_cache,
+                               dash_dtype_t dt, const float* kbar, const int32_t* ctx_lens,
+                               int batch, int n_ctx, int h_q, int h_kv, int head_dim, int block,
+                               float alpha, float gamma, float sigma, int window_blocks,
+                               float scale, uint32_t* mask, float* bias, void* o, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    return decode_step_call("dash_decode_step", q, k_cache, v_cache, dt, kbar, ctx_lens, batch,
+                            n_ctx, h_q, h_kv, head_dim, block, alpha, gamma, sigma, window_blocks,
+                            scale, mask, bias, o, workspace, workspace_bytes, false, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+dash_status_t decode_step_call(const char* fn, const void* q, const void* k_cache,
+                               const void* v_cache, dash_dtype_t dt, const float* kbar,
+                               const int32_t* ctx_lens, int batch, int n_ctx, int h_q, int h_kv,
+                               int head_dim, int block, float alpha, float gamma, float sigma,
+                               int window_blocks, float scale, uint32_t* mask, float* bias,
+                               void* o, void* workspace, size_t workspace_bytes, bool use_scratch,
+                               hipStream_t stream) {
+    dash_status_t s = check_shape(fn, dt, batch, n_ctx, h_q, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (window_blocks < 1) return fail(DASH_ERR_INVALID, "%s: window_blocks=%d must be >= 1", fn, window_blocks);
+    if (!(alpha > 1.0f && alpha <= 2.0f)) return fail(DASH_ERR_INVALID, "%s: alpha=%g not in (1, 2]", fn, alpha);
+    if (!(gamma > 0.0f) || isinf(gamma)) return fail(DASH_ERR_INVALID, "%s: gamma=%g must be positive and finite", fn, gamma);
+    if (!(sigma > 0.0f)) return fail(DASH_ERR_INVALID, "%s: sigma=%g must be positive (or +inf)", fn, sigma);
+    if (!(scale > 0.0f) || isinf(scale)) return fail(DASH_ERR_INVALID, "%s: scale=%g must be positive and finite", fn, scale);
+    if (!q || !k_cache || !v_cache || (!kbar && n_ctx / block > 0) || !mask || !bias || !o)
+        return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    dash::RouteParams rp = route_params(batch, 1, n_ctx - 1, n_ctx, h_q, h_kv, head_dim, block,
+                                        alpha, gamma, sigma);
+    rp.win = window_blocks - 1;
+    rp.ctx_lens = ctx_lens;
+    dash::AttnParams p = attn_params(batch, 1, n_ctx - 1, n_ctx, h_q, h_kv, head_dim, block, scale);
+    p.ctx_lens = ctx_lens;
+    const size_t need = dash::decode_step_workspace_bytes(rp, p);
+    (void)use_scratch;
+    if (!workspace || workspace_bytes < need)
+        return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    return hip_status(dash::launch_decode_step(q, k_cache, v_cache, (int)dt, kbar, rp, p, mask,
+                                               bias, o, workspace, stream), fn);
 }
 
 }  // namespace

@@ -98,19 +98,17 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ q,
 // k, k + 4, ... of the row (all of its loads in flight at once), forms partial dot products
 // with every head of the group (the group's queries sit in LDS and are read as broadcasts), and
 // two DPP steps sum the quad; lane k then writes heads k, k + 4, ....
+// One workgroup of nthreads threads scores chunks c0 .. c0 + nthreads / 4 - 1 of (b, r); qs holds
+// g * D floats of LDS. Ends without a barrier after its stores.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void score_one_kernel(const T* __restrict__ q,
-                                                        const float* __restrict__ kbar,
-                                                        float* __restrict__ x, RouteParams p,
-                                                        float coef) {
+__device__ __forceinline__ void score_one_chunks(const T* __restrict__ q, const float* __restrict__ kbar,
+                                                 float* x, const RouteParams& p, float coef, int b,
+                                                 int r, int c0, int m, float* qs) {
     constexpr int NV = D / 16;  // float4 pieces per lane
-    __shared__ __align__(16) float qs[16 * D];
-    const int b = blockIdx.y / p.h_kv, r = blockIdx.y % p.h_kv;
-    const int m = route_cands(p, route_pos(p, b, 0));  // complete chunks before the window
     const int tid = threadIdx.x;
-    const int c = blockIdx.x * 64 + tid / 4;
+    const int c = c0 + tid / 4;
     const int k = tid & 3;
-    for (int e = tid; e < p.g * D; e += 256) {
+    for (int e = tid; e < p.g * D; e += blockDim.x) {
         const int gg = e / D, d = e % D;
         qs[gg * D + d] = to_f32(q[(((int64_t)b * p.n_q) * p.h_q + r * p.g + gg) * D + d]);
     }
@@ -145,6 +143,17 @@ __global__ __launch_bounds__(256) void score_one_kernel(const T* __restrict__ q,
         if (c < m && gg < p.g)
             x[(((int64_t)b * p.n_q) * p.h_q + r * p.g + gg) * p.nc + c] = coef * part[k];
     }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void score_one_kernel(const T* __restrict__ q,
+                                                        const float* __restrict__ kbar,
+                                                        float* __restrict__ x, RouteParams p,
+                                                        float coef) {
+    __shared__ __align__(16) float qs[16 * D];
+    const int b = blockIdx.y / p.h_kv, r = blockIdx.y % p.h_kv;
+    const int m = route_cands(p, route_pos(p, b, 0));  // complete chunks before the window
+    score_one_chunks<T, D>(q, kbar, x, p, coef, b, r, blockIdx.x * 64, m, qs);
 }
 
 // ----------------------------------------------------------------------------- routing
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(1024) void route_decode_kernel(const float* __restr
     const int pos = route_pos(p, b, 0);
     const DecodeRouteLds lds{red, stat_s, stat_n, cand_n, tau_h, cand, wsum};
     const float* xg = x + ((int64_t)b * p.h_q + (int64_t)r * p.g) * p.nc;
-    decode_route_group<NS, KIND, WPH>([&](int hh) { return xg + (int64_t)hh * p.nc; },
+    decode_route_group<NS, KIND, WPH>([&](int hh, int c) { return xg[(int64_t)hh * p.nc + c]; },
                                       route_cands(p, pos), pos / p.block, p, lds,
                                       mask + ((int64_t)b * p.h_kv + r) * p.nw,
                                       bias + ((int64_t)b * p.h_kv + r) * p.nc,

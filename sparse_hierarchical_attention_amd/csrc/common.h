@@ -74,6 +74,16 @@ __device__ __forceinline__ float halves_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// Rows of 16 lanes in pairs (rows 0 and 1, rows 2 and 3): v_permlane16_swap hands each lane
+// the value of the same lane in the other row of its pair; every lane gets its pair's result.
+__device__ __forceinline__ float rowpair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float rowpair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_f<0xb1, 0xf>(-INFINITY, v));
     v = fmaxf(v, dpp_f<0x4e, 0xf>(-INFINITY, v));
@@ -103,5 +113,34 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 }
 
 __host__ __device__ constexpr int div_up(int a, int b) { return (a + b - 1) / b; }
+
+// Hand-over of data between the workgroups of one launch. Each XCD of the MI355X has its own L2,
+// and a device-scope fence writes back and invalidates the whole L2 (a walk of every line), far
+// too slow to issue from every workgroup. Data that one workgroup hands to another is therefore
+// stored and loaded as device-scope relaxed atomics, which the hardware keeps coherent across the
+// XCDs line by line (write-through stores, loads that do not trust a stale L2 copy). The writer
+// waits until its stores are acknowledged before it takes a ticket (device-scope atomic add on a
+// per-item counter); the workgroup that draws the last ticket then reads everything the others
+// stored. Nothing ever waits for another workgroup.
+__device__ __forceinline__ void handoff_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float handoff_load(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Called by every thread of the workgroup after its hand-over stores: true in the workgroup that
+// took ticket n - 1 of *counter (n tickets are drawn per item), which also resets the counter to
+// zero for the next launch. `flag` is one int of LDS.
+__device__ __forceinline__ bool handoff_last(unsigned* counter, unsigned n, int* flag) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned t = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = t == n - 1;
+        if (t == n - 1) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return *flag != 0;
+}
 
 }  // namespace dash

@@ -5,11 +5,15 @@
 // unit u to slot u % S, where S grows with the selection: 32 slots up to 256 units, then one per
 // 8 units up to 128 (dec_slots), so that a (sequence, group) that routed hundreds of chunks (a
 // short sequence whose candidates hold no clear peak) does not serialise the step while the
-// others wait. decode_split_kernel: each wave owns one slot (and, for groups of more than four
-// heads, one set of four heads); a workgroup whose slots are all past S leaves at once; the waves
-// of a workgroup merge their slots in LDS and write one partial (unnormalised output, max, sum)
-// per head to the workspace. decode_combine_kernel recounts S from the mask and merges the
-// partials of the S / (slots per workgroup) workgroups in order.
+// others wait. Each wave owns one slot (and, for groups of more than four heads, one set of four
+// heads); a workgroup whose slots are all past S leaves at once; the waves of a workgroup merge
+// their slots in LDS and write one partial (unnormalised output, max, sum) per head to the
+// workspace as a hand-over (common.h). The last workgroup of a (sequence, group) to finish merges
+// the partials of all of them, in slot order, into the output: every workgroup stores its
+// partial, then takes a ticket from the (sequence, group)'s counter; the one that draws the last
+// ticket merges and resets the counter to zero for the next call. No workgroup ever waits for
+// another, and the merge order does not depend on which workgroup is last, so the output is
+// deterministic.
 #include <math.h>
 
 #include "common.h"
@@ -35,57 +39,43 @@ __host__ __device__ constexpr int dec_workgroups(int g, int slots = kDecodeMaxSl
     return slots * dec_waves_per_slot(g) / 4;
 }
 
-// units of the (sequence, group)'s selection: its chunks below the own chunk cp whose bit is set
-// (whole chunks) and the own chunk (all of its units counted; those past the query are empty)
-__device__ __forceinline__ int dec_units(const uint32_t* mrow, int cp) {
-    int total = 0;
-    for (int wd = threadIdx.x; wd <= cp / 32; wd += blockDim.x) {
-        uint32_t word = mrow[wd];
-        const int hi = cp - 32 * wd;
-        if (hi < 31) word &= (2u << hi) - 1u;
-        if (hi < 32) word |= 1u << hi;
-        total += __popc(word);
-    }
-    return total;  // this thread's share; the caller sums over the workgroup
-}
-
-// workspace: [B, H_kv, dec_workgroups(g), g, D + 4] floats: D unnormalised outputs, max (log2),
-// sum, two floats of padding (16-byte aligned records)
+// LDS of one (sequence, group)'s attention in a workgroup of four waves.
 template <typename T, int D, int GQ>
-__global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__ q,
-                                                           const T* __restrict__ k,
-                                                           const T* __restrict__ v,
-                                                           const uint32_t* __restrict__ mask,
-                                                           const float* __restrict__ bias,
-                                                           float* __restrict__ ws, AttnParams p) {
+struct DecodeLds {
+    static constexpr int HPW = dec_heads_per_wave(GQ);
+    T qs[GQ * D];                          // the group's queries
+    float part[4][HPW][D + 4];             // the waves' partials
+    int wtot[4];
+    uint16_t chunks[kDecMaxWords * 32];    // rank -> chunk (then the merge's (max, sum) pairs)
+};
+
+// The attention of query (b, r) by slot set s of the grid's gridDim.z (four waves; the group's
+// queries already in L.qs, visible after the next barrier): the selected chunks come from
+// word_of(i), the mask words, and bias_of(c); the workgroup's partial goes to the group's records
+// in ws as a hand-over, and the last of the group's working workgroups merges them into o.
+// ws: partial records [B, H_kv, gridDim.z, g, D + 4] floats (D unnormalised outputs, max (log2),
+// sum, two floats of padding: 16-byte aligned records); tickets: one counter per (sequence,
+// group), zero between calls.
+template <typename T, int D, int GQ, class WORD, class BIAS>
+__device__ __forceinline__ void decode_attend_group(const T* __restrict__ k, const T* __restrict__ v,
+                                                    WORD word_of, BIAS bias_of, float* ws,
+                                                    unsigned* tickets, T* __restrict__ o,
+                                                    const AttnParams& p, int b, int r, int s,
+                                                    DecodeLds<T, D, GQ>& L) {
     constexpr int WPS = dec_waves_per_slot(GQ);  // waves per slot (sets of four heads)
     constexpr int HPW = dec_heads_per_wave(GQ);  // heads per wave
     constexpr int SPW = 4 / WPS;                 // slots per workgroup
     constexpr int DS = D + 4;                    // workspace record
     using Wave = DecodeWave<T, D, HPW>;
-    __shared__ __align__(16) T qs[GQ * D];
-    __shared__ __align__(16) float part[4][HPW][DS];
-    __shared__ int wtot[4];
-    __shared__ uint16_t chunks[kDecMaxWords * 32];  // rank -> chunk
-
-    // the slot-set index is the slowest grid dimension: the workgroups every (sequence, group)
-    // uses (the first 32 slots) are dispatched first, the extra ones for long selections last
-    const int r = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = p.n_kv;  // cache capacity (the row stride of K and V)
     const int pos = seq_pos(p.ctx_lens, n - 1, n, b, 0);
     const int cp = pos / p.block;
-    const uint32_t* mrow = mask + ((int64_t)b * p.h_kv + r) * p.nw;
-    const float* brow = bias + ((int64_t)b * p.h_kv + r) * p.nc;
 
-    const int total = chunk_list([&](int i) { return mrow[i]; }, cp, wtot, chunks);
+    const int total = chunk_list(word_of, cp, L.wtot, L.chunks);  // ends with a barrier
     const int upc = (p.block + kDecUnit - 1) / kDecUnit;  // units per chunk
-    const int slots = dec_slots(total * upc);
+    const int slots = min(dec_slots(total * upc), (int)gridDim.z * SPW);
     if (s * SPW >= slots) return;  // every slot of this workgroup is idle (uniform)
-    for (int e = tid; e < GQ * D / Wave::EPL; e += 256)
-        reinterpret_cast<uint4*>(qs)[e] =
-            reinterpret_cast<const uint4*>(q + ((int64_t)b * p.h_q + r * GQ) * D)[e];
-    __syncthreads();
 
     const int cs = wave / WPS;              // slot within the workgroup
     const int h0 = (wave % WPS) * HPW;      // first head of this wave within the group
@@ -97,100 +87,118 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__
     uint4 qp[HPW];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
-        qp[hh] = *reinterpret_cast<const uint4*>(&qs[(h0 + hh) * D + li * Wave::EPL]);
+        qp[hh] = *reinterpret_cast<const uint4*>(&L.qs[(h0 + hh) * D + li * Wave::EPL]);
     Wave st;
     st.init();
-    st.run(kb, vb, kv_stride, qp, chunks, total * upc, s * SPW + cs, slots, upc, p.block,
-           pos, cp, p.scale * kDecLog2e, [&](int c) { return brow[c]; });
-    st.store(&part[wave][0][0]);
+    st.run(kb, vb, kv_stride, qp, L.chunks, total * upc, s * SPW + cs, slots, upc, p.block,
+           pos, cp, p.scale * kDecLog2e, bias_of);
+    st.store(&L.part[wave][0][0]);
     __syncthreads();
     // merge the workgroup's slots (waves cs * WPS + set, in slot order) per head; an empty slot
     // has max = -inf and sum = 0
-    for (int e = tid; e < GQ * D; e += 256) {
+    float* grp = ws + ((int64_t)b * p.h_kv + r) * gridDim.z * GQ * DS;  // this group's records
+    for (int e = tid; e < GQ * D; e += blockDim.x) {
         const int hg = e / D, d = e % D;
         const int set = hg / HPW, hh = hg % HPW;
         float mx = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < SPW; ++c) mx = fmaxf(mx, part[c * WPS + set][hh][D]);
-        const float2 ol = merge_parts([&](int c) { return &part[c * WPS + set][hh][0]; }, SPW, D, d);
-        float* out = ws + ((((int64_t)b * p.h_kv + r) * gridDim.z + s) * GQ + hg) * DS;
-        out[d] = ol.x;
+        for (int c = 0; c < SPW; ++c) mx = fmaxf(mx, L.part[c * WPS + set][hh][D]);
+        const float2 ol = merge_parts([&](int c) { return &L.part[c * WPS + set][hh][0]; }, SPW, D, d);
+        float* out = grp + ((int64_t)s * GQ + hg) * DS;
+        handoff_store(out + d, ol.x);
         if (d == 0) {
-            out[D] = mx;
-            out[D + 1] = ol.y;
+            handoff_store(out + D, mx);
+            handoff_store(out + D + 1, ol.y);
         }
+    }
+
+    // take a ticket; the last of the group's np working workgroups merges all partials in order
+    const int np = slots / SPW;
+    __shared__ int last;
+    if (!handoff_last(&tickets[(int64_t)b * p.h_kv + r], (unsigned)np, &last)) return;
+    // every partial's (max, sum) into LDS (over the chunk list, no longer needed), then each
+    // thread merges its outputs in record order, eight records' loads in flight at a time
+    float* ml = reinterpret_cast<float*>(L.chunks);  // [np][GQ][2]
+    for (int i = tid; i < np * GQ; i += blockDim.x) {
+        const float* pr = grp + (int64_t)i * DS;
+        ml[2 * i] = handoff_load(pr + D);
+        ml[2 * i + 1] = handoff_load(pr + D + 1);
+    }
+    __syncthreads();
+    T* orow = o + ((int64_t)b * p.h_q + r * GQ) * D;
+    for (int e = tid; e < GQ * D; e += blockDim.x) {
+        const int hg = e / D, d = e % D;
+        float mx = -INFINITY;
+        for (int c = 0; c < np; ++c) mx = fmaxf(mx, ml[2 * (c * GQ + hg)]);
+        float acc = 0.f, l = 0.f;
+        for (int c0 = 0; c0 < np; c0 += 8) {
+            float ov[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                ov[j] = c0 + j < np ? handoff_load(grp + ((int64_t)(c0 + j) * GQ + hg) * DS + d) : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (c0 + j >= np) break;
+                const float mc = ml[2 * ((c0 + j) * GQ + hg)];
+                const float f = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - mx);
+                acc = f > 0.f ? fmaf(f, ov[j], acc) : acc;
+                l = fmaf(f, ml[2 * ((c0 + j) * GQ + hg) + 1], l);
+            }
+        }
+        store_elem(orow + e, acc / l);
     }
 }
 
-template <typename T, int D, int WPS>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const uint32_t* __restrict__ mask,
-                                                            const float* __restrict__ ws,
-                                                            T* __restrict__ o, AttnParams p) {
-    constexpr int DPL = D / 64;
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int r = h / p.g, hh = h % p.g;
-    const int lane = threadIdx.x;
-    const int n = p.n_kv;
-    const int cp = seq_pos(p.ctx_lens, n - 1, n, b, 0) / p.block;
-    const int upc = (p.block + kDecUnit - 1) / kDecUnit;
-    const int units = wave_sum_int(dec_units(mask + ((int64_t)b * p.h_kv + r) * p.nw, cp)) * upc;
-    const int np = dec_slots(units) * WPS / 4;  // workgroups that wrote a partial, in order
-    const int nmax = dec_workgroups(p.g);
-    const float* base = ws + (((int64_t)b * p.h_kv + r) * nmax * p.g + hh) * (D + 4);
-    const int64_t part_stride = (int64_t)p.g * (D + 4);
-    // batches of 8 partials: their loads are issued together, then merged into a running
-    // (max, sum, output) in partial order
-    constexpr int NB = 8;
-    float mx = -INFINITY, l = 0.f, acc[DPL];
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) acc[dd] = 0.f;
-    for (int s0 = 0; s0 < np; s0 += NB) {
-        float ms[NB], ls[NB], os[NB][DPL];
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const bool in = s0 + i < np;
-            const float* pr = base + (int64_t)(in ? s0 + i : 0) * part_stride;
-            ms[i] = in ? pr[D] : -INFINITY;
-            ls[i] = in ? pr[D + 1] : 0.f;
-#pragma unroll
-            for (int dd = 0; dd < DPL; ++dd) os[i][dd] = in ? pr[lane + 64 * dd] : 0.f;
-        }
-        float bm = mx;
-#pragma unroll
-        for (int i = 0; i < NB; ++i) bm = fmaxf(bm, ms[i]);
-        const float fr = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - bm);
-        l *= fr;
-#pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) acc[dd] *= fr;
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const float f = ms[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[i] - bm);
-            l = fmaf(f, ls[i], l);
-#pragma unroll
-            for (int dd = 0; dd < DPL; ++dd) acc[dd] = f > 0.f ? fmaf(f, os[i][dd], acc[dd]) : acc[dd];
-        }
-        mx = bm;
-    }
-    const float inv = 1.0f / l;
-    T* orow = o + ((int64_t)b * p.h_q + h) * D;
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) store_elem(orow + lane + 64 * dd, acc[dd] * inv);
+// the group's queries into LDS (16-byte loads; visible after the next barrier)
+template <typename T, int D, int GQ>
+__device__ __forceinline__ void decode_load_q(const T* __restrict__ q, int b, int r,
+                                              const AttnParams& p, T* qs) {
+    for (int e = threadIdx.x; e < GQ * D * (int)sizeof(T) / 16; e += blockDim.x)
+        reinterpret_cast<uint4*>(qs)[e] =
+            reinterpret_cast<const uint4*>(q + ((int64_t)b * p.h_q + r * GQ) * D)[e];
+}
+
+// Stage 2 from a given mask and bias. The slot-set index is the slowest grid dimension: the
+// workgroups every (sequence, group) uses (the first 32 slots) are dispatched first, the extra
+// ones for long selections last.
+template <typename T, int D, int GQ>
+__global__ __launch_bounds__(256) void decode_split_kernel(const T* __restrict__ q,
+                                                           const T* __restrict__ k,
+                                                           const T* __restrict__ v,
+                                                           const uint32_t* __restrict__ mask,
+                                                           const float* __restrict__ bias,
+                                                           float* ws, unsigned* tickets,
+                                                           T* __restrict__ o, AttnParams p) {
+    __shared__ __align__(16) DecodeLds<T, D, GQ> L;
+    const int r = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
+    const uint32_t* mrow = mask + ((int64_t)b * p.h_kv + r) * p.nw;
+    const float* brow = bias + ((int64_t)b * p.h_kv + r) * p.nc;
+    decode_load_q<T, D, GQ>(q, b, r, p, L.qs);
+    decode_attend_group<T, D, GQ>(k, v, [&](int i) { return mrow[i]; },
+                                  [&](int c) { return brow[c]; }, ws, tickets, o, p, b, r, s, L);
+}
+
+// one ticket counter per (sequence, group) at the start of the workspace (so that calls of any
+// batch size share the same words), padded to 256 bytes, then the partial records
+static size_t decode_ticket_bytes(const AttnParams& p) {
+    return ((size_t)p.batch * p.h_kv * sizeof(unsigned) + 255) / 256 * 256;
 }
 
 size_t decode_workspace_bytes(const AttnParams& p) {
-    return (size_t)p.batch * p.h_kv * dec_workgroups(p.g) * p.g * (p.head_dim + 4) * sizeof(float);
+    return decode_ticket_bytes(p) +
+           (size_t)p.batch * p.h_kv * dec_workgroups(p.g) * p.g * (p.head_dim + 4) * sizeof(float);
 }
 
 template <typename T, int D>
 static void launch_decode_t(const void* q, const void* k, const void* v, const uint32_t* mask,
                             const float* bias, void* o, const AttnParams& p, float* ws,
                             hipStream_t st) {
+    unsigned* tickets = reinterpret_cast<unsigned*>(ws);
+    ws = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + decode_ticket_bytes(p));
 #define DASH_DEC(GG)                                                                           \
     hipLaunchKernelGGL((decode_split_kernel<T, D, GG>), dim3(p.h_kv, p.batch, dec_workgroups(GG)), \
                        dim3(256), 0, st, static_cast<const T*>(q), static_cast<const T*>(k),     \
-                       static_cast<const T*>(v), mask, bias, ws, p);                             \
-    hipLaunchKernelGGL((decode_combine_kernel<T, D, dec_waves_per_slot(GG)>), dim3(p.h_q, p.batch), \
-                       dim3(64), 0, st, mask, ws, static_cast<T*>(o), p)
+                       static_cast<const T*>(v), mask, bias, ws, tickets, static_cast<T*>(o), p)
     switch (p.g) {
         case 1: DASH_DEC(1); break;
         case 2: DASH_DEC(2); break;
@@ -213,6 +221,21 @@ hipError_t launch_attn_decode(const void* q, const void* k, const void* v, int d
         else launch_decode_t<float, 128>(q, k, v, mask, bias, o, p, w, st);
     }
     return hipGetLastError();
+}
+
+// The decode step: [tickets | partial records] as dash_sparse_attn_decode's workspace, then the
+// scores [B, H_q, Nc] fp32 that Stage 1 of decode works through.
+size_t decode_step_workspace_bytes(const RouteParams& rp, const AttnParams& p) {
+    return decode_workspace_bytes(p) + route_workspace_bytes(rp, kF32);
+}
+
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, int dt,
+                              const float* kbar, const RouteParams& rp, const AttnParams& p,
+                              uint32_t* mask, float* bias, void* o, void* ws, hipStream_t st) {
+    void* route_ws = static_cast<char*>(ws) + decode_workspace_bytes(p);
+    const hipError_t e = launch_block_entmax(q, dt, kbar, rp, mask, bias, nullptr, route_ws, st);
+    if (e != hipSuccess) return e;
+    return launch_attn_decode(q, k, v, dt, mask, bias, o, p, ws, st);
 }
 
 }  // namespace dash

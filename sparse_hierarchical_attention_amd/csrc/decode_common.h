@@ -29,8 +29,23 @@ __device__ __forceinline__ float seg_sum(float v) {
     v += dpp_f<0x4e, 0xf>(0.f, v);       // quads
     v += dpp_f<0x141, 0xf>(0.f, v);      // half rows (8 lanes)
     if (LANES >= 16) v += dpp_f<0x140, 0xf>(0.f, v);  // rows (16 lanes)
-    if (LANES >= 32) v += __shfl_xor(v, 16, 64);
+    if (LANES >= 32) v = rowpair_sum(v);
     return v;
+}
+
+// Sum / maximum over the lanes l, l + LANES, l + 2 LANES, ... (LANES = 8, 16 or 32): the lanes of a
+// wave that hold the same position of different key rows. Every lane gets the result.
+template <int LANES>
+__device__ __forceinline__ float cross_sum(float v) {
+    if (LANES == 8) v += dpp_f<0x128, 0xf>(0.f, v);  // row_ror:8, the other half of the row
+    if (LANES <= 16) v = rowpair_sum(v);
+    return halves_sum(v);
+}
+template <int LANES>
+__device__ __forceinline__ float cross_max(float v) {
+    if (LANES == 8) v = fmaxf(v, dpp_f<0x128, 0xf>(-INFINITY, v));
+    if (LANES <= 16) v = rowpair_max(v);
+    return halves_max(v);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -170,8 +185,7 @@ struct DecodeWave {
                 float mx = sc[hh][0];
 #pragma unroll
                 for (int i = 1; i < NI; ++i) mx = fmaxf(mx, sc[hh][i]);
-#pragma unroll
-                for (int o = LPK; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                mx = cross_max<LPK>(mx);
                 const float m_new = fmaxf(m_run[hh], mx);
                 const float corr = __builtin_amdgcn_exp2f(m_run[hh] - m_new);
                 m_run[hh] = m_new;
@@ -204,12 +218,9 @@ struct DecodeWave {
         const int seg = lane / LPK, li = lane % LPK;
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
+            l_run[hh] = cross_sum<LPK>(l_run[hh]);
 #pragma unroll
-            for (int o = LPK; o < 64; o <<= 1) {
-                l_run[hh] += __shfl_xor(l_run[hh], o, 64);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], o, 64);
-            }
+            for (int e = 0; e < EPL; ++e) acc[hh][e] = cross_sum<LPK>(acc[hh][e]);
         }
         if (seg == 0) {
 #pragma unroll

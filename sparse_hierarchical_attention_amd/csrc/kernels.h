@@ -86,6 +86,11 @@ size_t decode_workspace_bytes(const AttnParams& p);
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, int dt,
                               const uint32_t* mask, const float* bias, void* o,
                               const AttnParams& p, void* ws, hipStream_t st);
+// the decode step (dash_decode_step): scores, then routing and attention in one kernel
+size_t decode_step_workspace_bytes(const RouteParams& rp, const AttnParams& p);
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, int dt,
+                              const float* kbar, const RouteParams& rp, const AttnParams& p,
+                              uint32_t* mask, float* bias, void* o, void* ws, hipStream_t st);
 size_t attn_backward_workspace_bytes(const AttnParams& p);
 hipError_t launch_attn_backward_mfma(const void* q, const void* k, const void* v,
                                      const float* lse, const void* dout, const uint32_t* mask,

@@ -134,12 +134,12 @@ struct DecodeRouteLds {
 // are each spread over WPH waves (entry c in lane c % 64 of the head's wave (c / 64) % WPH, slot
 // c / (64 WPH)), which solve the head's threshold together; the heads' probabilities are added
 // in head order in LDS; then every wave takes part in writing the mask words and the bias.
-// xrow(hh): the scores of head hh of the group (m entries, c < m the routing candidates; cp
+// xat(hh, c): score c of head hh of the group (m entries, c < m the routing candidates; cp
 // the query's own chunk, chunks m .. cp its window). Outputs, each optional (null): the global
 // mask row mrow and bias row brow (routed entries and the window), tau_out[hh], the mask words
 // mw and, for every chunk whose bit is set, its bias bl[c] (both in LDS, for a fused Stage 2).
-template <int NS, int KIND, int WPH, class XROW>
-__device__ __forceinline__ void decode_route_group(XROW xrow, int m, int cp, const RouteParams& p,
+template <int NS, int KIND, int WPH, class XAT>
+__device__ __forceinline__ void decode_route_group(XAT xat, int m, int cp, const RouteParams& p,
                                                    const DecodeRouteLds& s, uint32_t* mrow,
                                                    float* brow, float* tau_out, uint32_t* mw,
                                                    float* bl) {
@@ -158,11 +158,10 @@ __device__ __forceinline__ void decode_route_group(XROW xrow, int m, int cp, con
     const float e = 1.0f / (p.alpha - 1.0f);
 
     // the row, loads unconditional (clamped into the row) so that all are in flight together
-    const float* xr = xrow(hh);
     const int last = m > 0 ? m - 1 : 0;
     float xv[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) xv[i] = xr[min(i * L + wq * 64 + lane, last)];
+    for (int i = 0; i < NS; ++i) xv[i] = xat(hh, min(i * L + wq * 64 + lane, last));
 #pragma unroll
     for (int i = 0; i < NS; ++i)
         if (i * L + wq * 64 + lane >= m) xv[i] = -INFINITY;

@@ -100,7 +100,9 @@ def test_attention_rejects_bad_arguments(L):
     assert "scale" in err(L)
     assert L.dash_sparse_attn_prefill(p, p, p, 1, p, p, None, None, 1, 64, 4, 2, 128, 64, 0.1, None) == 1
     need = L.dash_decode_workspace_bytes(2, 4096, 8, 2, 128, 64)
-    assert need > 0
+    # ticket counters (256 B), then the partial records of up to 128 slots (32 workgroups of
+    # four slots at g = 4) for each (sequence, group)
+    assert need == 256 + 2 * 2 * 32 * 4 * (128 + 4) * 4
     assert L.dash_sparse_attn_decode(p, p, p, 1, p, p, p, 2, 4096, 8, 2, 128, 64, 0.1, p,
                                      need - 1, None) == 3
     assert L.dash_sparse_attn_decode(p, p, p, 1, p, p, p, 2, 4096, 8, 2, 128, 64, 0.1, None,

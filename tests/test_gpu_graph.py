@@ -33,8 +33,9 @@ def capture(step):
     return g
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("varlen", [False, True])
-def test_decode_step_graph_replays(dash, varlen):
+def test_decode_step_graph_replays(dash, varlen, fused):
     w = wl.Workload("graph decode", 4, 4096 + 17, 32, 8, 128, 64, 1.5, 1.5, 1.0, decode=True,
                     plant="decode", plant_args=dict(lo=1, hi=8), seed=41)
     inp = wl.make_inputs(w, DEV)
@@ -44,16 +45,24 @@ def test_decode_step_graph_replays(dash, varlen):
     mask = torch.empty((w.batch, 1, w.h_kv, -(-nc // 32)), dtype=torch.int32, device=DEV)
     bias = torch.empty((w.batch, 1, w.h_kv, nc), dtype=torch.float32, device=DEV)
     o = torch.empty_like(q)
-    rws = torch.empty(max(1, dash.dash_block_entmax_workspace_bytes(
+    rws = torch.zeros(max(1, dash.dash_block_entmax_workspace_bytes(
         q.dtype, w.batch, 1, w.n_kv - 1, w.n_kv, w.h_q, w.h_kv, w.head_dim, w.block)),
         dtype=torch.uint8, device=DEV)
     awb = dash.dash_decode_workspace_bytes(w.batch, w.n_kv, w.h_q, w.h_kv, w.head_dim, w.block)
-    aws = torch.empty(awb, dtype=torch.uint8, device=DEV) if awb else None
+    aws = torch.zeros(awb, dtype=torch.uint8, device=DEV) if awb else None
+    sws = torch.zeros(dash.dash_decode_step_workspace_bytes(w.batch, w.n_kv, w.h_q, w.h_kv,
+                                                            w.head_dim, w.block),
+                      dtype=torch.uint8, device=DEV)
     lens = wl.ragged_lengths(w.batch, w.n_kv, 42, DEV)
     kw = dict(block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma)
 
     def step():
-        if varlen:
+        if fused:
+            if varlen:
+                dash.dash_pool_keys_append(k, lens, kbar, w.block)
+            dash.dash_decode_step(q, k, v, kbar, ctx_lens=lens if varlen else None, mask=mask,
+                                  bias=bias, o=o, workspace=sws, **kw)
+        elif varlen:
             dash.dash_pool_keys_append(k, lens, kbar, w.block)
             dash.dash_block_entmax_ex(q, kbar, n_kv=w.n_kv, h_kv=w.h_kv, ctx_lens=lens, mask=mask,
                                       bias=bias, want_tau=False, workspace=rws, **kw)

@@ -253,6 +253,63 @@ def test_decode_small(dash, orc, n_ctx, block):
                          max_flip_frac=0.34)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_tickets_reset_between_calls(dash, fused):
+    """Decode attention hands the merge to the last workgroup of each (sequence, group) through
+    ticket counters kept in its workspace: calls that reuse the same workspaces, with another
+    batch size in between, give bit for bit the outputs of calls on fresh workspaces (the two
+    separate calls, and the fused decode step)."""
+    big = wl.Workload("decode tickets", 6, 4096 + 17, 32, 8, 128, 64, 1.5, 1.5, 1.0, decode=True,
+                      plant="decode", plant_args=dict(lo=1, hi=8), seed=44)
+    small = big.with_(batch=2, seed=45)
+    if fused:
+        ws = torch.zeros(dash.dash_decode_step_workspace_bytes(big.batch, big.n_kv, 32, 8, 128, 64),
+                         dtype=torch.uint8, device=DEV)
+        kw = lambda: dict(workspace=ws)
+    else:
+        rws = torch.zeros(dash.dash_block_entmax_workspace_bytes(
+            torch.bfloat16, big.batch, 1, big.n_kv - 1, big.n_kv, 32, 8, 128, 64),
+            dtype=torch.uint8, device=DEV)
+        ws = torch.zeros(dash.dash_decode_workspace_bytes(big.batch, big.n_kv, 32, 8, 128, 64),
+                         dtype=torch.uint8, device=DEV)
+        kw = lambda: dict(route_ws=rws, attn_ws=ws)
+
+    def run(w, reuse):
+        inp = wl.make_inputs(w, DEV)
+        kbar = dash.dash_pool_keys(inp["k"], w.block)
+        o, mask, bias = dash.decode_step(inp["q"], inp["k"], inp["v"], kbar, block=w.block,
+                                         alpha=w.alpha, gamma=w.gamma, sigma=w.sigma,
+                                         fused=fused, **(kw() if reuse else {}))
+        torch.cuda.synchronize()
+        return o.clone(), mask.clone()
+
+    fresh_big, fresh_small = run(big, False), run(small, False)
+    for _ in range(2):
+        for w, want in ((big, fresh_big), (small, fresh_small), (big, fresh_big)):
+            got = run(w, True)
+            assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1])
+    # the ticket words at the start of the attention workspace are zero again after the calls
+    assert not torch.any(ws[:4 * big.batch * 8]) and torch.any(ws[4 * big.batch * 8:])
+
+
+def test_decode_step_matches_two_calls(dash):
+    """dash_decode_step gives bit for bit the outputs of dash_block_entmax followed by
+    dash_sparse_attn_decode."""
+    w = wl.Workload("decode step", 5, 8192 + 33, 32, 8, 128, 64, 1.5, 1.5, 1.0, decode=True,
+                    plant="decode", plant_args=dict(lo=1, hi=8), seed=46)
+    inp = wl.make_inputs(w, DEV)
+    kbar = dash.dash_pool_keys(inp["k"], w.block)
+    a = dash.decode_step(inp["q"], inp["k"], inp["v"], kbar, block=w.block, alpha=w.alpha,
+                         gamma=w.gamma, sigma=w.sigma, fused=True)
+    b = dash.decode_step(inp["q"], inp["k"], inp["v"], kbar, block=w.block, alpha=w.alpha,
+                         gamma=w.gamma, sigma=w.sigma, fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1]), "masks differ"
+    m = parity.bits(parity.to_host(a[1]), -(-w.n_kv // w.block))
+    assert np.array_equal(parity.to_host(a[2])[m], parity.to_host(b[2])[m])
+    assert torch.equal(a[0], b[0])
+
+
 # ------------------------------------------------------------------------------ properties
 
 def test_deterministic(dash):

@@ -57,25 +57,32 @@ def test_window_prefill(dash, orc, window, dtype, n, hq, hkv, d, block):
     window_bias_is_zero(flat_rows(bias, rows), ref["mask"], ref["w"], -(-n // block))
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("window", [1, 2, 4])
-def test_window_decode(dash, orc, window):
+def test_window_decode(dash, orc, window, fused):
     n, block = 4096 + 40, 64
     w = wl.Workload("window decode", 3, n, 8, 2, 128, block, 1.5, 1.5, 1.0, decode=True,
                     plant="decode", plant_args=dict(lo=1, hi=8), seed=82)
     inp = wl.make_inputs(w, DEV)
     q, k, v = inp["q"], inp["k"], inp["v"]
     kbar = dash.dash_pool_keys(k, block)
-    mask, bias, tau = dash.dash_block_entmax_ex(q, kbar, n_kv=n, block=block, alpha=1.5,
-                                                gamma=1.5, sigma=1.0, q_pos0=n - 1, h_kv=2,
-                                                window_blocks=window)
-    o = dash.dash_sparse_attn_decode(q, k, v, mask, bias, block=block)
+    if fused:
+        o, mask, bias = dash.dash_decode_step(q, k, v, kbar, block=block, alpha=1.5, gamma=1.5,
+                                              sigma=1.0, window_blocks=window)
+        tau = None
+    else:
+        mask, bias, tau = dash.dash_block_entmax_ex(q, kbar, n_kv=n, block=block, alpha=1.5,
+                                                    gamma=1.5, sigma=1.0, q_pos0=n - 1, h_kv=2,
+                                                    window_blocks=window)
+        o = dash.dash_sparse_attn_decode(q, k, v, mask, bias, block=block)
     torch.cuda.synchronize()
     ref = orc.forward(host(q), host(k), host(v), block=block, alpha=1.5, gamma=1.5, sigma=1.0,
                       q_pos0=n - 1, window=window)
     rows = np.arange(w.batch)
     parity.check_forward(orc, host(q), host(k), host(v), ref, mask=flat_rows(mask, rows),
-                         bias=flat_rows(bias, rows), tau=flat_rows(tau, rows), o=flat_rows(o, rows),
-                         rows=rows, n_kv=n, block=block, h_kv=2, q_pos=np.full(w.batch, n - 1),
+                         bias=flat_rows(bias, rows), tau=None if tau is None else flat_rows(tau, rows),
+                         o=flat_rows(o, rows), rows=rows, n_kv=n, block=block, h_kv=2,
+                         q_pos=np.full(w.batch, n - 1),
                          q_pos0=n - 1, alpha=1.5, sigma=1.0, dtype="bf16",
                          vmax=float(v.abs().max()), max_flip_frac=0.34)
     window_bias_is_zero(flat_rows(bias, rows), ref["mask"], ref["w"], -(-n // block))
@@ -114,8 +121,9 @@ def orc_module():
     return oracle
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("window", [1, 2])
-def test_varlen_decode(dash, orc, window):
+def test_varlen_decode(dash, orc, window, fused):
     """One cache of capacity 5000 holding sequences of different lengths: a single token, chunk
     edges on both sides, a ragged middle length and a full cache."""
     cap, block = 5000, 64
@@ -126,15 +134,21 @@ def test_varlen_decode(dash, orc, window):
     q, k, v = inp["q"], inp["k"], inp["v"]
     ctx = torch.tensor(lens, dtype=torch.int32, device=DEV)
     kbar = dash.dash_pool_keys(k, block)  # summaries past a sequence's length are never read
-    mask, bias, tau = dash.dash_block_entmax_ex(q, kbar, n_kv=cap, block=block, alpha=1.5,
-                                                gamma=1.5, sigma=1.0, h_kv=2, ctx_lens=ctx,
-                                                window_blocks=window)
-    o = dash.dash_sparse_attn_decode_varlen(q, k, v, ctx, mask, bias, block=block)
+    if fused:
+        o, mask, bias = dash.dash_decode_step(q, k, v, kbar, block=block, alpha=1.5, gamma=1.5,
+                                              sigma=1.0, ctx_lens=ctx, window_blocks=window)
+        tau = None
+    else:
+        mask, bias, tau = dash.dash_block_entmax_ex(q, kbar, n_kv=cap, block=block, alpha=1.5,
+                                                    gamma=1.5, sigma=1.0, h_kv=2, ctx_lens=ctx,
+                                                    window_blocks=window)
+        o = dash.dash_sparse_attn_decode_varlen(q, k, v, ctx, mask, bias, block=block)
     torch.cuda.synchronize()
     refs = _varlen_reference(orc, q, k, v, lens, block, 1.5, 1.5, 1.0, window)
     rows = np.arange(len(lens))
-    _check_varlen_rows(q, k, v, flat_rows(mask, rows), flat_rows(bias, rows), flat_rows(tau, rows),
-                       flat_rows(o, rows), refs, lens, block, 2, 1.5, 1.0, float(v.abs().max()))
+    _check_varlen_rows(q, k, v, flat_rows(mask, rows), flat_rows(bias, rows),
+                       None if tau is None else flat_rows(tau, rows), flat_rows(o, rows), refs,
+                       lens, block, 2, 1.5, 1.0, float(v.abs().max()))
 
 
 @pytest.mark.parametrize("learned", [False, True])
