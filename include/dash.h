@@ -313,6 +313,25 @@ dash_status_t dash_decode_step(const void* q, const void* k_cache, const void* v
                                float scale, uint32_t* mask, float* bias, void* o, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * dash_decode_step without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Arguments and
+ * outputs as dash_decode_step; the workspace is a scratch array of 32 MiB that the library holds
+ * on every GPU it runs on until the process ends. Call it with the stream's device current (the
+ * scratch's address on that device is looked up on its first call there and kept). A call whose
+ * dash_decode_step_workspace_bytes() exceeds 32 MiB returns DASH_ERR_WORKSPACE and launches
+ * nothing (16 sequences of 128K tokens at 32 query / 8 KV heads, D 128, chunk 64 need 13 MiB).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (other streams,
+ * other threads) race, so serialise them. The scratch's ticket counters start at zero and every
+ * call leaves them zero. Nothing is allocated or freed, by the library or by HIP on its behalf.
+ */
+dash_status_t dash_decode_step_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       dash_dtype_t dt, const float* kbar, const int32_t* ctx_lens,
+                                       int batch, int n_ctx, int h_q, int h_kv, int head_dim,
+                                       int block, float alpha, float gamma, float sigma,
+                                       int window_blocks, float scale, uint32_t* mask, float* bias,
+                                       void* o, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

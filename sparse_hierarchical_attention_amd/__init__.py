@@ -24,7 +24,7 @@ __all__ = [
     "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
     "dash_sparse_attn_backward_workspace_bytes", "dash_sparse_attn_prefill_backward",
     "dash_block_entmax_backward_workspace_bytes", "dash_block_entmax_backward",
-    "dash_decode_step_workspace_bytes", "dash_decode_step",
+    "dash_decode_step_workspace_bytes", "dash_decode_step", "dash_decode_step_noalloc",
     "dash_version", "backward", "forward", "decode_step",
 ]
 
@@ -91,6 +91,9 @@ def lib():
         L.dash_decode_step.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, f, f, f, i, f, vp,
                                        vp, vp, vp, sz, vp]
         L.dash_decode_step.restype = i
+        L.dash_decode_step_noalloc.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, f, f, f,
+                                               i, f, vp, vp, vp, vp]
+        L.dash_decode_step_noalloc.restype = i
         for fn in ("dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append",
                    "dash_block_entmax", "dash_block_entmax_ex", "dash_sparse_attn_prefill",
                    "dash_sparse_attn_prefill_ex", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
@@ -480,6 +483,27 @@ def dash_decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
         n_ctx, hq, hkv, d, block, float(alpha), float(gamma), float(sigma), int(window_blocks),
         float(scale), _ptr(mask), _ptr(bias), _ptr(o), _ptr(workspace), wsb, _stream(dev)))
     return o, mask, bias
+
+
+def dash_decode_step_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             kbar: torch.Tensor, *, mask: torch.Tensor, bias: torch.Tensor,
+                             o: torch.Tensor, block: int, alpha: float, gamma: float,
+                             sigma: float, ctx_lens: torch.Tensor | None = None,
+                             window_blocks: int = 1, scale: float | None = None) -> None:
+    """dash_decode_step on the library's own device scratch: nothing is allocated, so the
+    caller passes every output (mask, bias, o) in. Calls that overlap on one GPU race."""
+    _f32(kbar=kbar, bias=bias)
+    b, n_ctx, hkv, d = k_cache.shape
+    hq = q.shape[-2]
+    if ctx_lens is not None and ctx_lens.dtype != torch.int32:
+        raise TypeError("ctx_lens must be int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = _dev(q, k_cache, v_cache, kbar, ctx_lens, mask, bias, o)
+    _check(lib().dash_decode_step_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(kbar), _ptr(ctx_lens), b,
+        n_ctx, hq, hkv, d, block, float(alpha), float(gamma), float(sigma), int(window_blocks),
+        float(scale), _ptr(mask), _ptr(bias), _ptr(o), _stream(dev)))
 
 
 def decode_step(q, k_cache, v_cache, kbar, *, block: int, alpha: float, gamma: float,

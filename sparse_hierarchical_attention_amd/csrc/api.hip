@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "dash.h"
@@ -393,6 +394,34 @@ dash_status_t dash_decode_step(const void* q, const void* k_cache, const void* v
 
 namespace {
 
+// Scratch of dash_decode_step_noalloc: one copy on every GPU the library runs on, held until the
+// process ends. Its address on the current device is looked up once per device and kept; kernels
+// get that address, never the array's host-side name. Zero at load, so its ticket counters start
+// at zero, and every call leaves them zero.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// the scratch's device address on the current device, or nullptr (with the error recorded)
+void* scratch_address(const char* fn) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        fail(DASH_ERR_HIP, "%s: no current device", fn);
+        return nullptr;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            fail(DASH_ERR_HIP, "%s: scratch address: %s", fn, hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 dash_status_t decode_step_call(const char* fn, const void* q, const void* k_cache,
                                const void* v_cache, dash_dtype_t dt, const float* kbar,
                                const int32_t* ctx_lens, int batch, int n_ctx, int h_q, int h_kv,
@@ -416,7 +445,14 @@ dash_status_t decode_step_call(const char* fn, const void* q, const void* k_cach
     dash::AttnParams p = attn_params(batch, 1, n_ctx - 1, n_ctx, h_q, h_kv, head_dim, block, scale);
     p.ctx_lens = ctx_lens;
     const size_t need = dash::decode_step_workspace_bytes(rp, p);
-    (void)use_scratch;
+    if (use_scratch) {
+        if (need > kScratchBytes)
+            return fail(DASH_ERR_WORKSPACE, "%s: the call needs %zu bytes of scratch, more than the "
+                        "%zu the library holds per device", fn, need, kScratchBytes);
+        workspace = scratch_address(fn);
+        if (!workspace) return DASH_ERR_HIP;
+        workspace_bytes = kScratchBytes;
+    }
     if (!workspace || workspace_bytes < need)
         return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -425,3 +461,18 @@ dash_status_t decode_step_call(const char* fn, const void* q, const void* k_cach
 }
 
 }  // namespace
+
+extern "C" {
+
+dash_status_t dash_decode_step_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       dash_dtype_t dt, const float* kbar, const int32_t* ctx_lens,
+                                       int batch, int n_ctx, int h_q, int h_kv, int head_dim,
+                                       int block, float alpha, float gamma, float sigma,
+                                       int window_blocks, float scale, uint32_t* mask, float* bias,
+                                       void* o, hipStream_t stream) {
+    return decode_step_call("dash_decode_step_noalloc", q, k_cache, v_cache, dt, kbar, ctx_lens,
+                            batch, n_ctx, h_q, h_kv, head_dim, block, alpha, gamma, sigma,
+                            window_blocks, scale, mask, bias, o, nullptr, 0, true, stream);
+}
+
+}  // extern "C"
