@@ -60,6 +60,32 @@ def selected_pairs_prefill(mask: torch.Tensor, w: wl.Workload) -> tuple[int, flo
     return int(pairs), float(routed.sum() / max(1, cand))
 
 
+def issued_pairs_prefill(mask: torch.Tensor, w: wl.Workload, rows_per_wg: int = 128,
+                         rows_per_wave: int = 32, tile_keys: int = 32) -> int:
+    """(query head, key) pairs the bf16 D = 128 prefill kernel multiplies on its matrix cores for
+    this mask: a workgroup of rows_per_wg rows (tokens x the group's heads) walks the union of its
+    tokens' chunks (their own chunks included) in tiles of tile_keys keys, and a wave of
+    rows_per_wave rows multiplies a tile unless none of its tokens selected the chunk; each
+    multiplied tile costs rows_per_wave x tile_keys pairs (masked causal keys and rows that did not
+    select the chunk included)."""
+    m = mask.cpu().numpy().view(np.uint32)                  # [B, n, Hkv, W]
+    g = w.h_q // w.h_kv
+    nc = -(-w.n_kv // w.block)
+    cw = np.arange(nc)
+    bits = ((m[..., cw // 32] >> (cw % 32).astype(np.uint32)) & 1).astype(bool)  # [B, n, Hkv, Nc]
+    pos = np.arange(w.n_q)
+    cp = pos // w.block
+    bits &= cw[None, None, None, :] <= cp[None, :, None, None]
+    bits[:, pos, :, cp] = True                              # the own chunk
+    tw = rows_per_wave // g                                 # tokens per wave
+    n_pad = -(-w.n_q // tw) * tw
+    if n_pad != w.n_q:
+        bits = np.concatenate([bits, np.zeros((bits.shape[0], n_pad - w.n_q) + bits.shape[2:], bool)], 1)
+    wave_sel = bits.reshape(bits.shape[0], n_pad // tw, tw, w.h_kv, nc).any(axis=2)
+    sub = max(1, w.block // tile_keys)
+    return int(wave_sel.sum()) * sub * rows_per_wave * min(tile_keys, w.block)
+
+
 def decode_bytes(mask: torch.Tensor, w: wl.Workload) -> tuple[int, float]:
     """Algorithmic HBM bytes of one decode step: the cached summaries of the complete chunks
     before the new token's chunk (fp32), the selected K and V chunks including the new token's
@@ -118,11 +144,17 @@ def extras_leg(dash, pre, dec, wp: wl.Workload, wd: wl.Workload, reps: int) -> d
     k, kd = pre["k"], dec["k"]
     qbar = wl.summary_query(wp.h_kv, wp.head_dim, 91, dev)
     pool = {}
-    for name, kk, blk in (("prefill_32k", k, wp.block), ("decode_cache_16x128k", kd, wd.block)):
+    for name, kk, blk, per_chunk in (("prefill_32k", k, wp.block, False),
+                                     ("prefill_32k_per_chunk_query", k, wp.block, True),
+                                     ("decode_cache_16x128k", kd, wd.block, False)):
         kb = torch.empty((kk.shape[0], kk.shape[1] // blk, kk.shape[2], kk.shape[3]),
                          dtype=torch.float32, device=dev)
-        t = _time_ms(lambda: dash.dash_pool_keys_query(kk, qbar, blk, kbar=kb), reps)
-        nbytes = kk.numel() * kk.element_size() + kb.numel() * 4
+        qb = qbar
+        if per_chunk:  # one query per chunk and KV head, as Alg. 1 takes it
+            qb = (torch.randn((kk.shape[1] // blk,) + tuple(qbar.shape),
+                              generator=torch.Generator().manual_seed(93)) * 0.3).to(dev)
+        t = _time_ms(lambda: dash.dash_pool_keys_query(kk, qb, blk, kbar=kb), reps)
+        nbytes = kk.numel() * kk.element_size() + kb.numel() * 4 + (qb.numel() * 4 if per_chunk else 0)
         gbs = nbytes / (t * 1e-3) / 1e9
         pool[name] = {"ms": round(t, 4), "algorithmic_bytes": nbytes, "gb_per_s": round(gbs, 1),
                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS,
@@ -203,6 +235,92 @@ def extras_leg(dash, pre, dec, wp: wl.Workload, wd: wl.Workload, reps: int) -> d
         "end_to_end_tflops": round(flops / ((t_pool + t_route + t_attn) * 1e-3) / 1e12, 3),
         "roofline": {"bound": "mfma", "achieved": round(at, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(at / MFMA_BF16_PEAK_TFLOPS, 4)}}
+    return out
+
+
+def config_point(dash, w: wl.Workload, dev, reps: int, oracle_rows: int) -> dict:
+    """One prefill workload through the three stages (pool, route, attend), each timed as the
+    median of `reps` HIP-event spans, with its selected-pair work, roofline, and the oracle timed
+    on `oracle_rows` sampled query rows of the same inputs (its TFLOP/s on those rows' pairs)."""
+    import oracle
+    inp = wl.make_inputs(w, dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    nc = -(-w.n_kv // w.block)
+    kbar = torch.empty((w.batch, w.n_kv // w.block, w.h_kv, w.head_dim), dtype=torch.float32,
+                       device=dev)
+    mask = torch.empty((w.batch, w.n_q, w.h_kv, -(-nc // 32)), dtype=torch.int32, device=dev)
+    bias = torch.empty((w.batch, w.n_q, w.h_kv, nc), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.n_q, w.h_q), dtype=torch.float32, device=dev)
+    wsb = dash.dash_block_entmax_workspace_bytes(q.dtype, w.batch, w.n_q, 0, w.n_kv, w.h_q, w.h_kv,
+                                                 w.head_dim, w.block)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
+    t = Timer()
+    for i in range(reps + 1):
+        spans = [t.span(n) if i else (None, None) for n in ("pool", "entmax", "attn")]
+        spans[0][0] and spans[0][0].record()
+        dash.dash_pool_keys(k, w.block, kbar=kbar)
+        spans[0][1] and spans[0][1].record()
+        spans[1][0] and spans[1][0].record()
+        dash.dash_block_entmax(q, kbar, n_kv=w.n_kv, block=w.block, alpha=w.alpha, gamma=w.gamma,
+                               sigma=w.sigma, mask=mask, bias=bias, want_tau=False, workspace=ws)
+        spans[1][1] and spans[1][1].record()
+        spans[2][0] and spans[2][0].record()
+        dash.dash_sparse_attn_prefill(q, k, v, mask, bias, block=w.block, o=o, lse=lse)
+        spans[2][1] and spans[2][1].record()
+    torch.cuda.synchronize()
+    ms = {n: t.median_ms(n) for n in ("pool", "entmax", "attn")}
+    pairs, frac = selected_pairs_prefill(mask, w)
+    flops = 4.0 * w.head_dim * pairs
+    at = flops / (ms["attn"] * 1e-3) / 1e12
+    fp32 = w.dtype == "f32"
+    peak = 157.3 if fp32 else MFMA_BF16_PEAK_TFLOPS  # fp32 runs on the vector ALUs
+    # the oracle on sampled rows (the chunk edges and the last rows, then spread), Stage 0 in full
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([np.arange(w.n_q - 4, w.n_q),
+                                     rng.choice(w.n_q, size=max(0, oracle_rows - 4), replace=False)]))
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    t0 = time.perf_counter()
+    ref = oracle.forward(qh, kh, vh, block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma,
+                         rows=rows)
+    t_orc = time.perf_counter() - t0
+    pos = rows % w.n_q
+    cp = pos // w.block
+    routed = popcount32(ref["mask"]).sum(axis=-1).astype(np.int64) - 1
+    orc_pairs = (routed * w.block).sum() * (w.h_q // w.h_kv) + w.h_q * (pos - cp * w.block + 1).sum()
+    del inp, q, k, v, kbar, mask, bias, o, lse, ws, qh, kh, vh, ref
+    torch.cuda.empty_cache()
+    return {
+        "workload": w.name, "alpha": w.alpha, "block": w.block, "gamma": w.gamma,
+        "dtype": w.dtype, "ms": {n: round(x, 4) for n, x in ms.items()},
+        "selected_pairs": pairs, "routed_fraction": round(frac, 4),
+        "algorithmic_tflop": round(flops / 1e12, 4),
+        "attn_tflops": round(at, 3),
+        "end_to_end_tflops": round(flops / (sum(ms.values()) * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "alu" if fp32 else "mfma", "achieved": round(at, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(at / peak, 4)},
+        "cpu_baseline": {"kind": "oracle", "cores": oracle.num_threads(), "rows": int(len(rows)),
+                         "seconds": round(t_orc, 3),
+                         "tflops": round(4.0 * w.head_dim * orc_pairs / t_orc / 1e12, 6)},
+    }
+
+
+def configs_leg(dash, dev, reps: int) -> dict:
+    """The other workloads of the measurement plan, each timed on its own: the tiny fp32
+    workload, the nine alpha / block points of the sweep at 16K and the 256K prefill."""
+    out = {}
+    print("[bench] configs: tiny fp32", file=sys.stderr, flush=True)
+    out["tiny_fp32"] = config_point(dash, wl.TINY, dev, reps, oracle_rows=1024)
+    with open(os.path.join(ROOT, "tests", "golden", "sweep_gamma.json")) as f:
+        points = json.load(f)["points"]
+    sweep = []
+    for pt in points:
+        w = wl.sweep_workload(pt["alpha"], pt["block"], pt["gamma"])
+        print(f"[bench] configs: {w.name}", file=sys.stderr, flush=True)
+        sweep.append(config_point(dash, w, dev, reps, oracle_rows=32))
+    out["sweep_16k"] = sweep
+    print("[bench] configs: prefill 256K", file=sys.stderr, flush=True)
+    out["prefill_256k"] = config_point(dash, wl.PREFILL_256K, dev, max(2, reps // 4), oracle_rows=16)
     return out
 
 
@@ -475,6 +593,10 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the learned-summary-query and streaming legs (timed on their own "
                          "after the step)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (tiny fp32, the 16K alpha / block sweep, the "
+                         "256K prefill), each timed on its own after the step with an oracle "
+                         "baseline on sampled rows")
     ap.add_argument("--random-mask-sweep", action="store_true",
                     help="run the pages' random-selection efficiency sweep instead of the step "
                          "(Hq 32, Hkv 2, N 16-96K, three sparsities); one JSON line per point")
@@ -606,8 +728,11 @@ def main():
         return
     backward = None if args.no_backward else backward_leg(dash, pre, wp, args)
     extras = None if args.no_extras else extras_leg(dash, pre, dec, wp, wd, max(1, args.steps))
+    if extras is not None and not args.no_configs:
+        extras["configs"] = configs_leg(dash, dev, reps=max(3, args.steps // 2))
 
     pairs, frac = selected_pairs_prefill(mask, wp)
+    issued = issued_pairs_prefill(mask, wp)
     flops = 4.0 * wp.head_dim * pairs
     t_pool, t_ent, t_attn = timer.median_ms("pool"), timer.median_ms("entmax"), timer.median_ms("attn")
     t_pre = t_pool + t_ent + t_attn
@@ -653,6 +778,7 @@ def main():
         },
         "prefill": {
             "selected_pairs": pairs, "routed_fraction": round(frac, 4),
+            "issued_pairs": issued, "useful_fraction_of_issued": round(pairs / issued, 4),
             "algorithmic_tflop": round(flops / 1e12, 4),
             "ms": {"pool": round(t_pool, 4), "entmax": round(t_ent, 4), "attn": round(t_attn, 4)},
             "attn_tflops": round(attn_tflops, 3),

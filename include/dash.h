@@ -96,6 +96,20 @@ dash_status_t dash_pool_keys_query(const void* k, dash_dtype_t dt, const float* 
                                    hipStream_t stream);
 
 /*
+ * Stage 0 with one learned summary query per chunk [DA App. G, Alg. 1: qbar has one row per
+ * chunk and KV head, rotary position embedding already applied by the caller]: as
+ * dash_pool_keys_query, with the query of sequence b, chunk c, KV head r read at
+ *   qbar + b * qbar_batch_stride + c * qbar_chunk_stride + r * D      (strides in floats)
+ * so qbar [Tc, H_kv, D] shared by the batch is (0, H_kv * D), qbar [B, Tc, H_kv, D] is
+ * (Tc * H_kv * D, H_kv * D), and (0, 0) is dash_pool_keys_query's one query per KV head. Strides
+ * are non-negative multiples of 4 (16-byte rows); the caller keeps every addressed row in bounds.
+ */
+dash_status_t dash_pool_keys_query_ex(const void* k, dash_dtype_t dt, const float* qbar,
+                                      int64_t qbar_batch_stride, int64_t qbar_chunk_stride,
+                                      float* kbar, int batch, int n_kv, int h_kv, int head_dim,
+                                      int block, hipStream_t stream);
+
+/*
  * Stage 0, streaming [DA §3.1 (a summary is final once its chunk is complete), §3.5 (the chunk
  * cache persisted across decoding steps)]: after the newest token of sequence b was appended
  * (ctx_lens[b] tokens in the cache, device int32 [B]), the summary of chunk ctx_lens[b] / Bc - 1
@@ -108,6 +122,14 @@ dash_status_t dash_pool_keys_query(const void* k, dash_dtype_t dt, const float* 
 dash_status_t dash_pool_keys_append(const void* k_cache, dash_dtype_t dt, const float* qbar,
                                     const int32_t* ctx_lens, float* kbar, int batch, int n_cap,
                                     int h_kv, int head_dim, int block, hipStream_t stream);
+
+/* dash_pool_keys_append with one summary query per chunk, addressed as in
+ * dash_pool_keys_query_ex (the query of the chunk being completed is used; qbar NULL: the
+ * mean, strides ignored). */
+dash_status_t dash_pool_keys_append_ex(const void* k_cache, dash_dtype_t dt, const float* qbar,
+                                       int64_t qbar_batch_stride, int64_t qbar_chunk_stride,
+                                       const int32_t* ctx_lens, float* kbar, int batch, int n_cap,
+                                       int h_kv, int head_dim, int block, hipStream_t stream);
 
 /*
  * Stage 1 [DA §3.2, Eq. 4; DA App. G, Alg. 2]. Query row t (t < n_q) sits at absolute position

@@ -45,6 +45,7 @@ def lib():
         vp, i, d, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_int64
         L.orc_pool_keys.argtypes = [vp, i, i, i, i, i, i, vp]
         L.orc_pool_keys_query.argtypes = [vp, i, vp, i, i, i, i, i, vp]
+        L.orc_pool_keys_query_ex.argtypes = [vp, i, vp, i64, i64, i, i, i, i, i, vp]
         L.orc_entmax_tau_sort.argtypes = [vp, i, d]
         L.orc_entmax_tau_sort.restype = d
         L.orc_entmax_tau_bisect.argtypes = [vp, i, d, i]
@@ -128,14 +129,23 @@ def pool_keys(k, block: int) -> np.ndarray:
 
 
 def pool_keys_query(k, qbar, block: int) -> np.ndarray:
-    """Stage 0 with a learned summary query qbar [Hkv, D] (Eq. 3)."""
+    """Stage 0 with learned summary queries (Eq. 3): qbar [Hkv, D] (one per KV head), [Tc, Hkv, D]
+    (one per chunk, Alg. 1) or [B, Tc, Hkv, D] (one per sequence and chunk)."""
     ka, dt = _host(k)
     qb = np.ascontiguousarray(np.asarray(qbar, dtype=np.float64))
     b, n, hkv, d = ka.shape
-    assert qb.shape == (hkv, d)
-    out = np.zeros((b, n // block, hkv, d), dtype=np.float64)
-    _check(lib().orc_pool_keys_query(_ptr(ka), dt, _ptr(qb), b, n, hkv, d, block, _ptr(out)),
-           "pool_keys_query")
+    tc = n // block
+    if qb.shape == (hkv, d):
+        sb, sc = 0, 0
+    elif qb.shape == (tc, hkv, d):
+        sb, sc = 0, hkv * d
+    elif qb.shape == (b, tc, hkv, d):
+        sb, sc = tc * hkv * d, hkv * d
+    else:
+        raise ValueError(f"qbar shape {qb.shape} is none of [Hkv, D], [Tc, Hkv, D], [B, Tc, Hkv, D]")
+    out = np.zeros((b, tc, hkv, d), dtype=np.float64)
+    _check(lib().orc_pool_keys_query_ex(_ptr(ka), dt, _ptr(qb), sb, sc, b, n, hkv, d, block,
+                                        _ptr(out)), "pool_keys_query")
     return out
 
 

@@ -55,9 +55,11 @@ int orc_pool_keys(const void* k, int dtype, int batch, int n_kv, int h_kv, int h
     return 0;
 }
 
-int orc_pool_keys_query(const void* k, int dtype, const double* qbar, int batch, int n_kv,
-                        int h_kv, int head_dim, int block, double* kbar) {
-    if (!k || !qbar || !kbar || batch <= 0 || n_kv <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0)
+int orc_pool_keys_query_ex(const void* k, int dtype, const double* qbar, int64_t qbar_batch_stride,
+                           int64_t qbar_chunk_stride, int batch, int n_kv, int h_kv, int head_dim,
+                           int block, double* kbar) {
+    if (!k || !qbar || !kbar || batch <= 0 || n_kv <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0 ||
+        qbar_batch_stride < 0 || qbar_chunk_stride < 0)
         return -1;
     const int tc = n_kv / block;
     const double inv_sqrt_d = 1.0 / sqrt((double)head_dim);
@@ -65,14 +67,16 @@ int orc_pool_keys_query(const void* k, int dtype, const double* qbar, int batch,
     for (int b = 0; b < batch; ++b)
         for (int c = 0; c < tc; ++c)
             for (int r = 0; r < h_kv; ++r) {
-                /* logits <qbar^(r), k_t> / sqrt(D) over the chunk's own tokens */
+                /* the summary query of this chunk and KV head [DA App. G, Alg. 1: one per chunk] */
+                const double* qc = qbar + b * qbar_batch_stride + c * qbar_chunk_stride + (int64_t)r * head_dim;
+                /* logits <qbar_c^(r), k_t> / sqrt(D) over the chunk's own tokens */
                 double* s = malloc(sizeof(double) * block);
                 double smax = -INFINITY;
                 for (int u = 0; u < block; ++u) {
                     int64_t base = (((int64_t)b * n_kv + c * block + u) * h_kv + r) * head_dim;
                     double dot = 0.0;
                     for (int e = 0; e < head_dim; ++e)
-                        dot += qbar[(int64_t)r * head_dim + e] * orc_load(k, dtype, base + e);
+                        dot += qc[e] * orc_load(k, dtype, base + e);
                     s[u] = dot * inv_sqrt_d;
                     if (s[u] > smax) smax = s[u];
                 }
@@ -89,6 +93,11 @@ int orc_pool_keys_query(const void* k, int dtype, const double* qbar, int batch,
                 free(s);
             }
     return 0;
+}
+
+int orc_pool_keys_query(const void* k, int dtype, const double* qbar, int batch, int n_kv,
+                        int h_kv, int head_dim, int block, double* kbar) {
+    return orc_pool_keys_query_ex(k, dtype, qbar, 0, 0, batch, n_kv, h_kv, head_dim, block, kbar);
 }
 
 /* ------------------------------------------------ alpha-entmax [DA §2, Eq. 2; App. A, Eq. 13] */

@@ -57,6 +57,13 @@ int orc_pool_keys(const void* k, int dtype, int batch, int n_kv, int h_kv, int h
  * Eq. 3, a softmax over the chunk's own keys of <qbar, k_t>/sqrt(D), used to weigh the keys. */
 int orc_pool_keys_query(const void* k, int dtype, const double* qbar, int batch, int n_kv,
                         int h_kv, int head_dim, int block, double* kbar);
+/* The same with a summary query per chunk [DA App. G, Alg. 1, which takes qbar with one row per
+ * chunk and KV head]: the query of sequence b, chunk c, KV head r is the head_dim values at
+ * qbar + b * qbar_batch_stride + c * qbar_chunk_stride + r * head_dim (strides in elements;
+ * 0 and 0 give one query per KV head, shared by all chunks). */
+int orc_pool_keys_query_ex(const void* k, int dtype, const double* qbar, int64_t qbar_batch_stride,
+                           int64_t qbar_chunk_stride, int batch, int n_kv, int h_kv, int head_dim,
+                           int block, double* kbar);
 
 /* alpha-entmax threshold for x[0..m-1] (x already holds (alpha-1) * scores):
  * the unique tau with sum_c [x_c - tau]_+^(1/(alpha-1)) = 1.

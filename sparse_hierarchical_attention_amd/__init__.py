@@ -19,6 +19,7 @@ import torch
 __all__ = [
     "DashError", "lib", "library_path",
     "dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append", "dash_block_entmax",
+    "dash_pool_keys_query_ex", "dash_pool_keys_append_ex",
     "dash_block_entmax_ex", "dash_block_entmax_workspace_bytes", "dash_sparse_attn_prefill",
     "dash_sparse_attn_prefill_ex",
     "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
@@ -59,8 +60,11 @@ def lib():
         L.dash_last_error.restype = ctypes.c_char_p
         L.dash_version.restype = i
         L.dash_pool_keys.argtypes = [vp, i, vp, i, i, i, i, i, vp]
+        i64 = ctypes.c_int64
         L.dash_pool_keys_query.argtypes = [vp, i, vp, vp, i, i, i, i, i, vp]
+        L.dash_pool_keys_query_ex.argtypes = [vp, i, vp, i64, i64, vp, i, i, i, i, i, vp]
         L.dash_pool_keys_append.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, vp]
+        L.dash_pool_keys_append_ex.argtypes = [vp, i, vp, i64, i64, vp, vp, i, i, i, i, i, vp]
         L.dash_block_entmax_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
         L.dash_block_entmax_workspace_bytes.restype = sz
         L.dash_block_entmax.argtypes = [vp, i, vp, i, i, i, i, i, i, i, i, f, f, f, vp, vp, vp,
@@ -95,6 +99,7 @@ def lib():
                                                i, f, vp, vp, vp, vp]
         L.dash_decode_step_noalloc.restype = i
         for fn in ("dash_pool_keys", "dash_pool_keys_query", "dash_pool_keys_append",
+                   "dash_pool_keys_query_ex", "dash_pool_keys_append_ex",
                    "dash_block_entmax", "dash_block_entmax_ex", "dash_sparse_attn_prefill",
                    "dash_sparse_attn_prefill_ex", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
                    "dash_sparse_attn_prefill_backward"):
@@ -161,16 +166,30 @@ def dash_pool_keys(k: torch.Tensor, block: int, kbar: torch.Tensor | None = None
     return kbar
 
 
+def _qbar_strides(qbar: torch.Tensor, batch: int, tc: int, hkv: int, d: int) -> tuple[int, int]:
+    """Strides (in floats) of summary queries [Hkv, D], [Tc, Hkv, D] or [B, Tc, Hkv, D]."""
+    if tuple(qbar.shape) == (hkv, d):
+        return 0, 0
+    if tuple(qbar.shape) == (tc, hkv, d):
+        return 0, hkv * d
+    if tuple(qbar.shape) == (batch, tc, hkv, d):
+        return tc * hkv * d, hkv * d
+    raise ValueError(f"qbar shape {tuple(qbar.shape)} is none of [Hkv, D], [Tc, Hkv, D], "
+                     f"[B, Tc, Hkv, D] (B={batch}, Tc={tc}, Hkv={hkv}, D={d})")
+
+
 def dash_pool_keys_query(k: torch.Tensor, qbar: torch.Tensor, block: int,
                          kbar: torch.Tensor | None = None) -> torch.Tensor:
-    """Stage 0 with a learned summary query qbar [Hkv, D] fp32 (Eq. 3)."""
+    """Stage 0 with learned summary queries (Eq. 3), fp32: qbar [Hkv, D] (one per KV head),
+    [Tc, Hkv, D] (one per chunk, as Alg. 1 takes it) or [B, Tc, Hkv, D]."""
     _f32(qbar=qbar, kbar=kbar)
     b, n, hkv, d = k.shape
     if kbar is None:
         kbar = torch.empty((b, n // block, hkv, d), dtype=torch.float32, device=k.device)
+    sb, sc = _qbar_strides(qbar, b, n // block, hkv, d)
     dev = _dev(k, qbar, kbar)
-    _check(lib().dash_pool_keys_query(_ptr(k), _dtype_code(k), _ptr(qbar), _ptr(kbar), b, n, hkv,
-                                      d, block, _stream(dev)))
+    _check(lib().dash_pool_keys_query_ex(_ptr(k), _dtype_code(k), _ptr(qbar), sb, sc, _ptr(kbar),
+                                         b, n, hkv, d, block, _stream(dev)))
     return kbar
 
 
@@ -185,15 +204,18 @@ def dash_block_entmax_workspace_bytes(dtype, batch, n_q, q_pos0, n_kv, h_q, h_kv
 def dash_pool_keys_append(k_cache: torch.Tensor, ctx_lens: torch.Tensor, kbar: torch.Tensor,
                           block: int, qbar: torch.Tensor | None = None) -> torch.Tensor:
     """Streaming Stage 0: write the summary of the chunk each sequence's newest token completed
-    (ctx_lens int32 [B] a positive multiple of block) into kbar [B, n_cap // block, Hkv, D]."""
+    (ctx_lens int32 [B] a positive multiple of block) into kbar [B, n_cap // block, Hkv, D].
+    qbar: None (mean), or summary queries [Hkv, D], [Tc, Hkv, D] or [B, Tc, Hkv, D] for the
+    cache's Tc = n_cap // block chunks."""
     _f32(kbar=kbar, qbar=qbar)
     b, n_cap, hkv, d = k_cache.shape
     if ctx_lens.dtype != torch.int32:
         raise TypeError("ctx_lens must be int32")
+    sb, sc = (0, 0) if qbar is None else _qbar_strides(qbar, b, n_cap // block, hkv, d)
     dev = _dev(k_cache, ctx_lens, kbar, qbar)
-    _check(lib().dash_pool_keys_append(_ptr(k_cache), _dtype_code(k_cache), _ptr(qbar),
-                                       _ptr(ctx_lens), _ptr(kbar), b, n_cap, hkv, d, block,
-                                       _stream(dev)))
+    _check(lib().dash_pool_keys_append_ex(_ptr(k_cache), _dtype_code(k_cache), _ptr(qbar), sb, sc,
+                                          _ptr(ctx_lens), _ptr(kbar), b, n_cap, hkv, d, block,
+                                          _stream(dev)))
     return kbar
 
 

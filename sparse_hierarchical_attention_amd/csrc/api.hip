@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <atomic>
 #include <string>
@@ -149,26 +150,53 @@ dash_status_t dash_pool_keys(const void* k, dash_dtype_t dt, float* kbar, int ba
                       "dash_pool_keys");
 }
 
+dash_status_t dash_pool_keys_query_ex(const void* k, dash_dtype_t dt, const float* qbar,
+                                      int64_t qbar_batch_stride, int64_t qbar_chunk_stride,
+                                      float* kbar, int batch, int n_kv, int h_kv, int head_dim,
+                                      int block, hipStream_t stream) {
+    const char* fn = "dash_pool_keys_query_ex";
+    dash_status_t s = check_shape(fn, dt, batch, n_kv, h_kv, h_kv, head_dim, block);
+    if (s != DASH_OK) return s;
+    if (!k || !qbar || (!kbar && n_kv / block > 0)) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    if (qbar_batch_stride < 0 || qbar_chunk_stride < 0 || qbar_batch_stride % 4 || qbar_chunk_stride % 4)
+        return fail(DASH_ERR_INVALID, "%s: qbar strides must be non-negative multiples of 4 (%lld, %lld)",
+                    fn, (long long)qbar_batch_stride, (long long)qbar_chunk_stride);
+    return hip_status(dash::launch_pool_query(k, dt, qbar, qbar_batch_stride, qbar_chunk_stride, kbar,
+                                              batch, n_kv, h_kv, head_dim, block, stream), fn);
+}
+
 dash_status_t dash_pool_keys_query(const void* k, dash_dtype_t dt, const float* qbar, float* kbar,
                                    int batch, int n_kv, int h_kv, int head_dim, int block,
                                    hipStream_t stream) {
-    dash_status_t s = check_shape("dash_pool_keys_query", dt, batch, n_kv, h_kv, h_kv, head_dim, block);
+    const dash_status_t s = dash_pool_keys_query_ex(k, dt, qbar, 0, 0, kbar, batch, n_kv, h_kv,
+                                                    head_dim, block, stream);
+    if (s != DASH_OK) g_last_error.replace(0, strlen("dash_pool_keys_query_ex"), "dash_pool_keys_query");
+    return s;
+}
+
+dash_status_t dash_pool_keys_append_ex(const void* k_cache, dash_dtype_t dt, const float* qbar,
+                                       int64_t qbar_batch_stride, int64_t qbar_chunk_stride,
+                                       const int32_t* ctx_lens, float* kbar, int batch, int n_cap,
+                                       int h_kv, int head_dim, int block, hipStream_t stream) {
+    const char* fn = "dash_pool_keys_append_ex";
+    dash_status_t s = check_shape(fn, dt, batch, n_cap, h_kv, h_kv, head_dim, block);
     if (s != DASH_OK) return s;
-    if (!k || !qbar || (!kbar && n_kv / block > 0))
-        return fail(DASH_ERR_INVALID, "dash_pool_keys_query: null pointer");
-    return hip_status(dash::launch_pool_query(k, dt, qbar, kbar, batch, n_kv, h_kv, head_dim, block, stream),
-                      "dash_pool_keys_query");
+    if (!k_cache || !ctx_lens || (!kbar && n_cap / block > 0)) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    if (qbar_batch_stride < 0 || qbar_chunk_stride < 0 || qbar_batch_stride % 4 || qbar_chunk_stride % 4)
+        return fail(DASH_ERR_INVALID, "%s: qbar strides must be non-negative multiples of 4 (%lld, %lld)",
+                    fn, (long long)qbar_batch_stride, (long long)qbar_chunk_stride);
+    return hip_status(dash::launch_pool_append(k_cache, dt, qbar, qbar_batch_stride, qbar_chunk_stride,
+                                               ctx_lens, kbar, batch, n_cap, h_kv, head_dim, block,
+                                               stream), fn);
 }
 
 dash_status_t dash_pool_keys_append(const void* k_cache, dash_dtype_t dt, const float* qbar,
                                     const int32_t* ctx_lens, float* kbar, int batch, int n_cap,
                                     int h_kv, int head_dim, int block, hipStream_t stream) {
-    const char* fn = "dash_pool_keys_append";
-    dash_status_t s = check_shape(fn, dt, batch, n_cap, h_kv, h_kv, head_dim, block);
-    if (s != DASH_OK) return s;
-    if (!k_cache || !ctx_lens || (!kbar && n_cap / block > 0)) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
-    return hip_status(dash::launch_pool_append(k_cache, dt, qbar, ctx_lens, kbar, batch, n_cap, h_kv,
-                                               head_dim, block, stream), fn);
+    const dash_status_t s = dash_pool_keys_append_ex(k_cache, dt, qbar, 0, 0, ctx_lens, kbar, batch,
+                                                     n_cap, h_kv, head_dim, block, stream);
+    if (s != DASH_OK) g_last_error.replace(0, strlen("dash_pool_keys_append_ex"), "dash_pool_keys_append");
+    return s;
 }
 
 size_t dash_block_entmax_workspace_bytes(dash_dtype_t dt, int batch, int n_q, int q_pos0,

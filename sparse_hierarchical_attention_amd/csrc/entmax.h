@@ -51,9 +51,10 @@ __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp_f<0x140, 0xf>(-INFINITY, v));
     return v;
 }
-// Sums across the four 16-lane rows: partner lanes l ^ 16 and l ^ 32 through ds_bpermute.
-__device__ __forceinline__ float pair16_sum(float v) { return v + __shfl_xor(v, 16, 64); }
-__device__ __forceinline__ float pair32_sum(float v) { return v + __shfl_xor(v, 32, 64); }
+// Sums across the four 16-lane rows: partner lanes l ^ 16 and l ^ 32 through the permlane swaps
+// of gfx950 (common.h); the same sums, in the same order, as adding the partner's value.
+__device__ __forceinline__ float pair16_sum(float v) { return rowpair_sum(v); }
+__device__ __forceinline__ float pair32_sum(float v) { return halves_sum(v); }
 
 // Reductions over a lane group: a 16-lane DPP row, or the whole wave (common.h).
 template <int LANES> __device__ __forceinline__ float grp_sum(float v) {

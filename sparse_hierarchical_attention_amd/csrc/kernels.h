@@ -14,11 +14,13 @@ constexpr int kBF16 = 1;
 // ---- Stage 0 (pool_keys.hip)
 hipError_t launch_pool_mean(const void* k, int dt, float* kbar, int batch, int n_kv, int h_kv,
                             int head_dim, int block, hipStream_t st);
-hipError_t launch_pool_query(const void* k, int dt, const float* qbar, float* kbar, int batch,
-                             int n_kv, int h_kv, int head_dim, int block, hipStream_t st);
-hipError_t launch_pool_append(const void* k, int dt, const float* qbar, const int* ctx_lens,
-                              float* kbar, int batch, int n_cap, int h_kv, int head_dim, int block,
-                              hipStream_t st);
+// qbar of (sequence b, chunk c, KV head r) at qbar + b sb + c sc + r D (sb = sc = 0: per head)
+hipError_t launch_pool_query(const void* k, int dt, const float* qbar, int64_t sb, int64_t sc,
+                             float* kbar, int batch, int n_kv, int h_kv, int head_dim, int block,
+                             hipStream_t st);
+hipError_t launch_pool_append(const void* k, int dt, const float* qbar, int64_t sb, int64_t sc,
+                              const int* ctx_lens, float* kbar, int batch, int n_cap, int h_kv,
+                              int head_dim, int block, hipStream_t st);
 
 // ---- Stage 1 (block_entmax.hip)
 // n_kv, tc = n_kv / block, nc and nw describe the key range (for decode: the cache capacity).

@@ -7,6 +7,7 @@
 // w, w + 4, ...; the four partial sums meet in LDS and are added in wave order, so the result
 // does not depend on scheduling.
 #include "common.h"
+#include "decode_common.h"
 #include "kernels.h"
 
 namespace dash {
@@ -59,61 +60,90 @@ __global__ __launch_bounds__(256) void pool_mean_kernel(const T* __restrict__ k,
     }
 }
 
-// Learned summary query (Eq. 3): one wave per (sequence, chunk, KV head). Lanes own tokens for
-// the local logits <qbar, k_t> / sqrt(D) and their softmax, then own dimensions for the
-// weighted sum of the chunk's keys.
+// Learned summary query (Eq. 3): one wave per (sequence, chunk, KV head) streams the chunk's keys
+// once, in units of 16 rows: a row of D elements spans LPK lanes with one 16-byte piece each, so
+// one load instruction covers 64 / LPK whole rows and the wave's loads are 256- or 512-byte
+// segments. Each lane keeps its piece of the summary query in fp32; a row's logit
+// <qbar, k_t> / sqrt(D) is summed over its lanes by DPP, the softmax over the chunk runs online
+// (running maximum and sum per lane), and the weighted keys accumulate per lane until the lanes
+// holding the same dimensions of different rows are folded at the end. The summary query of
+// (b, c, r) is read at qbar + b sb + c sc + r D (sb = sc = 0: one query per KV head).
 template <typename T, int D>
 __global__ __launch_bounds__(64) void pool_query_kernel(const T* __restrict__ k,
                                                         const float* __restrict__ qbar,
+                                                        int64_t sb, int64_t sc,
                                                         float* __restrict__ kbar, int n_kv,
                                                         int h_kv, int block, int tc,
                                                         const int* __restrict__ ctx_lens) {
+    constexpr int EPL = 16 / sizeof(T);   // elements per 16-byte piece
+    constexpr int LPK = D / EPL;          // lanes per key row
+    constexpr int KPI = 64 / LPK;         // rows per load instruction
+    constexpr int UNIT = 16;              // rows per unit
+    constexpr int NI = UNIT / KPI;        // load instructions per unit
+    constexpr float kLog2e = 1.4426950408889634f;
     const int r = blockIdx.y, b = blockIdx.z;
     const int c = ctx_lens ? completed_chunk(ctx_lens, b, n_kv, block) : (int)blockIdx.x;
-    if (c < 0) return;  // the whole workgroup
+    if (c < 0) return;  // the whole wave
     const int lane = threadIdx.x;
-    __shared__ float qs[D];
-    __shared__ float pw[128];
-    for (int e = lane; e < D; e += kWave) qs[e] = qbar[(int64_t)r * D + e];
-    __syncthreads();
+    const int seg = lane / LPK, li = lane % LPK;
 
-    const float inv_sqrt_d = rsqrtf((float)D);
+    float qv[EPL];
+    const float* qp = qbar + b * sb + c * sc + (int64_t)r * D + li * EPL;
+#pragma unroll
+    for (int j = 0; j < EPL; j += 4) {
+        const float4 u = *reinterpret_cast<const float4*>(qp + j);
+        qv[j] = u.x; qv[j + 1] = u.y; qv[j + 2] = u.z; qv[j + 3] = u.w;
+    }
+    const float scale = rsqrtf((float)D) * kLog2e;  // logits in the log2 domain
     const int64_t row_stride = (int64_t)h_kv * D;
-    const T* base = k + ((int64_t)b * n_kv + (int64_t)c * block) * row_stride + (int64_t)r * D;
-    float s[2];
-    float smax = -INFINITY;
+    const T* base = k + ((int64_t)b * n_kv + (int64_t)c * block) * row_stride + (int64_t)r * D + li * EPL;
+    float acc[EPL];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = lane + i * kWave;
-        s[i] = -INFINITY;
-        if (u < block) {
-            float dot = 0.f;
-            for (int e = 0; e < D; e += 8) {
-                float kv[8];
-                load8(base + u * row_stride + e, kv);
+    for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    for (int u0 = 0; u0 < block; u0 += UNIT) {
+        uint4 kr[NI];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) dot = fmaf(qs[e + j], kv[j], dot);
-            }
-            s[i] = dot * inv_sqrt_d;
+        for (int i = 0; i < NI; ++i)
+            kr[i] = *reinterpret_cast<const uint4*>(base + (int64_t)(u0 + i * KPI + seg) * row_stride);
+        float sc_[NI], mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float kf[EPL];
+            unpack(kr[i], kf);
+            float d = 0.f;
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) d = fmaf(qv[j], kf[j], d);
+            sc_[i] = seg_sum<LPK>(d) * scale;
+            mx = fmaxf(mx, sc_[i]);
         }
-        smax = fmaxf(smax, s[i]);
-    }
-    smax = wave_max(smax);
-    float z = 0.f;
+        mx = cross_max<LPK>(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= corr;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = lane + i * kWave;
-        const float p = u < block ? __expf(s[i] - smax) : 0.f;
-        if (u < block) pw[u] = p;
-        z += p;
+        for (int j = 0; j < EPL; ++j) acc[j] *= corr;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float pw = __builtin_amdgcn_exp2f(sc_[i] - m_new);
+            l_run += pw;
+            float kf[EPL];
+            unpack(kr[i], kf);
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) acc[j] = fmaf(pw, kf[j], acc[j]);
+        }
     }
-    z = wave_sum(z);
-    __syncthreads();
-    const float inv_z = 1.0f / z;
-    for (int e = lane; e < D; e += kWave) {
-        float acc = 0.f;
-        for (int u = 0; u < block; ++u) acc = fmaf(pw[u], to_f32(base[u * row_stride + e]), acc);
-        kbar[(((int64_t)b * tc + c) * h_kv + r) * D + e] = acc * inv_z;
+    l_run = cross_sum<LPK>(l_run);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[j] = cross_sum<LPK>(acc[j]);
+    if (seg == 0) {
+        const float inv = 1.0f / l_run;
+        float* out = kbar + (((int64_t)b * tc + c) * h_kv + r) * D + li * EPL;
+#pragma unroll
+        for (int j = 0; j < EPL; j += 4)
+            *reinterpret_cast<float4*>(out + j) = make_float4(acc[j] * inv, acc[j + 1] * inv,
+                                                              acc[j + 2] * inv, acc[j + 3] * inv);
     }
 }
 
@@ -132,14 +162,15 @@ hipError_t launch_pool_mean(const void* k, int dt, float* kbar, int batch, int n
     return hipGetLastError();
 }
 
-hipError_t launch_pool_query(const void* k, int dt, const float* qbar, float* kbar, int batch,
-                             int n_kv, int h_kv, int head_dim, int block, hipStream_t st) {
+hipError_t launch_pool_query(const void* k, int dt, const float* qbar, int64_t sb, int64_t sc,
+                             float* kbar, int batch, int n_kv, int h_kv, int head_dim, int block,
+                             hipStream_t st) {
     const int tc = n_kv / block;
     if (tc == 0) return hipSuccess;
     dim3 grid(tc, h_kv, batch);
 #define DASH_POOLQ(T, DD)                                                                  \
     hipLaunchKernelGGL((pool_query_kernel<T, DD>), grid, dim3(64), 0, st,                  \
-                       static_cast<const T*>(k), qbar, kbar, n_kv, h_kv, block, tc, nullptr)
+                       static_cast<const T*>(k), qbar, sb, sc, kbar, n_kv, h_kv, block, tc, nullptr)
     if (dt == kBF16) {
         if (head_dim == 64) DASH_POOLQ(bf16_t, 64); else DASH_POOLQ(bf16_t, 128);
     } else {
@@ -151,9 +182,9 @@ hipError_t launch_pool_query(const void* k, int dt, const float* qbar, float* kb
 
 // Summaries of the chunks completed by each sequence's newest token (streaming decode): one
 // workgroup per sequence (and column slab, or KV head), idle where no chunk completed.
-hipError_t launch_pool_append(const void* k, int dt, const float* qbar, const int* ctx_lens,
-                              float* kbar, int batch, int n_cap, int h_kv, int head_dim, int block,
-                              hipStream_t st) {
+hipError_t launch_pool_append(const void* k, int dt, const float* qbar, int64_t sb, int64_t sc,
+                              const int* ctx_lens, float* kbar, int batch, int n_cap, int h_kv,
+                              int head_dim, int block, hipStream_t st) {
     const int tc = n_cap / block;
     if (tc == 0) return hipSuccess;
     if (!qbar) {
@@ -170,7 +201,7 @@ hipError_t launch_pool_append(const void* k, int dt, const float* qbar, const in
     dim3 grid(1, h_kv, batch);
 #define DASH_POOLQ(T, DD)                                                                  \
     hipLaunchKernelGGL((pool_query_kernel<T, DD>), grid, dim3(64), 0, st,                  \
-                       static_cast<const T*>(k), qbar, kbar, n_cap, h_kv, block, tc, ctx_lens)
+                       static_cast<const T*>(k), qbar, sb, sc, kbar, n_cap, h_kv, block, tc, ctx_lens)
     if (dt == kBF16) {
         if (head_dim == 64) DASH_POOLQ(bf16_t, 64); else DASH_POOLQ(bf16_t, 128);
     } else {

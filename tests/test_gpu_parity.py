@@ -39,9 +39,11 @@ def sample_rows(n_q: int, block: int, count: int, seed: int, batch: int = 1) -> 
 
 
 def flat_rows(t: torch.Tensor, rows: np.ndarray) -> np.ndarray:
-    """[B, n_q, ...] GPU tensor -> host array of the listed rows rho = b * n_q + t."""
-    a = parity.to_host(t)
-    return a.reshape((-1,) + a.shape[2:])[rows]
+    """[B, n_q, ...] GPU tensor -> host array of the listed rows rho = b * n_q + t (gathered on
+    the device, so that a multi-GiB bias never crosses to the host whole)."""
+    flat = t.reshape((-1,) + tuple(t.shape[2:]))
+    idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
+    return parity.to_host(flat.index_select(0, idx))
 
 
 def run_and_compare(dash, orc, w: wl.Workload, alpha, gamma, sigma, rows=None, max_flip_frac=0.02):
@@ -89,6 +91,30 @@ def test_pool_keys_learned_query(dash, orc, dtype):
     torch.cuda.synchronize()
     ref = orc.pool_keys_query(host(inp["k"]), qbar.double().numpy(), 64)
     np.testing.assert_allclose(kb.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("per", ["chunk", "sequence_chunk"])
+@pytest.mark.parametrize("d,block", [(128, 64), (64, 32), (128, 128)])
+def test_pool_keys_per_chunk_query(dash, orc, dtype, per, d, block):
+    """Stage 0 with one summary query per chunk (Alg. 1's qbar [Tc, Hkv, D]) or per sequence and
+    chunk, against the oracle; a ragged tail chunk gets no summary."""
+    w = wl.Workload("poolq chunks", 2, 5 * block + 7, 4, 4, d, block, 1.5, 1.0, 1.0, dtype=dtype,
+                    seed=23)
+    inp = wl.make_inputs(w, DEV)
+    tc = w.n_kv // block
+    shape = (tc, 4, d) if per == "chunk" else (2, tc, 4, d)
+    qbar = torch.randn(shape, generator=torch.Generator().manual_seed(6)) * 0.4
+    kb = dash.dash_pool_keys_query(inp["k"], qbar.to(DEV), block)
+    torch.cuda.synchronize()
+    ref = orc.pool_keys_query(host(inp["k"]), qbar.double().numpy(), block)
+    np.testing.assert_allclose(kb.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
+    # equal queries in every chunk give the per-head result
+    same = qbar.reshape(-1, 4, d)[:1].expand(shape[:-2] + (4, d)).contiguous()
+    a = dash.dash_pool_keys_query(inp["k"], same.to(DEV), block)
+    bq = dash.dash_pool_keys_query(inp["k"], qbar.reshape(-1, 4, d)[0].contiguous().to(DEV), block)
+    torch.cuda.synchronize()
+    assert torch.equal(a, bq)
 
 
 # ------------------------------------------------------------------ tiny fp32 workload, in full

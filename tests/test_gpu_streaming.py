@@ -151,7 +151,7 @@ def test_varlen_decode(dash, orc, window, fused):
                        lens, block, 2, 1.5, 1.0, float(v.abs().max()))
 
 
-@pytest.mark.parametrize("learned", [False, True])
+@pytest.mark.parametrize("learned", [False, True, "per_chunk"])
 def test_streaming_decode(dash, orc, learned):
     """Decode steps that append one token per sequence: the summary of each chunk the new token
     completes is written by the append call (and nothing else is), and every step's route and
@@ -162,8 +162,9 @@ def test_streaming_decode(dash, orc, learned):
                     decode=True, plant="decode", plant_args=dict(lo=1, hi=6), seed=84)
     inp = wl.make_inputs(w, DEV)
     q, k, v = inp["q"], inp["k"], inp["v"]
-    qbar = (torch.randn(2, 128, generator=torch.Generator().manual_seed(9)) * 0.3).to(DEV) if learned else None
     tc = cap // block
+    qshape = (tc, 2, 128) if learned == "per_chunk" else (2, 128)
+    qbar = (torch.randn(qshape, generator=torch.Generator().manual_seed(9)) * 0.3).to(DEV) if learned else None
     kbar = torch.full((len(start), tc, 2, 128), float("nan"), dtype=torch.float32, device=DEV)
     # summaries of the chunks complete before the first step, written by the full pooling
     full = dash.dash_pool_keys_query(k, qbar, block) if learned else dash.dash_pool_keys(k, block)
@@ -184,7 +185,10 @@ def test_streaming_decode(dash, orc, learned):
             if learned:
                 refs = []
                 for b, n_b in enumerate(lens):
-                    kb_ref = orc.pool_keys_query(host(k[b:b + 1, :n_b]), host(qbar).double().numpy(), block)
+                    qb = host(qbar).double().numpy()
+                    if learned == "per_chunk":
+                        qb = qb[:n_b // block]
+                    kb_ref = orc.pool_keys_query(host(k[b:b + 1, :n_b]), qb, block)
                     st1 = orc.block_entmax(host(q[b:b + 1]), kb_ref, n_kv=n_b, block=block, alpha=1.5,
                                            gamma=1.5, sigma=1.0, q_pos0=n_b - 1, h_kv=2)
                     ob, _ = orc.sparse_attn(host(q[b:b + 1]), host(k[b:b + 1, :n_b]),
@@ -200,7 +204,10 @@ def test_streaming_decode(dash, orc, learned):
     kb = kbar.cpu().numpy()
     for b, n_b in enumerate(lens):
         t_b = n_b // block
-        ref = (orc.pool_keys_query(host(k[b:b + 1, :t_b * block]), host(qbar).double().numpy(), block)
+        qb = None if not learned else host(qbar).double().numpy()
+        if learned == "per_chunk":
+            qb = qb[:t_b]
+        ref = (orc.pool_keys_query(host(k[b:b + 1, :t_b * block]), qb, block)
                if learned else orc.pool_keys(host(k[b:b + 1, :t_b * block]), block))
         np.testing.assert_allclose(kb[b:b + 1, :t_b], ref, rtol=1e-5, atol=1e-5)
         assert np.all(np.isnan(kb[b, t_b:])), "a summary was written for an open chunk"

@@ -89,6 +89,19 @@ def test_prefill_rows_past_1024_chunks(dash, orc, n, hq, hkv, block):
     prefill_parity(dash, orc, w, w.sigma, sample_rows(w.n_q, w.block, 40, seed=68))
 
 
+def test_prefill_bf16_rows_past_2048_chunks(dash, orc):
+    """bf16 prefill whose rows reach 2049 to 8192 chunks: 160K tokens in chunks of 64 (2560
+    complete chunks) leave the fused Stage 1 for the score workspace, routed in slabs of query
+    rows; sampled rows against the oracle."""
+    w = wl.Workload("prefill 160K, 32q/8kv heads, D 128, block 64, 4 planted of every 16 chunks",
+                    1, 163840, 32, 8, 128, 64, 1.5, 0.5, 1e8, plant="span",
+                    plant_args=dict(span=16, per_span=4), seed=69)
+    need = dash.dash_block_entmax_workspace_bytes(torch.bfloat16, 1, w.n_q, 0, w.n_kv, 32, 8, 128, 64)
+    row_bytes = 32 * (w.n_kv // 64) * 4
+    assert need == (512 << 20) // row_bytes * row_bytes  # slabs of whole score rows
+    prefill_parity(dash, orc, w, w.sigma, sample_rows(w.n_q, w.block, 32, seed=70))
+
+
 def test_prefill_slabs_across_sequences(dash, orc):
     """Two fp32 sequences of 16K whose score rows (2 GiB) exceed the workspace: Stage 1 runs in
     four slabs of query rows, two per sequence; sampled rows of both against the oracle."""

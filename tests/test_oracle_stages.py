@@ -86,6 +86,40 @@ def test_learned_summary_query_selects_a_key(orc):
     np.testing.assert_allclose(kb[0, 1, 0], [-1 / 3, -1 / 3, 0, -1 / 3], atol=1e-12)
 
 
+def test_per_chunk_summary_queries_closed_form(orc):
+    """One summary query per chunk (and per sequence): two keys per chunk, D = 4 (sqrt(D) = 2),
+    each chunk's own query sets its logits to (ln 3, 0) / (0, ln 4) / ..., so the weights are
+    3/4, 1/4 and 1/5, 4/5 by hand; a query taken from the wrong chunk or sequence gives other
+    weights."""
+    e = np.eye(4)
+    k = np.zeros((2, 4, 1, 4))
+    k[:, 0, 0], k[:, 1, 0], k[:, 2, 0], k[:, 3, 0] = e[0], e[1], e[2], e[3]
+    q = np.zeros((2, 2, 1, 4))
+    q[0, 0, 0, 0] = 2 * np.log(3.0)      # seq 0, chunk 0: logits (ln 3, 0)
+    q[0, 1, 0, 3] = 2 * np.log(4.0)      # seq 0, chunk 1: logits (0, ln 4)
+    q[1, 0, 0, 1] = 2 * np.log(9.0)      # seq 1, chunk 0: logits (0, ln 9)
+    q[1, 1, 0, 2] = -2 * np.log(2.0)     # seq 1, chunk 1: logits (-ln 2, 0)
+    kb = orc.pool_keys_query(k, q, 2)
+    np.testing.assert_allclose(kb[0, 0, 0], [0.75, 0.25, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(kb[0, 1, 0], [0, 0, 0.2, 0.8], atol=1e-15)
+    np.testing.assert_allclose(kb[1, 0, 0], [0.1, 0.9, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(kb[1, 1, 0], [0, 0, 1 / 3, 2 / 3], atol=1e-15)
+    # one query per chunk shared by both sequences: sequence 1 takes sequence 0's queries
+    kc = orc.pool_keys_query(k, q[0], 2)
+    np.testing.assert_allclose(kc[1], kb[0], atol=1e-15)
+
+
+def test_per_chunk_queries_equal_across_chunks_give_the_per_head_form(orc):
+    rng = np.random.default_rng(3)
+    k = rng.normal(size=(2, 96, 3, 8)).astype(np.float32)
+    qh = rng.normal(size=(3, 8))
+    per_head = orc.pool_keys_query(k, qh, 32)
+    per_chunk = orc.pool_keys_query(k, np.broadcast_to(qh, (3, 3, 8)), 32)
+    per_seq_chunk = orc.pool_keys_query(k, np.broadcast_to(qh, (2, 3, 3, 8)), 32)
+    np.testing.assert_array_equal(per_head, per_chunk)
+    np.testing.assert_array_equal(per_head, per_seq_chunk)
+
+
 # ------------------------------------------------------------------------------- Stage 1
 
 @pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
