@@ -46,6 +46,7 @@ def lib():
         L.orc_pool_keys.argtypes = [vp, i, i, i, i, i, i, vp]
         L.orc_pool_keys_query.argtypes = [vp, i, vp, i, i, i, i, i, vp]
         L.orc_pool_keys_query_ex.argtypes = [vp, i, vp, i64, i64, i, i, i, i, i, vp]
+        L.orc_pool_keys_query_backward.argtypes = [vp, i, vp, i64, i64, vp, i, i, i, i, i, vp, vp]
         L.orc_entmax_tau_sort.argtypes = [vp, i, d]
         L.orc_entmax_tau_sort.restype = d
         L.orc_entmax_tau_bisect.argtypes = [vp, i, d, i]
@@ -147,6 +148,40 @@ def pool_keys_query(k, qbar, block: int) -> np.ndarray:
     _check(lib().orc_pool_keys_query_ex(_ptr(ka), dt, _ptr(qb), sb, sc, b, n, hkv, d, block,
                                         _ptr(out)), "pool_keys_query")
     return out
+
+
+def _qbar_strides(qb, b, tc, hkv, d):
+    if qb.shape == (hkv, d):
+        return 0, 0
+    if qb.shape == (tc, hkv, d):
+        return 0, hkv * d
+    if qb.shape == (b, tc, hkv, d):
+        return tc * hkv * d, hkv * d
+    raise ValueError(f"qbar shape {qb.shape} is none of [Hkv, D], [Tc, Hkv, D], [B, Tc, Hkv, D]")
+
+
+def pool_keys_query_backward(k, qbar, dkbar, block: int) -> dict:
+    """Gradients of Stage 0 with learned summary queries (Eq. 3) for dL/dkbar [B, Tc, Hkv, D]:
+    dict(dk [B, n, Hkv, D], dqbar in qbar's shape, each summed over the chunks and sequences that
+    share a query) in float64."""
+    ka, dt = _host(k)
+    qb = np.ascontiguousarray(np.asarray(qbar, dtype=np.float64))
+    b, n, hkv, d = ka.shape
+    tc = n // block
+    sb, sc = _qbar_strides(qb, b, tc, hkv, d)
+    dkb = np.ascontiguousarray(np.asarray(dkbar, dtype=np.float64).reshape(b, tc, hkv, d))
+    dk = np.zeros((b, n, hkv, d))
+    full = np.zeros((b, tc, hkv, d))
+    _check(lib().orc_pool_keys_query_backward(_ptr(ka), dt, _ptr(qb), sb, sc, _ptr(dkb), b, n, hkv,
+                                              d, block, _ptr(dk), _ptr(full)),
+           "pool_keys_query_backward")
+    if qb.shape == (hkv, d):
+        dq = full.sum(axis=(0, 1))
+    elif qb.shape == (tc, hkv, d):
+        dq = full.sum(axis=0)
+    else:
+        dq = full
+    return dict(dk=dk, dqbar=dq)
 
 
 def entmax_tau(x, alpha: float, method: str = "auto", iters: int = 200) -> float:

@@ -100,6 +100,69 @@ int orc_pool_keys_query(const void* k, int dtype, const double* qbar, int batch,
     return orc_pool_keys_query_ex(k, dtype, qbar, 0, 0, batch, n_kv, h_kv, head_dim, block, kbar);
 }
 
+/* Gradients of Eq. 3's local attention, chunk by chunk: with s_t = <qbar_c, k_t> / sqrt(D),
+ * a = softmax(s) over the chunk's keys and kbar_c = sum_t a_t k_t, a gradient dkbar_c gives
+ *   g_t = <dkbar_c, k_t>,  ds_t = a_t (g_t - sum_u a_u g_u)          (the softmax Jacobian)
+ *   dk_t += a_t dkbar_c + ds_t qbar_c / sqrt(D)                       (the weights, the logits)
+ *   dqbar_c = sum_t ds_t k_t / sqrt(D)
+ * dk [B, n_kv, h_kv, D] is added to; dqbar_full [B, Tc, h_kv, D] receives each chunk's own
+ * dqbar_c (a query shared by several chunks or sequences collects the sum of theirs). */
+int orc_pool_keys_query_backward(const void* k, int dtype, const double* qbar,
+                                 int64_t qbar_batch_stride, int64_t qbar_chunk_stride,
+                                 const double* dkbar, int batch, int n_kv, int h_kv, int head_dim,
+                                 int block, double* dk, double* dqbar_full) {
+    if (!k || !qbar || !dkbar || !dk || !dqbar_full || batch <= 0 || n_kv <= 0 || h_kv <= 0 ||
+        head_dim <= 0 || block <= 0 || qbar_batch_stride < 0 || qbar_chunk_stride < 0)
+        return -1;
+    const int tc = n_kv / block;
+    const double inv_sqrt_d = 1.0 / sqrt((double)head_dim);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < batch; ++b)
+        for (int c = 0; c < tc; ++c)
+            for (int r = 0; r < h_kv; ++r) {
+                const double* qc = qbar + b * qbar_batch_stride + c * qbar_chunk_stride + (int64_t)r * head_dim;
+                const double* dkb = dkbar + (((int64_t)b * tc + c) * h_kv + r) * head_dim;
+                double* a = malloc(sizeof(double) * block);
+                double* g = malloc(sizeof(double) * block);
+                double smax = -INFINITY;
+                for (int u = 0; u < block; ++u) {
+                    const int64_t base = (((int64_t)b * n_kv + c * block + u) * h_kv + r) * head_dim;
+                    double dot = 0.0, gd = 0.0;
+                    for (int e = 0; e < head_dim; ++e) {
+                        const double kv = orc_load(k, dtype, base + e);
+                        dot += qc[e] * kv;
+                        gd += dkb[e] * kv;
+                    }
+                    a[u] = dot * inv_sqrt_d;
+                    g[u] = gd;
+                    if (a[u] > smax) smax = a[u];
+                }
+                double z = 0.0;
+                for (int u = 0; u < block; ++u) {
+                    a[u] = exp(a[u] - smax);
+                    z += a[u];
+                }
+                double gbar = 0.0;
+                for (int u = 0; u < block; ++u) {
+                    a[u] /= z;
+                    gbar += a[u] * g[u];
+                }
+                double* dq = dqbar_full + (((int64_t)b * tc + c) * h_kv + r) * head_dim;
+                for (int e = 0; e < head_dim; ++e) dq[e] = 0.0;
+                for (int u = 0; u < block; ++u) {
+                    const double ds = a[u] * (g[u] - gbar);
+                    const int64_t base = (((int64_t)b * n_kv + c * block + u) * h_kv + r) * head_dim;
+                    for (int e = 0; e < head_dim; ++e) {
+                        dk[base + e] += a[u] * dkb[e] + ds * qc[e] * inv_sqrt_d;
+                        dq[e] += ds * orc_load(k, dtype, base + e) * inv_sqrt_d;
+                    }
+                }
+                free(a);
+                free(g);
+            }
+    return 0;
+}
+
 /* ------------------------------------------------ alpha-entmax [DA §2, Eq. 2; App. A, Eq. 13] */
 
 static int cmp_desc(const void* a, const void* b) {

@@ -65,6 +65,14 @@ int orc_pool_keys_query_ex(const void* k, int dtype, const double* qbar, int64_t
                            int64_t qbar_chunk_stride, int batch, int n_kv, int h_kv, int head_dim,
                            int block, double* kbar);
 
+/* Gradients of the learned-query pooling (Eq. 3) for dL/dkbar = dkbar [B, Tc, h_kv, D]: adds to
+ * dk [B, n_kv, h_kv, D] and writes each chunk's dL/dqbar_c into dqbar_full [B, Tc, h_kv, D]
+ * (queries addressed as in orc_pool_keys_query_ex). */
+int orc_pool_keys_query_backward(const void* k, int dtype, const double* qbar,
+                                 int64_t qbar_batch_stride, int64_t qbar_chunk_stride,
+                                 const double* dkbar, int batch, int n_kv, int h_kv, int head_dim,
+                                 int block, double* dk, double* dqbar_full);
+
 /* alpha-entmax threshold for x[0..m-1] (x already holds (alpha-1) * scores):
  * the unique tau with sum_c [x_c - tau]_+^(1/(alpha-1)) = 1.
  *   _sort:   exact sort-based solution, alpha = 2 (sparsemax) or alpha = 1.5 only (NaN otherwise)

@@ -176,3 +176,52 @@ def test_routing_gradient_rows_match_the_full_chain(orc):
     np.testing.assert_allclose(every["dq"], route_dq, rtol=1e-10, atol=1e-12)
     dk_route = np.repeat(every["dkbar"], 8, axis=1) / 8  # mean pooling: each key gets dkbar / Bc
     np.testing.assert_allclose(dk_route, full["dk"] - s2["dk"], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("per", ["head", "chunk", "sequence_chunk"])
+def test_learned_pooling_gradients_match_central_differences(orc, per):
+    """Eq. 3's local attention, differentiated: dk and dqbar of <dkbar, kbar(k, qbar)> against
+    central differences of the oracle's own pooling, for one query per KV head, per chunk, and per
+    sequence and chunk (a shared query collects the sum over what shares it)."""
+    rng = np.random.default_rng(21)
+    b, n, hkv, d, block = 2, 40, 2, 4, 8
+    tc = n // block
+    k = rng.standard_normal((b, n, hkv, d))
+    shape = {"head": (hkv, d), "chunk": (tc, hkv, d), "sequence_chunk": (b, tc, hkv, d)}[per]
+    qbar = rng.standard_normal(shape) * 1.5
+    dkbar = rng.standard_normal((b, tc, hkv, d))
+    g = orc.pool_keys_query_backward(k, qbar, dkbar, block)
+    f = lambda kk, qq: float((orc.pool_keys_query(kk, qq, block) * dkbar).sum())
+    eps = 1e-6
+    for idx in [(0, 3, 1, 2), (1, 17, 0, 0), (1, 39, 1, 3), (0, 8, 0, 1)]:
+        kp, km = k.copy(), k.copy()
+        kp[idx] += eps
+        km[idx] -= eps
+        num = (f(kp, qbar) - f(km, qbar)) / (2 * eps)
+        if idx[1] >= tc * block:   # the incomplete tail has no summary, so no gradient
+            assert g["dk"][idx] == 0.0
+        assert abs(num - g["dk"][idx]) <= 1e-7 * max(1.0, abs(num))
+    flat = qbar.reshape(-1)
+    for j in range(0, flat.size, max(1, flat.size // 6)):
+        qp, qm = flat.copy(), flat.copy()
+        qp[j] += eps
+        qm[j] -= eps
+        num = (f(k, qp.reshape(shape)) - f(k, qm.reshape(shape))) / (2 * eps)
+        assert abs(num - g["dqbar"].reshape(-1)[j]) <= 1e-7 * max(1.0, abs(num))
+
+
+def test_learned_pooling_gradient_at_zero_query_is_the_mean_pooling_gradient(orc):
+    """At qbar = 0 every weight is 1 / B, so dk_t = dkbar_c / B plus the logit term ds_t qbar = 0;
+    and dqbar_c = sum_t (1/B)(g_t - mean g) k_t / sqrt(D), the covariance of g and k in the chunk."""
+    rng = np.random.default_rng(22)
+    k = rng.standard_normal((1, 16, 1, 4))
+    dkbar = rng.standard_normal((1, 2, 1, 4))
+    g = orc.pool_keys_query_backward(k, np.zeros((1, 4)), dkbar, 8)
+    np.testing.assert_allclose(g["dk"][0, :8, 0], np.broadcast_to(dkbar[0, 0, 0] / 8, (8, 4)), atol=1e-15)
+    np.testing.assert_allclose(g["dk"][0, 8:, 0], np.broadcast_to(dkbar[0, 1, 0] / 8, (8, 4)), atol=1e-15)
+    want = np.zeros(4)
+    for c in range(2):
+        kc = k[0, 8 * c:8 * c + 8, 0]
+        gt = kc @ dkbar[0, c, 0]
+        want += ((gt - gt.mean())[:, None] * kc).sum(axis=0) / 8 / 2.0
+    np.testing.assert_allclose(g["dqbar"][0], want, atol=1e-14)
