@@ -274,6 +274,33 @@ dash_status_t dash_block_entmax_backward(const void* q, dash_dtype_t dt, const f
                                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dash_block_entmax_backward for learned summary queries [DA §3.1 Eq. 3 and Alg. 1: kbar_c is a
+ * softmax-weighted sum of chunk c's keys, a = softmax_j(<qbar_c, k_j> / sqrt(D))]: the same
+ * routing gradients, then the pooling's own chain rule. With dkbar_c as above and
+ * g_j = <dkbar_c, k_j>, ds_j = a_j (g_j - sum_i a_i g_i) (the softmax Jacobian), it ADDS
+ *   dk_j += a_j dkbar_c + ds_j qbar_c / sqrt(D)   to the keys of each complete chunk, and WRITES
+ *   dqbar = dL/dqbar: sum over the (sequence, chunk) pairs that use a query of their
+ *   sum_j ds_j k_j / sqrt(D), summed in a fixed order (deterministic).
+ *   k [B, n, H_kv, D] (dt, q's dtype): the keys kbar was pooled from; kbar [B, Tc, H_kv, D] fp32
+ *   from dash_pool_keys_query_ex with the same qbar and strides; qbar fp32, the query of
+ *   (sequence b, chunk c, KV head r) at qbar + b * qbar_batch_stride + c * qbar_chunk_stride +
+ *   r * D (strides in floats, non-negative multiples of 4: 0, 0 for [H_kv, D]; 0, H_kv D for
+ *   [Tc, H_kv, D]; Tc H_kv D, H_kv D for [B, Tc, H_kv, D]); queries of distinct (b, c) pairs may
+ *   coincide (a zero stride) but not partly overlap (else DASH_ERR_INVALID). dqbar: fp32 with
+ *   qbar's addressing, every query's D floats overwritten. qbar, dqbar 16-byte aligned.
+ *   workspace: dash_block_entmax_backward_query_workspace_bytes(B, n, H_q, H_kv, D, block)
+ *   bytes, 256-byte aligned. Other arguments as for dash_block_entmax_backward.
+ */
+size_t dash_block_entmax_backward_query_workspace_bytes(int batch, int n, int h_q, int h_kv,
+                                                        int head_dim, int block);
+dash_status_t dash_block_entmax_backward_query(
+    const void* q, const void* k, dash_dtype_t dt, const float* kbar, const float* qbar,
+    int64_t qbar_batch_stride, int64_t qbar_chunk_stride, const float* tau, const uint32_t* mask,
+    const float* dbias, float* dq, float* dk, float* dqbar, int batch, int n, int h_q, int h_kv,
+    int head_dim, int block, float alpha, float gamma, float sigma, int window_blocks,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Stage 2, decode [DA §3.5, split-KV variant]: the Stage 2 output of one new query per sequence
  * at position n_ctx - 1 of its cache. The selected chunks are split over many workgroups; their
  * partial (max, sum, output) triples are merged in a fixed order by the last of them to finish,

@@ -25,6 +25,7 @@ __all__ = [
     "dash_decode_workspace_bytes", "dash_sparse_attn_decode", "dash_sparse_attn_decode_varlen",
     "dash_sparse_attn_backward_workspace_bytes", "dash_sparse_attn_prefill_backward",
     "dash_block_entmax_backward_workspace_bytes", "dash_block_entmax_backward",
+    "dash_block_entmax_backward_query_workspace_bytes", "dash_block_entmax_backward_query",
     "dash_decode_step_workspace_bytes", "dash_decode_step", "dash_decode_step_noalloc",
     "dash_version", "backward", "forward", "decode_step",
 ]
@@ -90,6 +91,12 @@ def lib():
         L.dash_block_entmax_backward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
                                                  f, f, f, i, vp, sz, vp]
         L.dash_block_entmax_backward.restype = i
+        L.dash_block_entmax_backward_query_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.dash_block_entmax_backward_query_workspace_bytes.restype = sz
+        L.dash_block_entmax_backward_query.argtypes = [vp, vp, i, vp, vp, i64, i64, vp, vp, vp, vp,
+                                                       vp, vp, i, i, i, i, i, i, f, f, f, i, vp,
+                                                       sz, vp]
+        L.dash_block_entmax_backward_query.restype = i
         L.dash_decode_step_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.dash_decode_step_workspace_bytes.restype = sz
         L.dash_decode_step.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, i, f, f, f, i, f, vp,
@@ -381,6 +388,37 @@ def dash_block_entmax_backward(q: torch.Tensor, kbar: torch.Tensor, tau: torch.T
         int(window_blocks), _ptr(workspace), workspace.numel(), _stream(dev)))
 
 
+def dash_block_entmax_backward_query_workspace_bytes(batch, n, h_q, h_kv, head_dim, block) -> int:
+    return int(lib().dash_block_entmax_backward_query_workspace_bytes(batch, n, h_q, h_kv, head_dim,
+                                                                      block))
+
+
+def dash_block_entmax_backward_query(q: torch.Tensor, k: torch.Tensor, kbar: torch.Tensor,
+                                     qbar: torch.Tensor, tau: torch.Tensor, mask: torch.Tensor,
+                                     dbias: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, *,
+                                     block: int, alpha: float, gamma: float, sigma: float,
+                                     window_blocks: int = 1, dqbar: torch.Tensor | None = None,
+                                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Routing and learned-query pooling gradients for prefill: adds to dq and dk (fp32) and
+    returns dqbar, qbar's shape ([Hkv, D], [Tc, Hkv, D] or [B, Tc, Hkv, D]), fp32."""
+    _f32(kbar=kbar, qbar=qbar, tau=tau, dbias=dbias, dq=dq, dk=dk, dqbar=dqbar)
+    b, n, hq, d = q.shape
+    hkv = k.shape[2]
+    sb, sc = _qbar_strides(qbar, b, n // block, hkv, d)
+    if dqbar is None:
+        dqbar = torch.empty_like(qbar)
+    need = dash_block_entmax_backward_query_workspace_bytes(b, n, hq, hkv, d, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dev = _dev(q, k, kbar, qbar, tau, mask, dbias, dq, dk, dqbar, workspace)
+    _check(lib().dash_block_entmax_backward_query(
+        _ptr(q), _ptr(k), _dtype_code(q), _ptr(kbar), _ptr(qbar), sb, sc, _ptr(tau), _ptr(mask),
+        _ptr(dbias), _ptr(dq), _ptr(dk), _ptr(dqbar), b, n, hq, hkv, d, block, float(alpha),
+        float(gamma), float(sigma), int(window_blocks), _ptr(workspace), workspace.numel(),
+        _stream(dev)))
+    return dqbar
+
+
 def dash_decode_workspace_bytes(batch, n_ctx, h_q, h_kv, head_dim, block) -> int:
     return int(lib().dash_decode_workspace_bytes(batch, n_ctx, h_q, h_kv, head_dim, block))
 
@@ -437,11 +475,12 @@ def dash_sparse_attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cac
 
 
 def forward(q, k, v, *, block: int, alpha: float, gamma: float, sigma: float,
-            scale: float | None = None, window: int = 1):
+            scale: float | None = None, window: int = 1, qbar: torch.Tensor | None = None):
     """Whole prefill forward: pool -> route -> sparse attention. Returns a dict of every
     intermediate (kbar, mask, bias, tau, o, lse). window: blocks always attended (the query's
-    own and window - 1 before it)."""
-    kbar = dash_pool_keys(k, block)
+    own and window - 1 before it). qbar: learned summary queries (see dash_pool_keys_query);
+    None for mean pooling."""
+    kbar = dash_pool_keys(k, block) if qbar is None else dash_pool_keys_query(k, qbar, block)
     if window == 1:
         mask, bias, tau = dash_block_entmax(q, kbar, n_kv=k.shape[1], block=block, alpha=alpha,
                                             gamma=gamma, sigma=sigma, h_kv=k.shape[2])
@@ -454,16 +493,24 @@ def forward(q, k, v, *, block: int, alpha: float, gamma: float, sigma: float,
 
 
 def backward(q, k, v, dout, fwd: dict, *, block: int, alpha: float, gamma: float, sigma: float,
-             scale: float | None = None, window: int = 1) -> dict:
+             scale: float | None = None, window: int = 1,
+             qbar: torch.Tensor | None = None) -> dict:
     """Gradients of the prefill forward (pool, route, attend) for dL/do = dout, given the dict
-    that forward() returned with the same arguments: dict(dq, dk, dv, dbias), fp32. The
-    selection is held fixed (no gradient flows through which chunks are selected)."""
+    that forward() returned with the same arguments: dict(dq, dk, dv, dbias), fp32, plus dqbar
+    when qbar (learned summary queries) is given. The selection is held fixed (no gradient flows
+    through which chunks are selected)."""
     dq, dk, dv, dbias = dash_sparse_attn_prefill_backward(q, k, v, fwd["lse"], dout, fwd["mask"],
                                                           fwd["bias"], block=block, scale=scale)
-    dash_block_entmax_backward(q, fwd["kbar"], fwd["tau"], fwd["mask"], dbias, dq, dk,
-                               block=block, alpha=alpha, gamma=gamma, sigma=sigma,
-                               window_blocks=window)
-    return dict(dq=dq, dk=dk, dv=dv, dbias=dbias)
+    out = dict(dq=dq, dk=dk, dv=dv, dbias=dbias)
+    if qbar is None:
+        dash_block_entmax_backward(q, fwd["kbar"], fwd["tau"], fwd["mask"], dbias, dq, dk,
+                                   block=block, alpha=alpha, gamma=gamma, sigma=sigma,
+                                   window_blocks=window)
+    else:
+        out["dqbar"] = dash_block_entmax_backward_query(
+            q, k, fwd["kbar"], qbar, fwd["tau"], fwd["mask"], dbias, dq, dk, block=block,
+            alpha=alpha, gamma=gamma, sigma=sigma, window_blocks=window)
+    return out
 
 
 def dash_decode_step_workspace_bytes(batch, n_ctx, h_q, h_kv, head_dim, block) -> int:

@@ -315,14 +315,27 @@ size_t dash_block_entmax_backward_workspace_bytes(int batch, int n, int h_q, int
     return (size_t)batch * n * (h_q + h_kv) * sizeof(float);
 }
 
-dash_status_t dash_block_entmax_backward(const void* q, dash_dtype_t dt, const float* kbar,
-                                         const float* tau, const uint32_t* mask,
-                                         const float* dbias, float* dq, float* dk, int batch,
-                                         int n, int h_q, int h_kv, int head_dim, int block,
-                                         float alpha, float gamma, float sigma,
-                                         int window_blocks, void* workspace,
-                                         size_t workspace_bytes, hipStream_t stream) {
-    const char* fn = "dash_block_entmax_backward";
+size_t dash_block_entmax_backward_query_workspace_bytes(int batch, int n, int h_q, int h_kv,
+                                                        int head_dim, int block) {
+    if (batch <= 0 || n <= 0 || h_q <= 0 || h_kv <= 0 || head_dim <= 0 || block <= 0) return 0;
+    dash::RouteParams p{};
+    p.batch = batch;
+    p.n_q = n;
+    p.h_q = h_q;
+    p.h_kv = h_kv;
+    p.head_dim = head_dim;
+    p.tc = n / block;
+    return dash::route_backward_workspace_bytes(p, true);
+}
+
+namespace {
+
+dash_status_t route_backward_call(const char* fn, const void* q, dash_dtype_t dt,
+                                  const float* kbar, const dash::PoolGrad& pg, const float* tau,
+                                  const uint32_t* mask, const float* dbias, float* dq, float* dk,
+                                  int batch, int n, int h_q, int h_kv, int head_dim, int block,
+                                  float alpha, float gamma, float sigma, int window_blocks,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     dash_status_t s = check_shape(fn, dt, batch, n, h_q, h_kv, head_dim, block);
     if (s != DASH_OK) return s;
     if (window_blocks < 1) return fail(DASH_ERR_INVALID, "%s: window_blocks=%d must be >= 1", fn, window_blocks);
@@ -334,12 +347,59 @@ dash_status_t dash_block_entmax_backward(const void* q, dash_dtype_t dt, const f
     dash::RouteParams p = route_params(batch, n, 0, n, h_q, h_kv, head_dim, block, alpha, gamma,
                                        sigma);
     p.win = window_blocks - 1;
-    const size_t need = dash::route_backward_workspace_bytes(p);
+    const size_t need = dash::route_backward_workspace_bytes(p, pg.qbar != nullptr);
     if (!workspace || workspace_bytes < need)
         return fail(DASH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace ? workspace_bytes : (size_t)0);
-    return hip_status(dash::launch_route_backward(q, (int)dt, kbar, tau, mask, dbias, dq, dk, p,
-                                                  workspace, stream), fn);
+    if (pg.qbar && ((uintptr_t)workspace & 255))
+        return fail(DASH_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    return hip_status(dash::launch_route_backward(q, (int)dt, kbar, tau, mask, dbias, dq, dk, pg,
+                                                  p, workspace, stream), fn);
+}
+
+}  // namespace
+
+dash_status_t dash_block_entmax_backward(const void* q, dash_dtype_t dt, const float* kbar,
+                                         const float* tau, const uint32_t* mask,
+                                         const float* dbias, float* dq, float* dk, int batch,
+                                         int n, int h_q, int h_kv, int head_dim, int block,
+                                         float alpha, float gamma, float sigma,
+                                         int window_blocks, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+    const dash::PoolGrad pg{nullptr, nullptr, 0, 0, nullptr};
+    return route_backward_call("dash_block_entmax_backward", q, dt, kbar, pg, tau, mask, dbias,
+                               dq, dk, batch, n, h_q, h_kv, head_dim, block, alpha, gamma, sigma,
+                               window_blocks, workspace, workspace_bytes, stream);
+}
+
+dash_status_t dash_block_entmax_backward_query(
+    const void* q, const void* k, dash_dtype_t dt, const float* kbar, const float* qbar,
+    int64_t qbar_batch_stride, int64_t qbar_chunk_stride, const float* tau, const uint32_t* mask,
+    const float* dbias, float* dq, float* dk, float* dqbar, int batch, int n, int h_q, int h_kv,
+    int head_dim, int block, float alpha, float gamma, float sigma, int window_blocks,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "dash_block_entmax_backward_query";
+    if (!k || !qbar || !dqbar) return fail(DASH_ERR_INVALID, "%s: null pointer", fn);
+    const int64_t sb = qbar_batch_stride, sc = qbar_chunk_stride;
+    if (sb < 0 || sc < 0 || sb % 4 || sc % 4)
+        return fail(DASH_ERR_INVALID, "%s: qbar strides must be non-negative multiples of 4 (%lld, %lld)",
+                    fn, (long long)sb, (long long)sc);
+    if (((uintptr_t)qbar & 15) || ((uintptr_t)dqbar & 15))
+        return fail(DASH_ERR_INVALID, "%s: qbar and dqbar must be 16-byte aligned", fn);
+    // dqbar rows of distinct (sequence, chunk) pairs must not overlap unless they share the query
+    if (head_dim > 0 && block > 0 && batch > 0) {
+        const int64_t row = (int64_t)h_kv * head_dim, tc = n / block;
+        const int64_t eb = batch > 1 ? sb : 0, ec = tc > 1 ? sc : 0;
+        const bool ok = (eb == 0 || eb >= row) && (ec == 0 || ec >= row) &&
+                        (eb == 0 || ec == 0 || eb >= tc * ec || ec >= (int64_t)batch * eb);
+        if (!ok)
+            return fail(DASH_ERR_INVALID, "%s: qbar strides (%lld, %lld) make distinct chunks' queries overlap",
+                        fn, (long long)sb, (long long)sc);
+    }
+    const dash::PoolGrad pg{k, qbar, sb, sc, dqbar};
+    return route_backward_call(fn, q, dt, kbar, pg, tau, mask, dbias, dq, dk, batch, n, h_q, h_kv,
+                               head_dim, block, alpha, gamma, sigma, window_blocks, workspace,
+                               workspace_bytes, stream);
 }
 
 size_t dash_decode_workspace_bytes(int batch, int n_ctx, int h_q, int h_kv, int head_dim,

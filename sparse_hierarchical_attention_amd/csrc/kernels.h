@@ -43,10 +43,21 @@ hipError_t launch_block_entmax(const void* q, int dt, const float* kbar, const R
                                hipStream_t st);
 hipError_t launch_score_one(const void* q, int dt, const float* kbar, float* x,
                             const RouteParams& p, hipStream_t st);
-size_t route_backward_workspace_bytes(const RouteParams& p);
+// Stage 0 of the backward: qbar == nullptr for mean pooling; otherwise learned summary queries,
+// the query of (sequence b, chunk c, KV head r) at qbar + b sb + c sc + r D, its gradient written
+// at dqbar + b sb + c sc + r D (summed over the (b, c) that share it: sb = 0 or sc = 0)
+struct PoolGrad {
+    const void* k;  // [B, n, Hkv, D], q's dtype
+    const float* qbar;
+    int64_t sb, sc;
+    float* dqbar;
+};
+// with_query: room for each chunk's dqbar before the sum over shared queries
+size_t route_backward_workspace_bytes(const RouteParams& p, bool with_query);
 hipError_t launch_route_backward(const void* q, int dt, const float* kbar, const float* tau,
                                  const uint32_t* mask, const float* dbias, float* dq, float* dk,
-                                 const RouteParams& p, void* ws, hipStream_t st);
+                                 const PoolGrad& pg, const RouteParams& p, void* ws,
+                                 hipStream_t st);
 
 
 // ---- Stage 2 (sparse_attn.hip)

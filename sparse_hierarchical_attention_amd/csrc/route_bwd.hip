@@ -10,15 +10,21 @@
 //     App. A: tau moves so that the probabilities keep summing to one),
 //   x_h,c = coef <q_h, kbar_c>, coef = (alpha - 1) gamma / sqrt(D)  =>  dq_h += coef sum_c dx_h,c kbar_c,
 //     dkbar_c += coef sum over rows and heads of dx_h,c q_h,
-//   kbar_c = the mean of chunk c's keys                     =>  dk_j += dkbar_c / Bc for j in c.
+//   kbar_c = the mean of chunk c's keys                     =>  dk_j += dkbar_c / Bc for j in c,
+//   or, with a learned summary query qbar_c (Eq. 3's local attention over the chunk's keys),
+//   kbar_c = sum_j a_j k_j, a = softmax_j(<qbar_c, k_j> / sqrt(D)), g_j = <dkbar_c, k_j>:
+//     dk_j += a_j dkbar_c + a_j (g_j - sum_i a_i g_i) qbar_c / sqrt(D),
+//     dqbar_c = sum_j a_j (g_j - sum_i a_i g_i) k_j / sqrt(D)  (the softmax Jacobian).
 // Two kernels, each output element written by one thread in a fixed order (deterministic, no
 // atomics); both recompute x with the same lane layout and summation order, so they agree bit
 // for bit on p, w and the support:
 //   route_bwd_row_kernel, one workgroup per (row, group): three passes over R (the mean of dd,
 //     then rho per head, then dx) add the routing part of dq and leave mean_R dd and rho per row;
 //   route_bwd_col_kernel, one workgroup per (sequence, group, complete chunk): lists in order the
-//     rows whose R holds the chunk, recomputes their dx for it, and adds dkbar_c / Bc to the dk of
-//     the chunk's keys.
+//     rows whose R holds the chunk, recomputes their dx for it, and adds the pooling gradient to
+//     the dk of the chunk's keys (and writes the chunk's dqbar);
+//   pool_qbar_reduce_kernel sums the per-chunk dqbar over the chunks and sequences that share one
+//     summary query, in a fixed order.
 #include <math.h>
 
 #include "common.h"
@@ -34,6 +40,7 @@ constexpr int kRbWaves = kRbThreads / 64;
 constexpr int kRbMaxChunks = 8192;
 constexpr int kColThreads = 512;  // threads per workgroup of the column kernel (eight waves)
 constexpr int kColWaves = kColThreads / 64;
+constexpr int kMaxPoolBlock = 128;  // longest chunk the column kernel pools over
 
 // [t]_+^(e - 1) = p^(2 - alpha) on the support (t = x - tau > 0), 0 off it.
 template <int KIND>
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(kColThreads) void route_bwd_col_kernel(
     const T* __restrict__ q, const float* __restrict__ kbar, const float* __restrict__ tau,
     const uint32_t* __restrict__ mask, const float* __restrict__ dbias,
     const float* __restrict__ mean_ws, const float* __restrict__ rho_ws, float* __restrict__ dk,
-    RouteParams p) {
+    PoolGrad pg, int64_t fsb, int64_t fsc, RouteParams p) {
     constexpr int LPK = D / 4;
     constexpr int RPW = 64 / LPK;
     constexpr int kScan = kColThreads;  // rows examined per block of the scan
@@ -374,69 +381,218 @@ __global__ __launch_bounds__(kColThreads) void route_bwd_col_kernel(
         for (int i = 0; i < 4; ++i) dkred[wave][4 * li + i] = acc[i];
     }
     __syncthreads();
-    // dk_j += coef dkbar_c / Bc for the chunk's keys (complete chunk: Bc keys)
-    const float f = coef / (float)p.block;
-    for (int idx = tid; idx < p.block * D; idx += kColThreads) {
-        const int j = idx / D, d = idx % D;
+    if (!pg.qbar) {
+        // dk_j += coef dkbar_c / Bc for the chunk's keys (complete chunk: Bc keys)
+        const float f = coef / (float)p.block;
+        for (int idx = tid; idx < p.block * D; idx += kColThreads) {
+            const int j = idx / D, d = idx % D;
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < kColWaves; ++i) s += dkred[i][d];
+            dk[(((int64_t)b * p.n_kv + (int64_t)c * p.block + j) * p.h_kv + r) * D + d] += f * s;
+        }
+        return;
+    }
+
+    // learned summary query: back through the chunk's local attention
+    __shared__ float dkb[D], qs[D], sl[kMaxPoolBlock], gl[kMaxPoolBlock];
+    const float isd = 1.0f / sqrtf((float)D);
+    for (int d = tid; d < D; d += kColThreads) {
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < kColWaves; ++i) s += dkred[i][d];
-        dk[(((int64_t)b * p.n_kv + (int64_t)c * p.block + j) * p.h_kv + r) * D + d] += f * s;
+        dkb[d] = coef * s;
+        qs[d] = pg.qbar[b * pg.sb + c * pg.sc + (int64_t)r * D + d];
+    }
+    __syncthreads();  // dkred is free again from here
+    const T* kc = static_cast<const T*>(pg.k) + (((int64_t)b * p.n_kv + (int64_t)c * p.block) * p.h_kv + r) * D + 4 * li;
+    float* dkc = dk + (((int64_t)b * p.n_kv + (int64_t)c * p.block) * p.h_kv + r) * D + 4 * li;
+    const int64_t kstep = (int64_t)p.h_kv * D;
+    float qf4[4], df4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qf4[i] = qs[4 * li + i];
+        df4[i] = dkb[4 * li + i];
+    }
+    // logits s_j = <qbar, k_j> / sqrt(D) and g_j = <dkbar, k_j>; RPW keys per wave and pass (the
+    // chunk length is a multiple of kColWaves * RPW, so every lane group holds a key)
+    for (int j = wave * RPW + seg; j < p.block; j += kColWaves * RPW) {
+        float kf[4], s = 0.f, g = 0.f;
+        load4(kc + j * kstep, kf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s = fmaf(qf4[i], kf[i], s);
+            g = fmaf(df4[i], kf[i], g);
+        }
+        s = grp4_sum<LPK>(s);
+        g = grp4_sum<LPK>(g);
+        if (li == 0) {
+            sl[j] = s * isd;
+            gl[j] = g;
+        }
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int j = 0; j < p.block; ++j) mx = fmaxf(mx, sl[j]);
+    float z = 0.f, zg = 0.f;
+    for (int j = 0; j < p.block; ++j) {
+        const float a = __expf(sl[j] - mx);
+        z += a;
+        zg = fmaf(a, gl[j], zg);
+    }
+    const float iz = 1.0f / z, gbar = zg * iz;
+    float dqa[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = wave * RPW + seg; j < p.block; j += kColWaves * RPW) {
+        float kf[4];
+        load4(kc + j * kstep, kf);
+        const float a = __expf(sl[j] - mx) * iz, ds = a * (gl[j] - gbar);
+        float4* dst = reinterpret_cast<float4*>(dkc + j * kstep);
+        float4 cur = *dst;
+        cur.x += a * df4[0] + ds * qf4[0] * isd;
+        cur.y += a * df4[1] + ds * qf4[1] * isd;
+        cur.z += a * df4[2] + ds * qf4[2] * isd;
+        cur.w += a * df4[3] + ds * qf4[3] * isd;
+        *dst = cur;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dqa[i] = fmaf(ds, kf[i], dqa[i]);
+    }
+#pragma unroll
+    for (int o = LPK; o < 64; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dqa[i] += __shfl_xor(dqa[i], o, 64);
+    if (seg == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dkred[wave][4 * li + i] = dqa[i];
+    }
+    __syncthreads();
+    for (int d = tid; d < D; d += kColThreads) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < kColWaves; ++i) s += dkred[i][d];
+        pg.dqbar[b * fsb + c * fsc + (int64_t)r * D + d] = s * isd;
     }
 }
 
-size_t route_backward_workspace_bytes(const RouteParams& p) {
-    return (size_t)p.batch * p.n_q * (p.h_q + p.h_kv) * sizeof(float);
+// dL/dqbar of a summary query shared by several (sequence, chunk) pairs: the sum of their
+// per-chunk gradients part [B, Tc, Hkv, D], sequence-major then chunk, in a fixed order. One
+// workgroup per output row (b', c', r): b' runs over the sequences when sb != 0 (else 0), c' over
+// the chunks when sc != 0 (else 0); each of the SL slices of lanes sums every SL-th term.
+template <int D>
+__global__ __launch_bounds__(256) void pool_qbar_reduce_kernel(
+    const float* __restrict__ part, float* __restrict__ dqbar, int batch, int tc, int h_kv,
+    int64_t sb, int64_t sc) {
+    constexpr int LPR = D / 4;
+    constexpr int SL = 256 / LPR;
+    __shared__ float4 red[SL][LPR];
+    const int ncc = sc ? tc : 1;
+    const int r = blockIdx.x % h_kv, cc = (blockIdx.x / h_kv) % ncc, bb = blockIdx.x / (h_kv * ncc);
+    const int nb_sum = sb ? 1 : batch, nc_sum = sc ? 1 : tc;
+    const int li = threadIdx.x % LPR, sl = threadIdx.x / LPR;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = sl; u < nb_sum * nc_sum; u += SL) {
+        const int b = sb ? bb : u / nc_sum, c = sc ? cc : u % nc_sum;
+        const float4 x = *reinterpret_cast<const float4*>(part + (((int64_t)b * tc + c) * h_kv + r) * D + 4 * li);
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+    }
+    red[sl][li] = acc;
+    __syncthreads();
+    if (sl == 0) {
+        for (int i = 1; i < SL; ++i) {
+            acc.x += red[i][li].x;
+            acc.y += red[i][li].y;
+            acc.z += red[i][li].z;
+            acc.w += red[i][li].w;
+        }
+        *reinterpret_cast<float4*>(dqbar + bb * sb + cc * sc + (int64_t)r * D + 4 * li) = acc;
+    }
+}
+
+// mean_R dd per (row, group) and rho per (row, head); then, for learned summary queries, each
+// chunk's dqbar [B, Tc, Hkv, D] from a 256-byte boundary
+size_t route_backward_rows_bytes(const RouteParams& p) {
+    return ((size_t)p.batch * p.n_q * (p.h_q + p.h_kv) * sizeof(float) + 255) & ~(size_t)255;
+}
+size_t route_backward_workspace_bytes(const RouteParams& p, bool with_query) {
+    if (!with_query) return (size_t)p.batch * p.n_q * (p.h_q + p.h_kv) * sizeof(float);
+    return route_backward_rows_bytes(p) + (size_t)p.batch * p.tc * p.h_kv * p.head_dim * sizeof(float);
 }
 
 template <typename T, int D, int GQ, int KIND>
 static void launch_rb_k(const void* q, const float* kbar, const float* tau, const uint32_t* mask,
                         const float* dbias, float* dq, float* dk, float* mean_ws, float* rho_ws,
-                        const RouteParams& p, hipStream_t st) {
+                        const PoolGrad& pg, int64_t fsb, int64_t fsc, const RouteParams& p,
+                        hipStream_t st) {
     hipLaunchKernelGGL((route_bwd_row_kernel<T, D, GQ, KIND>), dim3(p.n_q, p.h_kv, p.batch),
                        dim3(kRbThreads), 0, st, static_cast<const T*>(q), kbar, tau, mask, dbias,
                        dq, mean_ws, rho_ws, p);
     if (p.tc > 0)
         hipLaunchKernelGGL((route_bwd_col_kernel<T, D, GQ, KIND>), dim3(p.tc * p.h_kv * p.batch),
                            dim3(kColThreads), 0, st, static_cast<const T*>(q), kbar, tau, mask,
-                           dbias, mean_ws, rho_ws, dk, p);
+                           dbias, mean_ws, rho_ws, dk, pg, fsb, fsc, p);
 }
 
 template <typename T, int D, int GQ>
 static void launch_rb_g(const void* q, const float* kbar, const float* tau, const uint32_t* mask,
                         const float* dbias, float* dq, float* dk, float* mean_ws, float* rho_ws,
-                        const RouteParams& p, hipStream_t st) {
+                        const PoolGrad& pg, int64_t fsb, int64_t fsc, const RouteParams& p,
+                        hipStream_t st) {
     switch (pow_kind(p.alpha)) {
-        case kPowOne: launch_rb_k<T, D, GQ, kPowOne>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st); break;
-        case kPowTwo: launch_rb_k<T, D, GQ, kPowTwo>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st); break;
-        default: launch_rb_k<T, D, GQ, kPowGeneral>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st); break;
+        case kPowOne: launch_rb_k<T, D, GQ, kPowOne>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, pg, fsb, fsc, p, st); break;
+        case kPowTwo: launch_rb_k<T, D, GQ, kPowTwo>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, pg, fsb, fsc, p, st); break;
+        default: launch_rb_k<T, D, GQ, kPowGeneral>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, pg, fsb, fsc, p, st); break;
     }
 }
 
 template <typename T, int D>
 static void launch_rb_d(const void* q, const float* kbar, const float* tau, const uint32_t* mask,
                         const float* dbias, float* dq, float* dk, float* mean_ws, float* rho_ws,
-                        const RouteParams& p, hipStream_t st) {
+                        const PoolGrad& pg, int64_t fsb, int64_t fsc, const RouteParams& p,
+                        hipStream_t st) {
     switch (p.g) {
-        case 1: launch_rb_g<T, D, 1>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st); break;
-        case 2: launch_rb_g<T, D, 2>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st); break;
-        case 4: launch_rb_g<T, D, 4>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st); break;
-        case 8: launch_rb_g<T, D, 8>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st); break;
-        default: launch_rb_g<T, D, 16>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st); break;
+        case 1: launch_rb_g<T, D, 1>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, pg, fsb, fsc, p, st); break;
+        case 2: launch_rb_g<T, D, 2>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, pg, fsb, fsc, p, st); break;
+        case 4: launch_rb_g<T, D, 4>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, pg, fsb, fsc, p, st); break;
+        case 8: launch_rb_g<T, D, 8>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, pg, fsb, fsc, p, st); break;
+        default: launch_rb_g<T, D, 16>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, pg, fsb, fsc, p, st); break;
     }
 }
 
 hipError_t launch_route_backward(const void* q, int dt, const float* kbar, const float* tau,
                                  const uint32_t* mask, const float* dbias, float* dq, float* dk,
-                                 const RouteParams& p, void* ws, hipStream_t st) {
+                                 const PoolGrad& pg, const RouteParams& p, void* ws,
+                                 hipStream_t st) {
     float* mean_ws = static_cast<float*>(ws);
     float* rho_ws = mean_ws + (size_t)p.batch * p.n_q * p.h_kv;
+    // each chunk's dqbar goes straight to dqbar when no two chunks share a query, else through
+    // the workspace and a fixed-order sum
+    const bool shared = pg.qbar && ((p.batch > 1 && pg.sb == 0) || (p.tc > 1 && pg.sc == 0));
+    PoolGrad g = pg;
+    int64_t fsb = pg.sb, fsc = pg.sc;
+    if (shared) {
+        g.dqbar = reinterpret_cast<float*>(static_cast<char*>(ws) + route_backward_rows_bytes(p));
+        fsb = (int64_t)p.tc * p.h_kv * p.head_dim;
+        fsc = (int64_t)p.h_kv * p.head_dim;
+    }
     if (dt == kBF16) {
-        if (p.head_dim == 64) launch_rb_d<bf16_t, 64>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st);
-        else launch_rb_d<bf16_t, 128>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st);
+        if (p.head_dim == 64) launch_rb_d<bf16_t, 64>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, g, fsb, fsc, p, st);
+        else launch_rb_d<bf16_t, 128>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, g, fsb, fsc, p, st);
     } else {
-        if (p.head_dim == 64) launch_rb_d<float, 64>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st);
-        else launch_rb_d<float, 128>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, p, st);
+        if (p.head_dim == 64) launch_rb_d<float, 64>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, g, fsb, fsc, p, st);
+        else launch_rb_d<float, 128>(q, kbar, tau, mask, dbias, dq, dk, mean_ws, rho_ws, g, fsb, fsc, p, st);
+    }
+    if (shared) {
+        const int nb = pg.sb ? p.batch : 1, ncc = pg.sc ? p.tc : 1;
+        if (nb * ncc > 0) {
+            if (p.head_dim == 64)
+                hipLaunchKernelGGL(pool_qbar_reduce_kernel<64>, dim3(nb * ncc * p.h_kv), dim3(256), 0, st,
+                                   g.dqbar, pg.dqbar, p.batch, p.tc, p.h_kv, pg.sb, pg.sc);
+            else
+                hipLaunchKernelGGL(pool_qbar_reduce_kernel<128>, dim3(nb * ncc * p.h_kv), dim3(256), 0, st,
+                                   g.dqbar, pg.dqbar, p.batch, p.tc, p.h_kv, pg.sb, pg.sc);
+        }
     }
     return hipGetLastError();
 }

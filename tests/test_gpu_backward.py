@@ -308,3 +308,110 @@ def test_full_backward_sigma_inf_is_stage2_only(dash):
     dq, dk, dv, _ = dash.dash_sparse_attn_prefill_backward(q, k, v, fwd["lse"], dout, fwd["mask"],
                                                             fwd["bias"], block=32)
     assert torch.equal(g["dq"], dq) and torch.equal(g["dk"], dk) and torch.equal(g["dv"], dv)
+
+
+# ------------------------------------------------- learned summary queries: the pooling's gradient
+
+QBAR_SHAPES = {"head": lambda b, tc, hkv, d: (hkv, d), "chunk": lambda b, tc, hkv, d: (tc, hkv, d),
+               "sequence_chunk": lambda b, tc, hkv, d: (b, tc, hkv, d)}
+
+
+def _learned_case(w: wl.Workload, per: str, seed: int):
+    inp = wl.make_inputs(w, DEV)
+    tc = w.n_kv // w.block
+    g = torch.Generator().manual_seed(seed)
+    qbar = (torch.randn(QBAR_SHAPES[per](w.batch, tc, w.h_kv, w.head_dim), generator=g) * 0.15)
+    return inp["q"], inp["k"], inp["v"], qbar.to(DEV)
+
+
+@pytest.mark.parametrize("per", list(QBAR_SHAPES))
+@pytest.mark.parametrize("dtype,d,block", [("f32", 64, 32), ("bf16", 128, 64), ("bf16", 128, 32)])
+def test_learned_query_routing_backward(dash, orc, per, dtype, d, block):
+    """dash_block_entmax_backward_query against the oracle's routing gradient (dq, dkbar) chained
+    into its learned-pooling gradient (dk, dqbar), on the oracle's selection and a random dL/dd.
+    Rows whose routing gradient is ill-conditioned get dL/dd = 0 on both sides. The route
+    backward runs in fp32 for either input dtype: 1e-4 of each tensor's scale, plus the rounding
+    of x - tau scaled by the kept rows' condition."""
+    n = 300 if block == 32 else 520
+    w = wl.Workload(f"learned-query routing backward {per} {dtype} D{d} block {block}", 2, n, 8, 2,
+                    d, block, 1.5, 8.0, 0.5, dtype=dtype, seed=360 + d + block)
+    print(f"case: {w.name}", flush=True)
+    q, k, _, qbar = _learned_case(w, per, 361)
+    kbar = dash.dash_pool_keys_query(k, qbar, w.block)
+    kbar_ref = orc.pool_keys_query(k.cpu(), qbar.cpu().numpy(), w.block)
+    np.testing.assert_allclose(kbar.cpu().numpy(), kbar_ref, rtol=1e-5, atol=1e-5)
+    kw = dict(block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma)
+    st = orc.block_entmax(q.cpu(), kbar_ref, n_kv=w.n_kv, h_kv=w.h_kv, **kw)
+    st["kbar"] = kbar_ref
+    cond = _row_condition(st, parity.to_host(q).astype(np.float64), w)
+    ill = cond > 1e4
+    rng = np.random.default_rng(362)
+    dd = rng.standard_normal(st["bias"].shape)
+    dd[ill] = 0.0
+    nw = st["mask"].shape[-1]
+    mask = torch.from_numpy(st["mask"].view(np.int32).reshape(w.batch, w.n_q, w.h_kv, nw).copy()).to(DEV)
+    tau = torch.from_numpy(st["tau"].astype(np.float32).reshape(w.batch, w.n_q, w.h_q)).to(DEV)
+    dbias = torch.from_numpy(dd.astype(np.float32).reshape(w.batch, w.n_q, w.h_kv, -1)).to(DEV)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=DEV)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
+    dqbar = dash.dash_block_entmax_backward_query(q, k, kbar, qbar, tau, mask, dbias, dq, dk, **kw)
+    torch.cuda.synchronize()
+    r1 = orc.block_entmax_backward(q.cpu(), kbar_ref, dd, n_kv=w.n_kv, want_dkbar=True, **kw)
+    r0 = orc.pool_keys_query_backward(k.cpu(), qbar.cpu().numpy(), r1["dkbar"], w.block)
+    kept = float(cond[~ill].max()) if (~ill).any() else 0.0
+    print(f"ill-conditioned rows zeroed: {int(ill.sum())}, condition of the rest {kept:.3g}",
+          flush=True)
+    assert ill.mean() <= 0.05
+    _compare_cond("dq", parity.to_host(dq), r1["dq"].reshape(q.shape), "f32", kept)
+    _compare_cond("dk", parity.to_host(dk), r0["dk"], "f32", kept)
+    _compare_cond("dqbar", parity.to_host(dqbar), r0["dqbar"], "f32", kept)
+    # the incomplete tail chunk has no summary: its keys get no pooling gradient
+    tail = w.n_kv // w.block * w.block
+    if tail < w.n_kv:
+        assert float(dk[:, tail:].abs().max()) == 0.0
+    # deterministic: a second call gives the same bits
+    dq2 = torch.zeros_like(dq)
+    dk2 = torch.zeros_like(dk)
+    dqbar2 = dash.dash_block_entmax_backward_query(q, k, kbar, qbar, tau, mask, dbias, dq2, dk2, **kw)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dqbar, dqbar2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_learned_query_full_backward(dash, orc, dtype):
+    """dash.backward with per-chunk summary queries, on the oracle's selection, against the
+    oracle's Stage 2 gradient chained into its routing and learned-pooling gradients. Rows whose
+    routing gradient is ill-conditioned get dL/do = 0 (so dL/dd = 0 too) on both sides."""
+    w = wl.Workload(f"full backward, per-chunk summary queries, {dtype}", 1, 320, 8, 2, 128, 32,
+                    1.5, 8.0, 0.5, dtype=dtype, seed=370)
+    print(f"case: {w.name}", flush=True)
+    q, k, v, qbar = _learned_case(w, "chunk", 371)
+    kw = dict(block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma)
+    kbar_ref = orc.pool_keys_query(k.cpu(), qbar.cpu().numpy(), w.block)
+    st = orc.block_entmax(q.cpu(), kbar_ref, n_kv=w.n_kv, h_kv=w.h_kv, **kw)
+    st["kbar"] = kbar_ref
+    cond = _row_condition(st, parity.to_host(q).astype(np.float64), w)
+    ill = cond > 1e4
+    assert ill.mean() <= 0.05
+    mask, bias, tau = _as_gpu_selection(st, w)
+    kbar = dash.dash_pool_keys_query(k, qbar, w.block)
+    o, lse = dash.dash_sparse_attn_prefill(q, k, v, mask, bias, block=w.block)
+    fwd = dict(kbar=kbar, mask=mask, bias=bias, tau=tau, o=o, lse=lse)
+    dout = wl.output_gradient(q.shape, 372, q.dtype, DEV)
+    dout.view(-1, w.h_q, w.head_dim)[torch.from_numpy(ill).to(DEV)] = 0
+    g = dash.backward(q, k, v, dout, fwd, qbar=qbar, **kw)
+    torch.cuda.synchronize()
+    dout_h = parity.to_host(dout).astype(np.float64)
+    s2 = orc.sparse_attn_backward(q.cpu(), k.cpu(), v.cpu(), st["mask"], st["bias"], dout_h,
+                                  block=w.block)
+    r1 = orc.block_entmax_backward(q.cpu(), kbar_ref, s2["dbias"].reshape(st["bias"].shape),
+                                   n_kv=w.n_kv, want_dkbar=True, **kw)
+    r0 = orc.pool_keys_query_backward(k.cpu(), qbar.cpu().numpy(), r1["dkbar"], w.block)
+    ref_dq = s2["dq"] + r1["dq"].reshape(q.shape)
+    ref_dk = s2["dk"] + r0["dk"]
+    c = float(cond[~ill].max())
+    print(f"ill-conditioned rows given dL/do = 0: {int(ill.sum())}, condition of the rest {c:.3g}",
+          flush=True)
+    _compare_cond("dq", parity.to_host(g["dq"]), ref_dq, w.dtype, c)
+    _compare_cond("dk", parity.to_host(g["dk"]), ref_dk, w.dtype, c)
+    _compare_cond("dv", parity.to_host(g["dv"]), s2["dv"], w.dtype, c)
+    _compare_cond("dqbar", parity.to_host(g["dqbar"]), r0["dqbar"], "f32", c)
