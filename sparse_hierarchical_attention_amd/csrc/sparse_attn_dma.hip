@@ -51,7 +51,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kD = 128;              // head dim of this kernel
 constexpr int kRows = 128;           // query rows per workgroup
 constexpr int kThreads = 256;
-constexpr int kTile = 32;            // keys per LDS tile (at most)
+constexpr int kTile = 64;            // keys per LDS tile (at most)
 constexpr int kWords = 256;          // mask words of the union (8192 chunks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -67,7 +67,7 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const bf16_t* p) {
 }  // namespace
 
 template <int BLK, int GQ>
-__global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
+__global__ __launch_bounds__(kThreads, BLK < 64 ? 3 : 2) void attn_dma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const uint32_t* __restrict__ mask, const float* __restrict__ bias, bf16_t* __restrict__ o,
     float* __restrict__ lse, AttnParams p, int n_tiles) {
@@ -163,9 +163,9 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
     // K rows in odd slots of a block hold their 16-byte pieces in the order piece ^ 8, so that the
     // 16 rows one 16-lane group reads (two slots of eight blocks) cover all 64 banks: reads of
     // pieces 0-7 (k-steps 0-3) start at kl_lo, pieces 8-15 at kl_hi, each plus a constant offset
-    static_assert(NB == 8 && MT == 1, "tiles of 32 keys");
+    static_assert((NB == 8 && MT == 1) || (NB == 16 && MT == 2), "tiles of 32 or 64 keys");
     const int kl_base = (j % NB) * kKBlock + (j / NB) * kD + 8 * G;   // + 16 ks
-    const int k_odd = (j / NB) & 1;
+    const int k_odd = NB == 8 ? (j / NB) & 1 : 0;
     const int kl_lo = kl_base + 64 * k_odd, kl_hi = kl_base - 64 * k_odd;
     int vl_base[2];                                                    // + ks (16 / NB) kD + 32 dt
     {
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
         const int rr = NLD * wave + i + NB * (lane >> 4);
         loff[i] = rr * row_bytes + (uint32_t)((lane & 15) * 16);
         // K: the slot's pieces swizzled (lane >> 4 is the row's slot in its block)
-        loff_k[i] = rr * row_bytes + (uint32_t)(((lane & 15) ^ (8 * ((lane >> 4) & 1))) * 16);
+        loff_k[i] = rr * row_bytes + (uint32_t)(((lane & 15) ^ (NB == 8 ? 8 * ((lane >> 4) & 1) : 0)) * 16);
     }
     auto dma = [&](bf16_t* Kd, bf16_t* Vd, int c, int sub) __attribute__((always_inline)) {
         const uint32_t soff = (uint32_t)(c * BLK + sub * KT) * row_bytes;
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_dma_kernel(
                 auto kread = [&](int ks, bf16x8 (&dst)[MT]) __attribute__((always_inline)) {
     #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        dst[mt] = *reinterpret_cast<const bf16x8*>(Kc + (ks < 4 ? kl_lo : kl_hi) + 16 * ks);
+                        dst[mt] = *reinterpret_cast<const bf16x8*>(Kc + (ks < 4 ? kl_lo : kl_hi) + 16 * ks + mt * (32 / NB) * kD);
                 };
                 kread(0, ka[0]);
                 kread(1, ka[1]);
