@@ -5,18 +5,20 @@
 // consecutive tokens times the g heads of the group, row = token * g + head. All rows share the
 // group's chunk selection per token, so the workgroup walks the union of its tokens' selected
 // chunks (their own diagonal chunks included) and masks, per row, the chunks its token did not
-// select. Chunks are cut into tiles of 32 keys, which keeps a workgroup at 35 KiB of LDS and
-// 156 VGPRs, so that three workgroups (three waves per SIMD) share a CU.
+// select. Chunks of 64 or 128 keys are cut into tiles of 64 keys (69 KiB of LDS, 183 VGPRs: two
+// workgroups per CU, one tile barrier per 64 keys); chunks of 32 keys are one tile each (35 KiB,
+// 156 VGPRs: three workgroups per CU).
 //
 // Tiles reach LDS through buffer_load_dwordx4 ... lds: each wave instruction writes 1 KiB (lane i
 // at byte 16 i) straight into LDS, so the next tile streams in while the current one is multiplied,
 // with no registers held and nothing for the compiler to reorder. A tile's rows are stored in
 // NB = KT / 4 blocks of four 256-byte rows (row r in block r % NB at slot r / NB, one load
 // instruction per block). The LDS has 64 banks and serves a 128-bit read 16 lanes per cycle and a
-// 64-bit read 32 lanes per cycle. K blocks are 1040 bytes apart and the K rows of odd slots hold
-// their 16-byte pieces in the order piece ^ 8, so the K reads of a 16-lane group (16 rows of two
-// slots, one piece) cover the 64 banks; V blocks are 1088 bytes apart, so the transposing V reads
-// of a 32-lane group (4 rows, 8 dims each) do too. Every read is a lane base plus a constant. Two
+// 64-bit read 32 lanes per cycle. K blocks are 1040 bytes apart, so the 16 rows a 16-lane group
+// reads cover the 64 banks when they lie in 16 blocks (64-key tiles); in 32-key tiles (8 blocks,
+// two slots) the K rows of odd slots hold their 16-byte pieces in the order piece ^ 8 for the
+// same effect. V blocks are 1088 bytes apart, so the transposing V reads of a 32-lane group
+// (4 rows, 8 dims each) cover the banks too. Every read is a lane base plus a constant. Two
 // buffers each for K and V are separate LDS objects and the tile loop is unrolled by two, so
 // the compiler sees that the reads of one buffer never wait for the loads into the other.
 //
