@@ -100,60 +100,70 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ q,
 // two DPP steps sum the quad; lane k then writes heads k, k + 4, ....
 // One workgroup of nthreads threads scores chunks c0 .. c0 + nthreads / 4 - 1 of (b, r); qs holds
 // g * D floats of LDS. Ends without a barrier after its stores.
-template <typename T, int D>
-__device__ __forceinline__ void score_one_chunks(const T* __restrict__ q, const float* __restrict__ kbar,
-                                                 float* x, const RouteParams& p, float coef, int b,
-                                                 int r, int c0, int m, float* qs) {
-    constexpr int NV = D / 16;  // float4 pieces per lane
-    const int tid = threadIdx.x;
-    const int c = c0 + tid / 4;
-    const int k = tid & 3;
-    for (int e = tid; e < p.g * D; e += blockDim.x) {
-        const int gg = e / D, d = e % D;
-        qs[gg * D + d] = to_f32(q[(((int64_t)b * p.n_q) * p.h_q + r * p.g + gg) * D + d]);
-    }
-    float4 kv[NV];
-    const float4* src = reinterpret_cast<const float4*>(kbar + (((int64_t)b * p.tc + min(c, p.tc - 1)) * p.h_kv + r) * D);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) kv[i] = src[k + 4 * i];
-    __syncthreads();
-    for (int g0 = 0; g0 < p.g; g0 += 4) {
-        float part[4];
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-            const int gg = g0 + hh;
-            float a = 0.f;
-            if (gg < p.g) {
-                const float4* qv = reinterpret_cast<const float4*>(&qs[gg * D]);
-#pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    const float4 qq = qv[k + 4 * i];
-                    a = fmaf(kv[i].x, qq.x, a);
-                    a = fmaf(kv[i].y, qq.y, a);
-                    a = fmaf(kv[i].z, qq.z, a);
-                    a = fmaf(kv[i].w, qq.w, a);
-                }
-            }
-            // sum over the quad: swap pairs, then halves
-            a += dpp_f<0xb1, 0xf>(0.f, a);
-            a += dpp_f<0x4e, 0xf>(0.f, a);
-            part[hh] = a;
-        }
-        const int gg = g0 + k;
-        if (c < m && gg < p.g)
-            x[(((int64_t)b * p.n_q) * p.h_q + r * p.g + gg) * p.nc + c] = coef * part[k];
-    }
-}
+// Decode scores: each workgroup takes kScoreOneIter groups of 64 consecutive chunks of one
+// (sequence, group), a quad of lanes per summary (16-byte loads, 128 or 64 bytes per lane and
+// summary); the loads of all its groups are issued before any is used. The quad's partial dot
+// products meet by two DPP swaps. One group per workgroup is the fastest on the 16 x 128K step
+// (60.9 us; two groups 62.1, four 65.1): more workgroups in flight beat more loads per lane.
+constexpr int kScoreOneIter = 1;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void score_one_kernel(const T* __restrict__ q,
                                                         const float* __restrict__ kbar,
                                                         float* __restrict__ x, RouteParams p,
                                                         float coef) {
+    constexpr int NV = D / 16;  // float4 pieces per lane and summary
+    constexpr int IT = kScoreOneIter;
     __shared__ __align__(16) float qs[16 * D];
     const int b = blockIdx.y / p.h_kv, r = blockIdx.y % p.h_kv;
     const int m = route_cands(p, route_pos(p, b, 0));  // complete chunks before the window
-    score_one_chunks<T, D>(q, kbar, x, p, coef, b, r, blockIdx.x * 64, m, qs);
+    const int c_wg = blockIdx.x * 64 * IT;
+    if (c_wg >= m) return;  // no chunk of this workgroup is a candidate (uniform)
+    const int tid = threadIdx.x;
+    const int k = tid & 3;
+    float4 kv[IT][NV];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int c = c_wg + 64 * it + tid / 4;
+        const float4* src = reinterpret_cast<const float4*>(kbar + (((int64_t)b * p.tc + min(c, p.tc - 1)) * p.h_kv + r) * D);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) kv[it][i] = src[k + 4 * i];
+    }
+    for (int e = tid; e < p.g * D; e += blockDim.x) {
+        const int gg = e / D, d = e % D;
+        qs[gg * D + d] = to_f32(q[(((int64_t)b * p.n_q) * p.h_q + r * p.g + gg) * D + d]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int c = c_wg + 64 * it + tid / 4;
+        for (int g0 = 0; g0 < p.g; g0 += 4) {
+            float part[4];
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) {
+                const int gg = g0 + hh;
+                float a = 0.f;
+                if (gg < p.g) {
+                    const float4* qv = reinterpret_cast<const float4*>(&qs[gg * D]);
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) {
+                        const float4 qq = qv[k + 4 * i];
+                        a = fmaf(kv[it][i].x, qq.x, a);
+                        a = fmaf(kv[it][i].y, qq.y, a);
+                        a = fmaf(kv[it][i].z, qq.z, a);
+                        a = fmaf(kv[it][i].w, qq.w, a);
+                    }
+                }
+                // sum over the quad: swap pairs, then halves
+                a += dpp_f<0xb1, 0xf>(0.f, a);
+                a += dpp_f<0x4e, 0xf>(0.f, a);
+                part[hh] = a;
+            }
+            const int gg = g0 + k;
+            if (c < m && gg < p.g)
+                x[(((int64_t)b * p.n_q) * p.h_q + r * p.g + gg) * p.nc + c] = coef * part[k];
+        }
+    }
 }
 
 // ----------------------------------------------------------------------------- routing
@@ -362,7 +372,7 @@ static void launch_route(bool group, const float* x, uint32_t* mask, float* bias
 hipError_t launch_score_one(const void* q, int dt, const float* kbar, float* x,
                             const RouteParams& p, hipStream_t st) {
     const float coef = (p.alpha - 1.0f) * p.gamma / sqrtf((float)p.head_dim);
-    dim3 grid(div_up(p.tc, 64), p.batch * p.h_kv);
+    dim3 grid(div_up(p.tc, 64 * kScoreOneIter), p.batch * p.h_kv);
 #define DASH_SCORE1(T, DD)                                                                 \
     hipLaunchKernelGGL((score_one_kernel<T, DD>), grid, dim3(256), 0, st,                  \
                        static_cast<const T*>(q), kbar, x, p, coef)

@@ -37,10 +37,15 @@ namespace {
 
 constexpr int kRbThreads = 256;  // threads per workgroup (four waves)
 constexpr int kRbWaves = kRbThreads / 64;
-constexpr int kRbMaxChunks = 8192;
 constexpr int kColThreads = 512;  // threads per workgroup of the column kernel (eight waves)
 constexpr int kColWaves = kColThreads / 64;
 constexpr int kMaxPoolBlock = 128;  // longest chunk the column kernel pools over
+constexpr int kRbCache = 2048;      // floats of the row kernel's pass-2 cache
+
+// bytes of the row kernel's routed list for tc complete chunks (16-byte multiple)
+__host__ __device__ constexpr size_t rb_list_bytes(int tc) {
+    return ((size_t)(tc > 0 ? tc : 1) * 2 + 15) / 16 * 16;
+}
 
 // [t]_+^(e - 1) = p^(2 - alpha) on the support (t = x - tau > 0), 0 off it.
 template <int KIND>
@@ -144,7 +149,11 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_row_kernel(
     float* __restrict__ mean_ws, float* __restrict__ rho_ws, RouteParams p) {
     constexpr int LPK = D / 4;       // lanes per row of D elements
     constexpr int RPW = 64 / LPK;    // chunks per wave step
-    __shared__ uint16_t list[kRbMaxChunks];
+    // dynamic LDS: the routed list (2 bytes per complete chunk, rounded to 16 bytes), then the
+    // per-chunk cache of pass 2 (u of each head and dp, kRbCache floats)
+    extern __shared__ __align__(16) unsigned char rb_dyn[];
+    uint16_t* list = reinterpret_cast<uint16_t*>(rb_dyn);
+    float* cache = reinterpret_cast<float*>(rb_dyn + rb_list_bytes(p.tc));
     __shared__ int wtot[kRbWaves];
     __shared__ float red[kRbWaves];
     __shared__ float hred[kRbWaves][2 * GQ];
@@ -160,6 +169,9 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_row_kernel(
     const float inv_g = 1.0f / (float)GQ;
 
     const int nl = routed_list(mask + (row * p.h_kv + r) * p.nw, m, wtot, list);
+    // pass 2 leaves u and dp of every routed chunk in LDS when they fit, so that pass 3 does not
+    // score the chunks again (the values are the same bits either way)
+    const bool cached = nl * (GQ + 1) <= kRbCache;
 
     float qf[GQ][4], th[GQ];
 #pragma unroll
@@ -204,7 +216,9 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_row_kernel(
                 const float u = u_of<KIND>(x[h] - th[h], eu);
                 A[h] = fmaf(u, dp, A[h]);
                 B[h] += u;
+                if (cached) cache[j * (GQ + 1) + h] = u;
             }
+            if (cached) cache[j * (GQ + 1) + GQ] = dp;
         }
     }
     __syncthreads();
@@ -241,18 +255,28 @@ __global__ __launch_bounds__(kRbThreads) void route_bwd_row_kernel(
         const int c = list[valid ? j : 0];
         float kf[4];
         load4(kb + c * kstride, kf);
-        float x[GQ], w = 0.f;
+        float u[GQ], dp;
+        if (cached) {
+            const int jc = valid ? j : 0;
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-            x[h] = score4<LPK>(qf[h], kf, coef);
-            w += pow_e<KIND>(x[h] - th[h], e);
+            for (int h = 0; h < GQ; ++h) u[h] = cache[jc * (GQ + 1) + h];
+            dp = cache[jc * (GQ + 1) + GQ];
+        } else {
+            float x[GQ], w = 0.f;
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+                x[h] = score4<LPK>(qf[h], kf, coef);
+                w += pow_e<KIND>(x[h] - th[h], e);
+            }
+            w *= inv_g;
+            const float dlogw = (ddrow[c] - mean) * p.inv_sigma;
+            dp = w > 0.f ? dlogw / (w * (float)GQ) : 0.f;
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) u[h] = u_of<KIND>(x[h] - th[h], eu);
         }
-        w *= inv_g;
-        const float dlogw = (ddrow[c] - mean) * p.inv_sigma;
-        const float dp = w > 0.f ? dlogw / (w * (float)GQ) : 0.f;
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
-            const float dx = valid ? e * u_of<KIND>(x[h] - th[h], eu) * (dp - rho[h]) : 0.f;
+            const float dx = valid ? e * u[h] * (dp - rho[h]) : 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[h][i] = fmaf(dx, kf[i], acc[h][i]);
         }
@@ -526,7 +550,7 @@ static void launch_rb_k(const void* q, const float* kbar, const float* tau, cons
                         const PoolGrad& pg, int64_t fsb, int64_t fsc, const RouteParams& p,
                         hipStream_t st) {
     hipLaunchKernelGGL((route_bwd_row_kernel<T, D, GQ, KIND>), dim3(p.n_q, p.h_kv, p.batch),
-                       dim3(kRbThreads), 0, st, static_cast<const T*>(q), kbar, tau, mask, dbias,
+                       dim3(kRbThreads), rb_list_bytes(p.tc) + kRbCache * sizeof(float), st, static_cast<const T*>(q), kbar, tau, mask, dbias,
                        dq, mean_ws, rho_ws, p);
     if (p.tc > 0)
         hipLaunchKernelGGL((route_bwd_col_kernel<T, D, GQ, KIND>), dim3(p.tc * p.h_kv * p.batch),
