@@ -564,8 +564,31 @@ def backward_leg(dash, pre, wp: wl.Workload, args) -> dict:
     flops = 10.0 * d * pairs
     t_attn, t_route = timer.median_ms("bwd_attn"), timer.median_ms("bwd_route")
     tf = flops / (t_attn * 1e-3) / 1e12
+
+    # the routing and pooling gradients with learned summary queries, one per chunk (Alg. 1's
+    # form), on the selection the forward with those queries makes
+    tc = wp.n_kv // wp.block
+    g = torch.Generator(device=q.device).manual_seed(78)
+    qbar = torch.randn((tc, hkv, d), generator=g, device=q.device, dtype=torch.float32) * 0.15
+    fq = dash.forward(q, k, v, qbar=qbar, **kw)
+    dq_q, dk_q, _, dbias_q = dash.dash_sparse_attn_prefill_backward(
+        q, k, v, fq["lse"], dout, fq["mask"], fq["bias"], block=wp.block, workspace=ws2)
+    wsq = torch.empty(dash.dash_block_entmax_backward_query_workspace_bytes(1, wp.n_q, hq, hkv, d,
+                                                                           wp.block),
+                      dtype=torch.uint8, device=q.device)
+    dqbar = torch.empty_like(qbar)
+    tq = Timer()
+    for it in range(args.warmup + args.steps):
+        s, e = tq.span("q") if it >= args.warmup else (None, None)
+        s and s.record()
+        dash.dash_block_entmax_backward_query(q, k, fq["kbar"], qbar, fq["tau"], fq["mask"],
+                                              dbias_q, dq_q, dk_q, dqbar=dqbar, workspace=wsq,
+                                              **kw)
+        e and e.record()
+    torch.cuda.synchronize()
     return {
-        "ms": {"attn": round(t_attn, 3), "route": round(t_route, 3)},
+        "ms": {"attn": round(t_attn, 3), "route": round(t_route, 3),
+               "route_learned_query_per_chunk": round(tq.median_ms("q"), 3)},
         "algorithmic_tflop": round(flops / 1e12, 4),
         "tflops": round(flops / ((t_attn + t_route) * 1e-3) / 1e12, 3),
         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
