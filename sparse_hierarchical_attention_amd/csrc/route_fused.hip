@@ -90,48 +90,59 @@ __device__ __forceinline__ void route_write_token(float (&wsum)[NSS], int tok, i
     const int cp = pos / p.block;
     const int m = route_cands(p, pos);  // chunks m .. cp: the window, always attended with d = 0
     const float inv_g = 1.0f / (float)GQ;
-    // log w on R (0 elsewhere), kept for the bias when the row is short enough to hold it in
-    // registers, else computed again there
-    constexpr bool kKeepLog = NSS <= 16;
-    float lw[kKeepLog ? NSS : 1];
-    auto logw = [&](int sl) { return wsum[sl] > 0.f ? __logf(wsum[sl]) : 0.f; };
-    float lsum = 0.f, lcnt = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < NSS; ++sl) {
-        wsum[sl] *= inv_g;
-        const float l = logw(sl);
-        if (kKeepLog) lw[kKeepLog ? sl : 0] = l;
-        lsum += l;
-        lcnt += wsum[sl] > 0.f ? 1.f : 0.f;
-    }
-    lsum = row16_sum(lsum);
-    lcnt = row16_sum(lcnt);
-    const float mu = lcnt > 0.f ? lsum / lcnt : 0.f;
     // the groups that write: one per token
     const bool writer = tvalid && (GQ >= 4 ? grp == 0 : (GQ == 2 ? (grp & 1) == 0 : true));
     const int64_t qrow = (int64_t)b * p.n_q + tok;
     uint32_t* mrow = mask + (qrow * p.h_kv + r) * p.nw;
     float* brow = bias + (qrow * p.h_kv + r) * p.nc;
+#pragma unroll
+    for (int sl = 0; sl < NSS; ++sl) wsum[sl] *= inv_g;
     if (GQ >= 4) {
-        // every group holds the token's row: group k stores the bias of slots k, k + 4, ...
+        // every group holds the token's row: group k takes the log of slots k, k + 4, ... once, for
+        // mu and for its own bias stores; the four groups' sums meet across the wave's rows
+        constexpr int NQ = (NSS + 3) / 4;
+        float lq[NQ];
+        float lsum = 0.f, lcnt = 0.f;
 #pragma unroll
         for (int s0 = 0; s0 < NSS; s0 += 4) {
             float w = wsum[s0];
 #pragma unroll
             for (int j = 1; j < 4; ++j)
                 if (s0 + j < NSS && grp == j) w = wsum[s0 + j];
-            float l;
-            if (kKeepLog) {
-                l = lw[kKeepLog ? s0 : 0];
+            const bool in = s0 + grp < NSS && w > 0.f;
+            const float l = in ? __logf(w) : 0.f;
+            lq[s0 / 4] = l;
+            lsum += l;
+            lcnt += in ? 1.f : 0.f;
+        }
+        lsum = halves_sum(rowpair_sum(row16_sum(lsum)));
+        lcnt = halves_sum(rowpair_sum(row16_sum(lcnt)));
+        const float mu = lcnt > 0.f ? lsum / lcnt : 0.f;
 #pragma unroll
-                for (int j = 1; j < 4; ++j)
-                    if (s0 + j < NSS && grp == j) l = lw[kKeepLog ? s0 + j : 0];
-            } else {
-                l = w > 0.f ? __logf(w) : 0.f;
-            }
-            if (tvalid && s0 + grp < NSS && w > 0.f) brow[16 * (s0 + grp) + li] = (l - mu) * p.inv_sigma;
+        for (int s0 = 0; s0 < NSS; s0 += 4) {
+            float w = wsum[s0];
+#pragma unroll
+            for (int j = 1; j < 4; ++j)
+                if (s0 + j < NSS && grp == j) w = wsum[s0 + j];
+            if (tvalid && s0 + grp < NSS && w > 0.f) brow[16 * (s0 + grp) + li] = (lq[s0 / 4] - mu) * p.inv_sigma;
         }
     } else {
+        // log w on R (0 elsewhere), kept for the bias when the row is short enough to hold it in
+        // registers, else computed again there
+        constexpr bool kKeepLog = NSS <= 16;
+        float lw[kKeepLog ? NSS : 1];
+        auto logw = [&](int sl) { return wsum[sl] > 0.f ? __logf(wsum[sl]) : 0.f; };
+        float lsum = 0.f, lcnt = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < NSS; ++sl) {
+            const float l = logw(sl);
+            if (kKeepLog) lw[kKeepLog ? sl : 0] = l;
+            lsum += l;
+            lcnt += wsum[sl] > 0.f ? 1.f : 0.f;
+        }
+        lsum = row16_sum(lsum);
+        lcnt = row16_sum(lcnt);
+        const float mu = lcnt > 0.f ? lsum / lcnt : 0.f;
 #pragma unroll
         for (int sl = 0; sl < NSS; ++sl)
             if (writer && wsum[sl] > 0.f)
