@@ -188,3 +188,47 @@ def test_table5_decode_96k_random_selection(dash, orc):
                                block=w.block, q_pos0=w.n_kv - 1)
     out = parity.compare_output(parity.to_host(o).reshape(w.batch, w.h_q, -1), ref_o, "bf16")
     log(f"out {out}")
+
+
+# ------------------------------------------------------------------ the documented chunk limit
+
+def test_decode_at_the_chunk_limit(dash, orc):
+    """Decode with 8192 chunk slots, the most the ABI accepts: 2 sequences of 262144 tokens in
+    chunks of 32 (the full length, and a length that ends one token into the last chunk)."""
+    w = wl.Workload("decode 2 x 256K, chunk 32 (8192 chunks)", 2, 8192 * 32, 32, 8, 128, 32, 1.5,
+                    1.5, 1.0, decode=True, plant="decode", plant_args=dict(lo=1, hi=16), seed=72)
+    log(f"{w.name}: generating inputs")
+    inp = wl.make_inputs(w, DEV)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    kbar = dash.dash_pool_keys(k, w.block)
+    lens = [w.n_kv, 8191 * 32 + 1]
+    ctx = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, mask, bias = dash.dash_decode_step(q, k, v, kbar, block=w.block, alpha=w.alpha,
+                                          gamma=w.gamma, sigma=w.sigma, ctx_lens=ctx)
+    torch.cuda.synchronize()
+    for b, n_b in enumerate(lens):
+        log(f"oracle on sequence {b} ({n_b} tokens)")
+        qh, kh, vh = q[b:b + 1].cpu(), k[b:b + 1, :n_b].cpu(), v[b:b + 1, :n_b].cpu()
+        ref = orc.forward(qh, kh, vh, block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma,
+                          q_pos0=n_b - 1)
+        nc_b = -(-n_b // w.block)
+        m = parity.to_host(mask[b]).view(np.uint32)[..., :-(-nc_b // 32)].copy()
+        words = -(-nc_b // 32)
+        if nc_b % 32:
+            m[..., words - 1] &= np.uint32((1 << (nc_b % 32)) - 1)
+        parity.check_forward(orc, qh, kh, vh, ref, mask=m, bias=parity.to_host(bias[b])[..., :nc_b],
+                             tau=None, o=parity.to_host(o[b]), rows=np.array([0]), n_kv=n_b,
+                             block=w.block, h_kv=w.h_kv, q_pos=np.array([n_b - 1]),
+                             q_pos0=n_b - 1, alpha=w.alpha, sigma=w.sigma, dtype="bf16",
+                             vmax=float(v[b].abs().max()), max_flip_frac=1.0)
+
+
+def test_prefill_at_the_chunk_limit(dash, orc):
+    """bf16 prefill with 8192 chunk slots: 262144 tokens in chunks of 32, 32 query heads over 2 KV
+    heads (routed in slabs of query rows through the score workspace); sampled rows, the last ones
+    included, against the oracle."""
+    w = wl.Workload("prefill 256K, chunk 32 (8192 chunks), 32q/2kv heads, D 128", 1, 8192 * 32, 32, 2,
+                    128, 32, 1.5, 0.5, 1e8, plant="span", plant_args=dict(span=16, per_span=4),
+                    seed=73)
+    rows = np.union1d(sample_rows(w.n_q, w.block, 10, seed=74), [w.n_q - 33, w.n_q - 1])
+    prefill_parity(dash, orc, w, w.sigma, rows)
