@@ -415,3 +415,43 @@ def test_learned_query_full_backward(dash, orc, dtype):
     _compare_cond("dk", parity.to_host(g["dk"]), ref_dk, w.dtype, c)
     _compare_cond("dv", parity.to_host(g["dv"]), s2["dv"], w.dtype, c)
     _compare_cond("dqbar", parity.to_host(g["dqbar"]), r0["dqbar"], "f32", c)
+
+
+@pytest.mark.parametrize("alpha,gamma", [(2.0, 0.002), (1.5, 0.01)])
+def test_routing_backward_many_routed_chunks(dash, orc, alpha, gamma):
+    """The routing gradient of rows that route more chunks than the row kernel keeps in LDS between
+    its passes (it then scores them again): 16384 tokens in chunks of 32 with a routing scale so
+    small that every candidate chunk is in every head's support with nearly equal weight (about 500
+    routed chunks per late row, each well above the threshold, so the gradient is well
+    conditioned). Sampled late rows of dq (routing part) against the oracle on the GPU's own
+    selection, for a random dL/dd."""
+    from tests.test_gpu_parity import flat_rows, sample_rows
+    w = wl.Workload(f"routing backward, 16384 tokens, chunk 32, alpha {alpha}, gamma {gamma}", 1,
+                    16384, 8, 2, 128, 32, alpha, gamma, 1.0, seed=380)
+    print(f"case: {w.name}", flush=True)
+    inp = wl.make_inputs(w, DEV)
+    q, k = inp["q"], inp["k"]
+    kw = dict(block=w.block, alpha=w.alpha, gamma=w.gamma, sigma=w.sigma)
+    kbar = dash.dash_pool_keys(k, w.block)
+    mask, bias, tau = dash.dash_block_entmax(q, kbar, n_kv=w.n_kv, h_kv=w.h_kv, **kw)
+    nc = -(-w.n_kv // w.block)
+    dd = torch.randn((1, w.n_q, w.h_kv, nc), generator=torch.Generator(device=DEV).manual_seed(381),
+                     device=DEV, dtype=torch.float32)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=DEV)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
+    dash.dash_block_entmax_backward(q, kbar, tau, mask, dd, dq, dk, **kw)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.n_q, w.block, 24, seed=382)
+    rows = rows[rows % w.n_q >= 14000]
+    kbar_h = kbar.cpu().numpy().astype(np.float64)
+    st = orc.block_entmax(q.cpu(), kbar_h, n_kv=w.n_kv, h_kv=w.h_kv, rows=rows, **kw)
+    st["kbar"] = kbar_h
+    gm = flat_rows(mask, rows).view(np.uint32)
+    same = np.array([np.array_equal(gm[i], st["mask"][i]) for i in range(len(rows))])
+    routed = (st["w"] > 0.0).sum(axis=2).min(axis=1)  # routed chunks of the row (per group)
+    print(f"rows {len(rows)}, same selection {int(same.sum())}, routed chunks per row "
+          f"{int(routed.min())}..{int(routed.max())}", flush=True)
+    assert same.all() and routed.min() > 2048 // 5  # past the row kernel's LDS cache (g = 4)
+    ref = orc.block_entmax_backward(q.cpu(), kbar_h, flat_rows(dd, rows).astype(np.float64),
+                                    n_kv=w.n_kv, rows=rows, **kw)
+    _compare_cond("dq (routing) rows", flat_rows(dq, rows), ref["dq"], "f32", 0.0)
