@@ -166,6 +166,35 @@ def test_backward_rejects_bad_arguments(L):
                                                None) == 3
 
 
+def test_learned_query_backward_rejects_bad_arguments(L):
+    """dash_block_entmax_backward_query: strides must be non-negative multiples of 4, queries of
+    distinct (sequence, chunk) pairs may coincide but not partly overlap, qbar and dqbar are
+    16-byte aligned, and the workspace (which includes each chunk's dqbar) is 256-byte aligned."""
+    i64 = ctypes.c_int64
+    a = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails validation
+    B, n, hq, hkv, d, blk = 2, 640, 8, 2, 128, 64
+    tc = n // blk
+    need = L.dash_block_entmax_backward_query_workspace_bytes(B, n, hq, hkv, d, blk)
+    assert need == ((B * n * (hq + hkv) * 4 + 255) // 256) * 256 + B * tc * hkv * d * 4
+
+    def call(sb, sc, qbar=a, dqbar=a, ws=a, ws_bytes=need, dt=1):
+        return L.dash_block_entmax_backward_query(
+            a, a, dt, a, qbar, i64(sb), i64(sc), a, a, a, a, a, dqbar, B, n, hq, hkv, d, blk,
+            ctypes.c_float(1.5), ctypes.c_float(1.0), ctypes.c_float(1.0), 1, ws,
+            ctypes.c_size_t(ws_bytes), None)
+
+    assert call(-4, 0) == 1 and "strides" in err(L)
+    assert call(0, 6) == 1 and "strides" in err(L)
+    assert call(hkv * d, 4) == 1 and "overlap" in err(L)      # chunks 4 floats apart
+    assert call(4, tc * hkv * d) == 1 and "overlap" in err(L)  # sequences 4 floats apart
+    assert call(0, 0, qbar=ctypes.c_void_p((1 << 20) + 4)) == 1 and "aligned" in err(L)
+    assert call(0, 0, dqbar=ctypes.c_void_p((1 << 20) + 8)) == 1 and "aligned" in err(L)
+    assert call(0, 0, ws_bytes=need - 1) == 3
+    assert call(0, 0, ws=ctypes.c_void_p((1 << 20) + 16)) == 1 and "256-byte" in err(L)
+    assert call(0, 0, qbar=None) == 1 and "null" in err(L)
+    assert call(0, 0, dt=7) == 1
+
+
 def test_binding_rejects_non_fp32_side_inputs():
     """The binding checks the fp32 operands' dtype before anything reaches the library (a float64
     buffer passed as float * would be read as garbage)."""
