@@ -18,15 +18,20 @@
 //   pass 2: the same products, ds = p (dp - Delta), dL/dd per (token, chunk) summed over the
 //           chunk's keys and the token's heads, and dQ^T += K^T dS^T with K^T read through
 //           transposing LDS loads (ds_read_b64_tr_b16), dS^T straight from the accumulator.
-// attn_bwd_dkv_mfma_kernel, column-parallel, one workgroup per (sequence, KV group, chunk), one
-// wave per 32 keys holding its keys and values as B operands, the chunks of one (sequence, group)
-// on one XCD: the tokens that attend the chunk
-// (its own, causally, and later ones whose mask bit is set) are listed in order, their rows
-// (token x head) gathered into LDS 32 at a time, and per tile
+// attn_bwd_dkv16_mfma_kernel, column-parallel, one workgroup per (sequence, KV group, chunk), one
+// wave per 16 keys holding its keys and values as B operands of v_mfma_f32_16x16x32_bf16 (two
+// waves fit each SIMD), the chunks of one (sequence, group) on one XCD: the tokens that attend the
+// chunk (its own, causally, and later ones whose mask bit is set) are listed in order, their rows
+// (token x head) gathered into LDS 64 at a time, and per tile
 //   S = Q K^T, dP = dO V^T, p, ds = p (dp - Delta), dV^T += dO^T P, dK^T += Q^T dS,
 // with dO^T and Q^T read through transposing LDS loads and P, dS from the accumulators.
+// Probabilities are formed without branches: a pair that does not attend gets exp2(-inf) = 0
+// (branches per element, each waiting on its own LDS read, had cost the dK / dV kernel a fifth
+// of its time).
 // Each output element is written once, by one lane: deterministic, no atomics.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -38,6 +43,7 @@ namespace {
 typedef __bf16 bw_bf16x8 __attribute__((ext_vector_type(8)));
 typedef short bw_i16x4 __attribute__((ext_vector_type(4)));
 typedef float bw_f32x16 __attribute__((ext_vector_type(16)));
+typedef float bw_f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bw_i16x4 bw_lds_i16x4;
 
 constexpr int kBwRows = 128;     // rows (token x head) per workgroup of the dq kernel
@@ -61,6 +67,19 @@ __device__ __forceinline__ bw_bf16x8 tr_operand(const bf16_t* base, int ks, int 
     const bf16_t* ptr = base + (16 * ks + r) * LS + 32 * dt + d;
     const bw_i16x4 lo = bw_read_tr16(ptr);
     const bw_i16x4 hi = bw_read_tr16(ptr + 8 * LS);
+    return __builtin_bit_cast(bw_bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A operand (16 dims x 32 rows) of X^T += Y^T Z on v_mfma_f32_16x16x32_bf16 for Y stored
+// row-major in LDS (stride LS): lane l receives dimension 16 db + (l % 16) of the rows
+// 32 kb + 4 (l / 16) + {0..3} and + 16, the order in which the B operand built from two 16-row
+// score accumulators holds its rows.
+template <int LS>
+__device__ __forceinline__ bw_bf16x8 tr_operand16(const bf16_t* base, int kb, int db, int lane) {
+    const int grp = lane >> 4, kl = lane & 15;
+    const bf16_t* ptr = base + (32 * kb + 4 * grp + (kl >> 2)) * LS + 16 * db + 4 * (kl & 3);
+    const bw_i16x4 lo = bw_read_tr16(ptr);
+    const bw_i16x4 hi = bw_read_tr16(ptr + 16 * LS);
     return __builtin_bit_cast(bw_bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -207,7 +226,10 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = bw_f32x16{};
 
-    for (int pass = 0; pass < 2; ++pass) {
+    // the two passes as separate code (PASS is a compile-time constant in each), so that the dQ
+    // accumulators live in the second only
+    auto walk = [&](auto pass_c) __attribute__((always_inline)) {
+        constexpr int pass = decltype(pass_c)::value;
         int c = next_chunk(-1), sub = 0;  // every tile has at least its own chunk
         uint32_t mw;
         float dv;
@@ -246,14 +268,16 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
                         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
                     }
                     // p = exp(scale s + d - lse) on the row's selected, causal keys; 0 elsewhere
+                    // (only tiles that hold some row's own chunk compare keys with positions)
+                    if (causal) {
     #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) {
-                        float pe = __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, off));
-                        if (causal) {
+                        for (int rr = 0; rr < 16; ++rr) {
                             const int key = key0 + 32 * mt + 8 * (rr >> 2) + 4 * G + (rr & 3);
-                            pe = key > pos ? 0.f : pe;
+                            s[rr] = __builtin_amdgcn_exp2f(key > pos ? -INFINITY : fmaf(s[rr], qk_scale, off));
                         }
-                        s[rr] = pe;
+                    } else {
+    #pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) s[rr] = __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, off));
                     }
                     if (pass == 0) {
     #pragma unroll
@@ -299,7 +323,9 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
             dv = dv_nx;
         }
         if (pass == 0) Delta = dsum + __shfl_xor(dsum, 32, kWave);
-    }
+    };
+    walk(std::integral_constant<int, 0>{});
+    walk(std::integral_constant<int, 1>{});
 
     if (!valid) return;
     if (G == 0) delta[qrow * p.h_q + r * GQ + hl] = Delta;
@@ -315,20 +341,32 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
         }
 }
 
+// dK and dV with one wave per 16 keys on v_mfma_f32_16x16x32_bf16: a wave holds its keys and
+// values as B operands (D / 32 registers of 8 bf16 each) and dK^T, dV^T as D / 16 accumulators of
+// 16 dims x 16 keys, so that two waves fit each SIMD (one wave per 32 keys on the 32 x 32 product
+// needed twice the registers and ran alone on its SIMD). One workgroup per (sequence, KV group,
+// chunk), BLK / 16 waves; the attending rows are listed in order and gathered 64 (32 for chunks
+// of 32) at a time, and per 32-row k-step kb of a tile
+//   S = Q K^T and dP = dO V^T on the two 16-row blocks 2 kb, 2 kb + 1 (A = the rows from LDS),
+//   p and ds per element (lane l: key l % 16, rows 4 (l / 16) + {0..3} of each block),
+//   dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read through transposing LDS loads and P,
+//   dS from the accumulators (rows 4 (l / 16) + {0..3} of both blocks, the order the transposing
+//   loads give).
 template <int D, int BLK, int GQ>
-__global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
+__global__ __launch_bounds__(4 * BLK, 2) void attn_bwd_dkv16_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ lse, const bf16_t* __restrict__ dout,
     const uint32_t* __restrict__ mask, const float* __restrict__ bias,
     const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
     AttnParams p) {
-    constexpr int NTH = 2 * BLK;             // one wave per 32 keys
+    constexpr int NTH = 4 * BLK;             // one wave per 16 keys
     constexpr int NWV = NTH / 64;
-    constexpr int LS = D + 24;               // row stride of the gathered Q / dO rows (as in the dq kernel)
+    constexpr int LS = D + 24;               // row stride of the gathered Q / dO rows
     constexpr int RT = BLK >= 64 ? 64 : 32;  // rows (token x head) per tile
-    constexpr int RM = RT / 32;              // 32-row M-tiles per tile
+    constexpr int KB = RT / 32;              // 32-row k-steps per tile
     constexpr int TPT = RT / GQ;             // tokens per tile
-    constexpr int DT = D / 32;
+    constexpr int KS = D / 32;               // 32-dim k-steps of S and dP
+    constexpr int DB = D / 16;               // 16-dim blocks of dK^T and dV^T
     constexpr int PIECES = RT * (D / 8);     // 16-byte pieces per tensor and tile
     constexpr int NP = PIECES / NTH;         // of them per thread
     static_assert(PIECES % NTH == 0 && NTH >= RT, "tile does not split over the threads");
@@ -354,29 +392,29 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
     }
     const int b = gr / p.h_kv, r = gr % p.h_kv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int j = lane & 31, G = lane >> 5;
+    const int kl = lane & 15, grp = lane >> 4;
     const int n = p.n_kv;
-    const int key = c * BLK + 32 * wave + j;  // this lane's key (B operand column)
+    const int key = c * BLK + 16 * wave + kl;  // this lane's key (B operand column)
     const bool key_ok = key < n;
     const int64_t kv_row_stride = (int64_t)p.h_kv * D;
 
-    // the wave's keys and values as B operands: lane (j, G) holds dims 16 ks + 8 G .. + 7
-    bw_bf16x8 kf[D / 16], vf[D / 16];
+    // the wave's keys and values as B operands: lane (kl, grp) holds dims 32 ks + 8 grp .. + 7
+    bw_bf16x8 kf[KS], vf[KS];
     {
-        const int64_t off = ((int64_t)b * n + (key_ok ? key : 0)) * kv_row_stride + (int64_t)r * D + 8 * G;
+        const int64_t off = ((int64_t)b * n + (key_ok ? key : 0)) * kv_row_stride + (int64_t)r * D + 8 * grp;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const uint4 uk = key_ok ? *reinterpret_cast<const uint4*>(k + off + 16 * s) : make_uint4(0, 0, 0, 0);
-            const uint4 uv = key_ok ? *reinterpret_cast<const uint4*>(v + off + 16 * s) : make_uint4(0, 0, 0, 0);
+        for (int s = 0; s < KS; ++s) {
+            const uint4 uk = key_ok ? *reinterpret_cast<const uint4*>(k + off + 32 * s) : make_uint4(0, 0, 0, 0);
+            const uint4 uv = key_ok ? *reinterpret_cast<const uint4*>(v + off + 32 * s) : make_uint4(0, 0, 0, 0);
             kf[s] = __builtin_bit_cast(bw_bf16x8, uk);
             vf[s] = __builtin_bit_cast(bw_bf16x8, uv);
         }
     }
-    bw_f32x16 acck[DT], accv[DT];
+    bw_f32x4 acck[DB], accv[DB];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        acck[dt] = bw_f32x16{};
-        accv[dt] = bw_f32x16{};
+    for (int db = 0; db < DB; ++db) {
+        acck[db] = bw_f32x4{};
+        accv[db] = bw_f32x4{};
     }
     const float qk_scale = p.scale * kBwLog2e;
 
@@ -386,7 +424,6 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
     const int nblk = div_up(n - c * BLK, NTH);
     for (int bi = nblk - 1; bi >= 0; --bi) {
         const int t0 = c * BLK + bi * NTH;
-        // ordered list of this block's tokens that attend chunk c
         const int t = t0 + tid;
         bool att = false;
         if (t < n) {
@@ -405,12 +442,12 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
         __syncthreads();
 
         // the rows of a tile (row m = token tl0 + m / g, head m % g) go global -> registers ->
-        // LDS; the next tile's loads are issued before the current tile's products
+        // LDS, the next tile's loads issued before the current tile's products; rows past the
+        // list read its first token and are zeroed after (no branches, so every load is issued
+        // back to back), and their record carries token -1, which no key pairs with
         uint4 gq[NP], gd[NP];
         float g_base = 0.f, g_dl = 0.f, g_tok = -1.f, g_ok = 0.f;
         auto gather = [&](int tl0) {
-            // rows past the list read its first token (tl0 < total) and are zeroed after: no
-            // branches, so every load is issued back to back
             int tok[NP];
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
@@ -455,9 +492,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
                 *reinterpret_cast<uint4*>(&Qs[m * LS + 8 * d8]) = gq[i];
                 *reinterpret_cast<uint4*>(&Ds[m * LS + 8 * d8]) = gd[i];
             }
-            if (tid < RT) {
-                meta[tid] = make_float4(g_base, g_dl, g_tok, g_ok);
-            }
+            if (tid < RT) meta[tid] = make_float4(g_base, g_dl, g_tok, g_ok);
         };
         if (total > 0) gather(0);
         for (int tl0 = 0; tl0 < total; tl0 += TPT) {
@@ -465,71 +500,68 @@ __global__ __launch_bounds__(2 * BLK) void attn_bwd_dkv_mfma_kernel(
             __syncthreads();
             if (tl0 + TPT < total) gather(tl0 + TPT);
 
-            // per 32-row M-tile: S = Q K^T and dP = dO V^T (lane (j, G) holds key j and rows
-            // 32 rm + 8 (rr / 4) + 4 G + rr % 4), p and ds, then the two 16-row k-steps of
-            // dV^T += dO^T P and dK^T += Q^T dS that these rows feed
 #pragma unroll
-            for (int rm = 0; rm < RM; ++rm) {
-                // every LDS operand of this M-tile is read before the products that use it, so
-                // that the reads overlap one another instead of each waiting in turn
-                bw_bf16x8 aq[D / 16], ad[D / 16];
+            for (int kb = 0; kb < KB; ++kb) {
+                bw_f32x4 s[2], dp[2];
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    aq[ks] = *reinterpret_cast<const bw_bf16x8*>(&Qs[(32 * rm + j) * LS + 16 * ks + 8 * G]);
-                    ad[ks] = *reinterpret_cast<const bw_bf16x8*>(&Ds[(32 * rm + j) * LS + 16 * ks + 8 * G]);
-                }
-                float4 mrow[16];
+                for (int h = 0; h < 2; ++h) {
+                    const int rb = 2 * kb + h;
+                    bw_bf16x8 aq[KS], ad[KS];
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) mrow[rr] = meta[32 * rm + 8 * (rr >> 2) + 4 * G + (rr & 3)];
-                bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], kf[ks], s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[ks], vf[ks], dp, 0, 0, 0);
-                }
-                bw_bf16x8 trd[2][DT], trq[2][DT];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        trd[kb][dt] = tr_operand<LS>(Ds, 2 * rm + kb, dt, lane);
-                        trq[kb][dt] = tr_operand<LS>(Qs, 2 * rm + kb, dt, lane);
+                    for (int ks = 0; ks < KS; ++ks) {
+                        aq[ks] = *reinterpret_cast<const bw_bf16x8*>(&Qs[(16 * rb + kl) * LS + 32 * ks + 8 * grp]);
+                        ad[ks] = *reinterpret_cast<const bw_bf16x8*>(&Ds[(16 * rb + kl) * LS + 32 * ks + 8 * grp]);
                     }
-                bw_bf16x8 pf[2], dsf[2];
+                    s[h] = bw_f32x4{};
+                    dp[h] = bw_f32x4{};
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const float4 mr = mrow[rr];  // (base, Delta, token, valid)
-                    const bool ok = mr.w != 0.f && key_ok && (float)key <= mr.z;
-                    const float pe = ok ? __builtin_amdgcn_exp2f(fmaf(s[rr], qk_scale, -mr.x)) : 0.f;
-                    const float ds = pe * (dp[rr] - mr.y);
-                    pf[rr >> 3][rr & 7] = (__bf16)pe;
-                    dsf[rr >> 3][rr & 7] = (__bf16)ds;
-                }
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        accv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trd[kb][dt], pf[kb], accv[dt], 0, 0, 0);
-                        acck[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trq[kb][dt], dsf[kb], acck[dt], 0, 0, 0);
+                    for (int ks = 0; ks < KS; ++ks) {
+                        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ks], kf[ks], s[h], 0, 0, 0);
+                        dp[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[ks], vf[ks], dp[h], 0, 0, 0);
                     }
+                }
+                // the eight rows' (base, Delta, token, valid) records read together, and p formed
+                // without a branch (exp2(-inf) = 0 on rows and keys that do not pair)
+                float4 mr[8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mr[4 * h + e] = meta[32 * kb + 16 * h + 4 * grp + e];
+                bw_bf16x8 pf, dsf;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // rows past the list carry token -1, and every listed token is below n,
+                        // so the one comparison also masks keys past the sequence
+                        const float4 m4 = mr[4 * h + e];
+                        const float x = fmaf(s[h][e], qk_scale, -m4.x);
+                        const float pe = __builtin_amdgcn_exp2f((float)key <= m4.z ? x : -INFINITY);
+                        const float ds = pe * (dp[h][e] - m4.y);
+                        pf[4 * h + e] = (__bf16)pe;
+                        dsf[4 * h + e] = (__bf16)ds;
+                    }
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const bw_bf16x8 trd = tr_operand16<LS>(Ds, kb, db, lane);
+                    const bw_bf16x8 trq = tr_operand16<LS>(Qs, kb, db, lane);
+                    accv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(trd, pf, accv[db], 0, 0, 0);
+                    acck[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(trq, dsf, acck[db], 0, 0, 0);
+                }
             }
             __syncthreads();  // Qs, Ds and meta are refilled by the next tile
         }
     }
     if (!key_ok) return;
+    // lane (kl, grp) holds dims 16 db + 4 grp + {0..3} of key kl
     const int64_t obase = (((int64_t)b * n + key) * p.h_kv + r) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const int d0 = 32 * dt + 8 * qd + 4 * G;
-            *reinterpret_cast<float4*>(dk + obase + d0) =
-                make_float4(acck[dt][4 * qd] * p.scale, acck[dt][4 * qd + 1] * p.scale,
-                            acck[dt][4 * qd + 2] * p.scale, acck[dt][4 * qd + 3] * p.scale);
-            *reinterpret_cast<float4*>(dv + obase + d0) =
-                make_float4(accv[dt][4 * qd], accv[dt][4 * qd + 1], accv[dt][4 * qd + 2],
-                            accv[dt][4 * qd + 3]);
-        }
+    for (int db = 0; db < DB; ++db) {
+        const int d0 = 16 * db + 4 * grp;
+        *reinterpret_cast<float4*>(dk + obase + d0) =
+            make_float4(acck[db][0] * p.scale, acck[db][1] * p.scale, acck[db][2] * p.scale, acck[db][3] * p.scale);
+        *reinterpret_cast<float4*>(dv + obase + d0) = make_float4(accv[db][0], accv[db][1], accv[db][2], accv[db][3]);
+    }
 }
 
 template <int D, int BLK, int GQ>
@@ -543,8 +575,8 @@ static void launch_bwd_mfma_g(const void* q, const void* k, const void* v, const
                        dim3(kBwThreads), 0, st, static_cast<const bf16_t*>(q),
                        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse,
                        static_cast<const bf16_t*>(dout), mask, bias, dq, dbias, delta, p, n_tiles);
-    hipLaunchKernelGGL((attn_bwd_dkv_mfma_kernel<D, BLK, GQ>), dim3(p.nc * p.h_kv * p.batch),
-                       dim3(2 * BLK), 0, st, static_cast<const bf16_t*>(q),
+    hipLaunchKernelGGL((attn_bwd_dkv16_mfma_kernel<D, BLK, GQ>), dim3(p.nc * p.h_kv * p.batch),
+                       dim3(4 * BLK), 0, st, static_cast<const bf16_t*>(q),
                        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), lse,
                        static_cast<const bf16_t*>(dout), mask, bias, delta, dk, dv, p);
 }
