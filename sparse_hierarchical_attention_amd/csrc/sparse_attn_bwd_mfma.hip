@@ -18,6 +18,8 @@
 //   pass 2: the same products, ds = p (dp - Delta), dL/dd per (token, chunk) summed over the
 //           chunk's keys and the token's heads, and dQ^T += K^T dS^T with K^T read through
 //           transposing LDS loads (ds_read_b64_tr_b16), dS^T straight from the accumulator.
+// Two workgroups share a CU (two waves per SIMD, 256 registers each): K and V fragments are read a
+// few k-steps ahead of their products rather than all at once, and K^T right at its product.
 // attn_bwd_dkv16_mfma_kernel, column-parallel, one workgroup per (sequence, KV group, chunk), one
 // wave per 16 keys holding its keys and values as B operands of v_mfma_f32_16x16x32_bf16 (two
 // waves fit each SIMD), the chunks of one (sequence, group) on one XCD: the tokens that attend the
@@ -86,7 +88,7 @@ __device__ __forceinline__ bw_bf16x8 tr_operand16(const bf16_t* base, int kb, in
 }  // namespace
 
 template <int D, int BLK, int GQ>
-__global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma_kernel(
+__global__ __launch_bounds__(kBwThreads, 2) void attn_bwd_dq_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ lse, const bf16_t* __restrict__ dout,
     const uint32_t* __restrict__ mask, const float* __restrict__ bias, float* __restrict__ dq,
@@ -254,18 +256,22 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
                 // two 16-key k-steps of dQ^T += K^T dS^T that this M-tile feeds)
     #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    // the M-tile's K and V rows are read before the products (the reads overlap)
-                    bw_bf16x8 ka[D / 16], va[D / 16];
-    #pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks) {
-                        ka[ks] = *reinterpret_cast<const bw_bf16x8*>(&Ks[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
-                        va[ks] = *reinterpret_cast<const bw_bf16x8*>(&Vs[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
-                    }
+                    // the M-tile's K and V rows, each k-step's read two steps ahead of its products
+                    // (two waves share each SIMD, so the other wave covers what latency remains)
+                    constexpr int KSN = D / 16;
+                    bw_bf16x8 ka[3], va[3];
+                    auto kvread = [&](int ks) __attribute__((always_inline)) {
+                        ka[ks % 3] = *reinterpret_cast<const bw_bf16x8*>(&Ks[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
+                        va[ks % 3] = *reinterpret_cast<const bw_bf16x8*>(&Vs[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
+                    };
+                    kvread(0);
+                    kvread(1);
                     bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
     #pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks) {
-                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
-                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
+                    for (int ks = 0; ks < KSN; ++ks) {
+                        if (ks + 2 < KSN) kvread(ks + 2);
+                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % 3], qf[ks], s, 0, 0, 0);
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks % 3], df[ks], dp, 0, 0, 0);
                     }
                     // p = exp(scale s + d - lse) on the row's selected, causal keys; 0 elsewhere
                     // (only tiles that hold some row's own chunk compare keys with positions)
@@ -283,11 +289,6 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
     #pragma unroll
                         for (int rr = 0; rr < 16; ++rr) dsum = fmaf(s[rr], dp[rr], dsum);
                     } else {
-                        bw_bf16x8 ktr[2][DT];
-    #pragma unroll
-                        for (int h2 = 0; h2 < 2; ++h2)
-    #pragma unroll
-                            for (int dt = 0; dt < DT; ++dt) ktr[h2][dt] = tr_operand<LS>(Ks[buf], 2 * mt + h2, dt, lane);
                         bw_bf16x8 dsf[2];
     #pragma unroll
                         for (int rr = 0; rr < 16; ++rr) {
@@ -300,7 +301,8 @@ __global__ __launch_bounds__(kBwThreads, D == 128 ? 1 : 2) void attn_bwd_dq_mfma
                         for (int h2 = 0; h2 < 2; ++h2)
     #pragma unroll
                             for (int dt = 0; dt < DT; ++dt)
-                                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr[h2][dt], dsf[h2], acc[dt], 0, 0, 0);
+                                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    tr_operand<LS>(Ks[buf], 2 * mt + h2, dt, lane), dsf[h2], acc[dt], 0, 0, 0);
                     }
                 }
             }
