@@ -27,6 +27,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kLongRows = 16;   // query rows per workgroup of route_long_kernel
 constexpr int kLongMax = 2048;  // chunks route_long_kernel holds per row
+constexpr int kLongCand = 256;  // packed candidates of a long row's threshold solve
 
 // The fp32 summaries as three bf16 terms, hi = bf16(kbar), mid = bf16(kbar - hi),
 // lo = bf16(kbar - hi - mid), each rounded to nearest even (together about 24 mantissa bits),
@@ -561,7 +562,49 @@ __global__ __launch_bounds__(1024) void route_long_kernel(
                 const int c = 64 * i + lane;
                 xv[i] = c < m ? xr[c] : -INFINITY;
             }
-            const float tau = solve_tau_exact<NS, KIND, 64>(xv, ns, m, p.alpha);
+            // Long rows: the threshold restricted to the lanes' maxima (a subset of the row) is a
+            // lower bound on the row's threshold, since dropping entries only lowers the sum of
+            // Eq. 2. Entries at or below it (less a margin) are outside the support, and when at
+            // most kLongCand remain they are packed into the wave's own LDS row (its scores are
+            // in xv) and the threshold is solved on that list, which has the same root. Otherwise
+            // the whole row is solved.
+            float tau;
+            bool packed = false;
+            if (NS >= 16 && m > kLongCand) {
+                float lm = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < NS; ++i) lm = fmaxf(lm, xv[i]);
+                const float lmv[1] = {lm};
+                const float tl = solve_tau_exact<1, KIND, 64>(lmv, 1, min(m, 64), p.alpha);
+                const float lo = tl - 1e-3f * fmaxf(1.0f, fabsf(tl));
+                int cnt = 0;
+#pragma unroll
+                for (int i = 0; i < NS; ++i) cnt += __popcll(__ballot(xv[i] > lo));
+                if (cnt <= kLongCand) {
+                    const uint64_t below = (1ull << lane) - 1ull;
+                    int before = 0;
+#pragma unroll
+                    for (int i = 0; i < NS; ++i) {
+                        const bool in = xv[i] > lo;
+                        const uint64_t bal = __ballot(in);
+                        if (in) xr[before + __popcll(bal & below)] = xv[i];
+                        before += __popcll(bal);
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    float cv[kLongCand / 64];
+#pragma unroll
+                    for (int i = 0; i < kLongCand / 64; ++i)
+                        cv[i] = 64 * i + lane < cnt ? xr[64 * i + lane] : -INFINITY;
+                    tau = solve_tau_exact<kLongCand / 64, KIND, 64>(cv, (cnt + 63) / 64, cnt, p.alpha);
+                    packed = true;
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                }
+            }
+            if (!packed) tau = solve_tau_exact<NS, KIND, 64>(xv, ns, m, p.alpha);
             if (tau_out && tvalid && lane == 0)
                 tau_out[((int64_t)b * p.n_q + tok) * p.h_q + r * GQ + row % GQ] = tau;
 #pragma unroll
