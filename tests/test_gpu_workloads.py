@@ -89,6 +89,18 @@ def test_prefill_rows_past_1024_chunks(dash, orc, n, hq, hkv, block):
     prefill_parity(dash, orc, w, w.sigma, sample_rows(w.n_q, w.block, 40, seed=68))
 
 
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
+def test_prefill_long_rows_packed_candidates(dash, orc, alpha):
+    """Rows of 1025 to 2048 chunks whose support is small (2 planted of every 16 chunks): the
+    long-row route solves the threshold on the entries above the bound from the lanes' maxima
+    (at most 256 of them) instead of the whole row; sampled rows against the oracle for the three
+    kinds of exponent."""
+    w = wl.Workload(f"prefill 40000 tokens, chunk 32, 2 planted of every 16 chunks, alpha {alpha}",
+                    1, 40000, 32, 8, 128, 32, alpha, 0.5, 1.0, plant="span",
+                    plant_args=dict(span=16, per_span=2), seed=71)
+    prefill_parity(dash, orc, w, w.sigma, sample_rows(w.n_q, w.block, 40, seed=72))
+
+
 def test_prefill_bf16_rows_past_2048_chunks(dash, orc):
     """bf16 prefill whose rows reach 2049 to 8192 chunks: 160K tokens in chunks of 64 (2560
     complete chunks) leave the fused Stage 1 for the score workspace, routed in slabs of query
