@@ -562,34 +562,34 @@ __global__ __launch_bounds__(1024) void route_long_kernel(
                 const int c = 64 * i + lane;
                 xv[i] = c < m ? xr[c] : -INFINITY;
             }
-            // Long rows: the threshold restricted to the lanes' maxima (a subset of the row) is a
-            // lower bound on the row's threshold, since dropping entries only lowers the sum of
-            // Eq. 2. Entries at or below it (less a margin) are outside the support, and when at
-            // most kLongCand remain they are packed into the wave's own LDS row (its scores are
-            // in xv) and the threshold is solved on that list, which has the same root. Otherwise
-            // the whole row is solved.
+            // Long rows: the threshold restricted to a subset of the row is a lower bound on the
+            // row's threshold, since dropping entries only lowers the sum of Eq. 2. The subset is
+            // the 16 maxima of lanes l, l + 16, l + 32, l + 48 (solved within each 16-lane row,
+            // all four rows alike). Entries at or below that bound (less a margin) are outside the
+            // support; one pass packs those above it into the wave's own LDS row (its scores are
+            // in xv) and counts them, and when at most kLongCand remain the threshold is solved on
+            // that list, which has the same root. Otherwise the whole row is solved.
             float tau;
             bool packed = false;
             if (NS >= 16 && m > kLongCand) {
                 float lm = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < NS; ++i) lm = fmaxf(lm, xv[i]);
+                lm = halves_max(rowpair_max(lm));  // lanes l, l ^ 16, l ^ 32, l ^ 48
                 const float lmv[1] = {lm};
-                const float tl = solve_tau_exact<1, KIND, 64>(lmv, 1, min(m, 64), p.alpha);
+                const float tl = solve_tau_exact<1, KIND, 16>(lmv, 1, 16, p.alpha);
                 const float lo = tl - 1e-3f * fmaxf(1.0f, fabsf(tl));
+                const uint64_t below = (1ull << lane) - 1ull;
                 int cnt = 0;
 #pragma unroll
-                for (int i = 0; i < NS; ++i) cnt += __popcll(__ballot(xv[i] > lo));
+                for (int i = 0; i < NS; ++i) {
+                    const bool in = xv[i] > lo;
+                    const uint64_t bal = __ballot(in);
+                    const int at = cnt + __popcll(bal & below);
+                    if (in && at < kLongCand) xr[at] = xv[i];
+                    cnt += __popcll(bal);
+                }
                 if (cnt <= kLongCand) {
-                    const uint64_t below = (1ull << lane) - 1ull;
-                    int before = 0;
-#pragma unroll
-                    for (int i = 0; i < NS; ++i) {
-                        const bool in = xv[i] > lo;
-                        const uint64_t bal = __ballot(in);
-                        if (in) xr[before + __popcll(bal & below)] = xv[i];
-                        before += __popcll(bal);
-                    }
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -599,10 +599,10 @@ __global__ __launch_bounds__(1024) void route_long_kernel(
                         cv[i] = 64 * i + lane < cnt ? xr[64 * i + lane] : -INFINITY;
                     tau = solve_tau_exact<kLongCand / 64, KIND, 64>(cv, (cnt + 63) / 64, cnt, p.alpha);
                     packed = true;
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
             if (!packed) tau = solve_tau_exact<NS, KIND, 64>(xv, ns, m, p.alpha);
             if (tau_out && tvalid && lane == 0)
