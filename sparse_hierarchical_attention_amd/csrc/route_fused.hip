@@ -24,6 +24,7 @@ namespace dash {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kLongRows = 16;   // query rows per workgroup of route_long_kernel
 constexpr int kLongMax = 2048;  // chunks route_long_kernel holds per row
@@ -449,8 +450,8 @@ static void launch_fused_g(const void* q, const bf16_t* kbar, uint32_t* mask, fl
 // Rows of 1025 to 2048 chunks. 32 score rows of that length do not fit the LDS, so a workgroup
 // of 16 waves owns 16 query rows (16 / g tokens times the g heads) of one (sequence b, KV group r)
 // and their score rows take 132 KiB:
-//   phase 1: X^T = Kbar Q^T on v_mfma_f32_32x32x16_bf16 as in route_fused_kernel, the 16 rows
-//            filling half of the N-tile (the other half multiplies zeros); wave w takes the
+//   phase 1: X^T = Kbar Q^T from the same three bf16 terms as route_fused_kernel, on
+//            v_mfma_f32_16x16x32_bf16 (16 chunks x 16 rows per product); wave w takes the
 //            chunk tiles w, w + 16, ..., two at a time, and writes their scores to LDS;
 //   phase 2: wave w solves row w's threshold with the row over the whole wave (entry c in lane
 //            c % 64, slot c / 64) and leaves the row's probabilities in its LDS row;
@@ -482,7 +483,6 @@ __global__ __launch_bounds__(1024) void route_long_kernel(
     const int ct_n = div_up(p.tc, 32);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int j = lane & 31, G = lane >> 5;
 
     // ---- phase 1
     for (int idx = tid; idx < kLongRows * (D / 8); idx += NW * 64) {
@@ -495,52 +495,64 @@ __global__ __launch_bounds__(1024) void route_long_kernel(
         *reinterpret_cast<uint4*>(&qs[row * QS + 8 * d8]) = u;
     }
     __syncthreads();
+    // 16 x 16 x 32 products: A = 16 chunks x 32 dims of a summary term (lane l: chunk l % 16,
+    // dims 8 (l / 16) .. + 7, one 16-byte piece of the fragment-ordered terms), B = the 16 rows'
+    // Q (lane l: row l % 16, the same dims), C = 16 chunks x 16 rows. Wave w takes the chunk tiles
+    // w, w + 16, ..., two at a time, each as two halves of 16 chunks.
+    const int ci = lane & 15, jg = lane >> 4;
+    bf16x8_t qb[D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        qb[kk] = *reinterpret_cast<const bf16x8_t*>(&qs[ci * QS + 32 * kk + 8 * jg]);
     for (int c0 = wave; c0 < n_ct; c0 += 2 * NW) {
         const bool two = c0 + NW < n_ct;
-        f32x16_t X[2] = {f32x16_t{}, f32x16_t{}};
-        const uint4* src[2];
+        f32x4_t X[2][2] = {{f32x4_t{}, f32x4_t{}}, {f32x4_t{}, f32x4_t{}}};
+        const uint4* base[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            src[i] = reinterpret_cast<const uint4*>(planes) +
-                     ((int64_t)(b * p.h_kv + r) * ct_n + min(c0 + NW * i, ct_n - 1)) * (D / 16) * 3 * 64 + lane;
-        uint4 cur[2][3], nxt[2][3];
+            base[i] = reinterpret_cast<const uint4*>(planes) +
+                      ((int64_t)(b * p.h_kv + r) * ct_n + min(c0 + NW * i, ct_n - 1)) * (D / 16) * 3 * 64;
+        // step s: k-step kk = s / 3 of 32 dims, term lo, mid, hi (the small terms first); the
+        // 16-dim slice ks = 2 kk + jg / 2 of the fragment order holds dims 8 (jg % 2) .. + 7 in
+        // lanes 32 .. 63 of its 64
+        constexpr int NSTEP = 3 * (D / 32);
+        auto load = [&](int st, uint4 (&dst)[2][2]) __attribute__((always_inline)) {
+            const int kk = st / 3, pl = 2 - st % 3;
+            const int ks = 2 * kk + (jg >> 1);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int pl = 0; pl < 3; ++pl) cur[i][pl] = src[i][pl * 64];
+                for (int h = 0; h < 2; ++h)
+                    dst[i][h] = base[i][(ks * 3 + pl) * 64 + 16 * h + ci + 32 * (jg & 1)];
+        };
+        uint4 cur[2][2], nxt[2][2];
+        load(0, cur);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            if (ks + 1 < D / 16) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int pl = 0; pl < 3; ++pl) nxt[i][pl] = src[i][((ks + 1) * 3 + pl) * 64];
-            }
-            bf16x8_t qf = bf16x8_t{};
-            if (j < kLongRows) qf = *reinterpret_cast<const bf16x8_t*>(&qs[j * QS + 16 * ks + 8 * G]);
+        for (int st = 0; st < NSTEP; ++st) {
+            if (st + 1 < NSTEP) load(st + 1, nxt);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 if (i == 1 && !two) break;
 #pragma unroll
-                for (int pl = 2; pl >= 0; --pl)  // lo, mid, hi: the small terms first
-                    X[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, cur[i][pl]), qf, X[i], 0, 0, 0);
+                for (int h = 0; h < 2; ++h)
+                    X[i][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, cur[i][h]), qb[st / 3], X[i][h], 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int pl = 0; pl < 3; ++pl) cur[i][pl] = nxt[i][pl];
+                for (int h = 0; h < 2; ++h) cur[i][h] = nxt[i][h];
         }
-        // lane (j, G) holds row j, chunks 32 ct + 8 (rr / 4) + 4 G + rr % 4
-        if (j < kLongRows) {
+        // lane l holds row l % 16, chunks 32 ct + 16 h + 4 (l / 16) + {0..3}
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                if (i == 1 && !two) break;
-                const int ct = c0 + NW * i;
+        for (int i = 0; i < 2; ++i) {
+            if (i == 1 && !two) break;
+            const int ct = c0 + NW * i;
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr)
-                    xs[j * XS + 32 * ct + 8 * (rr >> 2) + 4 * G + (rr & 3)] = coef * X[i][rr];
-            }
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2)
+                    xs[ci * XS + 32 * ct + 16 * h + 4 * jg + e2] = coef * X[i][h][e2];
         }
     }
     __syncthreads();
