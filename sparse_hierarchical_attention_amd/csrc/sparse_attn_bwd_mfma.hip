@@ -258,22 +258,22 @@ __global__ __launch_bounds__(kBwThreads, 2) void attn_bwd_dq_mfma_kernel(
                 // Stage 2 backward at 32K)
     #pragma unroll 1
                 for (int mt = 0; mt < MT; ++mt) {
-                    // the M-tile's K and V rows, each k-step's read two steps ahead of its products
-                    // (two waves share each SIMD, so the other wave covers what latency remains)
+                    // the M-tile's K and V rows, each k-step's read one step ahead of its products
+                    // (two waves share each SIMD, so the other wave covers what latency remains;
+                    // a ring of two holds fewer registers than three, 17.2 against 17.4 ms)
                     constexpr int KSN = D / 16;
-                    bw_bf16x8 ka[3], va[3];
+                    bw_bf16x8 ka[2], va[2];
                     auto kvread = [&](int ks) __attribute__((always_inline)) {
-                        ka[ks % 3] = *reinterpret_cast<const bw_bf16x8*>(&Ks[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
-                        va[ks % 3] = *reinterpret_cast<const bw_bf16x8*>(&Vs[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
+                        ka[ks % 2] = *reinterpret_cast<const bw_bf16x8*>(&Ks[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
+                        va[ks % 2] = *reinterpret_cast<const bw_bf16x8*>(&Vs[buf][(32 * mt + j) * LS + 16 * ks + 8 * G]);
                     };
                     kvread(0);
-                    kvread(1);
                     bw_f32x16 s = bw_f32x16{}, dp = bw_f32x16{};
     #pragma unroll
                     for (int ks = 0; ks < KSN; ++ks) {
-                        if (ks + 2 < KSN) kvread(ks + 2);
-                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % 3], qf[ks], s, 0, 0, 0);
-                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks % 3], df[ks], dp, 0, 0, 0);
+                        if (ks + 1 < KSN) kvread(ks + 1);
+                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % 2], qf[ks], s, 0, 0, 0);
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks % 2], df[ks], dp, 0, 0, 0);
                     }
                     // p = exp(scale s + d - lse) on the row's selected, causal keys; 0 elsewhere
                     // (only tiles that hold some row's own chunk compare keys with positions)
